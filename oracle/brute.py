@@ -1,0 +1,94 @@
+"""Brute-force twin of the oracle, in pure Python loops, for tiny inputs only.
+
+TEST INFRASTRUCTURE ONLY (same import rule as ``oracle/kivi.py``).
+
+It computes the same quantizer as ``oracle.kivi`` through a different arithmetic route:
+Python floats (IEEE binary64) with an explicit rounding to binary32 or binary16 after every
+operation, done with ``struct``. Rounding a binary64 result of one +, -, * or / on binary32
+operands back to binary32 gives the correctly rounded binary32 result (binary64 carries more
+than 2*24+2 significant bits), so this route reproduces IEEE single precision without numpy.
+Attention is written as explicit sums with ``math.exp``.
+
+Sources are the same passages as ``oracle.kivi``: "Changelog" v0.8.0 (KIVI: per-channel
+keys, per-token values, residual window), v0.42.0 (codes plus per-group (scale, zero),
+softmax attention over the reconstruction), v0.30.0 (lo/scale, fp16 metadata).
+"""
+from __future__ import annotations
+
+import math
+import struct
+
+
+def r32(x: float) -> float:
+    """Round a Python float to the nearest binary32 value (ties to even)."""
+    return struct.unpack("<f", struct.pack("<f", x))[0]
+
+
+def r16(x: float) -> float:
+    """Round a Python float to the nearest binary16 value (ties to even, subnormals kept)."""
+    return struct.unpack("<e", struct.pack("<e", x))[0]
+
+
+def round_half_even(x: float) -> float:
+    """Nearest integer, ties to the even neighbour (Python's round on floats does this)."""
+    return float(round(x))
+
+
+def quantize_group(xs: list[float], bits: int):
+    """One group of fp16 values -> (codes, scale16, zero16) with one rounding per op."""
+    L = float(2 ** bits - 1)
+    lo = r32(min(xs) + 0.0)
+    hi = r32(max(xs) + 0.0)
+    s32 = r32(r32(hi - lo) / L)
+    scale16 = r16(s32)
+    zero16 = r16(lo)
+    codes = []
+    if scale16 == 0.0:
+        return [0] * len(xs), scale16, zero16
+    inv = r32(1.0 / scale16)
+    for x in xs:
+        t = r32(r32(x - lo) * inv)
+        c = round_half_even(t)
+        c = min(max(c, 0.0), L)
+        codes.append(int(c))
+    return codes, scale16, zero16
+
+
+def encode_keys(K: list[list[float]], bits: int, g: int):
+    """K[t][d] -> codes[t][d], scale[j][d], zero[j][d]; group = g tokens of one channel."""
+    T, D = len(K), len(K[0])
+    codes = [[0] * D for _ in range(T)]
+    scale = [[0.0] * D for _ in range(T // g)]
+    zero = [[0.0] * D for _ in range(T // g)]
+    for j in range(T // g):
+        for d in range(D):
+            col = [K[j * g + i][d] for i in range(g)]
+            c, s, z = quantize_group(col, bits)
+            scale[j][d], zero[j][d] = s, z
+            for i in range(g):
+                codes[j * g + i][d] = c[i]
+    return codes, scale, zero
+
+
+def encode_values(V: list[list[float]], bits: int, g: int):
+    """V[t][d] -> codes[t][d], scale[t][k], zero[t][k]; group = g channels of one token."""
+    T, D = len(V), len(V[0])
+    codes = [[0] * D for _ in range(T)]
+    scale = [[0.0] * (D // g) for _ in range(T)]
+    zero = [[0.0] * (D // g) for _ in range(T)]
+    for t in range(T):
+        for k in range(D // g):
+            c, s, z = quantize_group(V[t][k * g:(k + 1) * g], bits)
+            scale[t][k], zero[t][k] = s, z
+            codes[t][k * g:(k + 1) * g] = c
+    return codes, scale, zero
+
+
+def attend(q: list[float], keys: list[list[float]], values: list[list[float]], sm_scale: float = 1.0):
+    """softmax(sm_scale * q . k_t) weighted sum of v_t, with explicit loops."""
+    scores = [sm_scale * sum(qd * kd for qd, kd in zip(q, k)) for k in keys]
+    m = max(scores)
+    w = [math.exp(s - m) for s in scores]
+    tot = sum(w)
+    D = len(values[0])
+    return [sum(w[t] * values[t][d] for t in range(len(values))) / tot for d in range(D)]
