@@ -1,0 +1,176 @@
+/*
+ * kvq.h - C ABI of libkvq: a KIVI-style quantized KV cache with decode attention that
+ * reads the quantized cache directly, for AMD Instinct MI355X (gfx950).
+ *
+ * The method (VeloxQuant-MLX documentation pages):
+ *  - "Changelog", v0.8.0 "New" (KIVI): asymmetric group quantization, keys grouped per
+ *    channel and values per token, no codebook, no rotation, an fp16 residual window of
+ *    the newest tokens; group size 32 by default ("veloxquant_mlx.cache package",
+ *    KVCacheConfig.kivi_group_size).
+ *  - "Changelog", v0.42.0 "Added": decode attention straight over b-bit codes plus a
+ *    per-group (scale, zero); k_hat / v_hat are rebuilt in registers inside an online
+ *    softmax accumulated in fp32, so no dequantized K/V is ever written to memory.
+ *  - "Changelog", v0.30.0 "New" / "Honest scope": parameters kept as low end and step,
+ *    integer bit widths, fp16 metadata.  "Changelog", v0.28.0: the residual window is
+ *    flushed through the quantizer one whole chunk at a time.
+ *
+ * Conventions shared by every call:
+ *  - Tensor arguments are DEVICE pointers owned by the caller. The library never allocates
+ *    or frees device memory; the cache state lives in one caller-allocated device buffer
+ *    of kvq_cache_bytes() bytes and decode scratch in a caller buffer of
+ *    kvq_workspace_bytes() bytes.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). Every call
+ *    that takes a stream is asynchronous and ordered on that stream; the caller keeps
+ *    the buffers alive until the work is done.
+ *  - Every call validates its arguments on the host before anything is launched and
+ *    returns a kvq_status; on failure nothing was enqueued and kvq_last_error() returns a
+ *    thread-local message. No C++ exception crosses the ABI.
+ *  - fp16 tensors are IEEE binary16. Layouts are row-major with the last index fastest.
+ *  - A kvq_cache handle is not thread safe; calls on one handle must come from one thread
+ *    (they may use any stream, but calls on different streams are not ordered).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kvq_status;
+#define KVQ_OK 0
+#define KVQ_E_INVALID (-1)     /* bad argument, shape or state */
+#define KVQ_E_UNSUPPORTED (-2) /* valid in principle, not built (e.g. group != 32) */
+#define KVQ_E_CAPACITY (-3)    /* a sequence would exceed max_tokens */
+#define KVQ_E_WORKSPACE (-4)   /* workspace too small */
+#define KVQ_E_NODEVICE (-5)    /* no gfx950 device visible */
+#define KVQ_E_HIP (-6)         /* a HIP runtime call failed */
+
+#define KVQ_MAX_BATCH 256
+
+/* Shape and precision of one layer's cache. */
+typedef struct kvq_config {
+  int32_t batch;      /* B sequences, 1..KVQ_MAX_BATCH */
+  int32_t n_kv_heads; /* H_kv >= 1 */
+  int32_t n_q_heads;  /* H_q = G * H_kv with G in {1, 2, 4, 8}; query head h reads KV head h / G */
+  int32_t head_dim;   /* D in {64, 128} */
+  int32_t key_bits;   /* b_k in {2, 4, 8} */
+  int32_t value_bits; /* b_v in {2, 4, 8} */
+  int32_t group;      /* g, must be 32 (the pages' default group size) */
+  int32_t residual;   /* R, fp16 window capacity: a multiple of 32, at most 256 */
+  int32_t max_tokens; /* per-sequence capacity in tokens, a positive multiple of 32 */
+} kvq_config;
+
+/* Byte offsets of the regions inside the cache buffer (see the layout description in the
+ * design notes; all offsets are multiples of 256). */
+typedef struct kvq_layout_info {
+  uint64_t lengths_offset;  /* int32 [B][H_kv][2]: (quantized tokens, window tokens) */
+  uint64_t records_offset;  /* [B][H_kv][max_tokens/32] group records */
+  uint64_t record_bytes;    /* 4*D*(b_k + b_v + 2) */
+  uint64_t rec_key_codes;   /* offset of the key codes inside a record (4*D*b_k bytes) */
+  uint64_t rec_value_codes; /* value codes (4*D*b_v bytes) */
+  uint64_t rec_key_params;  /* key (scale, zero) fp16 pairs, D dwords */
+  uint64_t rec_value_params;/* value (scale, zero) fp16 pairs, D dwords */
+  uint64_t window_k_offset; /* fp16 [B][H_kv][R][D] */
+  uint64_t window_v_offset; /* fp16 [B][H_kv][R][D] */
+  uint64_t total_bytes;     /* == kvq_cache_bytes() */
+} kvq_layout_info;
+
+typedef struct kvq_cache kvq_cache; /* opaque host handle */
+
+/* Capability probe, the counterpart of the capability probe and the auto/require backend
+ * flag of "Changelog" v0.5.1 "New": *has_gfx950 = 1 when a gfx950 device is visible to the
+ * HIP runtime, else 0. Returns KVQ_OK, or KVQ_E_INVALID for a NULL pointer; never fails
+ * for lack of a device. There is no CPU fallback behind it: every other call needs the GPU. */
+kvq_status kvq_probe(int32_t* has_gfx950);
+
+/* Validate a configuration (the pages' QuantizerConfigError checks). */
+kvq_status kvq_config_check(const kvq_config* cfg);
+
+/* Device bytes the caller allocates for one cache (0 if cfg is invalid). */
+size_t kvq_cache_bytes(const kvq_config* cfg);
+
+/* Region offsets of the cache buffer. */
+kvq_status kvq_layout(const kvq_config* cfg, kvq_layout_info* out);
+
+/* Device bytes of decode scratch for up to n_split splits per sequence (n_split = 0: the
+ * largest split count kvq_decode_attend picks by itself). 0 if cfg is invalid. */
+size_t kvq_workspace_bytes(const kvq_config* cfg, int32_t n_split);
+
+/* Create a host handle over a caller-owned device buffer of at least kvq_cache_bytes(cfg)
+ * bytes (256-byte aligned). Host-only: nothing is launched here; the first call that takes
+ * a stream zeroes the lengths on the device before its own work. The buffer's contents are
+ * otherwise left as they are. */
+kvq_status kvq_cache_create(const kvq_config* cfg, void* dev_buf, size_t bytes, kvq_cache** out);
+
+/* Free the host handle only (never the device buffer). NULL is ignored. */
+void kvq_cache_destroy(kvq_cache* cache);
+
+/* Empty every sequence (device lengths zeroed with a fill kernel on `stream`). */
+kvq_status kvq_reset(kvq_cache* cache, void* stream);
+
+/* Host mirror of the lengths: n_quantized[b], n_window[b] (arrays of `batch` entries,
+ * either may be NULL). Exact without a device sync: every length change is decided on the
+ * host before it is enqueued. */
+kvq_status kvq_cache_lengths(const kvq_cache* cache, int32_t* n_quantized, int32_t* n_window);
+
+/* North-star call 1 ("Changelog" v0.8.0 quantizer; v0.42.0 codes + (scale, zero)).
+ * Quantize n_tok[b] new tokens of every sequence b after its quantized region:
+ *   K, V: fp16 [B][H_kv][ld_tok][D]; tokens 0..n_tok[b]-1 of sequence b are encoded.
+ *   n_tok: HOST array of B entries, each a multiple of 32 (KVQ_E_INVALID otherwise); 0 skips
+ *   the sequence. A sequence with a non-empty window is KVQ_E_INVALID (its window tokens
+ *   are older than the new ones). Over capacity is KVQ_E_CAPACITY.
+ * Key groups: 32 consecutive tokens of one channel; value groups: 32 consecutive channels
+ * of one token. Per group: zero = min, scale = fp16((max - min) / (2^b - 1)) (fp32 ops),
+ * codes = clamp(rint((x - zero) * (1/scale)), 0, 2^b - 1) with the stored scale, all
+ * codes 0 when the stored scale is 0. Results are bit-identical on every run. */
+kvq_status kvq_encode(kvq_cache* cache, const void* K, const void* V, int64_t ld_tok,
+                      const int32_t* n_tok, void* stream);
+
+/* Fill an EMPTY cache with seq_len[b] tokens per sequence following the window rule of the
+ * residual window ("Changelog" v0.8.0, v0.28.0): the first S - n_r tokens are quantized and
+ * the last n_r = ((S - 1) mod R) + 1 stay fp16 (S = 0 leaves the sequence empty).
+ * K, V as in kvq_encode; seq_len is a HOST array of B entries. A sequence that is not
+ * empty is KVQ_E_INVALID; S > max_tokens is KVQ_E_CAPACITY. */
+kvq_status kvq_prefill(kvq_cache* cache, const void* K, const void* V, int64_t ld_tok,
+                       const int32_t* seq_len, void* stream);
+
+/* North-star call 2 (residual window and chunk flush, "Changelog" v0.8.0 / v0.28.0).
+ * Append one token to every sequence: k_tok, v_tok fp16 [B][H_kv][D]. A sequence whose
+ * window is full first quantizes all R window tokens (R/32 key groups, R value tokens)
+ * exactly as kvq_encode would, then stores the new token as window slot 0.
+ * KVQ_E_CAPACITY if any sequence would exceed max_tokens (nothing is enqueued). */
+kvq_status kvq_append(kvq_cache* cache, const void* k_tok, const void* v_tok, void* stream);
+
+/* North-star call 3 (fused decode + attention, "Changelog" v0.42.0).
+ * out[b][h] = softmax(sm_scale * q[b][h] . K_hat[b][h/G]^T) V_hat[b][h/G] over all
+ * quantized and window tokens of sequence b, with K_hat / V_hat rebuilt in registers from
+ * the codes and fp16 (scale, zero) and never written out; fp32 scores and accumulation.
+ *   q:   fp16 [B][H_q][D];  out: fp16 [B][H_q][D], or fp32 when out_fp32 != 0.
+ *   workspace: at least kvq_workspace_bytes(cfg, n_split) device bytes (KVQ_E_WORKSPACE).
+ *   n_split: maximum splits per sequence along the tokens (0 = chosen from the lengths).
+ * Every sequence must hold at least one token (KVQ_E_INVALID otherwise). */
+kvq_status kvq_decode_attend(kvq_cache* cache, const void* q, void* out, int32_t out_fp32,
+                             float sm_scale, void* workspace, size_t ws_bytes, int32_t n_split,
+                             void* stream);
+
+/* Timing hook for benchmarks: while enabled, kvq_decode_attend records a pair of HIP events
+ * around its split pass (the dominant kernel) on its stream. kvq_profile_read waits for the
+ * recorded events and returns their total elapsed milliseconds and count, then clears them.
+ * At most 4096 pairs are kept (KVQ_E_INVALID past that). */
+kvq_status kvq_profile_enable(kvq_cache* cache, int32_t enable);
+kvq_status kvq_profile_read(kvq_cache* cache, double* total_ms, int64_t* count);
+
+/* Thread-local message of the last failed call on this thread ("" if none). */
+const char* kvq_last_error(void);
+
+/* Name of a status code. */
+const char* kvq_status_string(kvq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

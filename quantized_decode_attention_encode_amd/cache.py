@@ -1,0 +1,172 @@
+"""Python binding of the C ABI: argument marshalling only.
+
+Every step of the hot path runs in the HIP kernels of libkvq.so. PyTorch supplies device
+memory (tensors) and the stream; this module checks shapes and dtypes, passes raw device
+pointers, and turns status codes into KVQError.
+
+The functions carry the C names (kvq_encode, kvq_prefill, kvq_append, kvq_decode_attend,
+...); KVQCache bundles a cache buffer, its handle and a decode workspace.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import KVQ_OK, Config, KVQError, LayoutInfo, check, lib
+
+__all__ = ["KVQCache", "KVQError", "make_config", "kvq_probe", "kvq_cache_bytes", "kvq_layout",
+           "kvq_workspace_bytes", "kvq_encode", "kvq_prefill", "kvq_append", "kvq_decode_attend"]
+
+
+def make_config(batch, n_kv_heads, n_q_heads, head_dim, key_bits=2, value_bits=2, group=32, residual=32,
+                max_tokens=4096) -> Config:
+    return Config(batch, n_kv_heads, n_q_heads, head_dim, key_bits, value_bits, group, residual, max_tokens)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _i32(values) -> ctypes.Array:
+    vals = [int(v) for v in values]
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=torch.float16) -> ctypes.c_void_p:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise KVQError(-1, f"{name} must be a CUDA tensor")
+    if t.dtype != dtype:
+        raise KVQError(-1, f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise KVQError(-1, f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def kvq_probe() -> bool:
+    has = ctypes.c_int32(0)
+    check(lib.kvq_probe(ctypes.byref(has)))
+    return bool(has.value)
+
+
+def kvq_cache_bytes(cfg: Config) -> int:
+    n = lib.kvq_cache_bytes(ctypes.byref(cfg))
+    if n == 0:
+        check(lib.kvq_config_check(ctypes.byref(cfg)))
+    return n
+
+
+def kvq_layout(cfg: Config) -> LayoutInfo:
+    info = LayoutInfo()
+    check(lib.kvq_layout(ctypes.byref(cfg), ctypes.byref(info)))
+    return info
+
+
+def kvq_workspace_bytes(cfg: Config, n_split: int = 0) -> int:
+    n = lib.kvq_workspace_bytes(ctypes.byref(cfg), int(n_split))
+    if n == 0:
+        check(lib.kvq_config_check(ctypes.byref(cfg)))
+    return n
+
+
+class KVQCache:
+    """One layer's quantized KV cache in a caller-owned (torch) device buffer."""
+
+    def __init__(self, cfg: Config, device="cuda", buffer: torch.Tensor | None = None):
+        self.cfg = cfg
+        nbytes = kvq_cache_bytes(cfg)
+        if buffer is None:
+            buffer = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.buffer = buffer
+        self.handle = ctypes.c_void_p()
+        check(lib.kvq_cache_create(ctypes.byref(cfg), ctypes.c_void_p(buffer.data_ptr()), buffer.numel(),
+                                   ctypes.byref(self.handle)))
+        self._ws = None
+
+    def close(self):
+        if self.handle:
+            lib.kvq_cache_destroy(self.handle)
+            self.handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def lengths(self):
+        nq = (ctypes.c_int32 * self.cfg.batch)()
+        nr = (ctypes.c_int32 * self.cfg.batch)()
+        check(lib.kvq_cache_lengths(self.handle, nq, nr))
+        return list(nq), list(nr)
+
+    def reset(self, stream=None):
+        check(lib.kvq_reset(self.handle, _stream(stream)))
+
+    def workspace(self, n_split: int = 0) -> torch.Tensor:
+        need = kvq_workspace_bytes(self.cfg, n_split)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.buffer.device)
+        return self._ws
+
+    def profile_enable(self, on: bool = True):
+        check(lib.kvq_profile_enable(self.handle, 1 if on else 0))
+
+    def profile_read(self):
+        ms = ctypes.c_double(0)
+        n = ctypes.c_int64(0)
+        check(lib.kvq_profile_read(self.handle, ctypes.byref(ms), ctypes.byref(n)))
+        return ms.value, n.value
+
+
+def _kv_shape_check(cache: KVQCache, K: torch.Tensor, V: torch.Tensor):
+    c = cache.cfg
+    if K.dim() != 4 or K.shape[0] != c.batch or K.shape[1] != c.n_kv_heads or K.shape[3] != c.head_dim:
+        raise KVQError(-1, f"K must be [B={c.batch}, H_kv={c.n_kv_heads}, T, D={c.head_dim}], got {tuple(K.shape)}")
+    if V.shape != K.shape:
+        raise KVQError(-1, f"V shape {tuple(V.shape)} differs from K shape {tuple(K.shape)}")
+
+
+def kvq_encode(cache: KVQCache, K: torch.Tensor, V: torch.Tensor, n_tok, stream=None) -> None:
+    """Quantize n_tok[b] tokens of K, V [B, H_kv, T, D] fp16 after each sequence's quantized region."""
+    _kv_shape_check(cache, K, V)
+    check(lib.kvq_encode(cache.handle, _dev(K, "K"), _dev(V, "V"), K.shape[2], _i32(n_tok), _stream(stream)))
+
+
+def kvq_prefill(cache: KVQCache, K: torch.Tensor, V: torch.Tensor, seq_len, stream=None) -> None:
+    """Fill an empty cache with seq_len[b] tokens per sequence (window rule applied)."""
+    _kv_shape_check(cache, K, V)
+    check(lib.kvq_prefill(cache.handle, _dev(K, "K"), _dev(V, "V"), K.shape[2], _i32(seq_len), _stream(stream)))
+
+
+def kvq_append(cache: KVQCache, k: torch.Tensor, v: torch.Tensor, stream=None) -> None:
+    """Append one token per sequence: k, v fp16 [B, H_kv, D]."""
+    c = cache.cfg
+    for name, t in (("k", k), ("v", v)):
+        if tuple(t.shape) != (c.batch, c.n_kv_heads, c.head_dim):
+            raise KVQError(-1, f"{name} must be [B, H_kv, D] = {(c.batch, c.n_kv_heads, c.head_dim)}")
+    check(lib.kvq_append(cache.handle, _dev(k, "k"), _dev(v, "v"), _stream(stream)))
+
+
+def kvq_decode_attend(cache: KVQCache, q: torch.Tensor, out: torch.Tensor | None = None, sm_scale: float = 1.0,
+                      n_split: int = 0, out_fp32: bool = False, workspace: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
+    """Attention of q [B, H_q, D] fp16 over the quantized cache; returns out [B, H_q, D]."""
+    c = cache.cfg
+    if tuple(q.shape) != (c.batch, c.n_q_heads, c.head_dim):
+        raise KVQError(-1, f"q must be [B, H_q, D] = {(c.batch, c.n_q_heads, c.head_dim)}")
+    odt = torch.float32 if out_fp32 else torch.float16
+    if out is None:
+        out = torch.empty(tuple(q.shape), dtype=odt, device=q.device)
+    if tuple(out.shape) != tuple(q.shape):
+        raise KVQError(-1, "out must have q's shape")
+    if workspace is None:
+        workspace = cache.workspace(n_split)
+    st = lib.kvq_decode_attend(cache.handle, _dev(q, "q"), _dev(out, "out", odt), 1 if out_fp32 else 0,
+                               float(sm_scale), _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+                               int(n_split), _stream(stream))
+    if st != KVQ_OK:
+        check(st)
+    return out

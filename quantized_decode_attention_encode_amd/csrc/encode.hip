@@ -1,0 +1,356 @@
+// encode.hip - group quantization kernels: prefill/encode, residual-window append + flush.
+//
+// The quantizer ("Changelog" v0.8.0 KIVI; v0.42.0 codes + per-group (scale, zero);
+// v0.30.0 lo/scale and fp16 metadata):
+//   key group   = 32 consecutive tokens of one channel,
+//   value group = 32 consecutive channels of one token,
+//   lo = min + 0, hi = max + 0 (turns -0 into +0),
+//   scale16 = fp16_rne((hi - lo) / (2^b - 1)), zero16 = lo,
+//   inv = 1 / float(scale16)  (0 when the stored scale is 0),
+//   code = clamp(rint((x - lo) * inv), 0, 2^b - 1).
+// Every step is one IEEE fp32 operation rounded to nearest even; this translation unit is
+// built with -ffp-contract=off and correctly rounded fp32 division, so the codes and
+// parameters are bit-identical to any other IEEE implementation of the same steps.
+//
+// One wavefront quantizes one record (32 tokens x D channels of K and of V):
+//   * the 32 x D fp16 tile is loaded with 16-byte loads, lane = (row r, 8-channel chunk c8);
+//   * key min/max: lane-local over the lane's tokens, then a cross-row butterfly
+//     (__shfl_xor over lane distances D/8, D/4, ...) leaves every channel's range in all
+//     lanes of its chunk;
+//   * value min/max: lane-local over 8 channels, then DPP quad butterflies (quad_perm)
+//     across the 4 chunks of a 32-channel value group;
+//   * codes are packed into the record image in LDS and the record leaves with coalesced
+//     16-byte stores.
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "kernels.h"
+#include "layout.h"
+
+namespace kvq {
+
+template <int D, int BK, int BV>
+struct EncodeLds {
+  static constexpr int kRecWords = D * (BK + BV + 2);
+  uint32_t rec[kRecWords];       // record image
+  uint8_t vbytes[D * kGroup];    // value codes, one byte each, [d][t]
+};
+
+__device__ __forceinline__ float dpp_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+}
+__device__ __forceinline__ float dpp_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+}
+
+struct GroupParams {
+  float lo, inv;
+  uint32_t packed;  // scale16 | zero16 << 16
+};
+
+// Parameters of one group from its exact min and max.
+template <int B>
+__device__ __forceinline__ GroupParams group_params(float mn, float mx) {
+  constexpr float L = float((1 << B) - 1);
+  GroupParams p;
+  const float lo = mn + 0.0f;
+  const float hi = mx + 0.0f;
+  const float s32 = (hi - lo) / L;
+  const __half sc16 = __float2half_rn(s32);
+  const float s = __half2float(sc16);
+  p.lo = lo;
+  p.inv = (s != 0.0f) ? 1.0f / s : 0.0f;
+  const uint32_t zb = __half_as_ushort(__float2half_rn(lo));  // exact: lo is an fp16 value
+  p.packed = uint32_t(__half_as_ushort(sc16)) | (zb << 16);
+  return p;
+}
+
+template <int B>
+__device__ __forceinline__ uint32_t code_of(float x, const GroupParams& p) {
+  constexpr float L = float((1 << B) - 1);
+  const float t = (x - p.lo) * p.inv;  // with inv = 0 this is 0, so a zero scale gives code 0
+  const float c = fminf(fmaxf(rintf(t), 0.0f), L);
+  return uint32_t(c);
+}
+
+// Quantize the 32-token tile (rows ks[0..31], vs[0..31], row stride D elements) into the
+// record at `rec_out`. Called by all 64 lanes of a single-wave workgroup.
+template <int D, int BK, int BV>
+__device__ void encode_record(const __half* __restrict__ ks, const __half* __restrict__ vs,
+                              uint32_t* __restrict__ rec_out, EncodeLds<D, BK, BV>& lds) {
+  constexpr int CH = D / 8;      // 16-byte chunks per row
+  constexpr int RPI = 64 / CH;   // rows covered by one load instruction
+  constexpr int NI = kGroup / RPI;
+  constexpr int DQ = D / 4;      // channels per key-code quarter
+  constexpr int WQ = D * BK / 128;  // words per (token, quarter)
+  constexpr int NKG = D / kGroup;   // value groups per token
+  constexpr uint32_t KC_W = 0;
+  constexpr uint32_t VC_W = D * BK;
+  constexpr uint32_t KP_W = D * (BK + BV);
+  constexpr uint32_t VP_W = KP_W + D;
+  const int lane = threadIdx.x & 63;
+  const int c8 = lane % CH, r = lane / CH;
+
+  float kx[NI][8], vx[NI][8];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int t = r + RPI * i;
+    const uint4 kr = *reinterpret_cast<const uint4*>(ks + t * D + 8 * c8);
+    const uint4 vr = *reinterpret_cast<const uint4*>(vs + t * D + 8 * c8);
+    const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w};
+    const uint32_t vw[4] = {vr.x, vr.y, vr.z, vr.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      kx[i][2 * e] = __half2float(__ushort_as_half(uint16_t(kw[e] & 0xFFFF)));
+      kx[i][2 * e + 1] = __half2float(__ushort_as_half(uint16_t(kw[e] >> 16)));
+      vx[i][2 * e] = __half2float(__ushort_as_half(uint16_t(vw[e] & 0xFFFF)));
+      vx[i][2 * e + 1] = __half2float(__ushort_as_half(uint16_t(vw[e] >> 16)));
+    }
+  }
+
+  // ---- keys: one group per channel over the 32 tokens
+  GroupParams kp[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float mn = kx[0][e], mx = kx[0][e];
+#pragma unroll
+    for (int i = 1; i < NI; ++i) {
+      mn = fminf(mn, kx[i][e]);
+      mx = fmaxf(mx, kx[i][e]);
+    }
+#pragma unroll
+    for (int m = CH; m < 64; m <<= 1) {
+      mn = fminf(mn, __shfl_xor(mn, m, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+    }
+    kp[e] = group_params<BK>(mn, mx);
+  }
+  if (r == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) lds.rec[KP_W + 8 * c8 + e] = kp[e].packed;
+  }
+  {
+    const int ch0 = 8 * c8;
+    const int Q = ch0 / DQ, cq = ch0 % DQ;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int t = r + RPI * i;
+      const int P = t >> 1, tp = t & 1;
+      uint64_t piece = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) piece |= uint64_t(code_of<BK>(kx[i][e], kp[e])) << (e * BK);
+      const uint32_t word = KC_W + ((P * 4 + Q) * 2 + tp) * WQ + (cq * BK) / 32;
+      const int bit = (cq * BK) % 32;
+      uint8_t* base = reinterpret_cast<uint8_t*>(&lds.rec[word]) + bit / 8;
+      if constexpr (BK == 2) {
+        *reinterpret_cast<uint16_t*>(base) = uint16_t(piece);
+      } else if constexpr (BK == 4) {
+        *reinterpret_cast<uint32_t*>(base) = uint32_t(piece);
+      } else {
+        reinterpret_cast<uint32_t*>(base)[0] = uint32_t(piece);
+        reinterpret_cast<uint32_t*>(base)[1] = uint32_t(piece >> 32);
+      }
+    }
+  }
+
+  // ---- values: one group per (token, 32 channels) = 4 adjacent chunks of the same row
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int t = r + RPI * i;
+    float mn = vx[i][0], mx = vx[i][0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) {
+      mn = fminf(mn, vx[i][e]);
+      mx = fmaxf(mx, vx[i][e]);
+    }
+    mn = fminf(mn, dpp_xor1(mn));
+    mx = fmaxf(mx, dpp_xor1(mx));
+    mn = fminf(mn, dpp_xor2(mn));
+    mx = fmaxf(mx, dpp_xor2(mx));
+    const GroupParams vp = group_params<BV>(mn, mx);
+    const int k = c8 / 4;
+    if ((c8 & 3) == 0) lds.rec[VP_W + ((t >> 1) * NKG + k) * 2 + (t & 1)] = vp.packed;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) lds.vbytes[(8 * c8 + e) * kGroup + t] = uint8_t(code_of<BV>(vx[i][e], vp));
+  }
+  __syncthreads();
+
+  // ---- pack value codes: word w = (channel d, sub-word sw), tokens sw*32/BV .. at bit t*BV
+  constexpr int PER_WORD = 32 / BV;
+  for (int w = lane; w < D * BV; w += 64) {
+    const int d = w / BV, sw = w % BV;
+    const uint8_t* src = &lds.vbytes[d * kGroup + sw * PER_WORD];
+    uint32_t word = 0;
+#pragma unroll
+    for (int n = 0; n < PER_WORD; ++n) word |= uint32_t(src[n]) << (n * BV);
+    lds.rec[VC_W + w] = word;
+  }
+  __syncthreads();
+
+  // ---- copy the record out, 16 bytes per lane per step
+  constexpr int NV4 = EncodeLds<D, BK, BV>::kRecWords / 4;
+  const uint4* src4 = reinterpret_cast<const uint4*>(lds.rec);
+  uint4* dst4 = reinterpret_cast<uint4*>(rec_out);
+  for (int v = lane; v < NV4; v += 64) dst4[v] = src4[v];
+  __syncthreads();
+}
+
+// Prefill / encode: record (j0[b] + blockIdx.x) of (b = blockIdx.z, h = blockIdx.y) from
+// tokens 32*blockIdx.x .. of the caller's K, V [B][H_kv][ld_tok][D].
+template <int D, int BK, int BV>
+__global__ __launch_bounds__(64) void encode_kernel(uint8_t* __restrict__ buf, Layout L,
+                                                    const __half* __restrict__ K,
+                                                    const __half* __restrict__ V, int64_t ld_tok,
+                                                    PerSeq seq /* a: first record, b: records */) {
+  __shared__ EncodeLds<D, BK, BV> lds;
+  const int jl = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  if (jl >= seq.b[b]) return;
+  const int j = seq.a[b] + jl;
+  if (j >= L.max_groups) return;
+  const int64_t row0 = ((int64_t(b) * L.Hkv + h) * ld_tok + int64_t(kGroup) * jl) * D;
+  encode_record<D, BK, BV>(K + row0, V + row0, reinterpret_cast<uint32_t*>(buf + L.record(b, h, j)), lds);
+}
+
+// Append one token per (b, h); a full window is flushed first (R/32 records).
+template <int D, int BK, int BV>
+__global__ __launch_bounds__(64) void append_kernel(uint8_t* __restrict__ buf, Layout L,
+                                                    const __half* __restrict__ k_tok,
+                                                    const __half* __restrict__ v_tok) {
+  __shared__ EncodeLds<D, BK, BV> lds;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x;
+  int32_t* len = reinterpret_cast<int32_t*>(buf + L.lengths(b, h));
+  int nq = len[0], nr = len[1];
+  __half* wk = reinterpret_cast<__half*>(buf + L.wk_off + L.window(b, h));
+  __half* wv = reinterpret_cast<__half*>(buf + L.wv_off + L.window(b, h));
+  if (nr >= L.R) {
+    const int j0 = nq / kGroup;
+    for (int m = 0; m < L.R / kGroup; ++m) {
+      if (j0 + m < L.max_groups)
+        encode_record<D, BK, BV>(wk + m * kGroup * D, wv + m * kGroup * D,
+                                 reinterpret_cast<uint32_t*>(buf + L.record(b, h, j0 + m)), lds);
+    }
+    nq += L.R;
+    nr = 0;
+  }
+  __syncthreads();
+  const int64_t src = (int64_t(b) * L.Hkv + h) * D;
+  constexpr int HPL = D / 64;  // halves per lane
+  if (nr < L.R) {
+    for (int e = 0; e < HPL; ++e) {
+      wk[nr * D + lane * HPL + e] = k_tok[src + lane * HPL + e];
+      wv[nr * D + lane * HPL + e] = v_tok[src + lane * HPL + e];
+    }
+  }
+  __syncthreads();
+  if (lane == 0) {
+    len[0] = nq;
+    len[1] = nr + 1;
+  }
+}
+
+// Prefill tail: copy tokens [n_q, n_q + n_r) of K, V into window slots 0.. and set the
+// lengths of (b, h) to (n_q, n_r). seq.a = n_q, seq.b = n_r per sequence.
+template <int D>
+__global__ __launch_bounds__(64) void window_fill_kernel(uint8_t* __restrict__ buf, Layout L,
+                                                         const __half* __restrict__ K,
+                                                         const __half* __restrict__ V,
+                                                         int64_t ld_tok, PerSeq seq) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int nq = seq.a[b], nr = seq.b[b];
+  __half* wk = reinterpret_cast<__half*>(buf + L.wk_off + L.window(b, h));
+  __half* wv = reinterpret_cast<__half*>(buf + L.wv_off + L.window(b, h));
+  const int64_t row0 = ((int64_t(b) * L.Hkv + h) * ld_tok + nq) * D;
+  constexpr int HPL = D / 64;
+  for (int t = 0; t < nr; ++t)
+    for (int e = 0; e < HPL; ++e) {
+      wk[t * D + lane * HPL + e] = K[row0 + int64_t(t) * D + lane * HPL + e];
+      wv[t * D + lane * HPL + e] = V[row0 + int64_t(t) * D + lane * HPL + e];
+    }
+  if (lane == 0) {
+    int32_t* len = reinterpret_cast<int32_t*>(buf + L.lengths(b, h));
+    len[0] = nq;
+    len[1] = nr;
+  }
+}
+
+// Set the lengths of every (b, h) to (seq.a[b], seq.b[b]).
+__global__ __launch_bounds__(64) void lengths_fill_kernel(uint8_t* __restrict__ buf, Layout L, PerSeq seq) {
+  const int i = blockIdx.x * 64 + threadIdx.x;
+  if (i >= L.B * L.Hkv) return;
+  const int b = i / L.Hkv;
+  int32_t* len = reinterpret_cast<int32_t*>(buf + L.len_off) + 2 * i;
+  len[0] = seq.a[b];
+  len[1] = seq.b[b];
+}
+
+// ------------------------------------------------------------------------------------
+// Host-side launchers
+// ------------------------------------------------------------------------------------
+template <int D, int BK, int BV>
+static hipError_t launch_encode_t(uint8_t* buf, const Layout& L, const void* K, const void* V,
+                                  int64_t ld_tok, const PerSeq& seq, int max_records, hipStream_t s) {
+  dim3 grid(max_records, L.Hkv, L.B);
+  hipLaunchKernelGGL((encode_kernel<D, BK, BV>), grid, dim3(64), 0, s, buf, L,
+                     static_cast<const __half*>(K), static_cast<const __half*>(V), ld_tok, seq);
+  return hipGetLastError();
+}
+
+template <int D, int BK, int BV>
+static hipError_t launch_append_t(uint8_t* buf, const Layout& L, const void* k, const void* v, hipStream_t s) {
+  dim3 grid(L.Hkv, L.B);
+  hipLaunchKernelGGL((append_kernel<D, BK, BV>), grid, dim3(64), 0, s, buf, L,
+                     static_cast<const __half*>(k), static_cast<const __half*>(v));
+  return hipGetLastError();
+}
+
+#define KVQ_DISPATCH_BITS(D, FN, ...)                                     \
+  switch (L.bk * 16 + L.bv) {                                             \
+    case 0x22: return FN<D, 2, 2>(__VA_ARGS__);                           \
+    case 0x24: return FN<D, 2, 4>(__VA_ARGS__);                           \
+    case 0x28: return FN<D, 2, 8>(__VA_ARGS__);                           \
+    case 0x42: return FN<D, 4, 2>(__VA_ARGS__);                           \
+    case 0x44: return FN<D, 4, 4>(__VA_ARGS__);                           \
+    case 0x48: return FN<D, 4, 8>(__VA_ARGS__);                           \
+    case 0x82: return FN<D, 8, 2>(__VA_ARGS__);                           \
+    case 0x84: return FN<D, 8, 4>(__VA_ARGS__);                           \
+    case 0x88: return FN<D, 8, 8>(__VA_ARGS__);                           \
+    default: return hipErrorInvalidValue;                                 \
+  }
+
+hipError_t launch_encode(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,
+                         const PerSeq& seq, int max_records, hipStream_t s) {
+  if (L.D == 128) { KVQ_DISPATCH_BITS(128, launch_encode_t, buf, L, K, V, ld_tok, seq, max_records, s) }
+  if (L.D == 64) { KVQ_DISPATCH_BITS(64, launch_encode_t, buf, L, K, V, ld_tok, seq, max_records, s) }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_append(uint8_t* buf, const Layout& L, const void* k, const void* v, hipStream_t s) {
+  if (L.D == 128) { KVQ_DISPATCH_BITS(128, launch_append_t, buf, L, k, v, s) }
+  if (L.D == 64) { KVQ_DISPATCH_BITS(64, launch_append_t, buf, L, k, v, s) }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_window_fill(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,
+                              const PerSeq& seq, hipStream_t s) {
+  dim3 grid(L.Hkv, L.B);
+  if (L.D == 128)
+    hipLaunchKernelGGL(window_fill_kernel<128>, grid, dim3(64), 0, s, buf, L, static_cast<const __half*>(K),
+                       static_cast<const __half*>(V), ld_tok, seq);
+  else if (L.D == 64)
+    hipLaunchKernelGGL(window_fill_kernel<64>, grid, dim3(64), 0, s, buf, L, static_cast<const __half*>(K),
+                       static_cast<const __half*>(V), ld_tok, seq);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_lengths_fill(uint8_t* buf, const Layout& L, const PerSeq& seq, hipStream_t s) {
+  const int n = L.B * L.Hkv;
+  hipLaunchKernelGGL(lengths_fill_kernel, dim3((n + 63) / 64), dim3(64), 0, s, buf, L, seq);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

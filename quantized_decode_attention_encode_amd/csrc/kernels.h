@@ -1,0 +1,39 @@
+// kernels.h - launchers of the HIP kernels, called by the C ABI in kvq.cpp.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.h"
+
+namespace kvq {
+
+// Two per-sequence int32 arrays passed by value as a kernel argument (2 KiB).
+struct PerSeq {
+  int32_t a[kMaxBatch];
+  int32_t b[kMaxBatch];
+};
+
+// Decode launch geometry: gridDim.x = n_split workgroups per (b, h_kv), each covering
+// `chunk` consecutive units (a unit is one 32-token record, or up to 32 window tokens).
+struct DecodeShape {
+  int n_split;
+  int chunk;
+  int G;            // query heads per KV head
+  int n_q_heads;
+  float qscale;     // sm_scale * log2(e): scores are kept in base-2 units
+  int out_fp32;
+};
+
+hipError_t launch_encode(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,
+                         const PerSeq& seq, int max_records, hipStream_t s);
+hipError_t launch_append(uint8_t* buf, const Layout& L, const void* k, const void* v, hipStream_t s);
+hipError_t launch_window_fill(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,
+                              const PerSeq& seq, hipStream_t s);
+hipError_t launch_lengths_fill(uint8_t* buf, const Layout& L, const PerSeq& seq, hipStream_t s);
+
+hipError_t launch_decode_split(const uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q,
+                               float* ws, hipStream_t s);
+hipError_t launch_decode_merge(const uint8_t* buf, const Layout& L, const DecodeShape& ds, const float* ws,
+                               void* out, hipStream_t s);
+
+}  // namespace kvq

@@ -1,0 +1,443 @@
+// kvq.cpp - host side of the C ABI declared in include/kvq.h.
+//
+// Validation happens here, on the host, before any launch; lengths are mirrored on the
+// host (every change is decided here) so capacity checks and decode geometry never need a
+// device synchronisation. The device copy of the lengths is what the kernels read.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/kvq.h"
+#include "kernels.h"
+#include "layout.h"
+
+using kvq::Layout;
+using kvq::PerSeq;
+
+struct kvq_cache {
+  kvq_config cfg;
+  Layout L;
+  uint8_t* buf;
+  size_t bytes;
+  std::vector<int32_t> nq, nr;  // host mirror of the lengths, per sequence
+  bool dev_ready;               // device lengths have been written at least once
+  bool profiling;
+  std::vector<hipEvent_t> ev;   // begin/end pairs
+  size_t ev_used;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+kvq_status fail(kvq_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+kvq_status fail(kvq_status st, const char* fmt, ...) {
+  char msg[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(msg, sizeof msg, fmt, ap);
+  va_end(ap);
+  g_err = msg;
+  return st;
+}
+
+kvq_status ok() {
+  g_err.clear();
+  return KVQ_OK;
+}
+
+kvq_status hip_fail(hipError_t e, const char* what) {
+  return fail(KVQ_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kMaxResidual = 256;
+constexpr int kMaxProfilePairs = 4096;
+constexpr int kTargetWorkgroups = 1024;  // ~4 workgroups (16 waves) per CU on 256 CUs
+
+kvq_status check_config(const kvq_config* c) {
+  if (!c) return fail(KVQ_E_INVALID, "config is NULL");
+  if (c->batch < 1 || c->batch > KVQ_MAX_BATCH)
+    return fail(KVQ_E_INVALID, "batch must be in [1, %d], got %d", KVQ_MAX_BATCH, c->batch);
+  if (c->n_kv_heads < 1) return fail(KVQ_E_INVALID, "n_kv_heads must be >= 1");
+  if (c->n_q_heads < c->n_kv_heads || c->n_q_heads % c->n_kv_heads)
+    return fail(KVQ_E_INVALID, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", c->n_q_heads, c->n_kv_heads);
+  const int G = c->n_q_heads / c->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(KVQ_E_UNSUPPORTED, "query heads per KV head must be 1, 2, 4 or 8, got %d", G);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(KVQ_E_UNSUPPORTED, "head_dim must be 64 or 128, got %d", c->head_dim);
+  for (int bits : {c->key_bits, c->value_bits})
+    if (bits != 2 && bits != 4 && bits != 8)
+      return fail(KVQ_E_UNSUPPORTED, "bit widths must be 2, 4 or 8, got %d", bits);
+  if (c->group != kvq::kGroup) return fail(KVQ_E_UNSUPPORTED, "group size must be 32, got %d", c->group);
+  if (c->residual < kvq::kGroup || c->residual > kMaxResidual || c->residual % kvq::kGroup)
+    return fail(KVQ_E_INVALID, "residual must be a multiple of 32 in [32, %d], got %d", kMaxResidual, c->residual);
+  if (c->max_tokens < kvq::kGroup || c->max_tokens % kvq::kGroup)
+    return fail(KVQ_E_INVALID, "max_tokens must be a positive multiple of 32, got %d", c->max_tokens);
+  if (c->max_tokens > (1 << 26)) return fail(KVQ_E_INVALID, "max_tokens above 2^26");
+  return ok();
+}
+
+Layout make_layout(const kvq_config* c) {
+  Layout L;
+  L.init(c->batch, c->n_kv_heads, c->head_dim, c->key_bits, c->value_bits, c->residual, c->max_tokens);
+  return L;
+}
+
+int units_of(int nq, int nr) { return nq / kvq::kGroup + (nr + kvq::kGroup - 1) / kvq::kGroup; }
+
+// Largest split count the automatic choice can produce.
+int max_auto_splits(const kvq_config* c) {
+  const int units_cap = c->max_tokens / kvq::kGroup + c->residual / kvq::kGroup;
+  return (units_cap + 3) / 4;
+}
+
+// Device check: the current HIP device must be a gfx950.
+kvq_status check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KVQ_E_NODEVICE, "no HIP device: %s", hipGetErrorString(e));
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return fail(KVQ_E_NODEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(KVQ_E_NODEVICE, "device %d is %s, this library is built for gfx950", dev, prop.gcnArchName);
+  return ok();
+}
+
+kvq_status ensure_ready(kvq_cache* c, hipStream_t s) {
+  kvq_status st = check_device();
+  if (st != KVQ_OK) return st;
+  if (!c->dev_ready) {
+    PerSeq z;
+    memset(&z, 0, sizeof z);
+    hipError_t e = kvq::launch_lengths_fill(c->buf, c->L, z, s);
+    if (e != hipSuccess) return hip_fail(e, "zeroing lengths");
+    c->dev_ready = true;
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_probe(int32_t* has_gfx950) {
+  if (!has_gfx950) return fail(KVQ_E_INVALID, "has_gfx950 is NULL");
+  *has_gfx950 = 0;
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess) {
+    (void)hipGetLastError();
+    return ok();
+  }
+  for (int d = 0; d < n; ++d) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, d) == hipSuccess && strncmp(prop.gcnArchName, "gfx950", 6) == 0) {
+      *has_gfx950 = 1;
+      break;
+    }
+  }
+  return ok();
+}
+
+kvq_status kvq_config_check(const kvq_config* cfg) { return check_config(cfg); }
+
+size_t kvq_cache_bytes(const kvq_config* cfg) {
+  if (check_config(cfg) != KVQ_OK) return 0;
+  return size_t(make_layout(cfg).total);
+}
+
+kvq_status kvq_layout(const kvq_config* cfg, kvq_layout_info* out) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (!out) return fail(KVQ_E_INVALID, "out is NULL");
+  const Layout L = make_layout(cfg);
+  out->lengths_offset = L.len_off;
+  out->records_offset = L.rec_off;
+  out->record_bytes = L.rec_bytes;
+  out->rec_key_codes = 0;
+  out->rec_value_codes = kvq::rec_off_vcodes(L.D, L.bk);
+  out->rec_key_params = kvq::rec_off_kparams(L.D, L.bk, L.bv);
+  out->rec_value_params = kvq::rec_off_vparams(L.D, L.bk, L.bv);
+  out->window_k_offset = L.wk_off;
+  out->window_v_offset = L.wv_off;
+  out->total_bytes = L.total;
+  return ok();
+}
+
+size_t kvq_workspace_bytes(const kvq_config* cfg, int32_t n_split) {
+  if (check_config(cfg) != KVQ_OK || n_split < 0) return 0;
+  const int ns = n_split > 0 ? n_split : max_auto_splits(cfg);
+  return size_t(cfg->batch) * cfg->n_q_heads * ns * (cfg->head_dim + 4) * sizeof(float);
+}
+
+kvq_status kvq_cache_create(const kvq_config* cfg, void* dev_buf, size_t bytes, kvq_cache** out) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (!out) return fail(KVQ_E_INVALID, "out is NULL");
+  *out = nullptr;
+  if (!dev_buf) return fail(KVQ_E_INVALID, "device buffer is NULL");
+  if (reinterpret_cast<uintptr_t>(dev_buf) % 256) return fail(KVQ_E_INVALID, "device buffer must be 256-byte aligned");
+  const Layout L = make_layout(cfg);
+  if (bytes < L.total)
+    return fail(KVQ_E_INVALID, "device buffer holds %zu bytes, the cache needs %llu", bytes,
+                (unsigned long long)L.total);
+  kvq_cache* c = new (std::nothrow) kvq_cache();
+  if (!c) return fail(KVQ_E_INVALID, "out of host memory");
+  c->cfg = *cfg;
+  c->L = L;
+  c->buf = static_cast<uint8_t*>(dev_buf);
+  c->bytes = bytes;
+  c->nq.assign(cfg->batch, 0);
+  c->nr.assign(cfg->batch, 0);
+  c->dev_ready = false;
+  c->profiling = false;
+  c->ev_used = 0;
+  *out = c;
+  return ok();
+}
+
+void kvq_cache_destroy(kvq_cache* cache) {
+  if (!cache) return;
+  for (hipEvent_t e : cache->ev) (void)hipEventDestroy(e);
+  delete cache;
+}
+
+kvq_status kvq_reset(kvq_cache* c, void* stream) {
+  if (!c) return fail(KVQ_E_INVALID, "cache is NULL");
+  kvq_status st = check_device();
+  if (st != KVQ_OK) return st;
+  PerSeq z;
+  memset(&z, 0, sizeof z);
+  hipError_t e = kvq::launch_lengths_fill(c->buf, c->L, z, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "reset");
+  std::fill(c->nq.begin(), c->nq.end(), 0);
+  std::fill(c->nr.begin(), c->nr.end(), 0);
+  c->dev_ready = true;
+  return ok();
+}
+
+kvq_status kvq_cache_lengths(const kvq_cache* c, int32_t* n_quantized, int32_t* n_window) {
+  if (!c) return fail(KVQ_E_INVALID, "cache is NULL");
+  for (int b = 0; b < c->cfg.batch; ++b) {
+    if (n_quantized) n_quantized[b] = c->nq[b];
+    if (n_window) n_window[b] = c->nr[b];
+  }
+  return ok();
+}
+
+kvq_status kvq_encode(kvq_cache* c, const void* K, const void* V, int64_t ld_tok, const int32_t* n_tok,
+                      void* stream) {
+  if (!c) return fail(KVQ_E_INVALID, "cache is NULL");
+  if (!n_tok) return fail(KVQ_E_INVALID, "n_tok is NULL");
+  int max_rec = 0, max_tok = 0;
+  for (int b = 0; b < c->cfg.batch; ++b) {
+    const int n = n_tok[b];
+    if (n < 0 || n % kvq::kGroup)
+      return fail(KVQ_E_INVALID, "n_tok[%d] = %d is not a non-negative multiple of 32", b, n);
+    if (n && c->nr[b]) return fail(KVQ_E_INVALID, "sequence %d has %d window tokens; encode needs an empty window", b, c->nr[b]);
+    if (int64_t(c->nq[b]) + n > c->cfg.max_tokens)
+      return fail(KVQ_E_CAPACITY, "sequence %d: %d + %d tokens exceed max_tokens %d", b, c->nq[b], n, c->cfg.max_tokens);
+    max_rec = std::max(max_rec, n / kvq::kGroup);
+    max_tok = std::max(max_tok, n);
+  }
+  if (max_tok == 0) return ok();
+  if (!K || !V) return fail(KVQ_E_INVALID, "K or V is NULL");
+  if (ld_tok < max_tok) return fail(KVQ_E_INVALID, "ld_tok %lld is below the longest block %d", (long long)ld_tok, max_tok);
+  if ((reinterpret_cast<uintptr_t>(K) | reinterpret_cast<uintptr_t>(V)) % 16)
+    return fail(KVQ_E_INVALID, "K and V must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  kvq_status st = ensure_ready(c, s);
+  if (st != KVQ_OK) return st;
+  PerSeq enc, len;
+  memset(&enc, 0, sizeof enc);
+  memset(&len, 0, sizeof len);
+  for (int b = 0; b < c->cfg.batch; ++b) {
+    enc.a[b] = c->nq[b] / kvq::kGroup;
+    enc.b[b] = n_tok[b] / kvq::kGroup;
+    len.a[b] = c->nq[b] + n_tok[b];
+    len.b[b] = c->nr[b];
+  }
+  hipError_t e = kvq::launch_encode(c->buf, c->L, K, V, ld_tok, enc, max_rec, s);
+  if (e != hipSuccess) return hip_fail(e, "encode launch");
+  e = kvq::launch_lengths_fill(c->buf, c->L, len, s);
+  if (e != hipSuccess) return hip_fail(e, "lengths launch");
+  for (int b = 0; b < c->cfg.batch; ++b) c->nq[b] += n_tok[b];
+  return ok();
+}
+
+kvq_status kvq_prefill(kvq_cache* c, const void* K, const void* V, int64_t ld_tok, const int32_t* seq_len,
+                       void* stream) {
+  if (!c) return fail(KVQ_E_INVALID, "cache is NULL");
+  if (!seq_len) return fail(KVQ_E_INVALID, "seq_len is NULL");
+  const int R = c->cfg.residual;
+  int max_rec = 0, max_S = 0;
+  PerSeq enc, win;
+  memset(&enc, 0, sizeof enc);
+  memset(&win, 0, sizeof win);
+  for (int b = 0; b < c->cfg.batch; ++b) {
+    const int S = seq_len[b];
+    if (S < 0) return fail(KVQ_E_INVALID, "seq_len[%d] = %d is negative", b, S);
+    if (c->nq[b] || c->nr[b]) return fail(KVQ_E_INVALID, "sequence %d is not empty; prefill needs an empty cache", b);
+    if (S > c->cfg.max_tokens) return fail(KVQ_E_CAPACITY, "seq_len[%d] = %d exceeds max_tokens %d", b, S, c->cfg.max_tokens);
+    const int nr = S ? (S - 1) % R + 1 : 0;
+    const int nq = S - nr;
+    enc.a[b] = 0;
+    enc.b[b] = nq / kvq::kGroup;
+    win.a[b] = nq;
+    win.b[b] = nr;
+    max_rec = std::max(max_rec, nq / kvq::kGroup);
+    max_S = std::max(max_S, S);
+  }
+  if (max_S && (!K || !V)) return fail(KVQ_E_INVALID, "K or V is NULL");
+  if (ld_tok < max_S) return fail(KVQ_E_INVALID, "ld_tok %lld is below the longest sequence %d", (long long)ld_tok, max_S);
+  if ((reinterpret_cast<uintptr_t>(K) | reinterpret_cast<uintptr_t>(V)) % 16)
+    return fail(KVQ_E_INVALID, "K and V must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  kvq_status st = check_device();
+  if (st != KVQ_OK) return st;
+  if (max_rec) {
+    hipError_t e = kvq::launch_encode(c->buf, c->L, K, V, ld_tok, enc, max_rec, s);
+    if (e != hipSuccess) return hip_fail(e, "encode launch");
+  }
+  hipError_t e = kvq::launch_window_fill(c->buf, c->L, K, V, ld_tok, win, s);  // also writes every length
+  if (e != hipSuccess) return hip_fail(e, "window launch");
+  c->dev_ready = true;
+  for (int b = 0; b < c->cfg.batch; ++b) {
+    c->nq[b] = win.a[b];
+    c->nr[b] = win.b[b];
+  }
+  return ok();
+}
+
+kvq_status kvq_append(kvq_cache* c, const void* k_tok, const void* v_tok, void* stream) {
+  if (!c) return fail(KVQ_E_INVALID, "cache is NULL");
+  if (!k_tok || !v_tok) return fail(KVQ_E_INVALID, "k_tok or v_tok is NULL");
+  for (int b = 0; b < c->cfg.batch; ++b)
+    if (int64_t(c->nq[b]) + c->nr[b] + 1 > c->cfg.max_tokens)
+      return fail(KVQ_E_CAPACITY, "sequence %d is full (%d tokens)", b, c->cfg.max_tokens);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  kvq_status st = ensure_ready(c, s);
+  if (st != KVQ_OK) return st;
+  hipError_t e = kvq::launch_append(c->buf, c->L, k_tok, v_tok, s);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  for (int b = 0; b < c->cfg.batch; ++b) {
+    if (c->nr[b] == c->cfg.residual) {
+      c->nq[b] += c->cfg.residual;
+      c->nr[b] = 0;
+    }
+    c->nr[b] += 1;
+  }
+  return ok();
+}
+
+kvq_status kvq_decode_attend(kvq_cache* c, const void* q, void* out, int32_t out_fp32, float sm_scale,
+                             void* workspace, size_t ws_bytes, int32_t n_split, void* stream) {
+  if (!c) return fail(KVQ_E_INVALID, "cache is NULL");
+  if (!q || !out) return fail(KVQ_E_INVALID, "q or out is NULL");
+  if (!workspace) return fail(KVQ_E_WORKSPACE, "workspace is NULL");
+  if (n_split < 0) return fail(KVQ_E_INVALID, "n_split must be >= 0");
+  if (!std::isfinite(sm_scale)) return fail(KVQ_E_INVALID, "sm_scale is not finite");
+  const kvq_config& cfg = c->cfg;
+  int max_units = 0;
+  int64_t total_units = 0;
+  for (int b = 0; b < cfg.batch; ++b) {
+    if (c->nq[b] + c->nr[b] == 0) return fail(KVQ_E_INVALID, "sequence %d is empty", b);
+    const int u = units_of(c->nq[b], c->nr[b]);
+    max_units = std::max(max_units, u);
+    total_units += int64_t(u) * cfg.n_kv_heads;
+  }
+  int chunk;
+  if (n_split > 0) {
+    chunk = (max_units + n_split - 1) / n_split;
+  } else {
+    chunk = int((total_units + kTargetWorkgroups - 1) / kTargetWorkgroups);
+    chunk = std::max(4, (chunk + 3) / 4 * 4);
+  }
+  const int ns = (max_units + chunk - 1) / chunk;
+  const size_t need = size_t(cfg.batch) * cfg.n_q_heads * ns * (cfg.head_dim + 4) * sizeof(float);
+  if (ws_bytes < need) return fail(KVQ_E_WORKSPACE, "workspace holds %zu bytes, this call needs %zu", ws_bytes, need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  kvq_status st = ensure_ready(c, s);
+  if (st != KVQ_OK) return st;
+  kvq::DecodeShape ds;
+  ds.n_split = ns;
+  ds.chunk = chunk;
+  ds.G = cfg.n_q_heads / cfg.n_kv_heads;
+  ds.n_q_heads = cfg.n_q_heads;
+  ds.qscale = sm_scale * 1.4426950408889634f;
+  ds.out_fp32 = out_fp32 ? 1 : 0;
+  float* ws = static_cast<float*>(workspace);
+  hipError_t e;
+  const bool prof = c->profiling;
+  if (prof) {
+    if (c->ev_used + 2 > c->ev.size()) {
+      if (c->ev.size() >= size_t(2 * kMaxProfilePairs)) return fail(KVQ_E_INVALID, "profile buffer full; call kvq_profile_read");
+      for (int i = 0; i < 2; ++i) {
+        hipEvent_t ev;
+        e = hipEventCreate(&ev);
+        if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+        c->ev.push_back(ev);
+      }
+    }
+    e = hipEventRecord(c->ev[c->ev_used], s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  e = kvq::launch_decode_split(c->buf, c->L, ds, q, ws, s);
+  if (e != hipSuccess) return hip_fail(e, "decode split launch");
+  if (prof) {
+    e = hipEventRecord(c->ev[c->ev_used + 1], s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    c->ev_used += 2;
+  }
+  e = kvq::launch_decode_merge(c->buf, c->L, ds, ws, out, s);
+  if (e != hipSuccess) return hip_fail(e, "decode merge launch");
+  return ok();
+}
+
+kvq_status kvq_profile_enable(kvq_cache* c, int32_t enable) {
+  if (!c) return fail(KVQ_E_INVALID, "cache is NULL");
+  c->profiling = enable != 0;
+  return ok();
+}
+
+kvq_status kvq_profile_read(kvq_cache* c, double* total_ms, int64_t* count) {
+  if (!c || !total_ms || !count) return fail(KVQ_E_INVALID, "NULL argument");
+  double tot = 0;
+  for (size_t i = 0; i + 1 < c->ev_used; i += 2) {
+    hipError_t e = hipEventSynchronize(c->ev[i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float ms = 0;
+    e = hipEventElapsedTime(&ms, c->ev[i], c->ev[i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    tot += ms;
+  }
+  *total_ms = tot;
+  *count = int64_t(c->ev_used / 2);
+  c->ev_used = 0;
+  return ok();
+}
+
+const char* kvq_last_error(void) { return g_err.c_str(); }
+
+const char* kvq_status_string(kvq_status st) {
+  switch (st) {
+    case KVQ_OK: return "KVQ_OK";
+    case KVQ_E_INVALID: return "KVQ_E_INVALID";
+    case KVQ_E_UNSUPPORTED: return "KVQ_E_UNSUPPORTED";
+    case KVQ_E_CAPACITY: return "KVQ_E_CAPACITY";
+    case KVQ_E_WORKSPACE: return "KVQ_E_WORKSPACE";
+    case KVQ_E_NODEVICE: return "KVQ_E_NODEVICE";
+    case KVQ_E_HIP: return "KVQ_E_HIP";
+    default: return "KVQ_E_UNKNOWN";
+  }
+}
+
+}  // extern "C"

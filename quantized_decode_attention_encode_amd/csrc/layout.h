@@ -1,0 +1,78 @@
+// layout.h - byte layout of the quantized cache in HBM (host and device).
+//
+// One cache buffer per layer:
+//   lengths  int32 [B][H_kv][2]                 (quantized tokens, window tokens)
+//   records  [B][H_kv][max_tokens/32][record]   one record per group of 32 quantized tokens
+//   window_k fp16  [B][H_kv][R][D]              the newest tokens, unquantized
+//   window_v fp16  [B][H_kv][R][D]
+// Every region starts on a 256-byte boundary.
+//
+// A record holds everything decode needs for 32 tokens, so one group streams from one
+// contiguous 4*D*(bk+bv+2)-byte block (3 KiB at D=128, 2/2 bits):
+//   key codes    4*D*bk bytes  u32 words [P=t/2 : 16][Q : 4][tp=t%2 : 2][D*bk/128 words]
+//                the words of (P, Q, tp) carry the codes of token t = 2P+tp for channels
+//                Q*D/4 .. Q*D/4 + D/4 - 1, channel c' (within the quarter) at bit c'*bk
+//                (little-endian across the words). A decode lane (P, Q) reads its two
+//                tokens' quarter as one contiguous 8*D*bk/64-byte piece, and the 64 lanes
+//                of a wave read the whole block contiguously.
+//   value codes  4*D*bv bytes  u32 words [d : D][bv words]: the 32 tokens of channel d,
+//                token t at bit t*bv. A lane owning channels d..d+D/64-1 reads one
+//                contiguous piece.
+//   key params   D dwords      [d]: (scale fp16 in bits 0-15, zero fp16 in bits 16-31)
+//                of the key group (32 tokens) of channel d.
+//   value params D dwords      [t/2][k : D/32][t%2]: (scale, zero) of value group k
+//                (channels 32k..32k+31) of token t.
+#pragma once
+#include <stdint.h>
+
+#ifdef __HIPCC__
+#define KVQ_HD __host__ __device__
+#else
+#define KVQ_HD
+#endif
+
+namespace kvq {
+
+constexpr int kGroup = 32;     // tokens per key group == channels per value group
+constexpr int kMaxBatch = 256;
+
+KVQ_HD constexpr uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+KVQ_HD constexpr uint64_t key_code_bytes(int D, int bk) { return 4ull * D * bk; }
+KVQ_HD constexpr uint64_t value_code_bytes(int D, int bv) { return 4ull * D * bv; }
+KVQ_HD constexpr uint64_t param_bytes(int D) { return 4ull * D; }
+KVQ_HD constexpr uint64_t record_bytes(int D, int bk, int bv) { return 4ull * D * (bk + bv + 2); }
+KVQ_HD constexpr uint64_t rec_off_vcodes(int D, int bk) { return key_code_bytes(D, bk); }
+KVQ_HD constexpr uint64_t rec_off_kparams(int D, int bk, int bv) {
+  return key_code_bytes(D, bk) + value_code_bytes(D, bv);
+}
+KVQ_HD constexpr uint64_t rec_off_vparams(int D, int bk, int bv) {
+  return rec_off_kparams(D, bk, bv) + param_bytes(D);
+}
+
+// Offsets of the regions of one cache buffer.
+struct Layout {
+  int B, Hkv, D, bk, bv, R, max_groups;
+  uint64_t len_off, rec_off, rec_bytes, wk_off, wv_off, total;
+
+  KVQ_HD void init(int B_, int Hkv_, int D_, int bk_, int bv_, int R_, int max_tokens) {
+    B = B_; Hkv = Hkv_; D = D_; bk = bk_; bv = bv_; R = R_;
+    max_groups = max_tokens / kGroup;
+    rec_bytes = record_bytes(D, bk, bv);
+    len_off = 0;
+    rec_off = align256(uint64_t(B) * Hkv * 2 * sizeof(int32_t));
+    wk_off = align256(rec_off + uint64_t(B) * Hkv * max_groups * rec_bytes);
+    uint64_t wbytes = uint64_t(B) * Hkv * R * D * 2;
+    wv_off = align256(wk_off + wbytes);
+    total = align256(wv_off + wbytes);
+  }
+  // record j of (b, h)
+  KVQ_HD uint64_t record(int b, int h, int j) const {
+    return rec_off + ((uint64_t(b) * Hkv + h) * max_groups + j) * rec_bytes;
+  }
+  // first window slot of (b, h), in bytes from the buffer start (K; V at wv_off)
+  KVQ_HD uint64_t window(int b, int h) const { return (uint64_t(b) * Hkv + h) * R * D * 2; }
+  KVQ_HD uint64_t lengths(int b, int h) const { return len_off + (uint64_t(b) * Hkv + h) * 8; }
+};
+
+}  // namespace kvq

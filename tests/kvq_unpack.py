@@ -1,0 +1,94 @@
+"""Test-side reader of the cache buffer: raw device bytes -> logical arrays.
+
+Written from the layout description (records of 32 tokens; key codes as
+[P=t/2][quarter][t%2][words] with channel c' of the quarter at bit c'*bk, value codes as
+[channel][words] with token t at bit t*bv, key params [channel], value params
+[t/2][value group][t%2], fp16 (scale, zero) pairs with the scale in the low half). It shares
+no code with the HIP library; parity tests compare its output with the CPU oracle.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def align256(x: int) -> int:
+    return (x + 255) // 256 * 256
+
+
+def offsets(B, Hkv, D, bk, bv, R, max_tokens):
+    max_groups = max_tokens // 32
+    rec = 4 * D * (bk + bv + 2)
+    o = {"lengths": 0}
+    o["records"] = align256(B * Hkv * 2 * 4)
+    o["record_bytes"] = rec
+    o["rec_key_codes"] = 0
+    o["rec_value_codes"] = 4 * D * bk
+    o["rec_key_params"] = 4 * D * (bk + bv)
+    o["rec_value_params"] = 4 * D * (bk + bv) + 4 * D
+    o["window_k"] = align256(o["records"] + B * Hkv * max_groups * rec)
+    wbytes = B * Hkv * R * D * 2
+    o["window_v"] = align256(o["window_k"] + wbytes)
+    o["total"] = align256(o["window_v"] + wbytes)
+    o["max_groups"] = max_groups
+    return o
+
+
+def _fields(u8: np.ndarray, nbits: int) -> np.ndarray:
+    """Little-endian bit strings along the last axis (bytes) -> unsigned nbits-wide fields."""
+    bits = np.unpackbits(u8, axis=-1, bitorder="little")
+    bits = bits.reshape(*bits.shape[:-1], bits.shape[-1] // nbits, nbits).astype(np.uint16)
+    return (bits << np.arange(nbits, dtype=np.uint16)).sum(-1).astype(np.uint8)
+
+
+def unpack_records(recs: np.ndarray, D: int, bk: int, bv: int):
+    """Records as bytes [n, record_bytes] -> logical arrays covering their 32*n tokens."""
+    n = recs.shape[0]
+    o_vc = 4 * D * bk
+    o_kp = o_vc + 4 * D * bv
+    o_vp = o_kp + 4 * D
+    # key codes [P][Q][tp][quarter bytes] -> [n, P, Q, tp, D/4]
+    kc = _fields(recs[:, :o_vc].reshape(n, 16, 4, 2, D * bk // 32), bk)
+    kc = kc.transpose(0, 1, 3, 2, 4).reshape(n * 32, D)  # token 2P+tp, channel Q*D/4 + c
+    # value codes [d][bytes of 32 tokens] -> [n, d, 32]
+    vc = _fields(recs[:, o_vc:o_kp].reshape(n, D, 4 * bv), bv).transpose(0, 2, 1).reshape(n * 32, D)
+    kp = np.ascontiguousarray(recs[:, o_kp:o_vp]).view("<u2").reshape(n, D, 2)
+    ks = kp[..., 0].view(np.float16)
+    kz = kp[..., 1].view(np.float16)
+    NKG = D // 32
+    vp = np.ascontiguousarray(recs[:, o_vp:o_vp + 4 * D]).view("<u2").reshape(n, 16, NKG, 2, 2)
+    vp = vp.transpose(0, 1, 3, 2, 4).reshape(n * 32, NKG, 2)  # token 2P+tp
+    vs = vp[..., 0].view(np.float16)
+    vz = vp[..., 1].view(np.float16)
+    return {"kc": kc, "ks": ks.reshape(n, D), "kz": kz.reshape(n, D), "vc": vc, "vs": vs, "vz": vz}
+
+
+def unpack_record(rec: np.ndarray, D: int, bk: int, bv: int):
+    return unpack_records(rec.reshape(1, -1), D, bk, bv)
+
+
+def lengths(buf: np.ndarray, B: int, Hkv: int) -> np.ndarray:
+    return buf[: B * Hkv * 8].view("<i4").reshape(B, Hkv, 2).copy()
+
+
+def unpack_sequence(buf: np.ndarray, cfg: dict, b: int, h: int, n_q: int | None = None, n_r: int | None = None):
+    """Logical arrays of (b, h): codes/params of the quantized region plus the window.
+
+    ``buf`` is the whole cache buffer as uint8 on the host; cfg has B, Hkv, D, bk, bv, R,
+    max_tokens. Lengths default to the ones stored in the buffer.
+    """
+    B, Hkv, D, bk, bv, R = (cfg[k] for k in ("B", "Hkv", "D", "bk", "bv", "R"))
+    o = offsets(B, Hkv, D, bk, bv, R, cfg["max_tokens"])
+    L = lengths(buf, B, Hkv)
+    n_q = int(L[b, h, 0]) if n_q is None else n_q
+    n_r = int(L[b, h, 1]) if n_r is None else n_r
+    ng = n_q // 32
+    start = o["records"] + (b * Hkv + h) * o["max_groups"] * o["record_bytes"]
+    recs = buf[start:start + ng * o["record_bytes"]].reshape(ng, o["record_bytes"])
+    cat = unpack_records(recs, D, bk, bv)
+    w0 = ((b * Hkv + h) * R) * D * 2
+    wk = buf[o["window_k"] + w0:o["window_k"] + w0 + R * D * 2].view(np.float16).reshape(R, D)[:n_r]
+    wv = buf[o["window_v"] + w0:o["window_v"] + w0 + R * D * 2].view(np.float16).reshape(R, D)[:n_r]
+    cat["wk"] = wk.copy()
+    cat["wv"] = wv.copy()
+    cat["n_q"], cat["n_r"] = n_q, n_r
+    return cat

@@ -1,0 +1,188 @@
+"""CPU-side checks of the C ABI: the library loads, exports every declared entry point, and
+rejects bad arguments on the host before anything is launched (no GPU needed).
+
+Validation mirrors the pages' fail-loudly configuration errors ("veloxquant_mlx.cache
+package", KVCacheBuilder / KVCacheFactory raising QuantizerConfigError).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from quantized_decode_attention_encode_amd import _lib
+from quantized_decode_attention_encode_amd._lib import (KVQ_E_CAPACITY, KVQ_E_INVALID, KVQ_E_NODEVICE,
+                                                        KVQ_E_UNSUPPORTED, KVQ_E_WORKSPACE, KVQ_OK, Config,
+                                                        LayoutInfo, lib)
+from tests import kvq_unpack
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+torch_cuda = False
+try:
+    import torch
+
+    torch_cuda = torch.cuda.is_available()
+except Exception:  # pragma: no cover
+    pass
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", text)))
+
+
+def cfg(**kw):
+    base = dict(batch=2, n_kv_heads=4, n_q_heads=8, head_dim=128, key_bits=2, value_bits=4, group=32,
+                residual=32, max_tokens=1024)
+    base.update(kw)
+    return Config(*(base[f] for f, _ in Config._fields_))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"kvq_encode", "kvq_append", "kvq_decode_attend"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (kvq_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(lib, n)
+    assert set(names) == set(_lib.EXPORTED)
+
+
+def test_probe_without_gpu_reports_absence():
+    has = ctypes.c_int32(7)
+    assert lib.kvq_probe(ctypes.byref(has)) == KVQ_OK
+    if not torch_cuda:
+        assert has.value == 0
+    assert lib.kvq_probe(None) == KVQ_E_INVALID
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("batch", 0, KVQ_E_INVALID), ("batch", 257, KVQ_E_INVALID), ("n_kv_heads", 0, KVQ_E_INVALID),
+    ("n_q_heads", 6, KVQ_E_INVALID), ("n_q_heads", 12, KVQ_E_UNSUPPORTED), ("head_dim", 96, KVQ_E_UNSUPPORTED),
+    ("key_bits", 3, KVQ_E_UNSUPPORTED), ("value_bits", 1, KVQ_E_UNSUPPORTED), ("group", 64, KVQ_E_UNSUPPORTED),
+    ("residual", 48, KVQ_E_INVALID), ("residual", 0, KVQ_E_INVALID), ("residual", 288, KVQ_E_INVALID),
+    ("max_tokens", 1000, KVQ_E_INVALID), ("max_tokens", 0, KVQ_E_INVALID),
+])
+def test_config_validation(field, value, status):
+    c = cfg(**{field: value})
+    assert lib.kvq_config_check(ctypes.byref(c)) == status
+    assert lib.kvq_last_error()  # a message is set
+    assert lib.kvq_cache_bytes(ctypes.byref(c)) == 0
+    assert lib.kvq_workspace_bytes(ctypes.byref(c), 0) == 0
+
+
+@pytest.mark.parametrize("D,bk,bv,R,B,H", [(128, 2, 2, 32, 1, 32), (64, 2, 2, 32, 1, 8), (128, 2, 4, 32, 16, 8),
+                                           (128, 8, 4, 64, 3, 2), (64, 4, 8, 128, 5, 3)])
+def test_layout_matches_independent_formula(D, bk, bv, R, B, H):
+    c = cfg(batch=B, n_kv_heads=H, n_q_heads=H, head_dim=D, key_bits=bk, value_bits=bv, residual=R, max_tokens=2048)
+    info = LayoutInfo()
+    assert lib.kvq_layout(ctypes.byref(c), ctypes.byref(info)) == KVQ_OK
+    o = kvq_unpack.offsets(B, H, D, bk, bv, R, 2048)
+    assert info.lengths_offset == o["lengths"] and info.records_offset == o["records"]
+    assert info.record_bytes == o["record_bytes"] == 4 * D * (bk + bv + 2)
+    assert (info.rec_key_codes, info.rec_value_codes, info.rec_key_params, info.rec_value_params) == (
+        o["rec_key_codes"], o["rec_value_codes"], o["rec_key_params"], o["rec_value_params"])
+    assert info.window_k_offset == o["window_k"] and info.window_v_offset == o["window_v"]
+    assert info.total_bytes == o["total"] == lib.kvq_cache_bytes(ctypes.byref(c))
+    for off in (info.records_offset, info.window_k_offset, info.window_v_offset, info.total_bytes):
+        assert off % 256 == 0
+
+
+def test_record_is_three_kib_at_the_headline_shape():
+    # D=128, 2-bit keys and values: 1 KiB key codes + 1 KiB value codes + 512 B + 512 B params
+    assert kvq_unpack.offsets(1, 32, 128, 2, 2, 32, 65536)["record_bytes"] == 3072
+
+
+def test_workspace_bytes():
+    c = cfg()
+    assert lib.kvq_workspace_bytes(ctypes.byref(c), 5) == 2 * 8 * 5 * (128 + 4) * 4
+    assert lib.kvq_workspace_bytes(ctypes.byref(c), 0) >= lib.kvq_workspace_bytes(ctypes.byref(c), 9)
+    assert lib.kvq_workspace_bytes(ctypes.byref(c), -1) == 0
+
+
+FAKE = 0x7F0000000000  # never dereferenced: every call below fails before any launch
+
+
+def make_handle(c):
+    h = ctypes.c_void_p()
+    nbytes = lib.kvq_cache_bytes(ctypes.byref(c))
+    assert lib.kvq_cache_create(ctypes.byref(c), ctypes.c_void_p(FAKE), nbytes, ctypes.byref(h)) == KVQ_OK
+    return h
+
+
+def i32(*v):
+    return (ctypes.c_int32 * len(v))(*v)
+
+
+def test_create_rejects_bad_buffers():
+    c = cfg()
+    h = ctypes.c_void_p()
+    n = lib.kvq_cache_bytes(ctypes.byref(c))
+    assert lib.kvq_cache_create(ctypes.byref(c), None, n, ctypes.byref(h)) == KVQ_E_INVALID
+    assert lib.kvq_cache_create(ctypes.byref(c), ctypes.c_void_p(FAKE + 8), n, ctypes.byref(h)) == KVQ_E_INVALID
+    assert lib.kvq_cache_create(ctypes.byref(c), ctypes.c_void_p(FAKE), n - 1, ctypes.byref(h)) == KVQ_E_INVALID
+    assert not h.value
+    lib.kvq_cache_destroy(None)
+
+
+def test_host_side_errors_before_any_launch():
+    c = cfg(batch=2, max_tokens=256)
+    h = make_handle(c)
+    P = ctypes.c_void_p(FAKE)
+    try:
+        # encode: n_tok not a multiple of 32, negative, over capacity, ld_tok too small
+        assert lib.kvq_encode(h, P, P, 64, i32(32, 33), None) == KVQ_E_INVALID
+        assert lib.kvq_encode(h, P, P, 64, i32(-32, 0), None) == KVQ_E_INVALID
+        assert lib.kvq_encode(h, P, P, 512, i32(288, 0), None) == KVQ_E_CAPACITY
+        assert lib.kvq_encode(h, P, P, 16, i32(32, 0), None) == KVQ_E_INVALID
+        assert lib.kvq_encode(h, None, P, 64, i32(32, 0), None) == KVQ_E_INVALID
+        assert lib.kvq_encode(h, P, P, 64, None, None) == KVQ_E_INVALID
+        # nothing to do is fine without a device
+        assert lib.kvq_encode(h, P, P, 64, i32(0, 0), None) == KVQ_OK
+        # prefill: negative, over capacity, short ld_tok
+        assert lib.kvq_prefill(h, P, P, 64, i32(-1, 3), None) == KVQ_E_INVALID
+        assert lib.kvq_prefill(h, P, P, 300, i32(257, 3), None) == KVQ_E_CAPACITY
+        assert lib.kvq_prefill(h, P, P, 10, i32(11, 3), None) == KVQ_E_INVALID
+        # decode on an empty cache
+        ws = ctypes.c_void_p(FAKE)
+        assert lib.kvq_decode_attend(h, P, P, 0, 1.0, ws, 1 << 30, 0, None) == KVQ_E_INVALID
+        assert b"empty" in lib.kvq_last_error()
+        assert lib.kvq_decode_attend(h, P, P, 0, 1.0, None, 1 << 30, 0, None) == KVQ_E_WORKSPACE
+        assert lib.kvq_decode_attend(h, P, P, 0, float("nan"), ws, 1 << 30, 0, None) == KVQ_E_INVALID
+        assert lib.kvq_decode_attend(h, P, P, 0, 1.0, ws, 1 << 30, -2, None) == KVQ_E_INVALID
+        assert lib.kvq_append(h, None, P, None) == KVQ_E_INVALID
+        # lengths mirror
+        nq, nr = (ctypes.c_int32 * 2)(), (ctypes.c_int32 * 2)()
+        assert lib.kvq_cache_lengths(h, nq, nr) == KVQ_OK and list(nq) == [0, 0] and list(nr) == [0, 0]
+    finally:
+        lib.kvq_cache_destroy(h)
+
+
+@pytest.mark.skipif(torch_cuda, reason="checks the no-device path")
+def test_device_calls_fail_cleanly_without_a_gpu():
+    c = cfg(batch=1, n_kv_heads=1, n_q_heads=1, max_tokens=256)
+    h = make_handle(c)
+    P = ctypes.c_void_p(FAKE)
+    try:
+        assert lib.kvq_append(h, P, P, None) == KVQ_E_NODEVICE
+        assert lib.kvq_encode(h, P, P, 64, i32(32), None) == KVQ_E_NODEVICE
+        assert lib.kvq_prefill(h, P, P, 64, i32(40), None) == KVQ_E_NODEVICE
+        assert lib.kvq_reset(h, None) == KVQ_E_NODEVICE
+        # the host mirror did not move
+        nq, nr = (ctypes.c_int32 * 1)(), (ctypes.c_int32 * 1)()
+        lib.kvq_cache_lengths(h, nq, nr)
+        assert (nq[0], nr[0]) == (0, 0)
+    finally:
+        lib.kvq_cache_destroy(h)
+
+
+def test_status_strings():
+    for st, name in [(KVQ_OK, "KVQ_OK"), (KVQ_E_INVALID, "KVQ_E_INVALID"), (KVQ_E_CAPACITY, "KVQ_E_CAPACITY"),
+                     (KVQ_E_NODEVICE, "KVQ_E_NODEVICE"), (-99, "KVQ_E_UNKNOWN")]:
+        assert lib.kvq_status_string(st).decode() == name

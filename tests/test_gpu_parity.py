@@ -1,0 +1,215 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same inputs.
+
+Codes, scales and zeros must match bit for bit; attention must be within 2e-3 absolute
+and 1e-2 relative (per row, L2) of the fp64 oracle. Cases cover several records and a
+ragged tail, both head dims, every supported bit width, GQA, window-only sequences, the
+window flush, the encode call, split-count invariance and poisoned outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import kivi
+from quantized_decode_attention_encode_amd import (KVQCache, KVQError, kvq_append, kvq_decode_attend, kvq_encode,
+                                                   kvq_prefill, make_config, workloads)
+from tests.gpu_helpers import (assert_close, assert_state_equal, host_buffer, oracle_attend, oracle_prefill, say)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+SMALL = [
+    # name, B, Hq, Hkv, D, bk, bv, ragged lengths
+    ("d64-b22", 3, 4, 4, 64, 2, 2, (1, 300)),
+    ("d128-b22", 2, 4, 4, 128, 2, 2, (1, 300)),
+    ("d128-b24-gqa4", 3, 8, 2, 128, 2, 4, (1, 400)),
+    ("d128-b42-gqa2", 2, 4, 2, 128, 4, 2, (1, 200)),
+    ("d64-b44-gqa8", 2, 8, 1, 64, 4, 4, (1, 200)),
+    ("d128-b88", 2, 2, 2, 128, 8, 8, (1, 200)),
+    ("d64-b28", 2, 2, 2, 64, 2, 8, (1, 200)),
+    ("d128-b82", 2, 2, 2, 128, 8, 2, (1, 200)),
+]
+
+
+def make(case, seed=11, residual=32, seq_lens=None, max_tokens=1024):
+    name, B, Hq, Hkv, D, bk, bv, rag = case
+    wl = workloads.custom(name=name, batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, key_bits=bk, value_bits=bv,
+                          n_outlier=2, seed=seed, residual=residual, ragged=rag)
+    draw = workloads.Draw(wl, seq_lens=seq_lens)
+    cfg = make_config(B, Hkv, Hq, D, bk, bv, 32, residual, max_tokens)
+    return wl, draw, cfg
+
+
+def gpu_prefill(draw, cfg):
+    cache = KVQCache(cfg, device=DEV)
+    K, V, lens = draw.padded()
+    kvq_prefill(cache, torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV), lens)
+    return cache
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_prefill_encode_bit_exact_and_decode_close(case):
+    wl, draw, cfg = make(case)
+    say("case", case, "lens", draw.seq_lens)
+    cache = gpu_prefill(draw, cfg)
+    torch.cuda.synchronize()
+    seqs = oracle_prefill(draw, cfg.residual)
+    assert_state_equal(host_buffer(cache), cfg, seqs, case[0])
+    ref = oracle_attend(draw.q.astype(np.float64), seqs, wl)
+    q = torch.from_numpy(draw.q).to(DEV)
+    for n_split in (0, 1, 2, 7):
+        o32 = kvq_decode_attend(cache, q, out_fp32=True, n_split=n_split)
+        o16 = kvq_decode_attend(cache, q, n_split=n_split)
+        e32 = assert_close(o32.cpu().numpy(), ref, f"{case[0]} fp32 n_split={n_split}")
+        e16 = assert_close(o16.float().cpu().numpy(), ref, f"{case[0]} fp16 n_split={n_split}")
+        say(f"  n_split={n_split} fp32 err {e32} fp16 err {e16}")
+
+
+@pytest.mark.parametrize("case", SMALL[:3], ids=[c[0] for c in SMALL[:3]])
+def test_split_count_does_not_change_result(case):
+    wl, draw, cfg = make(case, seed=12)
+    cache = gpu_prefill(draw, cfg)
+    q = torch.from_numpy(draw.q).to(DEV)
+    outs = [kvq_decode_attend(cache, q, out_fp32=True, n_split=n).cpu().numpy() for n in (0, 1, 2, 3, 7, 64)]
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) < 2e-5
+
+
+def test_window_only_and_single_token_sequences():
+    case = ("edge", 4, 4, 4, 128, 2, 2, None)
+    wl, draw, cfg = make(case, seq_lens=[1, 5, 32, 33])
+    cache = gpu_prefill(draw, cfg)
+    seqs = oracle_prefill(draw, 32)
+    assert_state_equal(host_buffer(cache), cfg, seqs, "edge")
+    ref = oracle_attend(draw.q.astype(np.float64), seqs, wl)
+    out = kvq_decode_attend(cache, torch.from_numpy(draw.q).to(DEV), out_fp32=True)
+    assert_close(out.cpu().numpy(), ref, "edge")
+    # S <= R: exact attention over raw fp16 (no quantization at all)
+    for b in range(3):
+        for hq in range(4):
+            exact = kivi.attend(draw.q[b, hq], draw.K[b][hq].astype(np.float64), draw.V[b][hq].astype(np.float64))
+            assert np.max(np.abs(out.cpu().numpy()[b, hq] - exact)) < 2e-3
+
+
+@pytest.mark.parametrize("residual", [32, 64])
+def test_append_path_independence(residual):
+    case = ("append", 2, 8, 2, 128, 2, 4, None)
+    S_full = [200, 150]
+    wl, draw, cfg = make(case, seed=13, residual=residual, seq_lens=S_full)
+    # GPU: prefill S0 then append token by token; compare with GPU prefill(S) and the oracle
+    S0 = [37, 1]
+    K, V, _ = draw.padded()
+    Kt, Vt = torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV)
+    a = KVQCache(cfg, device=DEV)
+    kvq_prefill(a, Kt, Vt, S0)
+    n_app = 150 - 1
+    for t in range(n_app):
+        idx = [min(S0[b] + t, S_full[b] - 1) for b in range(2)]
+        k = torch.stack([Kt[b, :, idx[b]] for b in range(2)]).contiguous()
+        v = torch.stack([Vt[b, :, idx[b]] for b in range(2)]).contiguous()
+        kvq_append(a, k, v)
+    # sequence 1 is exactly S_full[1] long; sequence 0 took its tokens 37..185
+    seqs = {}
+    for b in range(2):
+        for h in range(2):
+            s = kivi.KiviSequence(128, 2, 4, 32, residual)
+            s.prefill(draw.K[b][h][:S0[b]], draw.V[b][h][:S0[b]])
+            for t in range(n_app):
+                i = min(S0[b] + t, S_full[b] - 1)
+                s.append(draw.K[b][h][i], draw.V[b][h][i])
+            seqs[(b, h)] = s
+    assert a.lengths() == ([s.n_q for s in (seqs[(0, 0)], seqs[(1, 0)])], [s.n_r for s in (seqs[(0, 0)], seqs[(1, 0)])])
+    assert_state_equal(host_buffer(a), cfg, seqs, "appended")
+    # the straight prefill of the same 150 tokens of sequence 1 gives the same bytes
+    b_cache = KVQCache(cfg, device=DEV)
+    kvq_prefill(b_cache, Kt, Vt, [S_full[0], S_full[1]])
+    one = oracle_prefill(draw, residual, pairs={(1, 0), (1, 1)})
+    assert_state_equal(host_buffer(b_cache), cfg, one, "prefill")
+    ref = oracle_attend(draw.q.astype(np.float64), seqs, wl)
+    out = kvq_decode_attend(a, torch.from_numpy(draw.q).to(DEV), out_fp32=True)
+    assert_close(out.cpu().numpy(), ref, "appended decode")
+
+
+def test_encode_call_then_appends():
+    case = ("encode", 2, 4, 4, 64, 2, 2, None)
+    wl, draw, cfg = make(case, seed=14, seq_lens=[160, 160])
+    K, V, _ = draw.padded()
+    Kt, Vt = torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV)
+    c = KVQCache(cfg, device=DEV)
+    kvq_encode(c, Kt[:, :, :64].contiguous(), Vt[:, :, :64].contiguous(), [64, 32])
+    kvq_encode(c, Kt[:, :, 64:128].contiguous(), Vt[:, :, 64:128].contiguous(), [64, 0])
+    assert c.lengths() == ([128, 32], [0, 0])
+    with pytest.raises(KVQError):
+        kvq_encode(c, Kt, Vt, [31, 0])
+    seqs = {}
+    for b, n in ((0, 128), (1, 32)):
+        for h in range(4):
+            s = kivi.KiviSequence(64, 2, 2, 32, 32)
+            s.encode(draw.K[b][h][:n], draw.V[b][h][:n])
+            seqs[(b, h)] = s
+    for t in range(20):
+        k = torch.stack([Kt[0, :, 128 + t], Kt[1, :, 32 + t]]).contiguous()
+        v = torch.stack([Vt[0, :, 128 + t], Vt[1, :, 32 + t]]).contiguous()
+        kvq_append(c, k, v)
+        for h in range(4):
+            seqs[(0, h)].append(draw.K[0][h][128 + t], draw.V[0][h][128 + t])
+            seqs[(1, h)].append(draw.K[1][h][32 + t], draw.V[1][h][32 + t])
+    assert_state_equal(host_buffer(c), cfg, seqs, "encode+append")
+    ref = oracle_attend(draw.q.astype(np.float64), seqs, wl)
+    assert_close(kvq_decode_attend(c, torch.from_numpy(draw.q).to(DEV), out_fp32=True).cpu().numpy(), ref, "enc")
+
+
+def test_gqa_equals_mha_with_replicated_kv():
+    case = ("gqa", 2, 8, 2, 128, 2, 2, None)
+    wl, draw, cfg = make(case, seed=15, seq_lens=[300, 77])
+    g = gpu_prefill(draw, cfg)
+    K, V, lens = draw.padded()
+    Kr = np.repeat(K, 4, axis=1)
+    Vr = np.repeat(V, 4, axis=1)
+    cfg_m = make_config(2, 8, 8, 128, 2, 2, 32, 32, 1024)
+    m = KVQCache(cfg_m, device=DEV)
+    kvq_prefill(m, torch.from_numpy(Kr).to(DEV), torch.from_numpy(Vr).to(DEV), lens)
+    q = torch.from_numpy(draw.q).to(DEV)
+    og = kvq_decode_attend(g, q, out_fp32=True).cpu().numpy()
+    om = kvq_decode_attend(m, q, out_fp32=True).cpu().numpy()
+    assert np.max(np.abs(og - om)) < 1e-5
+
+
+def test_poisoned_outputs_are_fully_written_and_runs_repeat_exactly():
+    case = ("poison", 3, 8, 4, 128, 2, 4, (1, 500))
+    wl, draw, cfg = make(case, seed=16)
+    c1 = gpu_prefill(draw, cfg)
+    c2 = KVQCache(cfg, device=DEV, buffer=torch.full((c1.buffer.numel(),), 0xFF, dtype=torch.uint8, device=DEV))
+    K, V, lens = draw.padded()
+    kvq_prefill(c2, torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV), lens)
+    b1, b2 = host_buffer(c1), host_buffer(c2)
+    # every byte that belongs to a written record or window slot is identical across runs
+    seqs = oracle_prefill(draw, 32)
+    assert_state_equal(b1, cfg, seqs, "run1")
+    assert_state_equal(b2, cfg, seqs, "run2 (0xFF-filled buffer)")
+    q = torch.from_numpy(draw.q).to(DEV)
+    ws = c1.workspace(0)
+    ws.view(torch.uint8).fill_(0xFF)  # NaN pattern in every float slot
+    out = torch.full((3, 8, 128), float("nan"), dtype=torch.float32, device=DEV)
+    kvq_decode_attend(c1, q, out=out, out_fp32=True, workspace=ws)
+    assert torch.isfinite(out).all()
+    out16 = torch.full((3, 8, 128), float("nan"), dtype=torch.float16, device=DEV)
+    kvq_decode_attend(c1, q, out=out16)
+    assert torch.isfinite(out16).all()
+
+
+def test_capacity_and_state_errors_on_device():
+    cfg = make_config(1, 1, 1, 64, 2, 2, 32, 32, 64)
+    c = KVQCache(cfg, device=DEV)
+    K = torch.zeros(1, 1, 64, 64, dtype=torch.float16, device=DEV)
+    kvq_prefill(c, K, K, [64])
+    assert c.lengths() == ([32], [32])
+    k = torch.zeros(1, 1, 64, dtype=torch.float16, device=DEV)
+    with pytest.raises(KVQError) as e:
+        kvq_append(c, k, k)
+    assert e.value.status == -3
+    with pytest.raises(KVQError):
+        kvq_prefill(c, K, K, [10])  # not empty
+    c.reset()
+    assert c.lengths() == ([0], [0])
+    with pytest.raises(KVQError):
+        kvq_decode_attend(c, torch.zeros(1, 1, 64, dtype=torch.float16, device=DEV))
