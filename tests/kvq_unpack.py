@@ -59,7 +59,8 @@ def unpack_records(recs: np.ndarray, D: int, bk: int, bv: int):
     vp = vp.transpose(0, 1, 3, 2, 4).reshape(n * 32, NKG, 2)  # token 2P+tp
     vs = vp[..., 0].view(np.float16)
     vz = vp[..., 1].view(np.float16)
-    return {"kc": kc, "ks": ks.reshape(n, D), "kz": kz.reshape(n, D), "vc": vc, "vs": vs, "vz": vz}
+    out = {"kc": kc, "ks": ks.reshape(n, D), "kz": kz.reshape(n, D), "vc": vc, "vs": vs, "vz": vz}
+    return {k: np.ascontiguousarray(v) for k, v in out.items()}
 
 
 def unpack_record(rec: np.ndarray, D: int, bk: int, bv: int):
