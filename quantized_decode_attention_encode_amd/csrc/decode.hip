@@ -3,31 +3,39 @@
 // What is computed ("Changelog" v0.42.0 "Added": fused group-affine decode + attention):
 //   out = softmax(sm_scale * q . K_hat^T) V_hat over every quantized and window token,
 //   k_hat = code * scale + zero per key group, v_hat likewise per value group, with the
-//   reconstruction done in registers inside an online softmax accumulated in fp32.
+//   reconstruction done in registers inside an online softmax accumulated in fp32; no
+//   dequantized K/V is written anywhere.
 //
-// Algebra used to avoid rebuilding k_hat / v_hat element by element:
-//   score_t = sum_d q_d * (s_{j,d} c_{t,d} + z_{j,d})
-//           = sum_d (q_d s_{j,d}) c_{t,d} + sum_d q_d z_{j,d}
-//   so per key group (32 tokens) the scaled query q~_d = q_d s_{j,d} and the offset
-//   beta_j = q . z_j are formed once, and each token costs one multiply-add per channel.
-//   out_d  = sum_t p_t (s_{t,k} c_{t,d} + z_{t,k})
-//          = sum_t (p_t s_{t,k}) c_{t,d} + sum_t p_t z_{t,k}
-//   so each (token, value group) weight a_{t,k} = p_t s_{t,k} is formed once and the zero
-//   terms collapse into one bias per value group.
-// Scores are carried in base-2 units (q is pre-multiplied by sm_scale * log2 e) so the
-// softmax uses exp2.
+// Algebra used so that each cached code costs one multiply-add:
+//   score_t = sum_d q_d (s_{j,d} c_{t,d} + z_{j,d}) = sum_d q~_d c_{t,d} + beta_j,
+//     q~_d = q_d s_{j,d} and beta_j = q . z_j formed once per key group (32 tokens);
+//   out_d  = sum_t p_t (s_{t,k} c_{t,d} + z_{t,k}) = sum_t a_{t,k} c_{t,d} + sum_t p_t z_{t,k},
+//     a_{t,k} = p_t s_{t,k} formed once per (token, value group); the zero terms collapse
+//     into one bias per value group.
+//
+// Code -> float conversion: a b-bit code c sitting at bits [o, o+b) of a 16-bit half, with
+// o + b <= 10, becomes the exact fp16 number 1 + c * 2^(o-10) by OR-ing the exponent bits of
+// 1.0 (0x3C00) into that half. One v_and_or_b32 (mask, magic held in VGPRs) turns two codes
+// into such a pair, and v_fma_mix_f32 consumes either half directly as an fp32 operand. The
+// factor 2^(10-o) is folded into the partner operand (q~ or a) and the constant "1" terms
+// are removed exactly through beta and the value bias:
+//   sum_c x'_c (1 + c 2^(o_c-10)) - sum_c x'_c = sum_c x_c c,   x'_c = x_c 2^(10-o_c).
+// Codes not already at a usable bit position are first brought there by one shift per word
+// shared by every code it moves (two shifts per 16 two-bit codes).
+//
+// Scores are kept in base-2 units (q is pre-multiplied by sm_scale * log2 e): exp2 softmax.
 //
 // Work split: grid (n_split, H_kv, B); workgroup = 4 wavefronts; a workgroup owns `chunk`
 // consecutive units of one (b, h_kv) (unit = one 32-token record, or up to 32 window
-// tokens), its waves take every 4th unit, and it writes one (m, l, acc[D]) partial per
-// query head. The merge kernel combines the partials of a (b, h_q).
+// tokens), its waves take every 4th unit and prefetch their next record while computing
+// the current one, and the workgroup writes one (acc[D], m, l) partial per query head.
 //
-// Lane roles inside a wave for one record (they match the record layout in layout.h):
-//   q~ producer   lane l: channels l*D/64 .. (D/64 of them), i.e. quarter l/16
-//   key consumer  lane (P = l/4, Q = l%4): tokens 2P, 2P+1 x channels of quarter Q
-//   a producer    lane (P, Q): value params of tokens 2P, 2P+1 (D/64 entries)
-//   value consumer lane l: channels l*D/64 .., the 32 tokens of the record
-// The quarter partial scores are summed with two DPP quad butterflies.
+// Lane roles for a record (they follow the record layout, see layout.h):
+//   q~ producer    lane l: channels l*D/64 .. (D/64 of them) = quarter l/16
+//   key consumer   lane (P = l/4, Q = l%4): tokens 2P, 2P+1 x the channels of quarter Q
+//   a producer     lane (P, Q): value params of tokens 2P, 2P+1 (D/64 entries)
+//   value consumer lane l: channels l*D/64 .., all 32 tokens of the record
+// Quarter partial scores meet through two DPP quad butterflies.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 #include <stdint.h>
@@ -37,16 +45,53 @@
 
 namespace kvq {
 
-__device__ __forceinline__ float qxor1(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+// ---------------------------------------------------------------------------------------
+// small device helpers
+// ---------------------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {  // old = 0: lets the compiler fuse the move into the consumer
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float qxor2(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
-}
-__device__ __forceinline__ void wave_sync() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); __builtin_amdgcn_wave_barrier(); }
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowRor4 = 0x124, kRowRor8 = 0x128;
 
-__device__ __forceinline__ float lo_f(uint32_t w) { return __half2float(__ushort_as_half(uint16_t(w & 0xFFFF))); }
-__device__ __forceinline__ float hi_f(uint32_t w) { return __half2float(__ushort_as_half(uint16_t(w >> 16))); }
+__device__ __forceinline__ float row_sum16(float v) {  // sum over the 16 lanes of a row, in every lane
+  v += dpp<kQuadXor1>(v);
+  v += dpp<kQuadXor2>(v);
+  v += dpp<kRowRor4>(v);
+  v += dpp<kRowRor8>(v);
+  return v;
+}
+// Max over the wave when the 4 lanes of each quad hold equal values: row_ror 4 / 8 inside a
+// row, then the gfx950 row swaps: with both operands equal, permlane32_swap returns rows
+// (0,1,0,1) and (2,3,2,3), permlane16_swap rows (0,0,2,2) and (1,1,3,3).
+__device__ __forceinline__ float wave_max_of_quads(float v) {
+  v = fmaxf(v, dpp<kRowRor4>(v));
+  v = fmaxf(v, dpp<kRowRor8>(v));
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ float lo_f(uint32_t w) { return float(__builtin_bit_cast(_Float16, uint16_t(w & 0xFFFF))); }
+__device__ __forceinline__ float hi_f(uint32_t w) { return float(__builtin_bit_cast(_Float16, uint16_t(w >> 16))); }
+
+// A value the compiler must keep in a VGPR (so v_and_or_b32 can take it; gfx9 VOP3 has no literals).
+template <uint32_t C>
+__device__ __forceinline__ uint32_t vconst() {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(C));
+  return r;
+}
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+  return r;
+}
 
 template <int N>
 __device__ __forceinline__ void load_words(const uint32_t* __restrict__ p, uint32_t* out) {
@@ -68,28 +113,342 @@ __device__ __forceinline__ void load_words(const uint32_t* __restrict__ p, uint3
   }
 }
 
+// Where each code of a word goes before the OR with 1.0: in-half position j (bit j*B) is
+// shifted by sh(j) bits (left positive) to bit od(j) = j*B + sh(j), with od(j) + B <= 10.
+template <int B>
+struct Magic {
+  static constexpr int NH = 16 / B;  // codes per 16-bit half
+  static constexpr int NC = 32 / B;  // codes per word
+  __host__ __device__ static constexpr int sh(int j) {
+    return B == 2 ? (j < 2 ? 4 : (j < 5 ? 0 : -6))
+         : B == 4 ? (j == 0 ? 6 : (j == 1 ? 0 : (j == 2 ? -2 : -6)))
+                  : (j == 0 ? 2 : -6);
+  }
+  __host__ __device__ static constexpr int od(int j) { return j * B + sh(j); }
+  // factor 2^(10 - od) folded into the partner operand of the code at word position p
+  __host__ __device__ static constexpr float fold(int p) {
+    return float(1 << (10 - od(p % NH)));
+  }
+};
+
+// The NH fp16 pairs of one word: pair j holds the codes at positions j (low half) and
+// j + NH (high half).
+template <int B>
+struct Unpacker {
+  uint32_t magic, mk[10];  // mk[o]: the code bits at [o, o+B) of both halves
+  __device__ __forceinline__ void init() {
+    magic = vconst<0x3C003C00u>();
+#pragma unroll
+    for (int j = 0; j < Magic<B>::NH; ++j) {
+      const int o = Magic<B>::od(j);
+      const uint32_t m = ((1u << B) - 1) << o;
+      uint32_t r;
+      asm("v_mov_b32 %0, %1" : "=v"(r) : "v"(m | (m << 16)));
+      mk[o] = r;
+    }
+  }
+  __device__ __forceinline__ void run(uint32_t w, uint32_t* out) const {
+#pragma unroll
+    for (int j = 0; j < Magic<B>::NH; ++j) {
+      const int s = Magic<B>::sh(j);
+      const uint32_t v = s > 0 ? (w << s) : (s < 0 ? (w >> -s) : w);
+      out[j] = and_or(v, mk[Magic<B>::od(j)], magic);
+    }
+  }
+};
+
+// Value weights travel as fp16: A_t = fp16(p_t * s_t * 2^(10-o_t) * 2^-6). With p <= 1, an
+// fp16 scale s <= 43669 (2-bit) / 8734 (4-bit) / 514 (8-bit) and a fold factor 2^(10-o) <= 64
+// (2/4-bit) or 256 (8-bit), A never exceeds the fp16 range; accumulators then carry 2^-6 units.
+constexpr float kVScale = 1.0f / 64.0f;
+
 template <int D, int G>
 struct WaveLds {
-  float qt[G][4][D / 4 + 4];  // scaled query per quarter (padded rows)
-  float beta[G][4];           // quarter offsets q . z
-  float a[G][D / 32][32];     // value weights per (value group, token)
+  float qt[G][4][D / 4 + 4];      // scaled, folded query per quarter (padded rows)
+  float beta[G][4];               // quarter offsets (q . z minus the fold constant)
+  uint32_t A[G][D / 32][16 + 4];  // fp16 value weights per (value group, token pair), see kVScale
+  float pw[G][32 + 4];            // window tokens: softmax weights
   float red[G][64];
 };
 
-template <int D, int BK, int BV, int G>
-__global__ __launch_bounds__(256) void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L,
-                                                           DecodeShape ds, const __half* __restrict__ q,
-                                                           float* __restrict__ ws) {
-  constexpr int E = D / 64;       // channels per lane (producer / value consumer)
-  constexpr int DQ = D / 4;       // channels per key quarter
-  constexpr int NKG = D / 32;     // value groups
-  constexpr int WQ = D * BK / 128;
-  constexpr int KW = 2 * WQ;      // key-code words per key-consumer lane
-  constexpr int VW = E * BV;      // value-code words per value-consumer lane
-  constexpr uint32_t KMASK = (1u << BK) - 1, VMASK = (1u << BV) - 1;
-  constexpr int KPW = 32 / BK, VPW = 32 / BV;  // codes per word
+template <int D, int BK, int BV>
+struct RecordRegs {
+  uint32_t kc[2 * (D * BK / 128)];
+  uint32_t vc[(D / 64) * BV];
+  uint32_t kp[D / 64];
+  uint32_t vp[D / 64];
+};
 
-  __shared__ union {
+template <int D, int BK, int BV>
+__device__ __forceinline__ void load_record(const uint8_t* __restrict__ rec, int lane, RecordRegs<D, BK, BV>& r) {
+  constexpr int E = D / 64, KW = 2 * (D * BK / 128), VW = E * BV;
+  load_words<KW>(reinterpret_cast<const uint32_t*>(rec) + lane * KW, r.kc);
+  load_words<VW>(reinterpret_cast<const uint32_t*>(rec + rec_off_vcodes(D, BK)) + lane * VW, r.vc);
+  load_words<E>(reinterpret_cast<const uint32_t*>(rec + rec_off_kparams(D, BK, BV)) + lane * E, r.kp);
+  load_words<E>(reinterpret_cast<const uint32_t*>(rec + rec_off_vparams(D, BK, BV)) + lane * E, r.vp);
+}
+
+// State of one wavefront across the units it visits.
+template <int D, int G>
+struct WaveState {
+  float m[G], l[G], bias[G], acc[G][D / 64];
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Online-softmax step for one head: new scores s0, s1 (base-2 units) of tokens 2P, 2P+1.
+template <int D, int G>
+__device__ __forceinline__ void softmax_step(WaveState<D, G>& st, int i, float s0, float s1, float& p0, float& p1) {
+  const float mx = wave_max_of_quads(fmaxf(s0, s1));
+  if (mx > st.m[i]) {  // wave-uniform
+    const float alpha = fast_exp2(st.m[i] - mx);
+    st.m[i] = mx;
+    st.l[i] *= alpha;
+    st.bias[i] *= alpha;
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) st.acc[i][e] *= alpha;
+  }
+  p0 = fast_exp2(s0 - st.m[i]);
+  p1 = fast_exp2(s1 - st.m[i]);
+  st.l[i] += p0 + p1;
+}
+
+// One 32-token record of (b, h_kv), all G query heads.
+template <int D, int BK, int BV, int G>
+__device__ __forceinline__ void process_record(const RecordRegs<D, BK, BV>& cur, WaveLds<D, G>& W, WaveState<D, G>& st,
+                                               const Unpacker<BK>& upk, const Unpacker<BV>& upv,
+                                               const float (&qs)[G][D / 64], const float (&qf)[G][D / 64],
+                                               float vf0, float vf1, int lane) {
+  constexpr int E = D / 64, DQ = D / 4, WQ = D * BK / 128, NKG = D / 32;
+  using MK = Magic<BK>;
+  using MV = Magic<BV>;
+  const int P = lane >> 2, Q = lane & 3;
+  const int kcons = (lane * E) / 32;
+
+  // ---- producer: folded scaled query and quarter offsets
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    float bp = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int ch = lane * E + e;
+      const float qt = qf[i][e] * lo_f(cur.kp[e]);
+      W.qt[i][ch / DQ][ch % DQ] = qt;
+      bp += qs[i][e] * hi_f(cur.kp[e]) - qt;
+    }
+    bp = row_sum16(bp);
+    if ((lane & 15) == 0) W.beta[i][lane >> 4] = bp;
+  }
+  wave_sync();
+
+  // ---- keys
+  float s[G][2];
+#pragma unroll
+  for (int i = 0; i < G; ++i) s[i][0] = s[i][1] = W.beta[i][Q];
+  if constexpr (G == 1) {
+    // word by word: few live registers
+#pragma unroll
+    for (int w = 0; w < WQ; ++w) {
+      uint32_t k0[MK::NH], k1[MK::NH];
+      upk.run(cur.kc[w], k0);
+      upk.run(cur.kc[WQ + w], k1);
+      float qv[MK::NC];
+#pragma unroll
+      for (int c = 0; c < MK::NC; c += 4) {
+        const float4 t4 = *reinterpret_cast<const float4*>(&W.qt[0][Q][w * MK::NC + c]);
+        qv[c] = t4.x; qv[c + 1] = t4.y; qv[c + 2] = t4.z; qv[c + 3] = t4.w;
+      }
+#pragma unroll
+      for (int j = 0; j < MK::NH; ++j) {
+        s[0][0] = __builtin_fmaf(qv[j], lo_f(k0[j]), s[0][0]);
+        s[0][1] = __builtin_fmaf(qv[j], lo_f(k1[j]), s[0][1]);
+        s[0][0] = __builtin_fmaf(qv[j + MK::NH], hi_f(k0[j]), s[0][0]);
+        s[0][1] = __builtin_fmaf(qv[j + MK::NH], hi_f(k1[j]), s[0][1]);
+      }
+    }
+  } else {
+    // unpack the whole quarter once; every head reuses it
+    uint32_t kr[2][WQ][MK::NH];
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+      for (int w = 0; w < WQ; ++w) upk.run(cur.kc[tp * WQ + w], kr[tp][w]);
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      float qv[DQ];
+#pragma unroll
+      for (int c = 0; c < DQ; c += 4) {
+        const float4 t4 = *reinterpret_cast<const float4*>(&W.qt[i][Q][c]);
+        qv[c] = t4.x; qv[c + 1] = t4.y; qv[c + 2] = t4.z; qv[c + 3] = t4.w;
+      }
+#pragma unroll
+      for (int w = 0; w < WQ; ++w)
+#pragma unroll
+        for (int j = 0; j < MK::NH; ++j) {
+          const int c = w * MK::NC + j;
+          s[i][0] = __builtin_fmaf(qv[c], lo_f(kr[0][w][j]), s[i][0]);
+          s[i][1] = __builtin_fmaf(qv[c], lo_f(kr[1][w][j]), s[i][1]);
+          s[i][0] = __builtin_fmaf(qv[c + MK::NH], hi_f(kr[0][w][j]), s[i][0]);
+          s[i][1] = __builtin_fmaf(qv[c + MK::NH], hi_f(kr[1][w][j]), s[i][1]);
+        }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    float s0 = s[i][0], s1 = s[i][1];
+    s0 += dpp<kQuadXor1>(s0);
+    s1 += dpp<kQuadXor1>(s1);
+    s0 += dpp<kQuadXor2>(s0);
+    s1 += dpp<kQuadXor2>(s1);
+    float p0, p1;
+    softmax_step<D, G>(st, i, s0, s1, p0, p1);
+    // ---- producer: fp16 folded value weights and the zero-term bias (in kVScale units)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      // entry e of this lane: token t, value group k (the value-param dword lane*E + e)
+      const int idx = lane * E + e;
+      const int tp = idx & 1, k = (idx >> 1) % NKG, t = 2 * P + tp;
+      const float p = tp ? p1 : p0;
+      const float vfold = (tp ? vf1 : vf0);  // 2^(10-o_t) * kVScale
+      const __half a16 = __float2half_rn((p * vfold) * lo_f(cur.vp[e]));
+      st.bias[i] += (p * kVScale) * hi_f(cur.vp[e]) - __half2float(a16);
+      const int dw = (t / MV::NC) * MV::NH + (t % MV::NC) % MV::NH, hf = (t % MV::NC) / MV::NH;
+      reinterpret_cast<__half*>(&W.A[i][k][dw])[hf] = a16;
+    }
+  }
+  wave_sync();
+
+  // ---- values: v_dot2_f32_f16 of (weight pair) x (code pair); a word = NC tokens of a channel
+  using h2 = _Float16 __attribute__((ext_vector_type(2)));
+  if constexpr (G == 1) {
+#pragma unroll
+    for (int w = 0; w < BV; ++w) {
+      uint32_t vr[E][MV::NH];
+#pragma unroll
+      for (int e = 0; e < E; ++e) upv.run(cur.vc[e * BV + w], vr[e]);
+      uint32_t av[MV::NH];
+#pragma unroll
+      for (int j = 0; j < MV::NH; j += (MV::NH >= 4 ? 4 : 2)) {
+        if constexpr (MV::NH >= 4) {
+          const uint4 t4 = *reinterpret_cast<const uint4*>(&W.A[0][kcons][w * MV::NH + j]);
+          av[j] = t4.x; av[j + 1] = t4.y; av[j + 2] = t4.z; av[j + 3] = t4.w;
+        } else {
+          const uint2 t2 = *reinterpret_cast<const uint2*>(&W.A[0][kcons][w * MV::NH + j]);
+          av[j] = t2.x; av[j + 1] = t2.y;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        float x = st.acc[0][e];
+#pragma unroll
+        for (int j = 0; j < MV::NH; ++j)
+          x = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, av[j]), __builtin_bit_cast(h2, vr[e][j]), x, false);
+        st.acc[0][e] = x;
+      }
+    }
+  } else {
+    uint32_t vr[E][BV][MV::NH];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+#pragma unroll
+      for (int w = 0; w < BV; ++w) upv.run(cur.vc[e * BV + w], vr[e][w]);
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      uint32_t av[16];
+#pragma unroll
+      for (int j = 0; j < 16; j += 4) {
+        const uint4 t4 = *reinterpret_cast<const uint4*>(&W.A[i][kcons][j]);
+        av[j] = t4.x; av[j + 1] = t4.y; av[j + 2] = t4.z; av[j + 3] = t4.w;
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        float x = st.acc[i][e];
+#pragma unroll
+        for (int w = 0; w < BV; ++w)
+#pragma unroll
+          for (int j = 0; j < MV::NH; ++j)
+            x = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, av[w * MV::NH + j]), __builtin_bit_cast(h2, vr[e][w][j]),
+                                       x, false);
+        st.acc[i][e] = x;
+      }
+    }
+  }
+  wave_sync();
+}
+
+// Up to 32 fp16 window tokens (tokens tbase .. tbase + nvalid - 1 of the window).
+template <int D, int G>
+__device__ __forceinline__ void process_window(const __half* __restrict__ wk, const __half* __restrict__ wv, int nvalid,
+                                               WaveLds<D, G>& W, WaveState<D, G>& st, const float (&qs)[G][D / 64],
+                                               int lane) {
+  constexpr int E = D / 64, DQ = D / 4;
+  const int P = lane >> 2, Q = lane & 3;
+  const int kcons = (lane * E) / 32;
+#pragma unroll
+  for (int i = 0; i < G; ++i)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int ch = lane * E + e;
+      W.qt[i][ch / DQ][ch % DQ] = qs[i][e];
+    }
+  wave_sync();
+  const int t0 = 2 * P, t1 = 2 * P + 1;
+  const uint32_t* k0p = reinterpret_cast<const uint32_t*>(wk + min(t0, nvalid - 1) * D + Q * DQ);
+  const uint32_t* k1p = reinterpret_cast<const uint32_t*>(wk + min(t1, nvalid - 1) * D + Q * DQ);
+  uint32_t k0w[DQ / 2], k1w[DQ / 2];
+#pragma unroll
+  for (int c = 0; c < DQ / 2; ++c) {
+    k0w[c] = k0p[c];
+    k1w[c] = k1p[c];
+  }
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int c = 0; c < DQ / 2; ++c) {
+      const float qa = W.qt[i][Q][2 * c], qb = W.qt[i][Q][2 * c + 1];
+      s0 = __builtin_fmaf(qa, lo_f(k0w[c]), s0);
+      s0 = __builtin_fmaf(qb, hi_f(k0w[c]), s0);
+      s1 = __builtin_fmaf(qa, lo_f(k1w[c]), s1);
+      s1 = __builtin_fmaf(qb, hi_f(k1w[c]), s1);
+    }
+    s0 += dpp<kQuadXor1>(s0);
+    s0 += dpp<kQuadXor2>(s0);
+    s1 += dpp<kQuadXor1>(s1);
+    s1 += dpp<kQuadXor2>(s1);
+    if (t0 >= nvalid) s0 = -INFINITY;
+    if (t1 >= nvalid) s1 = -INFINITY;
+    float p0, p1;
+    softmax_step<D, G>(st, i, s0, s1, p0, p1);
+    if (Q == 0) *reinterpret_cast<float2*>(&W.pw[i][2 * P]) = make_float2(p0 * kVScale, p1 * kVScale);
+  }
+  wave_sync();
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    for (int t = 0; t < nvalid; ++t) {
+      const float a = W.pw[i][t];
+      if constexpr (E == 2) {
+        const uint32_t vw = reinterpret_cast<const uint32_t*>(wv + t * D)[lane];
+        st.acc[i][0] = __builtin_fmaf(a, lo_f(vw), st.acc[i][0]);
+        st.acc[i][1] = __builtin_fmaf(a, hi_f(vw), st.acc[i][1]);
+      } else {
+        st.acc[i][0] = __builtin_fmaf(a, __half2float(wv[t * D + lane]), st.acc[i][0]);
+      }
+    }
+  }
+  wave_sync();
+}
+
+template <int D, int BK, int BV, int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : (G <= 4 ? 2 : 1))))
+void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape ds, const __half* __restrict__ q,
+                         float* __restrict__ ws) {
+  constexpr int E = D / 64, DQ = D / 4, NKG = D / 32;
+  using MK = Magic<BK>;
+  using MV = Magic<BV>;
+
+  __shared__ __attribute__((aligned(16))) union {
     WaveLds<D, G> w[4];
     float res[4][G][D + 4];
   } sh;
@@ -104,160 +463,82 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const uint8_t* __rest
   const int u0 = sigma * ds.chunk;
   if (u0 >= nunits) return;
   const int u1 = min(u0 + ds.chunk, nunits);
+  const int uq = min(u1, ngroups);  // end of the quantized units of this split
 
   WaveLds<D, G>& W = sh.w[wave];
   const int P = lane >> 2, Q = lane & 3;
-  const int kprod = ((lane * E) >> 1) % NKG;
   const int kcons = (lane * E) / 32;
 
-  float qp[G][E];
+  Unpacker<BK> upk;
+  Unpacker<BV> upv;
+  upk.init();
+  upv.init();
+
+  float qs[G][E], qf[G][E];
 #pragma unroll
   for (int i = 0; i < G; ++i)
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      qp[i][e] = __half2float(q[(int64_t(b) * ds.n_q_heads + h * G + i) * D + lane * E + e]) * ds.qscale;
+    for (int e = 0; e < E; ++e) {
+      const int ch = lane * E + e;
+      qs[i][e] = __half2float(q[(int64_t(b) * ds.n_q_heads + h * G + i) * D + ch]) * ds.qscale;
+      qf[i][e] = qs[i][e] * MK::fold((ch % DQ) % MK::NC);
+    }
+  const float vf0 = MV::fold((2 * P) % MV::NC) * kVScale, vf1 = MV::fold((2 * P + 1) % MV::NC) * kVScale;
 
-  float m[G], l[G], bias[G], acc[G][E];
+  WaveState<D, G> st;
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    m[i] = -INFINITY;
-    l[i] = 0.f;
-    bias[i] = 0.f;
+    st.m[i] = -INFINITY;
+    st.l[i] = 0.f;
+    st.bias[i] = 0.f;
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[i][e] = 0.f;
+    for (int e = 0; e < E; ++e) st.acc[i][e] = 0.f;
   }
 
-  for (int u = u0 + wave; u < u1; u += 4) {
-    const bool quant = u < ngroups;
-    uint32_t kc[KW], vc[VW], kp[E], vp[E];
-    const __half* wk = nullptr;
-    const __half* wv = nullptr;
-    int nvalid = kGroup;
-    if (quant) {
-      const uint8_t* rec = buf + L.record(b, h, u);
-      load_words<KW>(reinterpret_cast<const uint32_t*>(rec) + lane * KW, kc);
-      load_words<VW>(reinterpret_cast<const uint32_t*>(rec + rec_off_vcodes(D, BK)) + lane * VW, vc);
-      load_words<E>(reinterpret_cast<const uint32_t*>(rec + rec_off_kparams(D, BK, BV)) + lane * E, kp);
-      load_words<E>(reinterpret_cast<const uint32_t*>(rec + rec_off_vparams(D, BK, BV)) + lane * E, vp);
-    } else {
-      // window tokens are plain fp16: scale 1.0 (0x3C00), zero 0
-#pragma unroll
-      for (int e = 0; e < E; ++e) kp[e] = vp[e] = 0x3C00u;
-      const int tbase = (u - ngroups) * kGroup;
-      nvalid = min(kGroup, nr - tbase);
-      wk = reinterpret_cast<const __half*>(buf + L.wk_off + L.window(b, h)) + tbase * D;
-      wv = reinterpret_cast<const __half*>(buf + L.wv_off + L.window(b, h)) + tbase * D;
+  // quantized records, the next one loaded while the current one is computed
+  const uint8_t* rec0 = buf + L.record(b, h, 0);
+  const uint64_t rb = L.rec_bytes;
+  int u = u0 + wave;
+  if constexpr (G == 1) {
+    // two register sets refilled alternately (no copies)
+    RecordRegs<D, BK, BV> ra, rbuf;
+    if (u < uq) load_record<D, BK, BV>(rec0 + u * rb, lane, ra);
+    while (u < uq) {
+      if (u + 4 < uq) load_record<D, BK, BV>(rec0 + (u + 4) * rb, lane, rbuf);
+      process_record<D, BK, BV, G>(ra, W, st, upk, upv, qs, qf, vf0, vf1, lane);
+      u += 4;
+      if (u >= uq) break;
+      if (u + 4 < uq) load_record<D, BK, BV>(rec0 + (u + 4) * rb, lane, ra);
+      process_record<D, BK, BV, G>(rbuf, W, st, upk, upv, qs, qf, vf0, vf1, lane);
+      u += 4;
     }
-
-    // ---- scaled query and quarter offsets
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-      float bp = 0.f;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int ch = lane * E + e;
-        const float s = lo_f(kp[e]);
-        const float z = hi_f(kp[e]);
-        W.qt[i][ch / DQ][ch % DQ] = qp[i][e] * s;
-        bp += qp[i][e] * z;
-      }
-      bp += __shfl_xor(bp, 1, 64);
-      bp += __shfl_xor(bp, 2, 64);
-      bp += __shfl_xor(bp, 4, 64);
-      bp += __shfl_xor(bp, 8, 64);
-      if ((lane & 15) == 0) W.beta[i][lane >> 4] = bp;
+  } else {
+    RecordRegs<D, BK, BV> cur, nxt;
+    if (u < uq) load_record<D, BK, BV>(rec0 + u * rb, lane, cur);
+    for (; u < uq; u += 4) {
+      if (u + 4 < uq) load_record<D, BK, BV>(rec0 + (u + 4) * rb, lane, nxt);
+      process_record<D, BK, BV, G>(cur, W, st, upk, upv, qs, qf, vf0, vf1, lane);
+      cur = nxt;
     }
-    wave_sync();
-
-    // ---- scores of tokens 2P, 2P+1, online softmax, value weights
-    const int t0 = 2 * P, t1 = 2 * P + 1;
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-      float s0 = W.beta[i][Q], s1 = s0;
-      if (quant) {
-#pragma unroll
-        for (int c = 0; c < DQ; ++c) {
-          const float qv = W.qt[i][Q][c];
-          const uint32_t c0 = (kc[(c * BK) / 32] >> ((c % KPW) * BK)) & KMASK;
-          const uint32_t c1 = (kc[WQ + (c * BK) / 32] >> ((c % KPW) * BK)) & KMASK;
-          s0 += qv * float(c0);
-          s1 += qv * float(c1);
-        }
-      } else {
-#pragma unroll 8
-        for (int c = 0; c < DQ; ++c) {
-          const float qv = W.qt[i][Q][c];
-          const float k0 = t0 < nvalid ? __half2float(wk[t0 * D + Q * DQ + c]) : 0.f;
-          const float k1 = t1 < nvalid ? __half2float(wk[t1 * D + Q * DQ + c]) : 0.f;
-          s0 += qv * k0;
-          s1 += qv * k1;
-        }
-      }
-      s0 += qxor1(s0);
-      s0 += qxor2(s0);
-      s1 += qxor1(s1);
-      s1 += qxor2(s1);
-      if (t0 >= nvalid) s0 = -INFINITY;
-      if (t1 >= nvalid) s1 = -INFINITY;
-
-      float mx = fmaxf(s0, s1);
-      mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 8, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(m[i], mx);
-      const float alpha = exp2f(m[i] - mnew);
-      m[i] = mnew;
-      l[i] *= alpha;
-      bias[i] *= alpha;
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[i][e] *= alpha;
-      const float p0 = exp2f(s0 - mnew), p1 = exp2f(s1 - mnew);
-      l[i] += p0 + p1;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int idx = lane * E + e;
-        const int tp = idx & 1, k = (idx >> 1) % NKG;
-        const float p = tp ? p1 : p0;
-        const float sv = lo_f(vp[e]);
-        const float zv = hi_f(vp[e]);
-        W.a[i][k][2 * P + tp] = p * sv;
-        bias[i] += p * zv;
-      }
-    }
-    wave_sync();
-
-    // ---- weighted sum of the value codes
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        float sacc = 0.f;
-        if (quant) {
-#pragma unroll
-          for (int t = 0; t < kGroup; ++t) {
-            const uint32_t c = (vc[e * BV + t / VPW] >> ((t % VPW) * BV)) & VMASK;
-            sacc += W.a[i][kcons][t] * float(c);
-          }
-        } else {
-          const int ch = lane * E + e;
-          for (int t = 0; t < nvalid; ++t) sacc += W.a[i][kcons][t] * __half2float(wv[t * D + ch]);
-        }
-        acc[i][e] += sacc;
-      }
-    }
-    wave_sync();
+  }
+  // window units
+  for (; u < u1; u += 4) {
+    const int tbase = (u - ngroups) * kGroup;
+    const int nvalid = min(kGroup, nr - tbase);
+    const __half* wk = reinterpret_cast<const __half*>(buf + L.wk_off + L.window(b, h)) + tbase * D;
+    const __half* wv = reinterpret_cast<const __half*>(buf + L.wv_off + L.window(b, h)) + tbase * D;
+    process_window<D, G>(wk, wv, nvalid, W, st, qs, lane);
   }
 
-  // ---- finish the wave: l counted once per quad, bias summed over its producers
+  // ---- finish the wave: l counted once per quad, bias summed over its producer lanes
   float lt[G], o[G][E];
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    float v = (Q == 0) ? l[i] : 0.f;
+    float v = (Q == 0) ? st.l[i] : 0.f;
 #pragma unroll
     for (int msk = 1; msk < 64; msk <<= 1) v += __shfl_xor(v, msk, 64);
     lt[i] = v;
-    W.red[i][lane] = bias[i];
+    W.red[i][lane] = st.bias[i];
   }
   wave_sync();
 #pragma unroll
@@ -266,16 +547,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const uint8_t* __rest
     for (int j = 0; j < 64; ++j)
       if (((j * E) >> 1) % NKG == kcons) bsum += W.red[i][j];
 #pragma unroll
-    for (int e = 0; e < E; ++e) o[i][e] = acc[i][e] + bsum;
+    for (int e = 0; e < E; ++e) o[i][e] = (st.acc[i][e] + bsum) * (1.0f / kVScale);
   }
-  (void)kprod;
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < G; ++i) {
 #pragma unroll
     for (int e = 0; e < E; ++e) sh.res[wave][i][lane * E + e] = o[i][e];
     if (lane == 0) {
-      sh.res[wave][i][D] = m[i];
+      sh.res[wave][i][D] = st.m[i];
       sh.res[wave][i][D + 1] = lt[i];
     }
   }
@@ -292,7 +572,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const uint8_t* __rest
     for (int w = 0; w < 4; ++w) {
       const float mw = sh.res[w][i][D];
       if (mw != -INFINITY) {
-        const float wgt = exp2f(mw - M);
+        const float wgt = fast_exp2(mw - M);
         O += wgt * sh.res[w][i][ch];
         Lsum += wgt * sh.res[w][i][D + 1];
       }
@@ -306,11 +586,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(const uint8_t* __rest
   }
 }
 
-// Combine the split partials of one (b, h_q) into the output row.
+// Combine the split partials of one (b, h_q): one lane per split for the softmax weights,
+// then one lane per channel pair for the weighted sum.
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape ds,
                                                           const float* __restrict__ ws, void* __restrict__ out) {
   constexpr int E = D / 64;
+  __shared__ float wn[64];
   const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int h = hq / ds.G;
   const int32_t* len = reinterpret_cast<const int32_t*>(buf + L.lengths(b, h));
@@ -319,28 +601,48 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(const uint8_t* __restr
   const int nunits = nq / kGroup + (nr + kGroup - 1) / kGroup;
   const int nvalid = min(ds.n_split, (nunits + ds.chunk - 1) / ds.chunk);
   const float* base = ws + (int64_t(b) * ds.n_q_heads + hq) * ds.n_split * (D + 4);
+
   float M = -INFINITY;
-  for (int s = 0; s < nvalid; ++s) M = fmaxf(M, base[s * (D + 4) + D]);
-  float Lsum = 0.f, O[E];
+  for (int s = lane; s < nvalid; s += 64) M = fmaxf(M, base[s * (D + 4) + D]);
+#pragma unroll
+  for (int msk = 1; msk < 64; msk <<= 1) M = fmaxf(M, __shfl_xor(M, msk, 64));
+  float Ls = 0.f;
+  for (int s = lane; s < nvalid; s += 64) {
+    const float ms = base[s * (D + 4) + D];
+    if (ms != -INFINITY) Ls += exp2f(ms - M) * base[s * (D + 4) + D + 1];
+  }
+#pragma unroll
+  for (int msk = 1; msk < 64; msk <<= 1) Ls += __shfl_xor(Ls, msk, 64);
+  const float inv = 1.f / Ls;
+
+  float O[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) O[e] = 0.f;
-  for (int s = 0; s < nvalid; ++s) {
-    const float ms = base[s * (D + 4) + D];
-    if (ms == -INFINITY) continue;
-    const float wgt = exp2f(ms - M);
-    Lsum += wgt * base[s * (D + 4) + D + 1];
+  for (int s0 = 0; s0 < nvalid; s0 += 64) {
+    const int s = s0 + lane;
+    float w = 0.f;
+    if (s < nvalid) {
+      const float ms = base[s * (D + 4) + D];
+      w = (ms != -INFINITY) ? exp2f(ms - M) * inv : 0.f;
+    }
+    __syncthreads();
+    wn[lane] = w;
+    __syncthreads();
+    const int n = min(64, nvalid - s0);
+    for (int j = 0; j < n; ++j) {
+      const float wj = wn[j];
+      const float* src = base + (s0 + j) * (D + 4) + lane * E;
 #pragma unroll
-    for (int e = 0; e < E; ++e) O[e] += wgt * base[s * (D + 4) + lane * E + e];
+      for (int e = 0; e < E; ++e) O[e] = __builtin_fmaf(wj, src[e], O[e]);
+    }
   }
-  const float inv = 1.f / Lsum;
   const int64_t row = (int64_t(b) * ds.n_q_heads + hq) * D;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const float v = O[e] * inv;
     if (ds.out_fp32)
-      static_cast<float*>(out)[row + lane * E + e] = v;
+      static_cast<float*>(out)[row + lane * E + e] = O[e];
     else
-      static_cast<__half*>(out)[row + lane * E + e] = __float2half_rn(v);
+      static_cast<__half*>(out)[row + lane * E + e] = __float2half_rn(O[e]);
   }
 }
 

@@ -70,8 +70,13 @@ def test_split_count_does_not_change_result(case):
     cache = gpu_prefill(draw, cfg)
     q = torch.from_numpy(draw.q).to(DEV)
     outs = [kvq_decode_attend(cache, q, out_fp32=True, n_split=n).cpu().numpy() for n in (0, 1, 2, 3, 7, 64)]
+    # The value weights p_t * s_t enter the value dot products as fp16 (relative rounding
+    # <= 2^-12 each), and a different split count changes the running maxima they are
+    # rounded under; each result is then within 2^-12 * max|v_hat| of the exact one.
+    vmax = max(np.abs(s.values_hat()).max() for s in oracle_prefill(draw, cfg.residual).values())
+    bound = 2 * 2.0 ** -12 * vmax + 2e-5
     for o in outs[1:]:
-        assert np.max(np.abs(o - outs[0])) < 2e-5
+        assert np.max(np.abs(o - outs[0])) < bound
 
 
 def test_window_only_and_single_token_sequences():
