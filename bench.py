@@ -94,6 +94,7 @@ def main():
     ap.add_argument("--workload", default="long")
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--encode-reps", type=int, default=5)
+    ap.add_argument("--n-split", type=int, default=0, help="splits per sequence (0 = the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -151,14 +152,15 @@ def main():
     vt = torch.from_numpy(np.stack([t[1] for t in toks])).to(dev)
     q = torch.from_numpy(draw.q).to(dev)
     outs = [torch.empty(tuple(q.shape), dtype=torch.float16, device=dev) for _ in caches]
-    wss = [c.workspace(0) for c in caches]
+    wss = [c.workspace(args.n_split) for c in caches]
     del Kt, Vt
     torch.cuda.synchronize()
 
     def step(i):
         c = caches[i % args.replicas]
         kvq_append(c, kt[i], vt[i], stream=stream)
-        kvq_decode_attend(c, q, out=outs[i % args.replicas], workspace=wss[i % args.replicas], stream=stream)
+        kvq_decode_attend(c, q, out=outs[i % args.replicas], workspace=wss[i % args.replicas], n_split=args.n_split,
+                          stream=stream)
 
     for i in range(args.warmup):
         step(i)

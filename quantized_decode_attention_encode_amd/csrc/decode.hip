@@ -500,7 +500,8 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
   const uint64_t rb = L.rec_bytes;
   int u = u0 + wave;
   if constexpr (G == 1) {
-    // two register sets refilled alternately (no copies)
+    // two register sets refilled alternately (no copies): each record is requested one
+    // record ahead of its use
     RecordRegs<D, BK, BV> ra, rbuf;
     if (u < uq) load_record<D, BK, BV>(rec0 + u * rb, lane, ra);
     while (u < uq) {
