@@ -29,6 +29,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 
+# HBM bytes per decode-split launch on the long workload from two rocprofv3 --pmc runs
+# (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, factors from a 1 GiB device copy; see
+# profiles/kvq_long_s64k_counters.md), valid only for the decode source they were taken on.
+MEASURED_TRAFFIC = {"workload": "long", "decode_src_sha256_16": "9486cf93d1fa114c", "bytes": 202243000}
+
 
 def algorithmic_decode_bytes(wl, n_q, n_r):
     """Bytes one decode launch must move: every record once per KV head (GQA query heads share
@@ -205,6 +210,15 @@ def main():
     copy_gbs = 2 * (1 << 30) * 10 / (e0.elapsed_time(e1) / 1e3) / 1e9
     del a, b
 
+    traffic = None
+    src = os.path.join(ROOT, "quantized_decode_attention_encode_amd", "csrc", "decode.hip")
+    if args.workload == MEASURED_TRAFFIC["workload"] and args.n_split == 0:
+        import hashlib
+
+        with open(src, "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest()[:16] == MEASURED_TRAFFIC["decode_src_sha256_16"]:
+                traffic = MEASURED_TRAFFIC["bytes"]
+
     result = {
         "metric": "decode-attend us/step + achieved HBM GB/s (% peak) at S_kv=64K; encode tokens/s",
         "value": round(step_ms * 1e3, 3),
@@ -230,7 +244,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "kernel": "decode_split_kernel",
             "kernel_avg_us": round(split_avg_ms * 1e3, 3),
             "algorithmic_bytes_per_launch": int(alg_bytes),
