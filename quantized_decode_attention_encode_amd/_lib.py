@@ -8,7 +8,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkvq.so")
+# KVQ_LIBRARY may point at another build of the same ABI (e.g. a tuning variant); the default
+# is the in-tree library.
+LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(HERE, "libkvq.so")
 
 KVQ_OK = 0
 KVQ_E_INVALID = -1

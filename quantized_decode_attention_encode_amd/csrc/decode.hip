@@ -188,6 +188,9 @@ __device__ __forceinline__ void load_record(const uint8_t* __restrict__ rec, int
   load_words<E>(reinterpret_cast<const uint32_t*>(rec + rec_off_vparams(D, BK, BV)) + lane * E, r.vp);
 }
 
+// Wavefronts per decode workgroup; each takes every kWaves-th unit of the workgroup's chunk.
+constexpr int kWaves = 4;
+
 // State of one wavefront across the units it visits.
 template <int D, int G>
 struct WaveState {
@@ -199,8 +202,10 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Online-softmax step for one head: new scores s0, s1 (base-2 units) of tokens 2P, 2P+1.
 template <int D, int G>
 __device__ __forceinline__ void softmax_step(WaveState<D, G>& st, int i, float s0, float s1, float& p0, float& p1) {
-  const float mx = wave_max_of_quads(fmaxf(s0, s1));
-  if (mx > st.m[i]) {  // wave-uniform
+  // The running max only moves when some lane holds a larger score; a wave vote finds out
+  // with one comparison, so the reduction and the rescale run only then.
+  if (__any(fmaxf(s0, s1) > st.m[i])) {  // wave-uniform
+    const float mx = wave_max_of_quads(fmaxf(s0, s1));
     const float alpha = fast_exp2(st.m[i] - mx);
     st.m[i] = mx;
     st.l[i] *= alpha;
@@ -441,7 +446,7 @@ __device__ __forceinline__ void process_window(const __half* __restrict__ wk, co
 }
 
 template <int D, int BK, int BV, int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : (G <= 4 ? 2 : 1))))
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : (G <= 4 ? 2 : 1))))
 void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape ds, const __half* __restrict__ q,
                          float* __restrict__ ws) {
   constexpr int E = D / 64, DQ = D / 4, NKG = D / 32;
@@ -449,8 +454,8 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
   using MV = Magic<BV>;
 
   __shared__ __attribute__((aligned(16))) union {
-    WaveLds<D, G> w[4];
-    float res[4][G][D + 4];
+    WaveLds<D, G> w[kWaves];
+    float res[kWaves][G][D + 4];
   } sh;
 
   const int sigma = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -495,35 +500,43 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
     for (int e = 0; e < E; ++e) st.acc[i][e] = 0.f;
   }
 
-  // quantized records, the next one loaded while the current one is computed
+  // Quantized records, the next one loaded while the current one is computed. Prefetch loads
+  // are unconditional (their record index is clamped into the buffer: the last one of a
+  // wave re-reads a record it never uses) so that the compiler's memory-counter waits stay
+  // exact: a conditional load at a control-flow merge makes it wait for the prefetch too.
   const uint8_t* rec0 = buf + L.record(b, h, 0);
   const uint64_t rb = L.rec_bytes;
+  const int ulast = max(uq - 1, 0);
   int u = u0 + wave;
   if constexpr (G == 1) {
-    // two register sets refilled alternately (no copies): each record is requested one
-    // record ahead of its use
     RecordRegs<D, BK, BV> ra, rbuf;
-    if (u < uq) load_record<D, BK, BV>(rec0 + u * rb, lane, ra);
-    while (u < uq) {
-      if (u + 4 < uq) load_record<D, BK, BV>(rec0 + (u + 4) * rb, lane, rbuf);
-      process_record<D, BK, BV, G>(ra, W, st, upk, upv, qs, qf, vf0, vf1, lane);
-      u += 4;
-      if (u >= uq) break;
-      if (u + 4 < uq) load_record<D, BK, BV>(rec0 + (u + 4) * rb, lane, ra);
-      process_record<D, BK, BV, G>(rbuf, W, st, upk, upv, qs, qf, vf0, vf1, lane);
-      u += 4;
+    if (u < uq) {
+      load_record<D, BK, BV>(rec0 + u * rb, lane, ra);
+      load_record<D, BK, BV>(rec0 + min(u + kWaves, ulast) * rb, lane, rbuf);
+      while (true) {
+        process_record<D, BK, BV, G>(ra, W, st, upk, upv, qs, qf, vf0, vf1, lane);
+        u += kWaves;
+        if (u >= uq) break;
+        load_record<D, BK, BV>(rec0 + min(u + kWaves, ulast) * rb, lane, ra);
+        process_record<D, BK, BV, G>(rbuf, W, st, upk, upv, qs, qf, vf0, vf1, lane);
+        u += kWaves;
+        if (u >= uq) break;
+        load_record<D, BK, BV>(rec0 + min(u + kWaves, ulast) * rb, lane, rbuf);
+      }
     }
   } else {
     RecordRegs<D, BK, BV> cur, nxt;
-    if (u < uq) load_record<D, BK, BV>(rec0 + u * rb, lane, cur);
-    for (; u < uq; u += 4) {
-      if (u + 4 < uq) load_record<D, BK, BV>(rec0 + (u + 4) * rb, lane, nxt);
-      process_record<D, BK, BV, G>(cur, W, st, upk, upv, qs, qf, vf0, vf1, lane);
-      cur = nxt;
+    if (u < uq) {
+      load_record<D, BK, BV>(rec0 + u * rb, lane, cur);
+      for (; u < uq; u += kWaves) {
+        load_record<D, BK, BV>(rec0 + min(u + kWaves, ulast) * rb, lane, nxt);
+        process_record<D, BK, BV, G>(cur, W, st, upk, upv, qs, qf, vf0, vf1, lane);
+        cur = nxt;
+      }
     }
   }
   // window units
-  for (; u < u1; u += 4) {
+  for (; u < u1; u += kWaves) {
     const int tbase = (u - ngroups) * kGroup;
     const int nvalid = min(kGroup, nr - tbase);
     const __half* wk = reinterpret_cast<const __half*>(buf + L.wk_off + L.window(b, h)) + tbase * D;
@@ -563,14 +576,14 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
   __syncthreads();
 
   // ---- combine the 4 waves and write the partial of each query head
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
     const int i = idx / D, ch = idx % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sh.res[w][i][D]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sh.res[w][i][D]);
     float O = 0.f, Lsum = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kWaves; ++w) {
       const float mw = sh.res[w][i][D];
       if (mw != -INFINITY) {
         const float wgt = fast_exp2(mw - M);
@@ -652,7 +665,7 @@ template <int D, int BK, int BV, int G>
 static hipError_t launch_split_t(const uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q,
                                  float* ws, hipStream_t s) {
   dim3 grid(ds.n_split, L.Hkv, L.B);
-  hipLaunchKernelGGL((decode_split_kernel<D, BK, BV, G>), grid, dim3(256), 0, s, buf, L, ds,
+  hipLaunchKernelGGL((decode_split_kernel<D, BK, BV, G>), grid, dim3(64 * kWaves), 0, s, buf, L, ds,
                      static_cast<const __half*>(q), ws);
   return hipGetLastError();
 }

@@ -14,7 +14,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/kvq.h"
+#include "kvq.h"  // include/ is on the include path
 #include "kernels.h"
 #include "layout.h"
 
