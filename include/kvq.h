@@ -64,7 +64,7 @@ typedef struct kvq_config {
 } kvq_config;
 
 /* Byte offsets of the regions inside the cache buffer (see the layout description in the
- * design notes; all offsets are multiples of 256). */
+ * design notes; all offsets but sync_offset are multiples of 256). */
 typedef struct kvq_layout_info {
   uint64_t lengths_offset;  /* int32 [B][H_kv][2]: (quantized tokens, window tokens) */
   uint64_t records_offset;  /* [B][H_kv][max_tokens/32] group records */
@@ -76,6 +76,9 @@ typedef struct kvq_layout_info {
   uint64_t window_k_offset; /* fp16 [B][H_kv][R][D] */
   uint64_t window_v_offset; /* fp16 [B][H_kv][R][D] */
   uint64_t total_bytes;     /* == kvq_cache_bytes() */
+  uint64_t sync_offset;     /* uint32 [B][H_kv] decode split counters, right after the lengths;
+                               zero between calls (decode's last split of a sequence clears its
+                               counter; every lengths update zeroes them) */
 } kvq_layout_info;
 
 typedef struct kvq_cache kvq_cache; /* opaque host handle */
@@ -151,15 +154,22 @@ kvq_status kvq_append(kvq_cache* cache, const void* k_tok, const void* v_tok, vo
  *   q:   fp16 [B][H_q][D];  out: fp16 [B][H_q][D], or fp32 when out_fp32 != 0.
  *   workspace: at least kvq_workspace_bytes(cfg, n_split) device bytes (KVQ_E_WORKSPACE).
  *   n_split: maximum splits per sequence along the tokens (0 = chosen from the lengths).
- * Every sequence must hold at least one token (KVQ_E_INVALID otherwise). */
+ * Every sequence must hold at least one token (KVQ_E_INVALID otherwise).
+ * One kernel: splits along the tokens write (acc, m, l) partials to the workspace and the
+ * last split of each sequence and KV head merges them (counted in the cache's sync region).
+ * Calls on one cache must therefore be ordered (one stream, or synchronised streams). */
 kvq_status kvq_decode_attend(kvq_cache* cache, const void* q, void* out, int32_t out_fp32,
                              float sm_scale, void* workspace, size_t ws_bytes, int32_t n_split,
                              void* stream);
 
-/* Timing hook for benchmarks: while enabled, kvq_decode_attend records a pair of HIP events
- * around its split pass (the dominant kernel) on its stream. kvq_profile_read waits for the
- * recorded events and returns their total elapsed milliseconds and count, then clears them.
- * At most 4096 pairs are kept (KVQ_E_INVALID past that). */
+/* Timing hook for benchmarks: while enabled, kvq_decode_attend launches its split pass (the
+ * dominant kernel) with a pair of HIP events that the kernel's own dispatch stamps at its start
+ * and end (hipExtLaunchKernelGGL), so each pair brackets that kernel's execution on the
+ * caller's stream and nothing else. enable = n > 0 turns this on and creates the events of
+ * min(n, 4096) launches up front (so that timed launches create none); 0 turns it off.
+ * kvq_profile_read waits for the recorded events and returns their total elapsed
+ * milliseconds and count, then clears them. At most 4096 pairs are kept (KVQ_E_INVALID past
+ * that). */
 kvq_status kvq_profile_enable(kvq_cache* cache, int32_t enable);
 kvq_status kvq_profile_read(kvq_cache* cache, double* total_ms, int64_t* count);
 

@@ -38,7 +38,8 @@ class Config(ctypes.Structure):
 class LayoutInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "lengths_offset", "records_offset", "record_bytes", "rec_key_codes", "rec_value_codes",
-        "rec_key_params", "rec_value_params", "window_k_offset", "window_v_offset", "total_bytes")]
+        "rec_key_params", "rec_value_params", "window_k_offset", "window_v_offset", "total_bytes",
+        "sync_offset")]
 
 
 def _load():

@@ -111,8 +111,10 @@ class KVQCache:
             self._ws = torch.empty(need, dtype=torch.uint8, device=self.buffer.device)
         return self._ws
 
-    def profile_enable(self, on: bool = True):
-        check(lib.kvq_profile_enable(self.handle, 1 if on else 0))
+    def profile_enable(self, on: bool = True, launches: int = 1):
+        """Time each decode kernel with dispatch-stamped events; events for `launches` calls are
+        created up front."""
+        check(lib.kvq_profile_enable(self.handle, max(1, int(launches)) if on else 0))
 
     def profile_read(self):
         ms = ctypes.c_double(0)

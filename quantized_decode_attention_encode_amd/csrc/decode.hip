@@ -1,4 +1,4 @@
-// decode.hip - decode attention straight over the quantized cache (split-K + merge).
+// decode.hip - decode attention straight over the quantized cache (split-K, merged in-kernel).
 //
 // What is computed ("Changelog" v0.42.0 "Added": fused group-affine decode + attention):
 //   out = softmax(sm_scale * q . K_hat^T) V_hat over every quantized and window token,
@@ -28,7 +28,9 @@
 // Work split: grid (n_split, H_kv, B); workgroup = 4 wavefronts; a workgroup owns `chunk`
 // consecutive units of one (b, h_kv) (unit = one 32-token record, or up to 32 window
 // tokens), its waves take every 4th unit and prefetch their next record while computing
-// the current one, and the workgroup writes one (acc[D], m, l) partial per query head.
+// the current one, and the workgroup writes one (acc[D], m, l) partial per query head. The
+// last workgroup of a (b, h_kv) to finish (a counter in the cache buffer decides) merges the
+// partials of that KV head's query heads into the output; a lone split writes it directly.
 //
 // Lane roles for a record (they follow the record layout, see layout.h):
 //   q~ producer    lane l: channels l*D/64 .. (D/64 of them) = quarter l/16
@@ -36,8 +38,9 @@
 //   a producer     lane (P, Q): value params of tokens 2P, 2P+1 (D/64 entries)
 //   value consumer lane l: channels l*D/64 .., all 32 tokens of the record
 // Quarter partial scores meet through two DPP quad butterflies.
-#include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "kernels.h"
@@ -445,10 +448,93 @@ __device__ __forceinline__ void process_window(const __half* __restrict__ wk, co
   wave_sync();
 }
 
+// Split partials cross workgroups (and XCDs, each with its own L2) inside one launch. They are
+// written and read with device-scope relaxed atomics, which the hardware performs coherently
+// across the XCDs (cache-policy bit sc1) without writing back or invalidating a whole L2, which
+// a device-scope fence would do in every wave.
+__device__ __forceinline__ void put_partial(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get_partial(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_out(void* out, int out_fp32, int64_t idx, float v) {
+  if (out_fp32)
+    static_cast<float*>(out)[idx] = v;
+  else
+    static_cast<__half*>(out)[idx] = __float2half_rn(v);
+}
+
+// Merge the nv split partials (acc[D], m, l) of the G query heads row0 .. row0+G-1 into the
+// output, by one workgroup of 64*kWaves threads: T threads per output element each fold a
+// strided share of the splits (batches of 8 loads in flight), then meet through LDS.
+template <int D, int G>
+__device__ __forceinline__ void merge_splits(const float* __restrict__ ws, int64_t row0, int n_split, int nv,
+                                             float (*mrg)[64 * kWaves], void* out, int out_fp32) {
+  constexpr int NT = 64 * kWaves, NOUT = G * D;
+  constexpr int T = NOUT >= NT ? 1 : NT / NOUT;
+  constexpr int NO = NOUT >= NT ? NT : NOUT;  // output elements per pass
+  const int tid = threadIdx.x, r = tid / NO;
+  for (int oi = tid % NO; oi < NOUT; oi += NO) {
+    const int i = oi / D, ch = oi % D;
+    const float* base = ws + (row0 + i) * n_split * (D + 4);
+    float M = -INFINITY, Ls = 0.f, O = 0.f;
+    for (int s0 = r; s0 < nv; s0 += 8 * T) {
+      float m[8], l[8], o[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int sk = s0 + k * T;
+        const float* p = base + min(sk, nv - 1) * (D + 4);  // clamped: every load in bounds
+        const float mv = get_partial(p + D);
+        m[k] = sk < nv ? mv : -INFINITY;
+        l[k] = get_partial(p + D + 1);
+        o[k] = get_partial(p + ch);
+      }
+      float mx = M;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) mx = fmaxf(mx, m[k]);
+      const float sc = fast_exp2(M - mx);  // 0 while M is still -inf
+      O *= sc;
+      Ls *= sc;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float w = fast_exp2(m[k] - mx);
+        O = __builtin_fmaf(w, o[k], O);
+        Ls = __builtin_fmaf(w, l[k], Ls);
+      }
+      M = mx;
+    }
+    if constexpr (T == 1) {
+      store_out(out, out_fp32, (row0 + i) * D + ch, O / Ls);
+    } else {
+      mrg[0][tid] = M;
+      mrg[1][tid] = Ls;
+      mrg[2][tid] = O;
+    }
+  }
+  if constexpr (T > 1) {
+    __syncthreads();
+    if (tid < NO) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < T; ++j) M = fmaxf(M, mrg[0][tid + j * NO]);
+      float Ls = 0.f, O = 0.f;
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        const float w = fast_exp2(mrg[0][tid + j * NO] - M);  // a share with no split: 0
+        Ls = __builtin_fmaf(w, mrg[1][tid + j * NO], Ls);
+        O = __builtin_fmaf(w, mrg[2][tid + j * NO], O);
+      }
+      store_out(out, out_fp32, (row0 + tid / D) * D + tid % D, O / Ls);
+    }
+  }
+}
+
 template <int D, int BK, int BV, int G>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : (G <= 4 ? 2 : 1))))
 void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape ds, const __half* __restrict__ q,
-                         float* __restrict__ ws) {
+                         float* __restrict__ ws, uint32_t* __restrict__ sync, void* __restrict__ out) {
   constexpr int E = D / 64, DQ = D / 4, NKG = D / 32;
   using MK = Magic<BK>;
   using MV = Magic<BV>;
@@ -456,7 +542,9 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
   __shared__ __attribute__((aligned(16))) union {
     WaveLds<D, G> w[kWaves];
     float res[kWaves][G][D + 4];
+    float mrg[3][64 * kWaves];
   } sh;
+  __shared__ int sh_last;
 
   const int sigma = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -575,7 +663,10 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
   }
   __syncthreads();
 
-  // ---- combine the 4 waves and write the partial of each query head
+  // ---- combine the waves: the partial of each query head, or the output when this
+  // workgroup is the sequence's only split
+  const int nvalid = min(ds.n_split, (nunits + ds.chunk - 1) / ds.chunk);
+  const int64_t row0 = int64_t(b) * ds.n_q_heads + h * G;  // first query head of this KV head
   for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
     const int i = idx / D, ch = idx % D;
     float M = -INFINITY;
@@ -591,131 +682,84 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
         Lsum += wgt * sh.res[w][i][D + 1];
       }
     }
-    float* dst = ws + ((int64_t(b) * ds.n_q_heads + h * G + i) * ds.n_split + sigma) * (D + 4);
-    dst[ch] = O;
+    if (nvalid == 1) {
+      store_out(out, ds.out_fp32, (row0 + i) * D + ch, O / Lsum);
+      continue;
+    }
+    float* dst = ws + ((row0 + i) * ds.n_split + sigma) * (D + 4);
+    put_partial(dst + ch, O);
     if (ch == 0) {
-      dst[D] = M;
-      dst[D + 1] = Lsum;
+      put_partial(dst + D, M);
+      put_partial(dst + D + 1, Lsum);
     }
   }
-}
+  if (nvalid == 1) return;
 
-// Combine the split partials of one (b, h_q): one lane per split for the softmax weights,
-// then one lane per channel pair for the weighted sum.
-template <int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape ds,
-                                                          const float* __restrict__ ws, void* __restrict__ out) {
-  constexpr int E = D / 64;
-  __shared__ float wn[64];
-  const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-  const int h = hq / ds.G;
-  const int32_t* len = reinterpret_cast<const int32_t*>(buf + L.lengths(b, h));
-  const int nq = max(0, min(len[0], L.max_groups * kGroup));
-  const int nr = max(0, min(len[1], L.R));
-  const int nunits = nq / kGroup + (nr + kGroup - 1) / kGroup;
-  const int nvalid = min(ds.n_split, (nunits + ds.chunk - 1) / ds.chunk);
-  const float* base = ws + (int64_t(b) * ds.n_q_heads + hq) * ds.n_split * (D + 4);
-
-  float M = -INFINITY;
-  for (int s = lane; s < nvalid; s += 64) M = fmaxf(M, base[s * (D + 4) + D]);
-#pragma unroll
-  for (int msk = 1; msk < 64; msk <<= 1) M = fmaxf(M, __shfl_xor(M, msk, 64));
-  float Ls = 0.f;
-  for (int s = lane; s < nvalid; s += 64) {
-    const float ms = base[s * (D + 4) + D];
-    if (ms != -INFINITY) Ls += exp2f(ms - M) * base[s * (D + 4) + D + 1];
-  }
-#pragma unroll
-  for (int msk = 1; msk < 64; msk <<= 1) Ls += __shfl_xor(Ls, msk, 64);
-  const float inv = 1.f / Ls;
-
-  float O[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) O[e] = 0.f;
-  for (int s0 = 0; s0 < nvalid; s0 += 64) {
-    const int s = s0 + lane;
-    float w = 0.f;
-    if (s < nvalid) {
-      const float ms = base[s * (D + 4) + D];
-      w = (ms != -INFINITY) ? exp2f(ms - M) * inv : 0.f;
-    }
-    __syncthreads();
-    wn[lane] = w;
-    __syncthreads();
-    const int n = min(64, nvalid - s0);
-    for (int j = 0; j < n; ++j) {
-      const float wj = wn[j];
-      const float* src = base + (s0 + j) * (D + 4) + lane * E;
-#pragma unroll
-      for (int e = 0; e < E; ++e) O[e] = __builtin_fmaf(wj, src[e], O[e]);
-    }
-  }
-  const int64_t row = (int64_t(b) * ds.n_q_heads + hq) * D;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    if (ds.out_fp32)
-      static_cast<float*>(out)[row + lane * E + e] = O[e];
-    else
-      static_cast<__half*>(out)[row + lane * E + e] = __float2half_rn(O[e]);
-  }
+  // ---- the last split of (b, h_kv) to finish merges every partial. Each wave waits until its
+  // partial stores are acknowledged at device scope, the workgroup meets, and only then does
+  // one thread move the counter (a device-scope atomic, performed coherently); the workgroup
+  // that brings it to nvalid reads every partial back the same coherent way, then clears the
+  // counter for the next call.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  uint32_t* cnt = sync + (int64_t(b) * L.Hkv + h);
+  if (threadIdx.x == 0) sh_last = atomicAdd(cnt, 1u) + 1u == uint32_t(nvalid);
+  __syncthreads();
+  if (!sh_last) return;
+  merge_splits<D, G>(ws, row0, ds.n_split, nvalid, sh.mrg, out, ds.out_fp32);
+  if (threadIdx.x == 0) atomicExch(cnt, 0u);
 }
 
 // ------------------------------------------------------------------------------------
 template <int D, int BK, int BV, int G>
-static hipError_t launch_split_t(const uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q,
-                                 float* ws, hipStream_t s) {
+static hipError_t launch_split_t(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q,
+                                 float* ws, void* out, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   dim3 grid(ds.n_split, L.Hkv, L.B);
-  hipLaunchKernelGGL((decode_split_kernel<D, BK, BV, G>), grid, dim3(64 * kWaves), 0, s, buf, L, ds,
-                     static_cast<const __half*>(q), ws);
+  uint32_t* sync = reinterpret_cast<uint32_t*>(buf + L.sync_off);
+  const __half* qh = static_cast<const __half*>(q);
+  if (e0 || e1)
+    hipExtLaunchKernelGGL((decode_split_kernel<D, BK, BV, G>), grid, dim3(64 * kWaves), 0, s, e0, e1, 0,
+                          static_cast<const uint8_t*>(buf), L, ds, qh, ws, sync, out);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<D, BK, BV, G>), grid, dim3(64 * kWaves), 0, s,
+                       static_cast<const uint8_t*>(buf), L, ds, qh, ws, sync, out);
   return hipGetLastError();
 }
 
 template <int D, int BK, int BV>
-static hipError_t launch_split_g(const uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q,
-                                 float* ws, hipStream_t s) {
+static hipError_t launch_split_g(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q,
+                                 float* ws, void* out, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   switch (ds.G) {
-    case 1: return launch_split_t<D, BK, BV, 1>(buf, L, ds, q, ws, s);
-    case 2: return launch_split_t<D, BK, BV, 2>(buf, L, ds, q, ws, s);
-    case 4: return launch_split_t<D, BK, BV, 4>(buf, L, ds, q, ws, s);
-    case 8: return launch_split_t<D, BK, BV, 8>(buf, L, ds, q, ws, s);
+    case 1: return launch_split_t<D, BK, BV, 1>(buf, L, ds, q, ws, out, s, e0, e1);
+    case 2: return launch_split_t<D, BK, BV, 2>(buf, L, ds, q, ws, out, s, e0, e1);
+    case 4: return launch_split_t<D, BK, BV, 4>(buf, L, ds, q, ws, out, s, e0, e1);
+    case 8: return launch_split_t<D, BK, BV, 8>(buf, L, ds, q, ws, out, s, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int D>
-static hipError_t launch_split_d(const uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q,
-                                 float* ws, hipStream_t s) {
+static hipError_t launch_split_d(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q,
+                                 float* ws, void* out, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   switch (L.bk * 16 + L.bv) {
-    case 0x22: return launch_split_g<D, 2, 2>(buf, L, ds, q, ws, s);
-    case 0x24: return launch_split_g<D, 2, 4>(buf, L, ds, q, ws, s);
-    case 0x28: return launch_split_g<D, 2, 8>(buf, L, ds, q, ws, s);
-    case 0x42: return launch_split_g<D, 4, 2>(buf, L, ds, q, ws, s);
-    case 0x44: return launch_split_g<D, 4, 4>(buf, L, ds, q, ws, s);
-    case 0x48: return launch_split_g<D, 4, 8>(buf, L, ds, q, ws, s);
-    case 0x82: return launch_split_g<D, 8, 2>(buf, L, ds, q, ws, s);
-    case 0x84: return launch_split_g<D, 8, 4>(buf, L, ds, q, ws, s);
-    case 0x88: return launch_split_g<D, 8, 8>(buf, L, ds, q, ws, s);
+    case 0x22: return launch_split_g<D, 2, 2>(buf, L, ds, q, ws, out, s, e0, e1);
+    case 0x24: return launch_split_g<D, 2, 4>(buf, L, ds, q, ws, out, s, e0, e1);
+    case 0x28: return launch_split_g<D, 2, 8>(buf, L, ds, q, ws, out, s, e0, e1);
+    case 0x42: return launch_split_g<D, 4, 2>(buf, L, ds, q, ws, out, s, e0, e1);
+    case 0x44: return launch_split_g<D, 4, 4>(buf, L, ds, q, ws, out, s, e0, e1);
+    case 0x48: return launch_split_g<D, 4, 8>(buf, L, ds, q, ws, out, s, e0, e1);
+    case 0x82: return launch_split_g<D, 8, 2>(buf, L, ds, q, ws, out, s, e0, e1);
+    case 0x84: return launch_split_g<D, 8, 4>(buf, L, ds, q, ws, out, s, e0, e1);
+    case 0x88: return launch_split_g<D, 8, 8>(buf, L, ds, q, ws, out, s, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_decode_split(const uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q,
-                               float* ws, hipStream_t s) {
-  if (L.D == 128) return launch_split_d<128>(buf, L, ds, q, ws, s);
-  if (L.D == 64) return launch_split_d<64>(buf, L, ds, q, ws, s);
+hipError_t launch_decode(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q, float* ws,
+                         void* out, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (L.D == 128) return launch_split_d<128>(buf, L, ds, q, ws, out, s, e0, e1);
+  if (L.D == 64) return launch_split_d<64>(buf, L, ds, q, ws, out, s, e0, e1);
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_decode_merge(const uint8_t* buf, const Layout& L, const DecodeShape& ds, const float* ws,
-                               void* out, hipStream_t s) {
-  dim3 grid(ds.n_q_heads, L.B);
-  if (L.D == 128)
-    hipLaunchKernelGGL(decode_merge_kernel<128>, grid, dim3(64), 0, s, buf, L, ds, ws, out);
-  else if (L.D == 64)
-    hipLaunchKernelGGL(decode_merge_kernel<64>, grid, dim3(64), 0, s, buf, L, ds, ws, out);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
 }
 
 }  // namespace kvq

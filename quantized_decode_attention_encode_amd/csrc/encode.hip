@@ -273,6 +273,7 @@ __global__ __launch_bounds__(64) void window_fill_kernel(uint8_t* __restrict__ b
     int32_t* len = reinterpret_cast<int32_t*>(buf + L.lengths(b, h));
     len[0] = nq;
     len[1] = nr;
+    *reinterpret_cast<uint32_t*>(buf + L.sync(b, h)) = 0;  // decode split counter starts at zero
   }
 }
 
@@ -284,6 +285,7 @@ __global__ __launch_bounds__(64) void lengths_fill_kernel(uint8_t* __restrict__ 
   int32_t* len = reinterpret_cast<int32_t*>(buf + L.len_off) + 2 * i;
   len[0] = seq.a[b];
   len[1] = seq.b[b];
+  reinterpret_cast<uint32_t*>(buf + L.sync_off)[i] = 0;  // decode split counters start at zero
 }
 
 // ------------------------------------------------------------------------------------

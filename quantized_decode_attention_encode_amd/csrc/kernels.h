@@ -31,9 +31,10 @@ hipError_t launch_window_fill(uint8_t* buf, const Layout& L, const void* K, cons
                               const PerSeq& seq, hipStream_t s);
 hipError_t launch_lengths_fill(uint8_t* buf, const Layout& L, const PerSeq& seq, hipStream_t s);
 
-hipError_t launch_decode_split(const uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q,
-                               float* ws, hipStream_t s);
-hipError_t launch_decode_merge(const uint8_t* buf, const Layout& L, const DecodeShape& ds, const float* ws,
-                               void* out, hipStream_t s);
+// Decode attention: split-K kernel whose last split per (b, h_kv) merges the partials into
+// `out`. start/stop, when not null, are stamped by the kernel's own dispatch (its execution
+// time).
+hipError_t launch_decode(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q, float* ws,
+                         void* out, hipStream_t s, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 }  // namespace kvq

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -35,6 +36,7 @@ struct kvq_cache {
 
 namespace {
 
+constexpr int kMaxDevices = 64;
 thread_local std::string g_err;
 
 kvq_status fail(kvq_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -99,16 +101,20 @@ int max_auto_splits(const kvq_config* c) {
   return (units_cap + 3) / 4;
 }
 
-// Device check: the current HIP device must be a gfx950.
+// Device check: the current HIP device must be a gfx950. The verdict is kept per device id
+// (querying the properties costs far more than a kernel launch).
 kvq_status check_device() {
+  static std::atomic<int8_t> verdict[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(KVQ_E_NODEVICE, "no HIP device: %s", hipGetErrorString(e));
+  if (dev >= 0 && dev < kMaxDevices && verdict[dev].load(std::memory_order_relaxed) == 1) return ok();
   hipDeviceProp_t prop;
   e = hipGetDeviceProperties(&prop, dev);
   if (e != hipSuccess) return fail(KVQ_E_NODEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
-  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
-    return fail(KVQ_E_NODEVICE, "device %d is %s, this library is built for gfx950", dev, prop.gcnArchName);
+  const bool good = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev >= 0 && dev < kMaxDevices) verdict[dev].store(good ? 1 : -1, std::memory_order_relaxed);
+  if (!good) return fail(KVQ_E_NODEVICE, "device %d is %s, this library is built for gfx950", dev, prop.gcnArchName);
   return ok();
 }
 
@@ -169,6 +175,7 @@ kvq_status kvq_layout(const kvq_config* cfg, kvq_layout_info* out) {
   out->window_k_offset = L.wk_off;
   out->window_v_offset = L.wv_off;
   out->total_bytes = L.total;
+  out->sync_offset = L.sync_off;
   return ok();
 }
 
@@ -387,24 +394,28 @@ kvq_status kvq_decode_attend(kvq_cache* c, const void* q, void* out, int32_t out
         c->ev.push_back(ev);
       }
     }
-    e = hipEventRecord(c->ev[c->ev_used], s);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   }
-  e = kvq::launch_decode_split(c->buf, c->L, ds, q, ws, s);
-  if (e != hipSuccess) return hip_fail(e, "decode split launch");
-  if (prof) {
-    e = hipEventRecord(c->ev[c->ev_used + 1], s);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-    c->ev_used += 2;
-  }
-  e = kvq::launch_decode_merge(c->buf, c->L, ds, ws, out, s);
-  if (e != hipSuccess) return hip_fail(e, "decode merge launch");
+  // With profiling on, the events are stamped by the kernel's own dispatch packet, so their
+  // interval is its execution time (no queue or launch latency).
+  e = kvq::launch_decode(c->buf, c->L, ds, q, ws, out, s, prof ? c->ev[c->ev_used] : nullptr,
+                         prof ? c->ev[c->ev_used + 1] : nullptr);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (prof) c->ev_used += 2;
   return ok();
 }
 
 kvq_status kvq_profile_enable(kvq_cache* c, int32_t enable) {
   if (!c) return fail(KVQ_E_INVALID, "cache is NULL");
+  if (enable < 0) return fail(KVQ_E_INVALID, "enable must be >= 0");
   c->profiling = enable != 0;
+  // Create the events of `enable` launches now, so that timed launches create none.
+  const size_t want = size_t(2) * std::min(enable, kMaxProfilePairs);
+  while (c->ev.size() < want) {
+    hipEvent_t ev;
+    hipError_t e = hipEventCreate(&ev);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+    c->ev.push_back(ev);
+  }
   return ok();
 }
 

@@ -2,10 +2,11 @@
 //
 // One cache buffer per layer:
 //   lengths  int32 [B][H_kv][2]                 (quantized tokens, window tokens)
+//   sync     uint32 [B][H_kv]                   decode split counters (zero between calls)
 //   records  [B][H_kv][max_tokens/32][record]   one record per group of 32 quantized tokens
 //   window_k fp16  [B][H_kv][R][D]              the newest tokens, unquantized
 //   window_v fp16  [B][H_kv][R][D]
-// Every region starts on a 256-byte boundary.
+// Every region but sync starts on a 256-byte boundary (sync follows lengths directly).
 //
 // A record holds everything decode needs for 32 tokens, so one group streams from one
 // contiguous 4*D*(bk+bv+2)-byte block (3 KiB at D=128, 2/2 bits):
@@ -53,14 +54,15 @@ KVQ_HD constexpr uint64_t rec_off_vparams(int D, int bk, int bv) {
 // Offsets of the regions of one cache buffer.
 struct Layout {
   int B, Hkv, D, bk, bv, R, max_groups;
-  uint64_t len_off, rec_off, rec_bytes, wk_off, wv_off, total;
+  uint64_t len_off, sync_off, rec_off, rec_bytes, wk_off, wv_off, total;
 
   KVQ_HD void init(int B_, int Hkv_, int D_, int bk_, int bv_, int R_, int max_tokens) {
     B = B_; Hkv = Hkv_; D = D_; bk = bk_; bv = bv_; R = R_;
     max_groups = max_tokens / kGroup;
     rec_bytes = record_bytes(D, bk, bv);
     len_off = 0;
-    rec_off = align256(uint64_t(B) * Hkv * 2 * sizeof(int32_t));
+    sync_off = uint64_t(B) * Hkv * 2 * sizeof(int32_t);
+    rec_off = align256(sync_off + uint64_t(B) * Hkv * sizeof(uint32_t));
     wk_off = align256(rec_off + uint64_t(B) * Hkv * max_groups * rec_bytes);
     uint64_t wbytes = uint64_t(B) * Hkv * R * D * 2;
     wv_off = align256(wk_off + wbytes);
@@ -73,6 +75,7 @@ struct Layout {
   // first window slot of (b, h), in bytes from the buffer start (K; V at wv_off)
   KVQ_HD uint64_t window(int b, int h) const { return (uint64_t(b) * Hkv + h) * R * D * 2; }
   KVQ_HD uint64_t lengths(int b, int h) const { return len_off + (uint64_t(b) * Hkv + h) * 8; }
+  KVQ_HD uint64_t sync(int b, int h) const { return sync_off + (uint64_t(b) * Hkv + h) * 4; }
 };
 
 }  // namespace kvq

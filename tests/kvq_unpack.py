@@ -18,8 +18,8 @@ def align256(x: int) -> int:
 def offsets(B, Hkv, D, bk, bv, R, max_tokens):
     max_groups = max_tokens // 32
     rec = 4 * D * (bk + bv + 2)
-    o = {"lengths": 0}
-    o["records"] = align256(B * Hkv * 2 * 4)
+    o = {"lengths": 0, "sync": B * Hkv * 2 * 4}
+    o["records"] = align256(o["sync"] + B * Hkv * 4)
     o["record_bytes"] = rec
     o["rec_key_codes"] = 0
     o["rec_value_codes"] = 4 * D * bk

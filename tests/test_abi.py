@@ -90,6 +90,7 @@ def test_layout_matches_independent_formula(D, bk, bv, R, B, H):
         o["rec_key_codes"], o["rec_value_codes"], o["rec_key_params"], o["rec_value_params"])
     assert info.window_k_offset == o["window_k"] and info.window_v_offset == o["window_v"]
     assert info.total_bytes == o["total"] == lib.kvq_cache_bytes(ctypes.byref(c))
+    assert info.sync_offset == o["sync"]
     for off in (info.records_offset, info.window_k_offset, info.window_v_offset, info.total_bytes):
         assert off % 256 == 0
 

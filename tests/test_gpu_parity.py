@@ -202,6 +202,36 @@ def test_poisoned_outputs_are_fully_written_and_runs_repeat_exactly():
     assert torch.isfinite(out16).all()
 
 
+@pytest.mark.parametrize("fill", ["prefill", "encode", "reset+encode"])
+def test_split_merge_on_a_reused_buffer(fill):
+    # The last split of a sequence merges the others, counted in the cache's sync region. Every
+    # call that sets lengths must also clear those counters, or a buffer that held another cache
+    # (here: all 0xFF) leaves them stale and no split ever merges.
+    case = ("reuse", 3, 8, 4, 128, 2, 2, None)
+    wl, draw, cfg = make(case, seed=21, seq_lens=[64 * 7, 64 * 3, 64 * 5])
+    nbytes = KVQCache(cfg, device=DEV).buffer.numel()
+    c = KVQCache(cfg, device=DEV, buffer=torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=DEV))
+    K, V, lens = draw.padded()
+    Kt, Vt = torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV)
+    if fill == "prefill":
+        kvq_prefill(c, Kt, Vt, lens)
+    else:
+        if fill == "reset+encode":
+            c.reset()
+        kvq_encode(c, Kt, Vt, lens)  # every length is a multiple of 32: all quantized, no window
+    q = torch.from_numpy(draw.q).to(DEV)
+    one = kvq_decode_attend(c, q, out_fp32=True, n_split=1).cpu().numpy()
+    vmax = float(np.abs(V).max()) * 1.1
+    for n_split in (2, 3, 7, 2):
+        for fp32 in (True, False):
+            out = torch.full(tuple(q.shape), float("nan"), dtype=torch.float32 if fp32 else torch.float16, device=DEV)
+            kvq_decode_attend(c, q, out=out, out_fp32=fp32, n_split=n_split)
+            o = out.float().cpu().numpy()
+            assert np.isfinite(o).all(), f"{fill} n_split={n_split} fp32={fp32}: outputs left unwritten"
+            bound = (2 * 2.0 ** -12 * vmax + 2e-5) if fp32 else 2e-3
+            assert np.max(np.abs(o - one)) < bound, f"{fill} n_split={n_split} fp32={fp32}"
+
+
 def test_capacity_and_state_errors_on_device():
     cfg = make_config(1, 1, 1, 64, 2, 2, 32, 32, 64)
     c = KVQCache(cfg, device=DEV)
