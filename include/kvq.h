@@ -132,6 +132,22 @@ kvq_status kvq_cache_lengths(const kvq_cache* cache, int32_t* n_quantized, int32
 kvq_status kvq_encode(kvq_cache* cache, const void* K, const void* V, int64_t ld_tok,
                       const int32_t* n_tok, void* stream);
 
+/* Stateless form of the same quantizer, for checking it element by element ("Changelog"
+ * v0.8.0 KIVI: per-channel keys, per-token values; v0.42.0 codes + per-group (scale, zero)).
+ * Quantizes one fp16 block X [n_tok][D] (device, row-major) to `bits`-bit codes in groups of
+ * `group` elements:
+ *   per_channel != 0: a group is `group` consecutive tokens of one channel (the key rule);
+ *     n_tok % group == 0; scales and zeros are fp16 [n_tok/group][D];
+ *   per_channel == 0: a group is `group` consecutive channels of one token (the value rule);
+ *     D % group == 0; scales and zeros are fp16 [n_tok][D/group].
+ *   codes: uint8 [n_tok][D], one unpacked code per element.
+ * bits in {2, 4, 8}, group == 32 (KVQ_E_UNSUPPORTED otherwise); n_tok >= 0, 1 <= D <= 4096
+ * (KVQ_E_INVALID otherwise). All buffers are caller-owned device memory; nothing is
+ * allocated. The arithmetic is exactly kvq_encode's, so codes, scales and zeros equal the
+ * record contents bit for bit. Asynchronous on `stream`. */
+kvq_status kvq_encode_block(const void* X, int32_t n_tok, int32_t D, int32_t bits, int32_t group,
+                            int32_t per_channel, void* codes, void* scales, void* zeros, void* stream);
+
 /* Fill an EMPTY cache with seq_len[b] tokens per sequence following the window rule of the
  * residual window ("Changelog" v0.8.0, v0.28.0): the first S - n_r tokens are quantized and
  * the last n_r = ((S - 1) mod R) + 1 stay fp16 (S = 0 leaves the sequence empty).

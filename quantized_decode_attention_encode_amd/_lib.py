@@ -44,7 +44,7 @@ class LayoutInfo(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m quantized_decode_attention_encode_amd.build` "
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python quantized_decode_attention_encode_amd/build.py` "
                           "(there is no CPU fallback)")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, SZ, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
@@ -61,6 +61,7 @@ def _load():
         "kvq_reset": (I32, [P, P]),
         "kvq_cache_lengths": (I32, [P, pi32, pi32]),
         "kvq_encode": (I32, [P, P, P, I64, pi32, P]),
+        "kvq_encode_block": (I32, [P, I32, I32, I32, I32, I32, P, P, P, P]),
         "kvq_prefill": (I32, [P, P, P, I64, pi32, P]),
         "kvq_append": (I32, [P, P, P, P]),
         "kvq_decode_attend": (I32, [P, P, P, I32, F32, P, SZ, I32, P]),
@@ -78,7 +79,7 @@ def _load():
 
 lib = _load()
 EXPORTED = ("kvq_probe", "kvq_config_check", "kvq_cache_bytes", "kvq_layout", "kvq_workspace_bytes",
-            "kvq_cache_create", "kvq_cache_destroy", "kvq_reset", "kvq_cache_lengths", "kvq_encode",
+            "kvq_cache_create", "kvq_cache_destroy", "kvq_reset", "kvq_cache_lengths", "kvq_encode", "kvq_encode_block",
             "kvq_prefill", "kvq_append", "kvq_decode_attend", "kvq_profile_enable", "kvq_profile_read",
             "kvq_last_error", "kvq_status_string")
 

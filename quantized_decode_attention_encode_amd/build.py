@@ -1,6 +1,7 @@
 """Builds libkvq.so (the C-ABI library with the gfx950 HIP kernels) in-tree with hipcc.
 
-Usage:  python -m quantized_decode_attention_encode_amd.build   (or call build())
+Usage:  python quantized_decode_attention_encode_amd/build.py   (or call build())
+Run it by path: importing the package loads the library this script builds.
 """
 from __future__ import annotations
 

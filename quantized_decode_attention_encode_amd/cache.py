@@ -137,6 +137,23 @@ def kvq_encode(cache: KVQCache, K: torch.Tensor, V: torch.Tensor, n_tok, stream=
     check(lib.kvq_encode(cache.handle, _dev(K, "K"), _dev(V, "V"), K.shape[2], _i32(n_tok), _stream(stream)))
 
 
+def kvq_encode_block(X: torch.Tensor, bits: int, per_channel: bool, group: int = 32, stream=None):
+    """Quantize one fp16 block X [n_tok, D] in groups of `group` (per_channel: along tokens, the
+    key rule; else along channels, the value rule). Returns (codes uint8 [n_tok, D], scale fp16,
+    zero fp16) with scale/zero [n_tok/group, D] or [n_tok, D/group]."""
+    if X.dim() != 2:
+        raise KVQError(-1, "X must be [n_tok, D]")
+    n_tok, D = X.shape
+    pshape = (n_tok // group, D) if per_channel else (n_tok, D // group)
+    codes = torch.empty((n_tok, D), dtype=torch.uint8, device=X.device)
+    scale = torch.empty(pshape, dtype=torch.float16, device=X.device)
+    zero = torch.empty(pshape, dtype=torch.float16, device=X.device)
+    check(lib.kvq_encode_block(_dev(X, "X"), n_tok, D, int(bits), int(group), 1 if per_channel else 0,
+                               _dev(codes, "codes", torch.uint8), _dev(scale, "scale"), _dev(zero, "zero"),
+                               _stream(stream)))
+    return codes, scale, zero
+
+
 def kvq_prefill(cache: KVQCache, K: torch.Tensor, V: torch.Tensor, seq_len, stream=None) -> None:
     """Fill an empty cache with seq_len[b] tokens per sequence (window rule applied)."""
     _kv_shape_check(cache, K, V)

@@ -277,6 +277,40 @@ __global__ __launch_bounds__(64) void window_fill_kernel(uint8_t* __restrict__ b
   }
 }
 
+// Stateless encode of one fp16 block X [n_tok][D] (the kvq_encode_block test hook): one
+// thread per group, with the same min/max, parameters and codes as the record encoder.
+// per_channel: groups of `group` consecutive tokens of a channel (keys), scales [n_tok/group][D];
+// else groups of `group` consecutive channels of a token (values), scales [n_tok][D/group].
+// codes: one byte per element of X.
+template <int B>
+__global__ __launch_bounds__(64) void encode_block_kernel(const __half* __restrict__ X, int n_tok, int D, int group,
+                                                          int per_channel, uint8_t* __restrict__ codes,
+                                                          uint16_t* __restrict__ scales,
+                                                          uint16_t* __restrict__ zeros) {
+  const int64_t gi = int64_t(blockIdx.x) * 64 + threadIdx.x;
+  const int64_t ngroups = per_channel ? int64_t(n_tok / group) * D : int64_t(n_tok) * (D / group);
+  if (gi >= ngroups) return;
+  int64_t base, stride;
+  if (per_channel) {
+    base = (gi / D) * group * D + gi % D;
+    stride = D;
+  } else {
+    base = (gi / (D / group)) * D + (gi % (D / group)) * group;
+    stride = 1;
+  }
+  float mn = __half2float(X[base]), mx = mn;
+  for (int j = 1; j < group; ++j) {
+    const float x = __half2float(X[base + j * stride]);
+    mn = fminf(mn, x);
+    mx = fmaxf(mx, x);
+  }
+  const GroupParams p = group_params<B>(mn, mx);
+  scales[gi] = uint16_t(p.packed & 0xFFFF);
+  zeros[gi] = uint16_t(p.packed >> 16);
+  for (int j = 0; j < group; ++j)
+    codes[base + j * stride] = uint8_t(code_of<B>(__half2float(X[base + j * stride]), p));
+}
+
 // Set the lengths of every (b, h) to (seq.a[b], seq.b[b]).
 __global__ __launch_bounds__(64) void lengths_fill_kernel(uint8_t* __restrict__ buf, Layout L, PerSeq seq) {
   const int i = blockIdx.x * 64 + threadIdx.x;
@@ -352,6 +386,24 @@ hipError_t launch_window_fill(uint8_t* buf, const Layout& L, const void* K, cons
 hipError_t launch_lengths_fill(uint8_t* buf, const Layout& L, const PerSeq& seq, hipStream_t s) {
   const int n = L.B * L.Hkv;
   hipLaunchKernelGGL(lengths_fill_kernel, dim3((n + 63) / 64), dim3(64), 0, s, buf, L, seq);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode_block(const void* X, int n_tok, int D, int bits, int group, int per_channel, void* codes,
+                               void* scales, void* zeros, hipStream_t s) {
+  const int64_t ngroups = per_channel ? int64_t(n_tok / group) * D : int64_t(n_tok) * (D / group);
+  if (ngroups == 0) return hipSuccess;
+  const dim3 grid(unsigned((ngroups + 63) / 64));
+  const __half* x = static_cast<const __half*>(X);
+  uint8_t* c = static_cast<uint8_t*>(codes);
+  uint16_t* sc = static_cast<uint16_t*>(scales);
+  uint16_t* z = static_cast<uint16_t*>(zeros);
+  switch (bits) {
+    case 2: hipLaunchKernelGGL(encode_block_kernel<2>, grid, dim3(64), 0, s, x, n_tok, D, group, per_channel, c, sc, z); break;
+    case 4: hipLaunchKernelGGL(encode_block_kernel<4>, grid, dim3(64), 0, s, x, n_tok, D, group, per_channel, c, sc, z); break;
+    case 8: hipLaunchKernelGGL(encode_block_kernel<8>, grid, dim3(64), 0, s, x, n_tok, D, group, per_channel, c, sc, z); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -29,6 +29,8 @@ hipError_t launch_encode(uint8_t* buf, const Layout& L, const void* K, const voi
 hipError_t launch_append(uint8_t* buf, const Layout& L, const void* k, const void* v, hipStream_t s);
 hipError_t launch_window_fill(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,
                               const PerSeq& seq, hipStream_t s);
+hipError_t launch_encode_block(const void* X, int n_tok, int D, int bits, int group, int per_channel, void* codes,
+                               void* scales, void* zeros, hipStream_t s);
 hipError_t launch_lengths_fill(uint8_t* buf, const Layout& L, const PerSeq& seq, hipStream_t s);
 
 // Decode attention: split-K kernel whose last split per (b, h_kv) merges the partials into

@@ -280,6 +280,25 @@ kvq_status kvq_encode(kvq_cache* c, const void* K, const void* V, int64_t ld_tok
   return ok();
 }
 
+kvq_status kvq_encode_block(const void* X, int32_t n_tok, int32_t D, int32_t bits, int32_t group,
+                            int32_t per_channel, void* codes, void* scales, void* zeros, void* stream) {
+  if (bits != 2 && bits != 4 && bits != 8) return fail(KVQ_E_UNSUPPORTED, "bits = %d; supported: 2, 4, 8", bits);
+  if (group != kvq::kGroup) return fail(KVQ_E_UNSUPPORTED, "group = %d; supported: %d", group, kvq::kGroup);
+  if (n_tok < 0) return fail(KVQ_E_INVALID, "n_tok = %d is negative", n_tok);
+  if (D < 1 || D > 4096) return fail(KVQ_E_INVALID, "D = %d is outside [1, 4096]", D);
+  if (per_channel && n_tok % group)
+    return fail(KVQ_E_INVALID, "per-channel groups need n_tok %% %d == 0 (n_tok = %d)", group, n_tok);
+  if (!per_channel && D % group) return fail(KVQ_E_INVALID, "per-token groups need D %% %d == 0 (D = %d)", group, D);
+  if (n_tok == 0) return ok();
+  if (!X || !codes || !scales || !zeros) return fail(KVQ_E_INVALID, "NULL buffer");
+  kvq_status st = check_device();
+  if (st != KVQ_OK) return st;
+  hipError_t e = kvq::launch_encode_block(X, n_tok, D, bits, group, per_channel ? 1 : 0, codes, scales, zeros,
+                                          static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "encode_block launch");
+  return ok();
+}
+
 kvq_status kvq_prefill(kvq_cache* c, const void* K, const void* V, int64_t ld_tok, const int32_t* seq_len,
                        void* stream) {
   if (!c) return fail(KVQ_E_INVALID, "cache is NULL");

@@ -165,6 +165,22 @@ def test_host_side_errors_before_any_launch():
         lib.kvq_cache_destroy(h)
 
 
+def test_encode_block_validates_on_the_host():
+    P = ctypes.c_void_p(FAKE)
+    # bit width and group size outside the supported set
+    assert lib.kvq_encode_block(P, 32, 64, 3, 32, 1, P, P, P, None) == KVQ_E_UNSUPPORTED
+    assert lib.kvq_encode_block(P, 32, 64, 2, 16, 1, P, P, P, None) == KVQ_E_UNSUPPORTED
+    # key rule needs 32 | n_tok, value rule needs 32 | D; D and n_tok ranges; NULL buffers
+    assert lib.kvq_encode_block(P, 33, 64, 2, 32, 1, P, P, P, None) == KVQ_E_INVALID
+    assert lib.kvq_encode_block(P, 33, 40, 2, 32, 0, P, P, P, None) == KVQ_E_INVALID
+    assert lib.kvq_encode_block(P, 32, 0, 2, 32, 1, P, P, P, None) == KVQ_E_INVALID
+    assert lib.kvq_encode_block(P, 32, 4097, 2, 32, 1, P, P, P, None) == KVQ_E_INVALID
+    assert lib.kvq_encode_block(P, -32, 64, 2, 32, 1, P, P, P, None) == KVQ_E_INVALID
+    assert lib.kvq_encode_block(P, 32, 64, 2, 32, 1, P, None, P, None) == KVQ_E_INVALID
+    # an empty block needs no device
+    assert lib.kvq_encode_block(None, 0, 64, 4, 32, 0, None, None, None, None) == KVQ_OK
+
+
 @pytest.mark.skipif(torch_cuda, reason="checks the no-device path")
 def test_device_calls_fail_cleanly_without_a_gpu():
     c = cfg(batch=1, n_kv_heads=1, n_q_heads=1, max_tokens=256)
