@@ -53,8 +53,9 @@ def algorithmic_encode_bytes(wl, n_q_tokens):
 
 
 def cpu_baseline(wl, draw, budget_s=12.0):
-    """The oracle's decode (reconstruct K_hat/V_hat, fp64 softmax attention) on sampled heads."""
-    import numpy as np
+    """The oracle's decode (reconstruct K_hat/V_hat, fp64 softmax attention) on a sample of the
+    KV heads of sequence 0, scaled by tokens to the whole step (every sequence, head and layer)."""
+    import numpy as np  # noqa: F401
 
     from oracle import kivi
 
@@ -68,14 +69,15 @@ def cpu_baseline(wl, draw, budget_s=12.0):
     heads = 0
     t_enc = 0.0
     H = wl.n_kv_heads
+    G = wl.n_q_heads // H
+    S0 = draw.seq_lens[0]
     for h in range(H):
         s = kivi.KiviSequence(wl.head_dim, wl.key_bits, wl.value_bits, 32, wl.residual)
         t0 = time.perf_counter()
         s.prefill(draw.K[0][h], draw.V[0][h])
         t1 = time.perf_counter()
         kh, vh = s.keys_hat(), s.values_hat()
-        hq0 = h * (wl.n_q_heads // H)
-        for hq in range(hq0, hq0 + wl.n_q_heads // H):
+        for hq in range(h * G, h * G + G):
             kivi.attend(draw.q[0, hq], kh, vh)
         t2 = time.perf_counter()
         t_enc += t1 - t0
@@ -83,13 +85,26 @@ def cpu_baseline(wl, draw, budget_s=12.0):
         heads += 1
         if t_dec + t_enc > budget_s:
             break
-    scale = (H / heads) * wl.batch
+    head_tokens = sum(draw.seq_lens) * H * wl.layers  # (KV head, token) pairs of one step
+    scale = head_tokens / (heads * S0)
     return {
         "value": t_dec * scale * 1e6, "unit": "us/step (decode-attend)", "cores": int(threads), "kind": "oracle",
-        "sample": f"{heads} of {H} KV heads of sequence 0, scaled x{scale:g}; oracle decode = dequantize "
-                  f"to fp64 + softmax attention; host os.cpu_count()={os.cpu_count()}",
-        "encode_tokens_per_s": wl.batch * (wl.seq_len or 0) / (t_enc * scale) if t_enc else None,
+        "sample": f"{heads} of {H} KV heads of sequence 0 ({S0} tokens), scaled by tokens x{scale:g} to every "
+                  f"sequence, head and layer; oracle decode = dequantize to fp64 + softmax attention; host "
+                  f"os.cpu_count()={os.cpu_count()}",
+        "encode_tokens_per_s": (heads * S0) / (t_enc * H) if t_enc else None,
     }
+
+
+def device_record(torch):
+    """What the run was measured on: the GPU's properties as HIP reports them, and the versions."""
+    p = torch.cuda.get_device_properties(0)
+    rec = {k: getattr(p, k) for k in ("name", "gcnArchName", "multi_processor_count", "total_memory",
+                                      "L2_cache_size", "clock_rate", "memory_clock_rate", "memory_bus_width")
+           if hasattr(p, k)}
+    rec["hip"] = torch.version.hip
+    rec["torch"] = torch.__version__
+    return rec
 
 
 def main():
@@ -119,14 +134,15 @@ def main():
         sys.exit(1)
     dev = "cuda"
     wl = workloads.WORKLOADS[args.workload]
-    if wl.layers != 1:
-        print("bench.py times single-layer workloads", file=sys.stderr)
-        sys.exit(2)
-    draw = workloads.Draw(wl)
+    # Single-layer workloads rotate over `replicas` copies of one cache (one cache per step);
+    # the multi-layer workload keeps one cache per layer and a step visits every layer.
+    multi = wl.layers > 1
+    n_caches = wl.layers if multi else args.replicas
+    draw = workloads.Draw(wl)  # multi-layer: layer 0's K/V fill every layer (costs do not depend on values)
     K, V, lens = draw.padded()
     n_steps_total = args.steps + args.warmup
-    per_rep = (n_steps_total + args.replicas - 1) // args.replicas
-    cap = (max(lens) + per_rep + 64 + 31) // 32 * 32
+    per_cache = n_steps_total if multi else (n_steps_total + n_caches - 1) // n_caches
+    cap = (max(lens) + per_cache + 64 + 31) // 32 * 32
     cfg = make_config(wl.batch, wl.n_kv_heads, wl.n_q_heads, wl.head_dim, wl.key_bits, wl.value_bits, 32,
                       wl.residual, cap)
     Kt, Vt = torch.from_numpy(K).to(dev), torch.from_numpy(V).to(dev)
@@ -134,7 +150,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     # ---- prefill encode rate (reset + prefill, prefill timed alone)
-    caches = [KVQCache(cfg, device=dev) for _ in range(args.replicas)]
+    caches = [KVQCache(cfg, device=dev) for _ in range(n_caches)]
     enc_ms = []
     for r in range(args.encode_reps):
         c = caches[0]
@@ -162,7 +178,7 @@ def main():
     del Kt, Vt
     torch.cuda.synchronize()
 
-    # The timed loop makes exactly the two C-ABI calls of a step, with every argument prepared
+    # The timed loop makes exactly the C-ABI calls of a step, with every argument prepared
     # beforehand (the checked Python wrappers cost more host time than the GPU work of a step).
     from quantized_decode_attention_encode_amd import _lib
     import ctypes
@@ -172,21 +188,22 @@ def main():
     vp = [ctypes.c_void_p(vt[i].data_ptr()) for i in range(n_steps_total)]
     dec_args = [(c.handle, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(o.data_ptr()), 0, 1.0,
                  ctypes.c_void_p(w.data_ptr()), w.numel(), args.n_split, sp) for c, o, w in zip(caches, outs, wss)]
+    visits = (lambda i: range(n_caches)) if multi else (lambda i: (i % n_caches,))
 
     def step(i):
-        r = i % args.replicas
-        st = lib.kvq_append(caches[r].handle, kp[i], vp[i], sp)
-        st = st or lib.kvq_decode_attend(*dec_args[r])
-        if st:
-            _lib.check(st)
+        for r in visits(i):
+            st = lib.kvq_append(caches[r].handle, kp[i], vp[i], sp)
+            st = st or lib.kvq_decode_attend(*dec_args[r])
+            if st:
+                _lib.check(st)
 
-    # lengths each decode sees, replayed from the window rule (one appended token per step)
+    # lengths each decode sees, replayed from the window rule (one appended token per visit)
     lens_now = [c.lengths() for c in caches]
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     for c in caches:
-        c.profile_enable(True, launches=(args.steps + args.replicas - 1) // args.replicas)
+        c.profile_enable(True, launches=args.steps if multi else (args.steps + n_caches - 1) // n_caches)
     t_ev0, t_ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_ev0.record(stream)
@@ -198,14 +215,15 @@ def main():
     wall1 = time.perf_counter()
     bytes_per_launch = []
     for i in range(n_steps_total):
-        nq, nr = lens_now[i % args.replicas]
-        for b in range(wl.batch):
-            if nr[b] == wl.residual:
-                nq[b] += wl.residual
-                nr[b] = 0
-            nr[b] += 1
-        if i >= args.warmup:
-            bytes_per_launch.append(algorithmic_decode_bytes(wl, nq, nr))
+        for r in visits(i):
+            nq, nr = lens_now[r]
+            for b in range(wl.batch):
+                if nr[b] == wl.residual:
+                    nq[b] += wl.residual
+                    nr[b] = 0
+                nr[b] += 1
+            if i >= args.warmup:
+                bytes_per_launch.append(algorithmic_decode_bytes(wl, nq, nr))
     for r, c in enumerate(caches):
         assert tuple(map(list, lens_now[r])) == tuple(map(list, c.lengths())), "length replay disagrees"
     step_ms = t_ev0.elapsed_time(t_ev1) / args.steps
@@ -257,8 +275,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: {wl.describe()}",
-            "step": "kvq_append (flush every 32nd append) + kvq_decode_attend (one kernel: splits + in-kernel merge)",
-            "replicas": args.replicas,
+            "step": ("every layer: " if multi else "")
+            + "kvq_append (flush every 32nd append) + kvq_decode_attend (one kernel: splits + in-kernel merge)",
+            "caches": f"{n_caches} layer caches" if multi else f"{n_caches} replicas of one cache, one per step",
             "codes": f"{wl.key_bits}-bit keys / {wl.value_bits}-bit values, fp16 (scale, zero), fp32 softmax",
         },
         "roofline": {
@@ -280,7 +299,11 @@ def main():
         "encode_gbps": round(enc_gbs, 1),
         "encode_prefill_us": round(enc_t * 1e6, 2),
         "wall_s_timed": round(wall1 - wall0, 3),
+        "device": device_record(torch),
     }
+    if multi:
+        result["encode_all_layers_us"] = round(enc_t * 1e6 * wl.layers, 1)
+        result["decode_launches_per_step"] = wl.layers
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, draw)
     print(json.dumps(result), flush=True)

@@ -61,7 +61,6 @@ kvq_status hip_fail(hipError_t e, const char* what) {
 
 constexpr int kMaxResidual = 256;
 constexpr int kMaxProfilePairs = 4096;
-constexpr int kTargetWorkgroups = 1024;  // ~4 workgroups (16 waves) per CU on 256 CUs
 
 kvq_status check_config(const kvq_config* c) {
   if (!c) return fail(KVQ_E_INVALID, "config is NULL");
@@ -101,21 +100,44 @@ int max_auto_splits(const kvq_config* c) {
   return (units_cap + 3) / 4;
 }
 
-// Device check: the current HIP device must be a gfx950. The verdict is kept per device id
-// (querying the properties costs far more than a kernel launch).
-kvq_status check_device() {
+// Device check: the current HIP device must be a gfx950. The verdict and the CU count are kept
+// per device id (querying the properties costs far more than a kernel launch).
+int g_cus[kMaxDevices];  // CUs of each checked gfx950 device
+
+kvq_status check_device(int* cus = nullptr) {
   static std::atomic<int8_t> verdict[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(KVQ_E_NODEVICE, "no HIP device: %s", hipGetErrorString(e));
-  if (dev >= 0 && dev < kMaxDevices && verdict[dev].load(std::memory_order_relaxed) == 1) return ok();
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached && verdict[dev].load(std::memory_order_acquire) == 1) {
+    if (cus) *cus = g_cus[dev];
+    return ok();
+  }
   hipDeviceProp_t prop;
   e = hipGetDeviceProperties(&prop, dev);
   if (e != hipSuccess) return fail(KVQ_E_NODEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
   const bool good = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-  if (dev >= 0 && dev < kMaxDevices) verdict[dev].store(good ? 1 : -1, std::memory_order_relaxed);
-  if (!good) return fail(KVQ_E_NODEVICE, "device %d is %s, this library is built for gfx950", dev, prop.gcnArchName);
+  if (!good) {
+    if (cached) verdict[dev].store(-1, std::memory_order_release);
+    return fail(KVQ_E_NODEVICE, "device %d is %s, this library is built for gfx950", dev, prop.gcnArchName);
+  }
+  if (cached) {
+    g_cus[dev] = prop.multiProcessorCount;
+    verdict[dev].store(1, std::memory_order_release);
+  }
+  if (cus) *cus = prop.multiProcessorCount;
   return ok();
+}
+
+// Workgroups the automatic split aims for: two per CU when the sequences are about equally
+// long, three when they are ragged (max > 1.5 x mean units), where smaller chunks fill the
+// gaps the short sequences leave. Both were the fastest of 2, 3 and 4 per CU on the uniform
+// (one 64K-token sequence; 8 x 32K tokens, 4 query heads per KV head) and ragged (16
+// sequences of 1K..16K tokens) workloads.
+int target_workgroups(int cus, int max_units, int64_t total_units, int64_t seq_heads) {
+  const bool ragged = double(max_units) * double(seq_heads) > 1.5 * double(total_units);
+  return std::max(1, cus) * (ragged ? 3 : 2);
 }
 
 kvq_status ensure_ready(kvq_cache* c, hipStream_t s) {
@@ -384,7 +406,11 @@ kvq_status kvq_decode_attend(kvq_cache* c, const void* q, void* out, int32_t out
   if (n_split > 0) {
     chunk = (max_units + n_split - 1) / n_split;
   } else {
-    chunk = int((total_units + kTargetWorkgroups - 1) / kTargetWorkgroups);
+    int cus = 0;
+    kvq_status dst = check_device(&cus);
+    if (dst != KVQ_OK) return dst;
+    const int64_t target = target_workgroups(cus, max_units, total_units, int64_t(cfg.batch) * cfg.n_kv_heads);
+    chunk = int((total_units + target - 1) / target);
     chunk = std::max(4, (chunk + 3) / 4 * 4);
   }
   const int ns = (max_units + chunk - 1) / chunk;
