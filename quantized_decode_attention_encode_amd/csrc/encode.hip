@@ -212,19 +212,28 @@ __global__ __launch_bounds__(64) void encode_kernel(uint8_t* __restrict__ buf, L
   encode_record<D, BK, BV>(K + row0, V + row0, reinterpret_cast<uint32_t*>(buf + L.record(b, h, j)), lds);
 }
 
-// Append one token per (b, h); a full window is flushed first (R/32 records).
+// Append one token per (b, h); a full window is flushed first (R/32 records). seq holds every
+// sequence's lengths before the append (the host's mirror of the device lengths), so the
+// token's loads and the flush decision wait for no device read.
 template <int D, int BK, int BV>
 __global__ __launch_bounds__(64) void append_kernel(uint8_t* __restrict__ buf, Layout L,
                                                     const __half* __restrict__ k_tok,
-                                                    const __half* __restrict__ v_tok) {
+                                                    const __half* __restrict__ v_tok, PerSeq seq) {
   __shared__ EncodeLds<D, BK, BV> lds;
   const int h = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x;
-  int32_t* len = reinterpret_cast<int32_t*>(buf + L.lengths(b, h));
-  int nq = len[0], nr = len[1];
+  constexpr int HPL = D / 64;  // halves per lane
+  const int64_t src = (int64_t(b) * L.Hkv + h) * D;
+  __half kt[HPL], vt[HPL];
+#pragma unroll
+  for (int e = 0; e < HPL; ++e) {
+    kt[e] = k_tok[src + lane * HPL + e];
+    vt[e] = v_tok[src + lane * HPL + e];
+  }
+  int nq = seq.a[b], nr = seq.b[b];
   __half* wk = reinterpret_cast<__half*>(buf + L.wk_off + L.window(b, h));
   __half* wv = reinterpret_cast<__half*>(buf + L.wv_off + L.window(b, h));
-  if (nr >= L.R) {
+  if (nr >= L.R) {  // uniform over the workgroup
     const int j0 = nq / kGroup;
     for (int m = 0; m < L.R / kGroup; ++m) {
       if (j0 + m < L.max_groups)
@@ -233,18 +242,15 @@ __global__ __launch_bounds__(64) void append_kernel(uint8_t* __restrict__ buf, L
     }
     nq += L.R;
     nr = 0;
+    __syncthreads();  // every lane has read the window before slot 0 is overwritten
   }
-  __syncthreads();
-  const int64_t src = (int64_t(b) * L.Hkv + h) * D;
-  constexpr int HPL = D / 64;  // halves per lane
-  if (nr < L.R) {
-    for (int e = 0; e < HPL; ++e) {
-      wk[nr * D + lane * HPL + e] = k_tok[src + lane * HPL + e];
-      wv[nr * D + lane * HPL + e] = v_tok[src + lane * HPL + e];
-    }
+#pragma unroll
+  for (int e = 0; e < HPL; ++e) {
+    wk[nr * D + lane * HPL + e] = kt[e];
+    wv[nr * D + lane * HPL + e] = vt[e];
   }
-  __syncthreads();
   if (lane == 0) {
+    int32_t* len = reinterpret_cast<int32_t*>(buf + L.lengths(b, h));
     len[0] = nq;
     len[1] = nr + 1;
   }
@@ -335,10 +341,11 @@ static hipError_t launch_encode_t(uint8_t* buf, const Layout& L, const void* K, 
 }
 
 template <int D, int BK, int BV>
-static hipError_t launch_append_t(uint8_t* buf, const Layout& L, const void* k, const void* v, hipStream_t s) {
+static hipError_t launch_append_t(uint8_t* buf, const Layout& L, const void* k, const void* v, const PerSeq& seq,
+                                  hipStream_t s) {
   dim3 grid(L.Hkv, L.B);
   hipLaunchKernelGGL((append_kernel<D, BK, BV>), grid, dim3(64), 0, s, buf, L,
-                     static_cast<const __half*>(k), static_cast<const __half*>(v));
+                     static_cast<const __half*>(k), static_cast<const __half*>(v), seq);
   return hipGetLastError();
 }
 
@@ -363,9 +370,10 @@ hipError_t launch_encode(uint8_t* buf, const Layout& L, const void* K, const voi
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_append(uint8_t* buf, const Layout& L, const void* k, const void* v, hipStream_t s) {
-  if (L.D == 128) { KVQ_DISPATCH_BITS(128, launch_append_t, buf, L, k, v, s) }
-  if (L.D == 64) { KVQ_DISPATCH_BITS(64, launch_append_t, buf, L, k, v, s) }
+hipError_t launch_append(uint8_t* buf, const Layout& L, const void* k, const void* v, const PerSeq& seq,
+                         hipStream_t s) {
+  if (L.D == 128) { KVQ_DISPATCH_BITS(128, launch_append_t, buf, L, k, v, seq, s) }
+  if (L.D == 64) { KVQ_DISPATCH_BITS(64, launch_append_t, buf, L, k, v, seq, s) }
   return hipErrorInvalidValue;
 }
 

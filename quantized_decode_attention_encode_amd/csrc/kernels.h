@@ -26,7 +26,8 @@ struct DecodeShape {
 
 hipError_t launch_encode(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,
                          const PerSeq& seq, int max_records, hipStream_t s);
-hipError_t launch_append(uint8_t* buf, const Layout& L, const void* k, const void* v, hipStream_t s);
+// seq: every sequence's lengths before the append (a = quantized, b = window tokens).
+hipError_t launch_append(uint8_t* buf, const Layout& L, const void* k, const void* v, const PerSeq& seq, hipStream_t s);
 hipError_t launch_window_fill(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,
                               const PerSeq& seq, hipStream_t s);
 hipError_t launch_encode_block(const void* X, int n_tok, int D, int bits, int group, int per_channel, void* codes,

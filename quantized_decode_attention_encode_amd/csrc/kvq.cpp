@@ -2,7 +2,10 @@
 //
 // Validation happens here, on the host, before any launch; lengths are mirrored on the
 // host (every change is decided here) so capacity checks and decode geometry never need a
-// device synchronisation. The device copy of the lengths is what the kernels read.
+// device synchronisation. The decode kernels read the device copy of the lengths; append
+// takes the mirror as kernel arguments (its token loads then wait for nothing). Each call
+// is planned from the mirror at enqueue time, so a captured graph of these calls replays
+// that plan: it is valid only for the lengths it was captured at.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -374,7 +377,12 @@ kvq_status kvq_append(kvq_cache* c, const void* k_tok, const void* v_tok, void* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   kvq_status st = ensure_ready(c, s);
   if (st != KVQ_OK) return st;
-  hipError_t e = kvq::launch_append(c->buf, c->L, k_tok, v_tok, s);
+  PerSeq len;  // lengths before the append: the host mirror of the device lengths
+  for (int b = 0; b < c->cfg.batch; ++b) {
+    len.a[b] = c->nq[b];
+    len.b[b] = c->nr[b];
+  }
+  hipError_t e = kvq::launch_append(c->buf, c->L, k_tok, v_tok, len, s);
   if (e != hipSuccess) return hip_fail(e, "append launch");
   for (int b = 0; b < c->cfg.batch; ++b) {
     if (c->nr[b] == c->cfg.residual) {
