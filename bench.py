@@ -30,10 +30,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 
-# HBM bytes per decode-split launch on the long workload from two rocprofv3 --pmc runs
+# HBM bytes per decode launch on the long workload from two rocprofv3 --pmc runs
 # (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, factors from a 1 GiB device copy; see
-# profiles/kvq_long_s64k_counters.md), valid only for the decode source they were taken on.
-MEASURED_TRAFFIC = {"workload": "long", "decode_src_sha256_16": "9486cf93d1fa114c", "bytes": 202243000}
+# profiles/kvq_long_s64k_counters.md), valid only for the decode kernel and split-plan
+# sources they were taken on (their hash).
+MEASURED_TRAFFIC = {"workload": "long", "src_sha256_16": "adca6b9b9165cf32", "bytes": 202248194}
 
 
 def algorithmic_decode_bytes(wl, n_q, n_r):
@@ -252,13 +253,16 @@ def main():
     del a, b
 
     traffic = None
-    src = os.path.join(ROOT, "quantized_decode_attention_encode_amd", "csrc", "decode.hip")
+    csrc = os.path.join(ROOT, "quantized_decode_attention_encode_amd", "csrc")
     if args.workload == MEASURED_TRAFFIC["workload"] and args.n_split == 0:
         import hashlib
 
-        with open(src, "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest()[:16] == MEASURED_TRAFFIC["decode_src_sha256_16"]:
-                traffic = MEASURED_TRAFFIC["bytes"]
+        h = hashlib.sha256()
+        for name in ("decode.hip", "kvq.cpp"):  # the kernel and the host's split plan
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest()[:16] == MEASURED_TRAFFIC["src_sha256_16"]:
+            traffic = MEASURED_TRAFFIC["bytes"]
 
     result = {
         "metric": "decode-attend us/step + achieved HBM GB/s (% peak) at S_kv=64K; encode tokens/s",
