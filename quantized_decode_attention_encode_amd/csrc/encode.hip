@@ -35,6 +35,7 @@ struct EncodeLds {
   static constexpr int kRecWords = D * (BK + BV + 2);
   uint32_t rec[kRecWords];       // record image
   uint8_t vbytes[D * kGroup];    // value codes, one byte each, [d][t]
+  float2 kpar[D];                // (lo, inv) of each channel's key group
 };
 
 __device__ __forceinline__ float dpp_xor1(float v) {
@@ -42,6 +43,41 @@ __device__ __forceinline__ float dpp_xor1(float v) {
 }
 __device__ __forceinline__ float dpp_xor2(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+}
+// Value of quad lane Q (quad_perm [Q,Q,Q,Q]) in every lane of the quad.
+template <int Q>
+__device__ __forceinline__ float dpp_quad_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), Q | (Q << 2) | (Q << 4) | (Q << 6), 0xF, 0xF, false));
+}
+
+// Min and max over the lanes that hold the same 8 channels of a row-major tile with CH
+// 16-byte chunks per row: lanes l, l ^ CH, l ^ 2 CH, ... (CH = 8: first the other half of
+// the 16-lane row by DPP row_ror 8); then the gfx950 row swaps: with both operands equal,
+// permlane16_swap returns rows (0,0,2,2) / (1,1,3,3) and permlane32_swap rows (0,1,0,1) /
+// (2,3,2,3), lane positions within a row kept. Min and max do not care which is which.
+template <int CH>
+__device__ __forceinline__ void column_minmax(float& mn, float& mx) {
+  if constexpr (CH == 8) {
+    mn = fminf(mn, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0x128, 0xF, 0xF, false)));
+    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0x128, 0xF, 0xF, false)));
+  }
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+  mn = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  mx = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
+  const auto d = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+  mn = fminf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+  mx = fmaxf(__uint_as_float(d[0]), __uint_as_float(d[1]));
+}
+
+// v[sel] for a lane-dependent sel < N, without dynamic register indexing (a select chain).
+template <int N>
+__device__ __forceinline__ float pick(const float (&v)[N], int sel) {
+  float r = v[0];
+#pragma unroll
+  for (int k = 1; k < N; ++k) r = sel == k ? v[k] : r;
+  return r;
 }
 
 struct GroupParams {
@@ -77,7 +113,7 @@ __device__ __forceinline__ uint32_t code_of(float x, const GroupParams& p) {
 // Quantize the 32-token tile (rows ks[0..31], vs[0..31], row stride D elements) into the
 // record at `rec_out`. Called by all 64 lanes of a single-wave workgroup.
 template <int D, int BK, int BV>
-__device__ void encode_record(const __half* __restrict__ ks, const __half* __restrict__ vs,
+__device__ __forceinline__ void encode_record(const __half* __restrict__ ks, const __half* __restrict__ vs,
                               uint32_t* __restrict__ rec_out, EncodeLds<D, BK, BV>& lds) {
   constexpr int CH = D / 8;      // 16-byte chunks per row
   constexpr int RPI = 64 / CH;   // rows covered by one load instruction
@@ -109,8 +145,11 @@ __device__ void encode_record(const __half* __restrict__ ks, const __half* __res
     }
   }
 
-  // ---- keys: one group per channel over the 32 tokens
-  GroupParams kp[8];
+  // ---- keys: one group per channel over the 32 tokens. Every lane of a chunk column ends up
+  // with the column's min/max; each of the RPI lanes of the column then computes the
+  // parameters of 8/RPI of its channels, and they meet in LDS.
+  constexpr int EK = 8 / RPI;  // key groups whose parameters this lane computes
+  float kmn[8], kmx[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     float mn = kx[0][e], mx = kx[0][e];
@@ -119,16 +158,32 @@ __device__ void encode_record(const __half* __restrict__ ks, const __half* __res
       mn = fminf(mn, kx[i][e]);
       mx = fmaxf(mx, kx[i][e]);
     }
-#pragma unroll
-    for (int m = CH; m < 64; m <<= 1) {
-      mn = fminf(mn, __shfl_xor(mn, m, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, m, 64));
-    }
-    kp[e] = group_params<BK>(mn, mx);
+    column_minmax<CH>(mn, mx);
+    kmn[e] = mn;
+    kmx[e] = mx;
   }
-  if (r == 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) lds.rec[KP_W + 8 * c8 + e] = kp[e].packed;
+  for (int j = 0; j < EK; ++j) {
+    float mn8[8 / EK], mx8[8 / EK];  // candidates e = k * EK + j, k = the lane's row
+#pragma unroll
+    for (int k = 0; k < 8 / EK; ++k) {
+      mn8[k] = kmn[k * EK + j];
+      mx8[k] = kmx[k * EK + j];
+    }
+    const GroupParams g = group_params<BK>(pick(mn8, r), pick(mx8, r));
+    const int ch = 8 * c8 + r * EK + j;
+    lds.kpar[ch] = make_float2(g.lo, g.inv);
+    lds.rec[KP_W + ch] = g.packed;
+  }
+  __syncthreads();
+  GroupParams kp[8];
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const float4 v = *reinterpret_cast<const float4*>(&lds.kpar[8 * c8 + e]);
+    kp[e].lo = v.x;
+    kp[e].inv = v.y;
+    kp[e + 1].lo = v.z;
+    kp[e + 1].inv = v.w;
   }
   {
     const int ch0 = 8 * c8;
@@ -154,10 +209,14 @@ __device__ void encode_record(const __half* __restrict__ ks, const __half* __res
     }
   }
 
-  // ---- values: one group per (token, 32 channels) = 4 adjacent chunks of the same row
+  // ---- values: one group per (token, 32 channels) = 4 adjacent chunks of the same row, i.e.
+  // the 4 lanes of a quad. Each quad lane computes the parameters of NI/4 of its rows'
+  // groups; DPP quad broadcasts hand them to the other three.
+  constexpr int NQ = NI / 4;  // value groups whose parameters this lane computes
+  const int q = c8 & 3;
+  float vmn[NI], vmx[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int t = r + RPI * i;
     float mn = vx[i][0], mx = vx[i][0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) {
@@ -168,9 +227,35 @@ __device__ void encode_record(const __half* __restrict__ ks, const __half* __res
     mx = fmaxf(mx, dpp_xor1(mx));
     mn = fminf(mn, dpp_xor2(mn));
     mx = fmaxf(mx, dpp_xor2(mx));
-    const GroupParams vp = group_params<BV>(mn, mx);
-    const int k = c8 / 4;
-    if ((c8 & 3) == 0) lds.rec[VP_W + ((t >> 1) * NKG + k) * 2 + (t & 1)] = vp.packed;
+    vmn[i] = mn;
+    vmx[i] = mx;
+  }
+  float own_lo[NQ], own_inv[NQ];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    float mn4[4], mx4[4];  // candidates: rows i = k * NQ + j, k = this lane's quad position
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      mn4[k] = vmn[k * NQ + j];
+      mx4[k] = vmx[k * NQ + j];
+    }
+    const GroupParams g = group_params<BV>(pick(mn4, q), pick(mx4, q));
+    own_lo[j] = g.lo;
+    own_inv[j] = g.inv;
+    const int t = r + RPI * (q * NQ + j);
+    lds.rec[VP_W + ((t >> 1) * NKG + c8 / 4) * 2 + (t & 1)] = g.packed;
+  }
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int t = r + RPI * i;
+    GroupParams vp;
+    // row i's parameters live in quad lane i / NQ, slot i % NQ
+    switch (i / NQ) {
+      case 0: vp.lo = dpp_quad_bcast<0>(own_lo[i % NQ]); vp.inv = dpp_quad_bcast<0>(own_inv[i % NQ]); break;
+      case 1: vp.lo = dpp_quad_bcast<1>(own_lo[i % NQ]); vp.inv = dpp_quad_bcast<1>(own_inv[i % NQ]); break;
+      case 2: vp.lo = dpp_quad_bcast<2>(own_lo[i % NQ]); vp.inv = dpp_quad_bcast<2>(own_inv[i % NQ]); break;
+      default: vp.lo = dpp_quad_bcast<3>(own_lo[i % NQ]); vp.inv = dpp_quad_bcast<3>(own_inv[i % NQ]); break;
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) lds.vbytes[(8 * c8 + e) * kGroup + t] = uint8_t(code_of<BV>(vx[i][e], vp));
   }
