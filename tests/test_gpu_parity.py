@@ -248,3 +248,73 @@ def test_capacity_and_state_errors_on_device():
     assert c.lengths() == ([0], [0])
     with pytest.raises(KVQError):
         kvq_decode_attend(c, torch.zeros(1, 1, 64, dtype=torch.float16, device=DEV))
+
+
+BIT_PAIRS = [(2, 2), (2, 4), (2, 8), (4, 2), (4, 4), (4, 8), (8, 2), (8, 4), (8, 8)]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bk,bv", BIT_PAIRS, ids=[f"b{k}{v}" for k, v in BIT_PAIRS])
+def test_every_bit_width_pair_and_head_dim(D, bk, bv):
+    # every decode instance the library dispatches to (head dim x key bits x value bits), with
+    # the query-head group size cycling through 1, 2, 4, 8 and a softmax scale other than 1
+    G = (1, 2, 4, 8)[(BIT_PAIRS.index((bk, bv)) + D // 64) % 4]
+    Hkv = 2 if G < 8 else 1
+    case = (f"d{D}-b{bk}{bv}-g{G}", 2, Hkv * G, Hkv, D, bk, bv, (1, 180))
+    wl, draw, cfg = make(case, seed=40 + bk * 10 + bv + D)
+    cache = gpu_prefill(draw, cfg)
+    seqs = oracle_prefill(draw, cfg.residual)
+    assert_state_equal(host_buffer(cache), cfg, seqs, case[0])
+    sm = 0.7
+    ref = oracle_attend(draw.q.astype(np.float64), seqs, wl, sm_scale=sm)
+    q = torch.from_numpy(draw.q).to(DEV)
+    for n_split in (0, 3):
+        out = kvq_decode_attend(cache, q, out_fp32=True, n_split=n_split, sm_scale=sm)
+        assert_close(out.cpu().numpy(), ref, f"{case[0]} n_split={n_split}")
+
+
+@pytest.mark.parametrize("residual", [128, 256])
+def test_large_windows_prefill_appends_and_decode(residual):
+    # windows of 4 and 8 units: several window units per sequence, and appends across a flush
+    case = ("bigwin", 2, 4, 2, 128, 2, 2, None)
+    S_full, S0, n_app = [800, 600], [600, 400], 200
+    wl, draw, cfg = make(case, seed=31, residual=residual, seq_lens=S_full, max_tokens=1024)
+    K, V, _ = draw.padded()
+    Kt, Vt = torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV)
+    c = KVQCache(cfg, device=DEV)
+    kvq_prefill(c, Kt, Vt, S0)
+    q = torch.from_numpy(draw.q).to(DEV)
+    pre = oracle_prefill(draw, residual)
+    seqs = {}
+    for (b, h) in pre:
+        s = kivi.KiviSequence(128, 2, 2, 32, residual)
+        s.prefill(draw.K[b][h][:S0[b]], draw.V[b][h][:S0[b]])
+        seqs[(b, h)] = s
+    assert_state_equal(host_buffer(c), cfg, seqs, f"R={residual} prefill")
+    out = kvq_decode_attend(c, q, out_fp32=True)
+    assert_close(out.cpu().numpy(), oracle_attend(draw.q.astype(np.float64), seqs, wl), f"R={residual} prefill decode")
+    for t in range(n_app):
+        k = torch.stack([Kt[b, :, S0[b] + t] for b in range(2)]).contiguous()
+        v = torch.stack([Vt[b, :, S0[b] + t] for b in range(2)]).contiguous()
+        kvq_append(c, k, v)
+    for (b, h), s in seqs.items():
+        for t in range(n_app):
+            s.append(draw.K[b][h][S0[b] + t], draw.V[b][h][S0[b] + t])
+    assert_state_equal(host_buffer(c), cfg, seqs, f"R={residual} appended")
+    out = kvq_decode_attend(c, q, out_fp32=True, n_split=5)
+    assert_close(out.cpu().numpy(), oracle_attend(draw.q.astype(np.float64), seqs, wl), f"R={residual} appended decode")
+
+
+def test_largest_batch_and_more_splits_than_units():
+    # B at its maximum (256 sequences, ragged 1..96 tokens), and a split count far above the
+    # units any sequence has (every split beyond them must stay idle)
+    case = ("maxb", 256, 2, 1, 64, 2, 2, (1, 96))
+    wl, draw, cfg = make(case, seed=50, max_tokens=128)
+    cache = gpu_prefill(draw, cfg)
+    seqs = oracle_prefill(draw, cfg.residual)
+    assert_state_equal(host_buffer(cache), cfg, seqs, "maxb")
+    ref = oracle_attend(draw.q.astype(np.float64), seqs, wl)
+    q = torch.from_numpy(draw.q).to(DEV)
+    for n_split in (0, 1000):
+        out = kvq_decode_attend(cache, q, out_fp32=True, n_split=n_split)
+        assert_close(out.cpu().numpy(), ref, f"maxb n_split={n_split}")
