@@ -2,11 +2,16 @@
 
 Workload (default "long"): B=1, H=32 (MHA), D=128, S_kv=65536, 2-bit keys and values,
 g=32, fp16 window of 32 tokens; seeded synthetic K/V (N(0,1), 8 outlier key channels x10).
-A step is one decode step of the cache: kvq_append (one token per sequence; every 32nd
-append per cache flushes the window through the quantizer) followed by kvq_decode_attend
-(one kernel: split-K, the last split of each sequence and KV head merging the partials).
+A step is one decode step of the cache through kvq_append_decode_attend: one token per
+sequence appended and one query per head attended, in one kernel launch (split-K, the last
+split of each sequence and KV head merging the partials), except on the 1 step in 32 per
+cache whose append flushes a full window through the quantizer (the append kernel runs
+first). The same steps through the separate kvq_append + kvq_decode_attend calls are timed
+too and reported as step_separate_calls_us.
 Steps rotate over 4 cache replicas (4 x 202 MB) so the 256 MB Infinity Cache cannot hold
-the working set. Inputs are resident in HBM before timing.
+the working set. Inputs are resident in HBM before timing. Before the warmup steps, 0.5 s of
+attend-only calls (which change no cache) let the GPU clocks settle, before the prefill
+encode is timed and again before the warmup steps.
 
 Printed: one JSON line with the step time, the decode kernel's achieved HBM bandwidth
 against the 8 TB/s peak (algorithmic bytes / kernel time from HIP events that the decode
@@ -118,6 +123,7 @@ def main():
     ap.add_argument("--encode-reps", type=int, default=5)
     ap.add_argument("--n-split", type=int, default=0, help="splits per sequence (0 = the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-s", type=float, default=0.5, help="seconds of attend-only calls before the warmup")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this path shards by "
@@ -141,7 +147,11 @@ def main():
     n_caches = wl.layers if multi else args.replicas
     draw = workloads.Draw(wl)  # multi-layer: layer 0's K/V fill every layer (costs do not depend on values)
     K, V, lens = draw.padded()
-    n_steps_total = args.steps + args.warmup
+    # warmup, then three passes of `steps` steps each: the timed steps through the one call (no
+    # instrumentation), the same through the two separate calls, and a pass through the one call
+    # with the decode kernel's dispatch-stamped events on (the kernel's execution time; the
+    # events themselves lengthen a step, so that pass is not the step time)
+    n_steps_total = args.warmup + 3 * args.steps
     per_cache = n_steps_total if multi else (n_steps_total + n_caches - 1) // n_caches
     cap = (max(lens) + per_cache + 64 + 31) // 32 * 32
     cfg = make_config(wl.batch, wl.n_kv_heads, wl.n_q_heads, wl.head_dim, wl.key_bits, wl.value_bits, 32,
@@ -150,8 +160,29 @@ def main():
     del K, V
     stream = torch.cuda.current_stream()
 
-    # ---- prefill encode rate (reset + prefill, prefill timed alone)
+    # ---- every cache prefilled (the prefill encode rate is timed below, once the clocks settled)
     caches = [KVQCache(cfg, device=dev) for _ in range(n_caches)]
+    for c in caches:
+        kvq_prefill(c, Kt, Vt, lens)
+    torch.cuda.synchronize()
+    q = torch.from_numpy(draw.q).to(dev)
+    outs = [torch.empty(tuple(q.shape), dtype=torch.float16, device=dev) for _ in caches]
+    wss = [c.workspace(args.n_split) for c in caches]
+
+    # Settle the GPU clocks first (they ramp up over the first ~0.1 s of sustained work, and a
+    # kernel timed before that reads up to 10% slow): attend-only calls, which leave every
+    # cache as it is, for at least `settle_s` seconds.
+    def settle():
+        t_settle = time.perf_counter()
+        while time.perf_counter() - t_settle < args.settle_s:
+            for _ in range(20):
+                for c, o, w in zip(caches, outs, wss):
+                    kvq_decode_attend(c, q, out=o, workspace=w, n_split=args.n_split, stream=stream)
+            torch.cuda.synchronize()
+
+    settle()
+
+    # ---- prefill encode rate (reset + prefill of cache 0, the prefill timed alone)
     enc_ms = []
     for r in range(args.encode_reps):
         c = caches[0]
@@ -162,8 +193,6 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         enc_ms.append(e0.elapsed_time(e1))
-    for c in caches[1:]:
-        kvq_prefill(c, Kt, Vt, lens)
     enc_t = statistics.median(enc_ms) / 1e3
     n_q0 = [s - ((s - 1) % wl.residual + 1) for s in lens]
     enc_tokens_per_s = sum(lens) / enc_t
@@ -173,9 +202,6 @@ def main():
     toks = [draw.next_token() for _ in range(n_steps_total)]
     kt = torch.from_numpy(np.stack([t[0] for t in toks])).to(dev)
     vt = torch.from_numpy(np.stack([t[1] for t in toks])).to(dev)
-    q = torch.from_numpy(draw.q).to(dev)
-    outs = [torch.empty(tuple(q.shape), dtype=torch.float16, device=dev) for _ in caches]
-    wss = [c.workspace(args.n_split) for c in caches]
     del Kt, Vt
     torch.cuda.synchronize()
 
@@ -191,7 +217,16 @@ def main():
                  ctypes.c_void_p(w.data_ptr()), w.numel(), args.n_split, sp) for c, o, w in zip(caches, outs, wss)]
     visits = (lambda i: range(n_caches)) if multi else (lambda i: (i % n_caches,))
 
-    def step(i):
+    fused_args = [(c.handle, None, None) + a[1:] for c, a in zip(caches, dec_args)]
+
+    def step(i):  # one decode step of the hot path: append + attend, one call
+        for r in visits(i):
+            a = fused_args[r]
+            st = lib.kvq_append_decode_attend(a[0], kp[i], vp[i], *a[3:])
+            if st:
+                _lib.check(st)
+
+    def step_separate(i):  # the same step through kvq_append, then kvq_decode_attend
         for r in visits(i):
             st = lib.kvq_append(caches[r].handle, kp[i], vp[i], sp)
             st = st or lib.kvq_decode_attend(*dec_args[r])
@@ -200,20 +235,32 @@ def main():
 
     # lengths each decode sees, replayed from the window rule (one appended token per visit)
     lens_now = [c.lengths() for c in caches]
+    settle()  # again: the host work since the prefill timing left the GPU idle
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    for c in caches:
-        c.profile_enable(True, launches=args.steps if multi else (args.steps + n_caches - 1) // n_caches)
     t_ev0, t_ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_ev0.record(stream)
     wall0 = time.perf_counter()
-    for i in range(args.warmup, n_steps_total):
+    for i in range(args.warmup, args.warmup + args.steps):
         step(i)
     t_ev1.record(stream)
     torch.cuda.synchronize()
     wall1 = time.perf_counter()
+    s_ev0, s_ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s_ev0.record(stream)
+    for i in range(args.warmup + args.steps, args.warmup + 2 * args.steps):
+        step_separate(i)
+    s_ev1.record(stream)
+    torch.cuda.synchronize()
+    step_sep_ms = s_ev0.elapsed_time(s_ev1) / args.steps
+    for c in caches:
+        c.profile_enable(True, launches=args.steps if multi else (args.steps + n_caches - 1) // n_caches)
+    first, last = args.warmup + 2 * args.steps, n_steps_total  # the pass the roofline is taken over
+    for i in range(first, last):
+        step(i)
+    torch.cuda.synchronize()
     bytes_per_launch = []
     for i in range(n_steps_total):
         for r in visits(i):
@@ -223,7 +270,7 @@ def main():
                     nq[b] += wl.residual
                     nr[b] = 0
                 nr[b] += 1
-            if i >= args.warmup:
+            if first <= i < last:
                 bytes_per_launch.append(algorithmic_decode_bytes(wl, nq, nr))
     for r, c in enumerate(caches):
         assert tuple(map(list, lens_now[r])) == tuple(map(list, c.lengths())), "length replay disagrees"
@@ -280,7 +327,8 @@ def main():
         "config": {
             "workload": f"{wl.name}: {wl.describe()}",
             "step": ("every layer: " if multi else "")
-            + "kvq_append (flush every 32nd append) + kvq_decode_attend (one kernel: splits + in-kernel merge)",
+            + "kvq_append_decode_attend (append + attend in one decode kernel; on the 1 step in 32 that "
+              "flushes a full window, the append kernel runs first)",
             "caches": f"{n_caches} layer caches" if multi else f"{n_caches} replicas of one cache, one per step",
             "codes": f"{wl.key_bits}-bit keys / {wl.value_bits}-bit values, fp16 (scale, zero), fp32 softmax",
         },
@@ -303,6 +351,7 @@ def main():
         "encode_gbps": round(enc_gbs, 1),
         "encode_prefill_us": round(enc_t * 1e6, 2),
         "wall_s_timed": round(wall1 - wall0, 3),
+        "step_separate_calls_us": round(step_sep_ms * 1e3, 3),
         "device": device_record(torch),
     }
     if multi:

@@ -178,6 +178,15 @@ kvq_status kvq_decode_attend(kvq_cache* cache, const void* q, void* out, int32_t
                              float sm_scale, void* workspace, size_t ws_bytes, int32_t n_split,
                              void* stream);
 
+/* North-star calls 2 and 3 in one: exactly kvq_append(cache, k_tok, v_tok) followed by
+ * kvq_decode_attend(cache, q, ...) on the same stream, same arguments and errors, same cache
+ * state and output. When no window is full (31 appends in 32 at R = 32) it is one kernel
+ * launch: the decode reads each new token from k_tok / v_tok, stores it in its window slot and
+ * advances the device lengths. Otherwise the window is flushed by the append kernel first. */
+kvq_status kvq_append_decode_attend(kvq_cache* cache, const void* k_tok, const void* v_tok, const void* q,
+                                    void* out, int32_t out_fp32, float sm_scale, void* workspace,
+                                    size_t ws_bytes, int32_t n_split, void* stream);
+
 /* Timing hook for benchmarks: while enabled, kvq_decode_attend launches its split pass (the
  * dominant kernel) with a pair of HIP events that the kernel's own dispatch stamps at its start
  * and end (hipExtLaunchKernelGGL), so each pair brackets that kernel's execution on the

@@ -7,6 +7,7 @@ from .cache import (  # noqa: F401
     KVQCache,
     KVQError,
     kvq_append,
+    kvq_append_decode_attend,
     kvq_cache_bytes,
     kvq_decode_attend,
     kvq_encode,

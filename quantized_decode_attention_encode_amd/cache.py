@@ -189,3 +189,30 @@ def kvq_decode_attend(cache: KVQCache, q: torch.Tensor, out: torch.Tensor | None
     if st != KVQ_OK:
         check(st)
     return out
+
+
+def kvq_append_decode_attend(cache: KVQCache, k_tok: torch.Tensor, v_tok: torch.Tensor, q: torch.Tensor,
+                             out: torch.Tensor | None = None, sm_scale: float = 1.0, n_split: int = 0,
+                             out_fp32: bool = False, workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """kvq_append(k_tok, v_tok) then kvq_decode_attend(q) as one call (one launch unless a window
+    is full)."""
+    c = cache.cfg
+    for name, t in (("k_tok", k_tok), ("v_tok", v_tok)):
+        if tuple(t.shape) != (c.batch, c.n_kv_heads, c.head_dim):
+            raise KVQError(-1, f"{name} must be [B, H_kv, D] = {(c.batch, c.n_kv_heads, c.head_dim)}")
+    if tuple(q.shape) != (c.batch, c.n_q_heads, c.head_dim):
+        raise KVQError(-1, f"q must be [B, H_q, D] = {(c.batch, c.n_q_heads, c.head_dim)}")
+    odt = torch.float32 if out_fp32 else torch.float16
+    if out is None:
+        out = torch.empty(tuple(q.shape), dtype=odt, device=q.device)
+    if tuple(out.shape) != tuple(q.shape):
+        raise KVQError(-1, "out must have q's shape")
+    if workspace is None:
+        workspace = cache.workspace(n_split)
+    st = lib.kvq_append_decode_attend(cache.handle, _dev(k_tok, "k_tok"), _dev(v_tok, "v_tok"), _dev(q, "q"),
+                                      _dev(out, "out", odt), 1 if out_fp32 else 0, float(sm_scale),
+                                      _dev(workspace, "workspace", torch.uint8), workspace.numel(), int(n_split),
+                                      _stream(stream))
+    if st != KVQ_OK:
+        check(st)
+    return out

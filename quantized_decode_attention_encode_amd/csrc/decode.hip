@@ -386,8 +386,11 @@ __device__ __forceinline__ void process_record(const RecordRegs<D, BK, BV>& cur,
 }
 
 // Up to 32 fp16 window tokens (tokens tbase .. tbase + nvalid - 1 of the window).
+// Token tnew of the unit (when 0 <= tnew < nvalid) is the one this launch appends: its rows
+// come from kn / vn instead of the window.
 template <int D, int G>
 __device__ __forceinline__ void process_window(const __half* __restrict__ wk, const __half* __restrict__ wv, int nvalid,
+                                               int tnew, const __half* kn, const __half* vn,
                                                WaveLds<D, G>& W, WaveState<D, G>& st, const float (&qs)[G][D / 64],
                                                int lane) {
   constexpr int E = D / 64, DQ = D / 4;
@@ -402,8 +405,9 @@ __device__ __forceinline__ void process_window(const __half* __restrict__ wk, co
     }
   wave_sync();
   const int t0 = 2 * P, t1 = 2 * P + 1;
-  const uint32_t* k0p = reinterpret_cast<const uint32_t*>(wk + min(t0, nvalid - 1) * D + Q * DQ);
-  const uint32_t* k1p = reinterpret_cast<const uint32_t*>(wk + min(t1, nvalid - 1) * D + Q * DQ);
+  const int t0c = min(t0, nvalid - 1), t1c = min(t1, nvalid - 1);
+  const uint32_t* k0p = reinterpret_cast<const uint32_t*>((t0c == tnew ? kn : wk + t0c * D) + Q * DQ);
+  const uint32_t* k1p = reinterpret_cast<const uint32_t*>((t1c == tnew ? kn : wk + t1c * D) + Q * DQ);
   uint32_t k0w[DQ / 2], k1w[DQ / 2];
 #pragma unroll
   for (int c = 0; c < DQ / 2; ++c) {
@@ -436,12 +440,13 @@ __device__ __forceinline__ void process_window(const __half* __restrict__ wk, co
   for (int i = 0; i < G; ++i) {
     for (int t = 0; t < nvalid; ++t) {
       const float a = W.pw[i][t];
+      const __half* vrow = t == tnew ? vn : wv + t * D;
       if constexpr (E == 2) {
-        const uint32_t vw = reinterpret_cast<const uint32_t*>(wv + t * D)[lane];
+        const uint32_t vw = reinterpret_cast<const uint32_t*>(vrow)[lane];
         st.acc[i][0] = __builtin_fmaf(a, lo_f(vw), st.acc[i][0]);
         st.acc[i][1] = __builtin_fmaf(a, hi_f(vw), st.acc[i][1]);
       } else {
-        st.acc[i][0] = __builtin_fmaf(a, __half2float(wv[t * D + lane]), st.acc[i][0]);
+        st.acc[i][0] = __builtin_fmaf(a, __half2float(vrow[lane]), st.acc[i][0]);
       }
     }
   }
@@ -534,7 +539,8 @@ __device__ __forceinline__ void merge_splits(const float* __restrict__ ws, int64
 template <int D, int BK, int BV, int G>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : (G <= 4 ? 2 : 1))))
 void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape ds, const __half* __restrict__ q,
-                         float* __restrict__ ws, uint32_t* __restrict__ sync, void* __restrict__ out) {
+                         float* __restrict__ ws, uint32_t* __restrict__ sync, void* __restrict__ out,
+                         const __half* __restrict__ k_app, const __half* __restrict__ v_app, uint8_t* bufw) {
   constexpr int E = D / 64, DQ = D / 4, NKG = D / 32;
   using MK = Magic<BK>;
   using MV = Magic<BV>;
@@ -550,7 +556,8 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int32_t* len = reinterpret_cast<const int32_t*>(buf + L.lengths(b, h));
   const int nq = max(0, min(len[0], L.max_groups * kGroup));
-  const int nr = max(0, min(len[1], L.R));
+  const int nr_old = max(0, min(len[1], L.R));
+  const int nr = min(nr_old + ds.append, L.R);  // with an append: the new token is window slot nr_old
   const int ngroups = nq / kGroup;
   const int nunits = ngroups + (nr + kGroup - 1) / kGroup;
   const int u0 = sigma * ds.chunk;
@@ -629,7 +636,20 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
     const int nvalid = min(kGroup, nr - tbase);
     const __half* wk = reinterpret_cast<const __half*>(buf + L.wk_off + L.window(b, h)) + tbase * D;
     const __half* wv = reinterpret_cast<const __half*>(buf + L.wv_off + L.window(b, h)) + tbase * D;
-    process_window<D, G>(wk, wv, nvalid, W, st, qs, lane);
+    const int tnew = ds.append ? nr_old - tbase : -1;  // the appended token in this unit, if 0 <= tnew < nvalid
+    const int64_t tok = (int64_t(b) * L.Hkv + h) * D;
+    const __half* kn = ds.append ? k_app + tok : nullptr;
+    const __half* vn = ds.append ? v_app + tok : nullptr;
+    process_window<D, G>(wk, wv, nvalid, tnew, kn, vn, W, st, qs, lane);
+    if (tnew >= 0 && tnew < nvalid) {  // store the appended token in its slot (no read of it here)
+      __half* dk = reinterpret_cast<__half*>(bufw + L.wk_off + L.window(b, h)) + nr_old * D;
+      __half* dv = reinterpret_cast<__half*>(bufw + L.wv_off + L.window(b, h)) + nr_old * D;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        dk[lane * E + e] = kn[lane * E + e];
+        dv[lane * E + e] = vn[lane * E + e];
+      }
+    }
   }
 
   // ---- finish the wave: l counted once per quad, bias summed over its producer lanes
@@ -693,7 +713,13 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
       put_partial(dst + D + 1, Lsum);
     }
   }
-  if (nvalid == 1) return;
+  // With an append, the split that finishes (b, h_kv) last advances its device lengths: every
+  // split of (b, h_kv) has read them by then.
+  int32_t* len_w = reinterpret_cast<int32_t*>(bufw + L.lengths(b, h));
+  if (nvalid == 1) {
+    if (ds.append && threadIdx.x == 0) len_w[1] = nr;
+    return;
+  }
 
   // ---- the last split of (b, h_kv) to finish merges every partial. Each wave waits until its
   // partial stores are acknowledged at device scope, the workgroup meets, and only then does
@@ -707,58 +733,66 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
   __syncthreads();
   if (!sh_last) return;
   merge_splits<D, G>(ws, row0, ds.n_split, nvalid, sh.mrg, out, ds.out_fp32);
-  if (threadIdx.x == 0) atomicExch(cnt, 0u);
+  if (threadIdx.x == 0) {
+    if (ds.append) len_w[1] = nr;
+    atomicExch(cnt, 0u);
+  }
 }
 
 // ------------------------------------------------------------------------------------
 template <int D, int BK, int BV, int G>
 static hipError_t launch_split_t(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q,
-                                 float* ws, void* out, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                                 float* ws, void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0,
+                                 hipEvent_t e1) {
   dim3 grid(ds.n_split, L.Hkv, L.B);
   uint32_t* sync = reinterpret_cast<uint32_t*>(buf + L.sync_off);
   const __half* qh = static_cast<const __half*>(q);
+  const __half* kh = static_cast<const __half*>(ka);
+  const __half* vh = static_cast<const __half*>(va);
   if (e0 || e1)
     hipExtLaunchKernelGGL((decode_split_kernel<D, BK, BV, G>), grid, dim3(64 * kWaves), 0, s, e0, e1, 0,
-                          static_cast<const uint8_t*>(buf), L, ds, qh, ws, sync, out);
+                          static_cast<const uint8_t*>(buf), L, ds, qh, ws, sync, out, kh, vh, buf);
   else
     hipLaunchKernelGGL((decode_split_kernel<D, BK, BV, G>), grid, dim3(64 * kWaves), 0, s,
-                       static_cast<const uint8_t*>(buf), L, ds, qh, ws, sync, out);
+                       static_cast<const uint8_t*>(buf), L, ds, qh, ws, sync, out, kh, vh, buf);
   return hipGetLastError();
 }
 
 template <int D, int BK, int BV>
 static hipError_t launch_split_g(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q,
-                                 float* ws, void* out, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                                 float* ws, void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0,
+                                 hipEvent_t e1) {
   switch (ds.G) {
-    case 1: return launch_split_t<D, BK, BV, 1>(buf, L, ds, q, ws, out, s, e0, e1);
-    case 2: return launch_split_t<D, BK, BV, 2>(buf, L, ds, q, ws, out, s, e0, e1);
-    case 4: return launch_split_t<D, BK, BV, 4>(buf, L, ds, q, ws, out, s, e0, e1);
-    case 8: return launch_split_t<D, BK, BV, 8>(buf, L, ds, q, ws, out, s, e0, e1);
+    case 1: return launch_split_t<D, BK, BV, 1>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 2: return launch_split_t<D, BK, BV, 2>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 4: return launch_split_t<D, BK, BV, 4>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 8: return launch_split_t<D, BK, BV, 8>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int D>
 static hipError_t launch_split_d(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q,
-                                 float* ws, void* out, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+                                 float* ws, void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0,
+                                 hipEvent_t e1) {
   switch (L.bk * 16 + L.bv) {
-    case 0x22: return launch_split_g<D, 2, 2>(buf, L, ds, q, ws, out, s, e0, e1);
-    case 0x24: return launch_split_g<D, 2, 4>(buf, L, ds, q, ws, out, s, e0, e1);
-    case 0x28: return launch_split_g<D, 2, 8>(buf, L, ds, q, ws, out, s, e0, e1);
-    case 0x42: return launch_split_g<D, 4, 2>(buf, L, ds, q, ws, out, s, e0, e1);
-    case 0x44: return launch_split_g<D, 4, 4>(buf, L, ds, q, ws, out, s, e0, e1);
-    case 0x48: return launch_split_g<D, 4, 8>(buf, L, ds, q, ws, out, s, e0, e1);
-    case 0x82: return launch_split_g<D, 8, 2>(buf, L, ds, q, ws, out, s, e0, e1);
-    case 0x84: return launch_split_g<D, 8, 4>(buf, L, ds, q, ws, out, s, e0, e1);
-    case 0x88: return launch_split_g<D, 8, 8>(buf, L, ds, q, ws, out, s, e0, e1);
+    case 0x22: return launch_split_g<D, 2, 2>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 0x24: return launch_split_g<D, 2, 4>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 0x28: return launch_split_g<D, 2, 8>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 0x42: return launch_split_g<D, 4, 2>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 0x44: return launch_split_g<D, 4, 4>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 0x48: return launch_split_g<D, 4, 8>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 0x82: return launch_split_g<D, 8, 2>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 0x84: return launch_split_g<D, 8, 4>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 0x88: return launch_split_g<D, 8, 8>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_decode(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q, float* ws,
-                         void* out, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  if (L.D == 128) return launch_split_d<128>(buf, L, ds, q, ws, out, s, e0, e1);
-  if (L.D == 64) return launch_split_d<64>(buf, L, ds, q, ws, out, s, e0, e1);
+                         void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (L.D == 128) return launch_split_d<128>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+  if (L.D == 64) return launch_split_d<64>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
   return hipErrorInvalidValue;
 }
 

@@ -22,6 +22,7 @@ struct DecodeShape {
   int n_q_heads;
   float qscale;     // sm_scale * log2(e): scores are kept in base-2 units
   int out_fp32;
+  int append;       // 1: the launch also appends one token per (b, h) (no window is full)
 };
 
 hipError_t launch_encode(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,
@@ -37,7 +38,10 @@ hipError_t launch_lengths_fill(uint8_t* buf, const Layout& L, const PerSeq& seq,
 // Decode attention: split-K kernel whose last split per (b, h_kv) merges the partials into
 // `out`. start/stop, when not null, are stamped by the kernel's own dispatch (its execution
 // time).
+// With ds.append, k_tok / v_tok (fp16 [B][H_kv][D]) are the appended tokens: the launch attends
+// over the window plus them, stores them in their window slots and advances the device lengths.
 hipError_t launch_decode(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q, float* ws,
-                         void* out, hipStream_t s, hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+                         void* out, const void* k_tok, const void* v_tok, hipStream_t s,
+                         hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 
 }  // namespace kvq

@@ -158,6 +158,80 @@ kvq_status ensure_ready(kvq_cache* c, hipStream_t s) {
 
 }  // namespace
 
+namespace {
+
+// Plan and enqueue one decode launch. With k_tok / v_tok set, the launch also appends one token
+// per sequence (the caller has checked that no window is full): it attends over the window
+// plus that token, stores the token in its slot and advances the device lengths.
+kvq_status decode_enqueue(kvq_cache* c, const void* q, void* out, int32_t out_fp32, float sm_scale,
+                          void* workspace, size_t ws_bytes, int32_t n_split, void* stream,
+                          const void* k_tok, const void* v_tok) {
+  if (!q || !out) return fail(KVQ_E_INVALID, "q or out is NULL");
+  if (!workspace) return fail(KVQ_E_WORKSPACE, "workspace is NULL");
+  if (n_split < 0) return fail(KVQ_E_INVALID, "n_split must be >= 0");
+  if (!std::isfinite(sm_scale)) return fail(KVQ_E_INVALID, "sm_scale is not finite");
+  const kvq_config& cfg = c->cfg;
+  const int add = k_tok ? 1 : 0;  // window tokens the launch appends
+  int max_units = 0;
+  int64_t total_units = 0;
+  for (int b = 0; b < cfg.batch; ++b) {
+    if (c->nq[b] + c->nr[b] + add == 0) return fail(KVQ_E_INVALID, "sequence %d is empty", b);
+    const int u = units_of(c->nq[b], c->nr[b] + add);
+    max_units = std::max(max_units, u);
+    total_units += int64_t(u) * cfg.n_kv_heads;
+  }
+  int chunk;
+  if (n_split > 0) {
+    chunk = (max_units + n_split - 1) / n_split;
+  } else {
+    int cus = 0;
+    kvq_status dst = check_device(&cus);
+    if (dst != KVQ_OK) return dst;
+    const int64_t target = target_workgroups(cus, max_units, total_units, int64_t(cfg.batch) * cfg.n_kv_heads);
+    chunk = int((total_units + target - 1) / target);
+    chunk = std::max(4, (chunk + 3) / 4 * 4);
+  }
+  const int ns = (max_units + chunk - 1) / chunk;
+  const size_t need = size_t(cfg.batch) * cfg.n_q_heads * ns * (cfg.head_dim + 4) * sizeof(float);
+  if (ws_bytes < need) return fail(KVQ_E_WORKSPACE, "workspace holds %zu bytes, this call needs %zu", ws_bytes, need);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  kvq_status st = ensure_ready(c, s);
+  if (st != KVQ_OK) return st;
+  kvq::DecodeShape ds;
+  ds.n_split = ns;
+  ds.chunk = chunk;
+  ds.G = cfg.n_q_heads / cfg.n_kv_heads;
+  ds.n_q_heads = cfg.n_q_heads;
+  ds.qscale = sm_scale * 1.4426950408889634f;
+  ds.out_fp32 = out_fp32 ? 1 : 0;
+  ds.append = add;
+  float* ws = static_cast<float*>(workspace);
+  hipError_t e;
+  const bool prof = c->profiling;
+  if (prof) {
+    if (c->ev_used + 2 > c->ev.size()) {
+      if (c->ev.size() >= size_t(2 * kMaxProfilePairs)) return fail(KVQ_E_INVALID, "profile buffer full; call kvq_profile_read");
+      for (int i = 0; i < 2; ++i) {
+        hipEvent_t ev;
+        e = hipEventCreate(&ev);
+        if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+        c->ev.push_back(ev);
+      }
+    }
+  }
+  // With profiling on, the events are stamped by the kernel's own dispatch packet, so their
+  // interval is its execution time (no queue or launch latency).
+  e = kvq::launch_decode(c->buf, c->L, ds, q, ws, out, k_tok, v_tok, s, prof ? c->ev[c->ev_used] : nullptr,
+                         prof ? c->ev[c->ev_used + 1] : nullptr);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  if (prof) c->ev_used += 2;
+  if (add)
+    for (int b = 0; b < cfg.batch; ++b) c->nr[b] += 1;
+  return ok();
+}
+
+}  // namespace
+
 extern "C" {
 
 kvq_status kvq_probe(int32_t* has_gfx950) {
@@ -397,64 +471,30 @@ kvq_status kvq_append(kvq_cache* c, const void* k_tok, const void* v_tok, void* 
 kvq_status kvq_decode_attend(kvq_cache* c, const void* q, void* out, int32_t out_fp32, float sm_scale,
                              void* workspace, size_t ws_bytes, int32_t n_split, void* stream) {
   if (!c) return fail(KVQ_E_INVALID, "cache is NULL");
+  return decode_enqueue(c, q, out, out_fp32, sm_scale, workspace, ws_bytes, n_split, stream, nullptr, nullptr);
+}
+
+kvq_status kvq_append_decode_attend(kvq_cache* c, const void* k_tok, const void* v_tok, const void* q, void* out,
+                                    int32_t out_fp32, float sm_scale, void* workspace, size_t ws_bytes,
+                                    int32_t n_split, void* stream) {
+  if (!c) return fail(KVQ_E_INVALID, "cache is NULL");
+  if (!k_tok || !v_tok) return fail(KVQ_E_INVALID, "k_tok or v_tok is NULL");
   if (!q || !out) return fail(KVQ_E_INVALID, "q or out is NULL");
   if (!workspace) return fail(KVQ_E_WORKSPACE, "workspace is NULL");
   if (n_split < 0) return fail(KVQ_E_INVALID, "n_split must be >= 0");
   if (!std::isfinite(sm_scale)) return fail(KVQ_E_INVALID, "sm_scale is not finite");
-  const kvq_config& cfg = c->cfg;
-  int max_units = 0;
-  int64_t total_units = 0;
-  for (int b = 0; b < cfg.batch; ++b) {
-    if (c->nq[b] + c->nr[b] == 0) return fail(KVQ_E_INVALID, "sequence %d is empty", b);
-    const int u = units_of(c->nq[b], c->nr[b]);
-    max_units = std::max(max_units, u);
-    total_units += int64_t(u) * cfg.n_kv_heads;
+  bool flush = false;
+  for (int b = 0; b < c->cfg.batch; ++b) {
+    if (int64_t(c->nq[b]) + c->nr[b] + 1 > c->cfg.max_tokens)
+      return fail(KVQ_E_CAPACITY, "sequence %d is full (%d tokens)", b, c->cfg.max_tokens);
+    flush = flush || c->nr[b] == c->cfg.residual;
   }
-  int chunk;
-  if (n_split > 0) {
-    chunk = (max_units + n_split - 1) / n_split;
-  } else {
-    int cus = 0;
-    kvq_status dst = check_device(&cus);
-    if (dst != KVQ_OK) return dst;
-    const int64_t target = target_workgroups(cus, max_units, total_units, int64_t(cfg.batch) * cfg.n_kv_heads);
-    chunk = int((total_units + target - 1) / target);
-    chunk = std::max(4, (chunk + 3) / 4 * 4);
+  if (flush) {  // some window is full: the append kernel quantizes it, then a plain decode
+    kvq_status st = kvq_append(c, k_tok, v_tok, stream);
+    if (st != KVQ_OK) return st;
+    return decode_enqueue(c, q, out, out_fp32, sm_scale, workspace, ws_bytes, n_split, stream, nullptr, nullptr);
   }
-  const int ns = (max_units + chunk - 1) / chunk;
-  const size_t need = size_t(cfg.batch) * cfg.n_q_heads * ns * (cfg.head_dim + 4) * sizeof(float);
-  if (ws_bytes < need) return fail(KVQ_E_WORKSPACE, "workspace holds %zu bytes, this call needs %zu", ws_bytes, need);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  kvq_status st = ensure_ready(c, s);
-  if (st != KVQ_OK) return st;
-  kvq::DecodeShape ds;
-  ds.n_split = ns;
-  ds.chunk = chunk;
-  ds.G = cfg.n_q_heads / cfg.n_kv_heads;
-  ds.n_q_heads = cfg.n_q_heads;
-  ds.qscale = sm_scale * 1.4426950408889634f;
-  ds.out_fp32 = out_fp32 ? 1 : 0;
-  float* ws = static_cast<float*>(workspace);
-  hipError_t e;
-  const bool prof = c->profiling;
-  if (prof) {
-    if (c->ev_used + 2 > c->ev.size()) {
-      if (c->ev.size() >= size_t(2 * kMaxProfilePairs)) return fail(KVQ_E_INVALID, "profile buffer full; call kvq_profile_read");
-      for (int i = 0; i < 2; ++i) {
-        hipEvent_t ev;
-        e = hipEventCreate(&ev);
-        if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
-        c->ev.push_back(ev);
-      }
-    }
-  }
-  // With profiling on, the events are stamped by the kernel's own dispatch packet, so their
-  // interval is its execution time (no queue or launch latency).
-  e = kvq::launch_decode(c->buf, c->L, ds, q, ws, out, s, prof ? c->ev[c->ev_used] : nullptr,
-                         prof ? c->ev[c->ev_used + 1] : nullptr);
-  if (e != hipSuccess) return hip_fail(e, "decode launch");
-  if (prof) c->ev_used += 2;
-  return ok();
+  return decode_enqueue(c, q, out, out_fp32, sm_scale, workspace, ws_bytes, n_split, stream, k_tok, v_tok);
 }
 
 kvq_status kvq_profile_enable(kvq_cache* c, int32_t enable) {

@@ -158,6 +158,12 @@ def test_host_side_errors_before_any_launch():
         assert lib.kvq_decode_attend(h, P, P, 0, float("nan"), ws, 1 << 30, 0, None) == KVQ_E_INVALID
         assert lib.kvq_decode_attend(h, P, P, 0, 1.0, ws, 1 << 30, -2, None) == KVQ_E_INVALID
         assert lib.kvq_append(h, None, P, None) == KVQ_E_INVALID
+        # fused append + decode: the same argument checks, before any launch
+        assert lib.kvq_append_decode_attend(h, None, P, P, P, 0, 1.0, ws, 1 << 30, 0, None) == KVQ_E_INVALID
+        assert lib.kvq_append_decode_attend(h, P, P, None, P, 0, 1.0, ws, 1 << 30, 0, None) == KVQ_E_INVALID
+        assert lib.kvq_append_decode_attend(h, P, P, P, P, 0, 1.0, None, 1 << 30, 0, None) == KVQ_E_WORKSPACE
+        assert lib.kvq_append_decode_attend(h, P, P, P, P, 0, float("inf"), ws, 1 << 30, 0, None) == KVQ_E_INVALID
+        assert lib.kvq_append_decode_attend(h, P, P, P, P, 0, 1.0, ws, 1 << 30, -1, None) == KVQ_E_INVALID
         # lengths mirror
         nq, nr = (ctypes.c_int32 * 2)(), (ctypes.c_int32 * 2)()
         assert lib.kvq_cache_lengths(h, nq, nr) == KVQ_OK and list(nq) == [0, 0] and list(nr) == [0, 0]

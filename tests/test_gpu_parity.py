@@ -10,7 +10,8 @@ import pytest
 import torch
 
 from oracle import kivi
-from quantized_decode_attention_encode_amd import (KVQCache, KVQError, kvq_append, kvq_decode_attend, kvq_encode,
+from quantized_decode_attention_encode_amd import (KVQCache, KVQError, kvq_append, kvq_append_decode_attend,
+                                                   kvq_decode_attend, kvq_encode,
                                                    kvq_prefill, make_config, workloads)
 from tests.gpu_helpers import (assert_close, assert_state_equal, host_buffer, oracle_attend, oracle_prefill, say)
 
@@ -318,3 +319,39 @@ def test_largest_batch_and_more_splits_than_units():
     for n_split in (0, 1000):
         out = kvq_decode_attend(cache, q, out_fp32=True, n_split=n_split)
         assert_close(out.cpu().numpy(), ref, f"maxb n_split={n_split}")
+
+
+@pytest.mark.parametrize("n_split", [0, 1, 3])
+@pytest.mark.parametrize("start", ["prefill", "encode", "window-only"])
+def test_fused_append_decode_equals_append_then_decode(start, n_split):
+    # kvq_append_decode_attend must leave the same cache bytes and give the same outputs as
+    # kvq_append followed by kvq_decode_attend, step after step, across window flushes (ragged
+    # lengths: some sequences flush while others append in one launch)
+    case = ("fused", 3, 8, 2, 128, 2, 4, None)
+    lens = {"prefill": [200, 97, 64], "encode": [192, 64, 96], "window-only": [5, 31, 1]}[start]
+    n_steps = 70
+    wl, draw, cfg = make(case, seed=60, seq_lens=[s + n_steps for s in lens], max_tokens=512)
+    K, V, _ = draw.padded()
+    Kt, Vt = torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV)
+    caches = [KVQCache(cfg, device=DEV) for _ in range(2)]
+    for c in caches:
+        if start == "encode":
+            kvq_encode(c, Kt, Vt, lens)
+        else:
+            kvq_prefill(c, Kt, Vt, lens)
+    q = torch.from_numpy(draw.q).to(DEV)
+    for t in range(n_steps):
+        k = torch.stack([Kt[b, :, lens[b] + t] for b in range(3)]).contiguous()
+        v = torch.stack([Vt[b, :, lens[b] + t] for b in range(3)]).contiguous()
+        kvq_append(caches[0], k, v)
+        o0 = kvq_decode_attend(caches[0], q, out_fp32=True, n_split=n_split)
+        o1 = kvq_append_decode_attend(caches[1], k, v, q, out_fp32=True, n_split=n_split)
+        assert torch.equal(o0, o1), f"{start} step {t}"
+        assert caches[0].lengths() == caches[1].lengths()
+    b0, b1 = host_buffer(caches[0]), host_buffer(caches[1])
+    seqs = oracle_prefill(draw, cfg.residual)  # every drawn token = the prefill plus the appends
+    assert_state_equal(b1, cfg, seqs, f"{start} fused")
+    assert_state_equal(b0, cfg, seqs, f"{start} separate")
+    ref = oracle_attend(draw.q.astype(np.float64), seqs, wl)
+    o = kvq_decode_attend(caches[1], q, out_fp32=True, n_split=n_split)
+    assert_close(o.cpu().numpy(), ref, f"{start} fused end state")
