@@ -71,13 +71,22 @@ __device__ __forceinline__ void column_minmax(float& mn, float& mx) {
   mx = fmaxf(__uint_as_float(d[0]), __uint_as_float(d[1]));
 }
 
-// v[sel] for a lane-dependent sel < N, without dynamic register indexing (a select chain).
+// v[sel] for a lane-dependent sel < N (N a power of two) as a tree of selects on the bits of
+// sel. (A chain of `sel == k` selects is folded back into an indexed read of the array, which a
+// lane-dependent index sends through scratch memory.)
 template <int N>
 __device__ __forceinline__ float pick(const float (&v)[N], int sel) {
-  float r = v[0];
+  static_assert((N & (N - 1)) == 0, "N must be a power of two");
+  float level[N];
 #pragma unroll
-  for (int k = 1; k < N; ++k) r = sel == k ? v[k] : r;
-  return r;
+  for (int k = 0; k < N; ++k) level[k] = v[k];
+#pragma unroll
+  for (int bit = 0, n = N; n > 1; ++bit, n >>= 1) {
+    const bool hi = (sel >> bit) & 1;
+#pragma unroll
+    for (int k = 0; k < n / 2; ++k) level[k] = hi ? level[2 * k + 1] : level[2 * k];
+  }
+  return level[0];
 }
 
 struct GroupParams {
