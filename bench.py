@@ -39,7 +39,7 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 # (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, factors from a 1 GiB device copy; see
 # profiles/kvq_long_s64k_counters.md), valid only for the decode kernel and split-plan
 # sources they were taken on (their hash).
-MEASURED_TRAFFIC = {"workload": "long", "src_sha256_16": "adca6b9b9165cf32", "bytes": 202248194}
+MEASURED_TRAFFIC = {"workload": "long", "src_sha256_16": "168ca50dfe41c89c", "bytes": 202605908}
 
 
 def algorithmic_decode_bytes(wl, n_q, n_r):
