@@ -11,7 +11,8 @@ Attention is written as explicit sums with ``math.exp``.
 
 Sources are the same passages as ``oracle.kivi``: "Changelog" v0.8.0 (KIVI: per-channel
 keys, per-token values, residual window), v0.42.0 (codes plus per-group (scale, zero),
-softmax attention over the reconstruction), v0.30.0 (lo/scale, fp16 metadata).
+softmax attention over the reconstruction), v0.30.0 (lo/scale, fp16 metadata), v0.9.0
+(KIVI-Sink: high key-norm tokens kept in fp16, outside the group statistics).
 """
 from __future__ import annotations
 
@@ -34,11 +35,15 @@ def round_half_even(x: float) -> float:
     return float(round(x))
 
 
-def quantize_group(xs: list[float], bits: int):
-    """One group of fp16 values -> (codes, scale16, zero16) with one rounding per op."""
+def quantize_group(xs: list[float], bits: int, skip=()):
+    """One group of fp16 values -> (codes, scale16, zero16) with one rounding per op.
+
+    Elements whose index is in ``skip`` are left out of the min and max (they still get codes).
+    """
     L = float(2 ** bits - 1)
-    lo = r32(min(xs) + 0.0)
-    hi = r32(max(xs) + 0.0)
+    kept = [x for i, x in enumerate(xs) if i not in skip]
+    lo = r32(min(kept) + 0.0)
+    hi = r32(max(kept) + 0.0)
     s32 = r32(r32(hi - lo) / L)
     scale16 = r16(s32)
     zero16 = r16(lo)
@@ -54,8 +59,9 @@ def quantize_group(xs: list[float], bits: int):
     return codes, scale16, zero16
 
 
-def encode_keys(K: list[list[float]], bits: int, g: int):
-    """K[t][d] -> codes[t][d], scale[j][d], zero[j][d]; group = g tokens of one channel."""
+def encode_keys(K: list[list[float]], bits: int, g: int, sinks=()):
+    """K[t][d] -> codes[t][d], scale[j][d], zero[j][d]; group = g tokens of one channel.
+    Tokens in ``sinks`` stay out of their groups' min and max."""
     T, D = len(K), len(K[0])
     codes = [[0] * D for _ in range(T)]
     scale = [[0.0] * D for _ in range(T // g)]
@@ -63,7 +69,8 @@ def encode_keys(K: list[list[float]], bits: int, g: int):
     for j in range(T // g):
         for d in range(D):
             col = [K[j * g + i][d] for i in range(g)]
-            c, s, z = quantize_group(col, bits)
+            skip = {i for i in range(g) if j * g + i in sinks}
+            c, s, z = quantize_group(col, bits, skip)
             scale[j][d], zero[j][d] = s, z
             for i in range(g):
                 codes[j * g + i][d] = c[i]
@@ -82,6 +89,18 @@ def encode_values(V: list[list[float]], bits: int, g: int):
             scale[t][k], zero[t][k] = s, z
             codes[t][k * g:(k + 1) * g] = c
     return codes, scale, zero
+
+
+def select_sinks(K: list[list[float]], n: int) -> list[int]:
+    """Positions of the n rows of largest squared norm (binary32 squares added channel by
+    channel), earlier row first on equal norms; returned in ascending order."""
+    norms = []
+    for t, row in enumerate(K):
+        acc = 0.0
+        for x in row:
+            acc = r32(acc + r32(x * x))
+        norms.append((-acc, t))
+    return sorted(t for _, t in sorted(norms)[:n])
 
 
 def attend(q: list[float], keys: list[list[float]], values: list[list[float]], sm_scale: float = 1.0):

@@ -23,6 +23,9 @@ What it follows (VeloxQuant-MLX documentation pages):
   min/max group quantizer.
 * "veloxquant_mlx.cache package", ``KVCacheConfig``: ``kivi_group_size`` defaults to 32 and
   the cache has a ``residual_length`` window; the standalone ``attend(q)`` returns fp16.
+* "Changelog", v0.9.0 "New" (KIVI-Sink): tokens whose key L2 norm stands out are kept in
+  fp16 and left out of the statistics the quantization parameters come from;
+  ``n_sink_tokens = 0`` is plain KIVI.
 
 Readings taken where the pages leave a step open (each is listed in the design doc):
 
@@ -37,6 +40,13 @@ Readings taken where the pages leave a step open (each is listed in the design doc):
   channels from channel 0;
 * window rule: with S tokens seen (S >= 1) the window holds ((S - 1) mod R) + 1 tokens and
   the rest are quantized; a full window is flushed whole on the next append.
+* sinks (KIVI-Sink): the n tokens of largest key norm, chosen per (sequence, KV head) once,
+  by the first step that quantizes tokens of it (a prefill or encode with a quantized part,
+  or the first window flush), among the tokens that step quantizes; the squared norm is an
+  fp32 sum of fp32 squares taken channel by channel in order; equal norms go to the earlier
+  token. A sink keeps its fp16 key and value rows; its quantized slot stays in its record
+  (codes from the group parameters, clamped) but is skipped by attention, and the stored
+  scale of each of its value groups carries the sign bit as the marker of that.
 """
 from __future__ import annotations
 
@@ -50,12 +60,16 @@ F64 = np.float64
 # ----------------------------------------------------------------------------------------
 # Group quantizer (one group = the last axis of the input)
 # ----------------------------------------------------------------------------------------
-def quantize_groups(x: np.ndarray, bits: int):
+def quantize_groups(x: np.ndarray, bits: int, exclude: np.ndarray | None = None):
     """Quantize every group along the last axis of fp16 array ``x`` to ``bits``-bit codes.
 
     Follows the min/max group quantizer of "Changelog" v0.8.0 (KIVI) and v0.42.0 (codes
     plus per-group (scale, zero)), with zero stored as the group low end ("Changelog"
     v0.30.0, lo/scale) in fp16 metadata ("Changelog" v0.30.0, Honest scope).
+
+    ``exclude`` (boolean, x's shape) marks elements left out of the min and max ("Changelog"
+    v0.9.0, KIVI-Sink); they are still given codes from the group's parameters. Every group
+    must keep at least one element.
 
     Returns ``(codes uint8 with x's shape, scale fp16, zero fp16)``; the parameter arrays
     have x's shape without its last axis.
@@ -67,8 +81,14 @@ def quantize_groups(x: np.ndarray, bits: int):
         raise ValueError("bits must be an integer in [2, 8]")
     levels = F32(2 ** bits - 1)
     x32 = x.astype(F32)  # exact widening
-    lo = x32.min(axis=-1) + F32(0.0)  # + 0.0 turns -0 into +0
-    hi = x32.max(axis=-1) + F32(0.0)
+    if exclude is None:
+        lo = x32.min(axis=-1) + F32(0.0)  # + 0.0 turns -0 into +0
+        hi = x32.max(axis=-1) + F32(0.0)
+    else:
+        if np.any(np.all(exclude, axis=-1)):
+            raise ValueError("a group with every element excluded has no range")
+        lo = np.where(exclude, F32(np.inf), x32).min(axis=-1) + F32(0.0)
+        hi = np.where(exclude, F32(-np.inf), x32).max(axis=-1) + F32(0.0)
     s32 = (hi - lo) / levels  # fp32 subtract, fp32 divide
     scale16 = s32.astype(F16)  # one RNE rounding, subnormals kept
     zero16 = lo.astype(F16)  # exact: lo is an fp16 value
@@ -90,31 +110,65 @@ def dequantize_groups(codes: np.ndarray, scale16: np.ndarray, zero16: np.ndarray
 # ----------------------------------------------------------------------------------------
 # Keys per channel, values per token ("Changelog" v0.8.0, KIVI)
 # ----------------------------------------------------------------------------------------
-def encode_keys(K: np.ndarray, bits: int, g: int = 32):
+def encode_keys(K: np.ndarray, bits: int, g: int = 32, sinks=()):
     """Per-channel key quantization of an fp16 block ``K[T, D]`` with T a multiple of g.
 
-    A group is g consecutive tokens of one channel. Returns ``codes[T, D]`` (uint8),
-    ``scale[T/g, D]`` and ``zero[T/g, D]`` (fp16).
+    A group is g consecutive tokens of one channel. Rows listed in ``sinks`` (positions in
+    the block) take no part in their groups' min/max ("Changelog" v0.9.0, KIVI-Sink).
+    Returns ``codes[T, D]`` (uint8), ``scale[T/g, D]`` and ``zero[T/g, D]`` (fp16).
     """
     T, D = K.shape
     if T % g:
         raise ValueError("key block length must be a multiple of the group size")
     blk = K.reshape(T // g, g, D).transpose(0, 2, 1)  # [T/g, D, g]: group along tokens
-    c, s, z = quantize_groups(np.ascontiguousarray(blk), bits)
+    exclude = None
+    if len(sinks):
+        rows = np.zeros(T, bool)
+        rows[np.asarray(sinks)] = True
+        exclude = np.broadcast_to(rows.reshape(T // g, 1, g), blk.shape)
+    c, s, z = quantize_groups(np.ascontiguousarray(blk), bits, exclude)
     return np.ascontiguousarray(c.transpose(0, 2, 1).reshape(T, D)), s, z
 
 
-def encode_values(V: np.ndarray, bits: int, g: int = 32):
+def encode_values(V: np.ndarray, bits: int, g: int = 32, sinks=()):
     """Per-token value quantization of an fp16 block ``V[T, D]`` with D a multiple of g.
 
     A group is g consecutive channels of one token. Returns ``codes[T, D]`` (uint8),
-    ``scale[T, D/g]`` and ``zero[T, D/g]`` (fp16).
+    ``scale[T, D/g]`` and ``zero[T, D/g]`` (fp16). The scales of the rows listed in
+    ``sinks`` are stored with their sign bit set: the marker that attention skips that slot.
     """
     T, D = V.shape
     if D % g:
         raise ValueError("head dim must be a multiple of the group size")
     c, s, z = quantize_groups(V.reshape(T, D // g, g), bits)
+    if len(sinks):
+        bits16 = s.view(np.uint16)
+        bits16[np.asarray(sinks)] |= np.uint16(0x8000)
     return c.reshape(T, D), s, z
+
+
+# ----------------------------------------------------------------------------------------
+# Sink tokens ("Changelog" v0.9.0, KIVI-Sink)
+# ----------------------------------------------------------------------------------------
+def key_norms_sq(K: np.ndarray) -> np.ndarray:
+    """Squared L2 norm of every row of fp16 ``K[T, D]``: in fp32, channel 0 first, each
+    square rounded to fp32 and then added (one rounding per operation, no fused multiply-add)."""
+    acc = np.zeros(K.shape[0], F32)
+    for d in range(K.shape[1]):
+        x = K[:, d].astype(F32)
+        acc = acc + x * x
+    return acc
+
+
+def select_sinks(K: np.ndarray, n: int) -> np.ndarray:
+    """Row positions (ascending) of the ``n`` rows of ``K`` with the largest key norm;
+    between equal norms the earlier row wins."""
+    n = min(int(n), K.shape[0])
+    if n <= 0:
+        return np.zeros(0, np.int64)
+    nrm = key_norms_sq(K)
+    order = np.lexsort((np.arange(len(nrm)), -nrm.astype(F64)))  # by -norm, then by position
+    return np.sort(order[:n]).astype(np.int64)
 
 
 def dequantize_keys(codes, scale, zero, g: int = 32) -> np.ndarray:
@@ -155,10 +209,16 @@ class KiviSequence:
     window (all R tokens, R/g key groups) through the quantizer before storing the new token.
     """
 
-    def __init__(self, D: int, key_bits: int, value_bits: int, g: int = 32, R: int = 32):
+    def __init__(self, D: int, key_bits: int, value_bits: int, g: int = 32, R: int = 32, n_sink: int = 0):
         if R % g or D % g:
             raise ValueError("R and D must be multiples of g")
+        if not 0 <= n_sink < g:
+            raise ValueError("n_sink must be in [0, g)")
         self.D, self.bk, self.bv, self.g, self.R = D, key_bits, value_bits, g, R
+        self.n_sink = n_sink
+        self.sink_pos = np.zeros(0, np.int64)  # token positions, ascending
+        self.sink_k = np.zeros((0, D), F16)
+        self.sink_v = np.zeros((0, D), F16)
         self.kc = np.zeros((0, D), np.uint8)
         self.ks = np.zeros((0, D), F16)
         self.kz = np.zeros((0, D), F16)
@@ -177,11 +237,18 @@ class KiviSequence:
         return self.wk.shape[0]
 
     def _quantize(self, K: np.ndarray, V: np.ndarray):
-        c, s, z = encode_keys(K, self.bk, self.g)
+        local = ()
+        if self.n_q == 0 and self.n_sink and K.shape[0]:
+            # the first step that quantizes tokens chooses the sinks among them
+            local = select_sinks(K, self.n_sink)
+            self.sink_pos = local.copy()  # nothing is quantized yet: block rows = positions
+            self.sink_k = K[local].copy()
+            self.sink_v = V[local].copy()
+        c, s, z = encode_keys(K, self.bk, self.g, local)
         self.kc = np.concatenate([self.kc, c])
         self.ks = np.concatenate([self.ks, s])
         self.kz = np.concatenate([self.kz, z])
-        c, s, z = encode_values(V, self.bv, self.g)
+        c, s, z = encode_values(V, self.bv, self.g, local)
         self.vc = np.concatenate([self.vc, c])
         self.vs = np.concatenate([self.vs, s])
         self.vz = np.concatenate([self.vz, z])
@@ -209,11 +276,14 @@ class KiviSequence:
         self.wv = np.concatenate([self.wv, v.astype(F16)[None]])
 
     def keys_hat(self) -> np.ndarray:
+        """Every cached key as attention sees it: reconstructed, except sinks and window rows."""
         kq = dequantize_keys(self.kc, self.ks, self.kz, self.g) if self.n_q else np.zeros((0, self.D))
+        kq[self.sink_pos] = self.sink_k.astype(F64)
         return np.concatenate([kq, self.wk.astype(F64)])
 
     def values_hat(self) -> np.ndarray:
-        vq = dequantize_values(self.vc, self.vs, self.vz, self.g) if self.n_q else np.zeros((0, self.D))
+        vq = dequantize_values(self.vc, np.abs(self.vs), self.vz, self.g) if self.n_q else np.zeros((0, self.D))
+        vq[self.sink_pos] = self.sink_v.astype(F64)
         return np.concatenate([vq, self.wv.astype(F64)])
 
 
