@@ -13,6 +13,9 @@
  *  - "Changelog", v0.30.0 "New" / "Honest scope": parameters kept as low end and step,
  *    integer bit widths, fp16 metadata.  "Changelog", v0.28.0: the residual window is
  *    flushed through the quantizer one whole chunk at a time.
+ *  - "Changelog", v0.9.0 "New" (KIVI-Sink): tokens with an outstanding key L2 norm stay in
+ *    fp16 and are left out of the statistics their groups' parameters come from;
+ *    n_sink_tokens = 0 is plain KIVI (kvq_config.n_sink).
  *
  * Conventions shared by every call:
  *  - Tensor arguments are DEVICE pointers owned by the caller. The library never allocates
@@ -61,6 +64,15 @@ typedef struct kvq_config {
   int32_t group;      /* g, must be 32 (the pages' default group size) */
   int32_t residual;   /* R, fp16 window capacity: a multiple of 32, at most 256 */
   int32_t max_tokens; /* per-sequence capacity in tokens, a positive multiple of 32 */
+  int32_t n_sink;     /* sink tokens per (sequence, KV head), 0..16 (KIVI-Sink); 0 = plain KIVI,
+                         and then the buffer is byte for byte the KIVI cache. The sinks are the
+                         n_sink tokens of largest key norm (squares added in fp32, channel 0
+                         first; the earlier token on equal norms) among the tokens quantized by
+                         the first call that quantizes any token of the sequence (a prefill or
+                         encode, or the first window flush); they never change afterwards. Their
+                         fp16 key and value rows are kept, they take no part in their key
+                         groups' min/max, and attention uses their fp16 rows in place of their
+                         quantized slots. */
 } kvq_config;
 
 /* Byte offsets of the regions inside the cache buffer (see the layout description in the
@@ -79,6 +91,11 @@ typedef struct kvq_layout_info {
   uint64_t sync_offset;     /* uint32 [B][H_kv] decode split counters, right after the lengths;
                                zero between calls (decode's last split of a sequence clears its
                                counter; every lengths update zeroes them) */
+  uint64_t sink_pos_offset; /* int32 [B][H_kv][n_sink]: sink token positions, ascending */
+  uint64_t sink_k_offset;   /* fp16 [B][H_kv][n_sink][D]: sink key rows */
+  uint64_t sink_v_offset;   /* fp16 [B][H_kv][n_sink][D]: sink value rows. The sink regions are
+                               valid once the sequence has quantized tokens; in the records a
+                               sink's value scales carry the sign bit (decode skips that slot). */
 } kvq_layout_info;
 
 typedef struct kvq_cache kvq_cache; /* opaque host handle */
@@ -128,7 +145,9 @@ kvq_status kvq_cache_lengths(const kvq_cache* cache, int32_t* n_quantized, int32
  * Key groups: 32 consecutive tokens of one channel; value groups: 32 consecutive channels
  * of one token. Per group: zero = min, scale = fp16((max - min) / (2^b - 1)) (fp32 ops),
  * codes = clamp(rint((x - zero) * (1/scale)), 0, 2^b - 1) with the stored scale, all
- * codes 0 when the stored scale is 0. Results are bit-identical on every run. */
+ * codes 0 when the stored scale is 0. Results are bit-identical on every run.
+ * With n_sink > 0, a sequence that had no quantized token first chooses its sinks among
+ * the n_tok[b] tokens (see kvq_config.n_sink); they stay out of their key groups' min/max. */
 kvq_status kvq_encode(kvq_cache* cache, const void* K, const void* V, int64_t ld_tok,
                       const int32_t* n_tok, void* stream);
 
@@ -152,14 +171,16 @@ kvq_status kvq_encode_block(const void* X, int32_t n_tok, int32_t D, int32_t bit
  * residual window ("Changelog" v0.8.0, v0.28.0): the first S - n_r tokens are quantized and
  * the last n_r = ((S - 1) mod R) + 1 stay fp16 (S = 0 leaves the sequence empty).
  * K, V as in kvq_encode; seq_len is a HOST array of B entries. A sequence that is not
- * empty is KVQ_E_INVALID; S > max_tokens is KVQ_E_CAPACITY. */
+ * empty is KVQ_E_INVALID; S > max_tokens is KVQ_E_CAPACITY. With n_sink > 0 the sinks are
+ * chosen among the S - n_r quantized tokens (none when that is 0). */
 kvq_status kvq_prefill(kvq_cache* cache, const void* K, const void* V, int64_t ld_tok,
                        const int32_t* seq_len, void* stream);
 
 /* North-star call 2 (residual window and chunk flush, "Changelog" v0.8.0 / v0.28.0).
  * Append one token to every sequence: k_tok, v_tok fp16 [B][H_kv][D]. A sequence whose
  * window is full first quantizes all R window tokens (R/32 key groups, R value tokens)
- * exactly as kvq_encode would, then stores the new token as window slot 0.
+ * exactly as kvq_encode would, then stores the new token as window slot 0 (with n_sink > 0,
+ * a sequence's first flush chooses its sinks among the R window tokens).
  * KVQ_E_CAPACITY if any sequence would exceed max_tokens (nothing is enqueued). */
 kvq_status kvq_append(kvq_cache* cache, const void* k_tok, const void* v_tok, void* stream);
 
@@ -170,7 +191,8 @@ kvq_status kvq_append(kvq_cache* cache, const void* k_tok, const void* v_tok, vo
  *   q:   fp16 [B][H_q][D];  out: fp16 [B][H_q][D], or fp32 when out_fp32 != 0.
  *   workspace: at least kvq_workspace_bytes(cfg, n_split) device bytes (KVQ_E_WORKSPACE).
  *   n_split: maximum splits per sequence along the tokens (0 = chosen from the lengths).
- * Every sequence must hold at least one token (KVQ_E_INVALID otherwise).
+ * Every sequence must hold at least one token (KVQ_E_INVALID otherwise). Sink tokens
+ * (n_sink > 0) enter with their fp16 rows, and their quantized slots are skipped.
  * One kernel: splits along the tokens write (acc, m, l) partials to the workspace and the
  * last split of each sequence and KV head merges them (counted in the cache's sync region).
  * Calls on one cache must therefore be ordered (one stream, or synchronised streams). */

@@ -27,6 +27,7 @@ PER_FILE = {
     # bit-exact quantizer: one rounding per fp32 operation
     "encode.hip": ["-ffp-contract=off"],
     "decode.hip": [],
+    "decode_sink.hip": [],
     "kvq.cpp": ["-x", "hip"],
 }
 

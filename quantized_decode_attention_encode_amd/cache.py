@@ -20,8 +20,10 @@ __all__ = ["KVQCache", "KVQError", "make_config", "kvq_probe", "kvq_cache_bytes"
 
 
 def make_config(batch, n_kv_heads, n_q_heads, head_dim, key_bits=2, value_bits=2, group=32, residual=32,
-                max_tokens=4096) -> Config:
-    return Config(batch, n_kv_heads, n_q_heads, head_dim, key_bits, value_bits, group, residual, max_tokens)
+                max_tokens=4096, n_sink=0) -> Config:
+    """n_sink > 0: KIVI-Sink, that many high key-norm tokens per (sequence, KV head) kept in fp16."""
+    return Config(batch, n_kv_heads, n_q_heads, head_dim, key_bits, value_bits, group, residual, max_tokens,
+                  n_sink)
 
 
 def _stream(stream) -> ctypes.c_void_p:

@@ -1,798 +1,13 @@
-// decode.hip - decode attention straight over the quantized cache (split-K, merged in-kernel).
-//
-// What is computed ("Changelog" v0.42.0 "Added": fused group-affine decode + attention):
-//   out = softmax(sm_scale * q . K_hat^T) V_hat over every quantized and window token,
-//   k_hat = code * scale + zero per key group, v_hat likewise per value group, with the
-//   reconstruction done in registers inside an online softmax accumulated in fp32; no
-//   dequantized K/V is written anywhere.
-//
-// Algebra used so that each cached code costs one multiply-add:
-//   score_t = sum_d q_d (s_{j,d} c_{t,d} + z_{j,d}) = sum_d q~_d c_{t,d} + beta_j,
-//     q~_d = q_d s_{j,d} and beta_j = q . z_j formed once per key group (32 tokens);
-//   out_d  = sum_t p_t (s_{t,k} c_{t,d} + z_{t,k}) = sum_t a_{t,k} c_{t,d} + sum_t p_t z_{t,k},
-//     a_{t,k} = p_t s_{t,k} formed once per (token, value group); the zero terms collapse
-//     into one bias per value group.
-//
-// Code -> float conversion: a b-bit code c sitting at bits [o, o+b) of a 16-bit half, with
-// o + b <= 10, becomes the exact fp16 number 1 + c * 2^(o-10) by OR-ing the exponent bits of
-// 1.0 (0x3C00) into that half. One v_and_or_b32 (mask, magic held in VGPRs) turns two codes
-// into such a pair, and v_fma_mix_f32 consumes either half directly as an fp32 operand. The
-// factor 2^(10-o) is folded into the partner operand (q~ or a) and the constant "1" terms
-// are removed exactly through beta and the value bias:
-//   sum_c x'_c (1 + c 2^(o_c-10)) - sum_c x'_c = sum_c x_c c,   x'_c = x_c 2^(10-o_c).
-// Codes not already at a usable bit position are first brought there by one shift per word
-// shared by every code it moves (two shifts per 16 two-bit codes).
-//
-// Scores are kept in base-2 units (q is pre-multiplied by sm_scale * log2 e): exp2 softmax.
-//
-// Work split: grid (n_split, H_kv, B); workgroup = 4 wavefronts; a workgroup owns `chunk`
-// consecutive units of one (b, h_kv) (unit = one 32-token record, or up to 32 window
-// tokens), its waves take every 4th unit and prefetch their next record while computing
-// the current one, and the workgroup writes one (acc[D], m, l) partial per query head. The
-// last workgroup of a (b, h_kv) to finish (a counter in the cache buffer decides) merges the
-// partials of that KV head's query heads into the output; a lone split writes it directly.
-//
-// Lane roles for a record (they follow the record layout, see layout.h):
-//   q~ producer    lane l: channels l*D/64 .. (D/64 of them) = quarter l/16
-//   key consumer   lane (P = l/4, Q = l%4): tokens 2P, 2P+1 x the channels of quarter Q
-//   a producer     lane (P, Q): value params of tokens 2P, 2P+1 (D/64 entries)
-//   value consumer lane l: channels l*D/64 .., all 32 tokens of the record
-// Quarter partial scores meet through two DPP quad butterflies.
-#include <hip/hip_ext.h>
-#include <hip/hip_fp16.h>
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-
-#include "kernels.h"
-#include "layout.h"
+// decode.hip - decode launches for caches without sink tokens (the kernel is in decode_kernel.h).
+#include "decode_kernel.h"
 
 namespace kvq {
 
-// ---------------------------------------------------------------------------------------
-// small device helpers
-// ---------------------------------------------------------------------------------------
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {  // old = 0: lets the compiler fuse the move into the consumer
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowRor4 = 0x124, kRowRor8 = 0x128;
-
-__device__ __forceinline__ float row_sum16(float v) {  // sum over the 16 lanes of a row, in every lane
-  v += dpp<kQuadXor1>(v);
-  v += dpp<kQuadXor2>(v);
-  v += dpp<kRowRor4>(v);
-  v += dpp<kRowRor8>(v);
-  return v;
-}
-// Max over the wave when the 4 lanes of each quad hold equal values: row_ror 4 / 8 inside a
-// row, then the gfx950 row swaps: with both operands equal, permlane32_swap returns rows
-// (0,1,0,1) and (2,3,2,3), permlane16_swap rows (0,0,2,2) and (1,1,3,3).
-__device__ __forceinline__ float wave_max_of_quads(float v) {
-  v = fmaxf(v, dpp<kRowRor4>(v));
-  v = fmaxf(v, dpp<kRowRor8>(v));
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
-}
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
-
-__device__ __forceinline__ float lo_f(uint32_t w) { return float(__builtin_bit_cast(_Float16, uint16_t(w & 0xFFFF))); }
-__device__ __forceinline__ float hi_f(uint32_t w) { return float(__builtin_bit_cast(_Float16, uint16_t(w >> 16))); }
-
-// A value the compiler must keep in a VGPR (so v_and_or_b32 can take it; gfx9 VOP3 has no literals).
-template <uint32_t C>
-__device__ __forceinline__ uint32_t vconst() {
-  uint32_t r;
-  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(C));
-  return r;
-}
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
-  return r;
-}
-
-template <int N>
-__device__ __forceinline__ void load_words(const uint32_t* __restrict__ p, uint32_t* out) {
-  if constexpr (N % 4 == 0) {
-#pragma unroll
-    for (int i = 0; i < N / 4; ++i) {
-      const uint4 v = reinterpret_cast<const uint4*>(p)[i];
-      out[4 * i] = v.x; out[4 * i + 1] = v.y; out[4 * i + 2] = v.z; out[4 * i + 3] = v.w;
-    }
-  } else if constexpr (N % 2 == 0) {
-#pragma unroll
-    for (int i = 0; i < N / 2; ++i) {
-      const uint2 v = reinterpret_cast<const uint2*>(p)[i];
-      out[2 * i] = v.x; out[2 * i + 1] = v.y;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < N; ++i) out[i] = p[i];
-  }
-}
-
-// Where each code of a word goes before the OR with 1.0: in-half position j (bit j*B) is
-// shifted by sh(j) bits (left positive) to bit od(j) = j*B + sh(j), with od(j) + B <= 10.
-template <int B>
-struct Magic {
-  static constexpr int NH = 16 / B;  // codes per 16-bit half
-  static constexpr int NC = 32 / B;  // codes per word
-  __host__ __device__ static constexpr int sh(int j) {
-    return B == 2 ? (j < 2 ? 4 : (j < 5 ? 0 : -6))
-         : B == 4 ? (j == 0 ? 6 : (j == 1 ? 0 : (j == 2 ? -2 : -6)))
-                  : (j == 0 ? 2 : -6);
-  }
-  __host__ __device__ static constexpr int od(int j) { return j * B + sh(j); }
-  // factor 2^(10 - od) folded into the partner operand of the code at word position p
-  __host__ __device__ static constexpr float fold(int p) {
-    return float(1 << (10 - od(p % NH)));
-  }
-};
-
-// The NH fp16 pairs of one word: pair j holds the codes at positions j (low half) and
-// j + NH (high half).
-template <int B>
-struct Unpacker {
-  uint32_t magic, mk[10];  // mk[o]: the code bits at [o, o+B) of both halves
-  __device__ __forceinline__ void init() {
-    magic = vconst<0x3C003C00u>();
-#pragma unroll
-    for (int j = 0; j < Magic<B>::NH; ++j) {
-      const int o = Magic<B>::od(j);
-      const uint32_t m = ((1u << B) - 1) << o;
-      uint32_t r;
-      asm("v_mov_b32 %0, %1" : "=v"(r) : "v"(m | (m << 16)));
-      mk[o] = r;
-    }
-  }
-  __device__ __forceinline__ void run(uint32_t w, uint32_t* out) const {
-#pragma unroll
-    for (int j = 0; j < Magic<B>::NH; ++j) {
-      const int s = Magic<B>::sh(j);
-      const uint32_t v = s > 0 ? (w << s) : (s < 0 ? (w >> -s) : w);
-      out[j] = and_or(v, mk[Magic<B>::od(j)], magic);
-    }
-  }
-};
-
-// Value weights travel as fp16: A_t = fp16(p_t * s_t * 2^(10-o_t) * 2^-6). With p <= 1, an
-// fp16 scale s <= 43669 (2-bit) / 8734 (4-bit) / 514 (8-bit) and a fold factor 2^(10-o) <= 64
-// (2/4-bit) or 256 (8-bit), A never exceeds the fp16 range; accumulators then carry 2^-6 units.
-constexpr float kVScale = 1.0f / 64.0f;
-
-template <int D, int G>
-struct WaveLds {
-  float qt[G][4][D / 4 + 4];      // scaled, folded query per quarter (padded rows)
-  float beta[G][4];               // quarter offsets (q . z minus the fold constant)
-  uint32_t A[G][D / 32][16 + 4];  // fp16 value weights per (value group, token pair), see kVScale
-  float pw[G][32 + 4];            // window tokens: softmax weights
-  float red[G][64];
-};
-
-template <int D, int BK, int BV>
-struct RecordRegs {
-  uint32_t kc[2 * (D * BK / 128)];
-  uint32_t vc[(D / 64) * BV];
-  uint32_t kp[D / 64];
-  uint32_t vp[D / 64];
-};
-
-template <int D, int BK, int BV>
-__device__ __forceinline__ void load_record(const uint8_t* __restrict__ rec, int lane, RecordRegs<D, BK, BV>& r) {
-  constexpr int E = D / 64, KW = 2 * (D * BK / 128), VW = E * BV;
-  load_words<KW>(reinterpret_cast<const uint32_t*>(rec) + lane * KW, r.kc);
-  load_words<VW>(reinterpret_cast<const uint32_t*>(rec + rec_off_vcodes(D, BK)) + lane * VW, r.vc);
-  load_words<E>(reinterpret_cast<const uint32_t*>(rec + rec_off_kparams(D, BK, BV)) + lane * E, r.kp);
-  load_words<E>(reinterpret_cast<const uint32_t*>(rec + rec_off_vparams(D, BK, BV)) + lane * E, r.vp);
-}
-
-// Wavefronts per decode workgroup; each takes every kWaves-th unit of the workgroup's chunk.
-constexpr int kWaves = 4;
-
-// State of one wavefront across the units it visits.
-template <int D, int G>
-struct WaveState {
-  float m[G], l[G], bias[G], acc[G][D / 64];
-};
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Online-softmax step for one head: new scores s0, s1 (base-2 units) of tokens 2P, 2P+1.
-template <int D, int G>
-__device__ __forceinline__ void softmax_step(WaveState<D, G>& st, int i, float s0, float s1, float& p0, float& p1) {
-  // The running max only moves when some lane holds a larger score; a wave vote finds out
-  // with one comparison, so the reduction and the rescale run only then.
-  if (__any(fmaxf(s0, s1) > st.m[i])) {  // wave-uniform
-    const float mx = wave_max_of_quads(fmaxf(s0, s1));
-    const float alpha = fast_exp2(st.m[i] - mx);
-    st.m[i] = mx;
-    st.l[i] *= alpha;
-    st.bias[i] *= alpha;
-#pragma unroll
-    for (int e = 0; e < D / 64; ++e) st.acc[i][e] *= alpha;
-  }
-  p0 = fast_exp2(s0 - st.m[i]);
-  p1 = fast_exp2(s1 - st.m[i]);
-  st.l[i] += p0 + p1;
-}
-
-// One 32-token record of (b, h_kv), all G query heads.
-template <int D, int BK, int BV, int G>
-__device__ __forceinline__ void process_record(const RecordRegs<D, BK, BV>& cur, WaveLds<D, G>& W, WaveState<D, G>& st,
-                                               const Unpacker<BK>& upk, const Unpacker<BV>& upv,
-                                               const float (&qs)[G][D / 64], const float (&qf)[G][D / 64],
-                                               float vf0, float vf1, int lane) {
-  constexpr int E = D / 64, DQ = D / 4, WQ = D * BK / 128, NKG = D / 32;
-  using MK = Magic<BK>;
-  using MV = Magic<BV>;
-  const int P = lane >> 2, Q = lane & 3;
-  const int kcons = (lane * E) / 32;
-
-  // ---- producer: folded scaled query and quarter offsets
-#pragma unroll
-  for (int i = 0; i < G; ++i) {
-    float bp = 0.f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int ch = lane * E + e;
-      const float qt = qf[i][e] * lo_f(cur.kp[e]);
-      W.qt[i][ch / DQ][ch % DQ] = qt;
-      bp += qs[i][e] * hi_f(cur.kp[e]) - qt;
-    }
-    bp = row_sum16(bp);
-    if ((lane & 15) == 0) W.beta[i][lane >> 4] = bp;
-  }
-  wave_sync();
-
-  // ---- keys
-  float s[G][2];
-#pragma unroll
-  for (int i = 0; i < G; ++i) s[i][0] = s[i][1] = W.beta[i][Q];
-  if constexpr (G == 1) {
-    // word by word: few live registers
-#pragma unroll
-    for (int w = 0; w < WQ; ++w) {
-      uint32_t k0[MK::NH], k1[MK::NH];
-      upk.run(cur.kc[w], k0);
-      upk.run(cur.kc[WQ + w], k1);
-      float qv[MK::NC];
-#pragma unroll
-      for (int c = 0; c < MK::NC; c += 4) {
-        const float4 t4 = *reinterpret_cast<const float4*>(&W.qt[0][Q][w * MK::NC + c]);
-        qv[c] = t4.x; qv[c + 1] = t4.y; qv[c + 2] = t4.z; qv[c + 3] = t4.w;
-      }
-#pragma unroll
-      for (int j = 0; j < MK::NH; ++j) {
-        s[0][0] = __builtin_fmaf(qv[j], lo_f(k0[j]), s[0][0]);
-        s[0][1] = __builtin_fmaf(qv[j], lo_f(k1[j]), s[0][1]);
-        s[0][0] = __builtin_fmaf(qv[j + MK::NH], hi_f(k0[j]), s[0][0]);
-        s[0][1] = __builtin_fmaf(qv[j + MK::NH], hi_f(k1[j]), s[0][1]);
-      }
-    }
-  } else {
-    // unpack the whole quarter once; every head reuses it
-    uint32_t kr[2][WQ][MK::NH];
-#pragma unroll
-    for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-      for (int w = 0; w < WQ; ++w) upk.run(cur.kc[tp * WQ + w], kr[tp][w]);
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-      float qv[DQ];
-#pragma unroll
-      for (int c = 0; c < DQ; c += 4) {
-        const float4 t4 = *reinterpret_cast<const float4*>(&W.qt[i][Q][c]);
-        qv[c] = t4.x; qv[c + 1] = t4.y; qv[c + 2] = t4.z; qv[c + 3] = t4.w;
-      }
-#pragma unroll
-      for (int w = 0; w < WQ; ++w)
-#pragma unroll
-        for (int j = 0; j < MK::NH; ++j) {
-          const int c = w * MK::NC + j;
-          s[i][0] = __builtin_fmaf(qv[c], lo_f(kr[0][w][j]), s[i][0]);
-          s[i][1] = __builtin_fmaf(qv[c], lo_f(kr[1][w][j]), s[i][1]);
-          s[i][0] = __builtin_fmaf(qv[c + MK::NH], hi_f(kr[0][w][j]), s[i][0]);
-          s[i][1] = __builtin_fmaf(qv[c + MK::NH], hi_f(kr[1][w][j]), s[i][1]);
-        }
-    }
-  }
-
-#pragma unroll
-  for (int i = 0; i < G; ++i) {
-    float s0 = s[i][0], s1 = s[i][1];
-    s0 += dpp<kQuadXor1>(s0);
-    s1 += dpp<kQuadXor1>(s1);
-    s0 += dpp<kQuadXor2>(s0);
-    s1 += dpp<kQuadXor2>(s1);
-    float p0, p1;
-    softmax_step<D, G>(st, i, s0, s1, p0, p1);
-    // ---- producer: fp16 folded value weights and the zero-term bias (in kVScale units)
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      // entry e of this lane: token t, value group k (the value-param dword lane*E + e)
-      const int idx = lane * E + e;
-      const int tp = idx & 1, k = (idx >> 1) % NKG, t = 2 * P + tp;
-      const float p = tp ? p1 : p0;
-      const float vfold = (tp ? vf1 : vf0);  // 2^(10-o_t) * kVScale
-      const __half a16 = __float2half_rn((p * vfold) * lo_f(cur.vp[e]));
-      st.bias[i] += (p * kVScale) * hi_f(cur.vp[e]) - __half2float(a16);
-      const int dw = (t / MV::NC) * MV::NH + (t % MV::NC) % MV::NH, hf = (t % MV::NC) / MV::NH;
-      reinterpret_cast<__half*>(&W.A[i][k][dw])[hf] = a16;
-    }
-  }
-  wave_sync();
-
-  // ---- values: v_dot2_f32_f16 of (weight pair) x (code pair); a word = NC tokens of a channel
-  using h2 = _Float16 __attribute__((ext_vector_type(2)));
-  if constexpr (G == 1) {
-#pragma unroll
-    for (int w = 0; w < BV; ++w) {
-      uint32_t vr[E][MV::NH];
-#pragma unroll
-      for (int e = 0; e < E; ++e) upv.run(cur.vc[e * BV + w], vr[e]);
-      uint32_t av[MV::NH];
-#pragma unroll
-      for (int j = 0; j < MV::NH; j += (MV::NH >= 4 ? 4 : 2)) {
-        if constexpr (MV::NH >= 4) {
-          const uint4 t4 = *reinterpret_cast<const uint4*>(&W.A[0][kcons][w * MV::NH + j]);
-          av[j] = t4.x; av[j + 1] = t4.y; av[j + 2] = t4.z; av[j + 3] = t4.w;
-        } else {
-          const uint2 t2 = *reinterpret_cast<const uint2*>(&W.A[0][kcons][w * MV::NH + j]);
-          av[j] = t2.x; av[j + 1] = t2.y;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        float x = st.acc[0][e];
-#pragma unroll
-        for (int j = 0; j < MV::NH; ++j)
-          x = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, av[j]), __builtin_bit_cast(h2, vr[e][j]), x, false);
-        st.acc[0][e] = x;
-      }
-    }
-  } else {
-    uint32_t vr[E][BV][MV::NH];
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-#pragma unroll
-      for (int w = 0; w < BV; ++w) upv.run(cur.vc[e * BV + w], vr[e][w]);
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-      uint32_t av[16];
-#pragma unroll
-      for (int j = 0; j < 16; j += 4) {
-        const uint4 t4 = *reinterpret_cast<const uint4*>(&W.A[i][kcons][j]);
-        av[j] = t4.x; av[j + 1] = t4.y; av[j + 2] = t4.z; av[j + 3] = t4.w;
-      }
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        float x = st.acc[i][e];
-#pragma unroll
-        for (int w = 0; w < BV; ++w)
-#pragma unroll
-          for (int j = 0; j < MV::NH; ++j)
-            x = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, av[w * MV::NH + j]), __builtin_bit_cast(h2, vr[e][w][j]),
-                                       x, false);
-        st.acc[i][e] = x;
-      }
-    }
-  }
-  wave_sync();
-}
-
-// Up to 32 fp16 window tokens (tokens tbase .. tbase + nvalid - 1 of the window).
-// Token tnew of the unit (when 0 <= tnew < nvalid) is the one this launch appends: its rows
-// come from kn / vn instead of the window.
-template <int D, int G>
-__device__ __forceinline__ void process_window(const __half* __restrict__ wk, const __half* __restrict__ wv, int nvalid,
-                                               int tnew, const __half* kn, const __half* vn,
-                                               WaveLds<D, G>& W, WaveState<D, G>& st, const float (&qs)[G][D / 64],
-                                               int lane) {
-  constexpr int E = D / 64, DQ = D / 4;
-  const int P = lane >> 2, Q = lane & 3;
-  const int kcons = (lane * E) / 32;
-#pragma unroll
-  for (int i = 0; i < G; ++i)
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int ch = lane * E + e;
-      W.qt[i][ch / DQ][ch % DQ] = qs[i][e];
-    }
-  wave_sync();
-  const int t0 = 2 * P, t1 = 2 * P + 1;
-  const int t0c = min(t0, nvalid - 1), t1c = min(t1, nvalid - 1);
-  const uint32_t* k0p = reinterpret_cast<const uint32_t*>((t0c == tnew ? kn : wk + t0c * D) + Q * DQ);
-  const uint32_t* k1p = reinterpret_cast<const uint32_t*>((t1c == tnew ? kn : wk + t1c * D) + Q * DQ);
-  uint32_t k0w[DQ / 2], k1w[DQ / 2];
-#pragma unroll
-  for (int c = 0; c < DQ / 2; ++c) {
-    k0w[c] = k0p[c];
-    k1w[c] = k1p[c];
-  }
-#pragma unroll
-  for (int i = 0; i < G; ++i) {
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-    for (int c = 0; c < DQ / 2; ++c) {
-      const float qa = W.qt[i][Q][2 * c], qb = W.qt[i][Q][2 * c + 1];
-      s0 = __builtin_fmaf(qa, lo_f(k0w[c]), s0);
-      s0 = __builtin_fmaf(qb, hi_f(k0w[c]), s0);
-      s1 = __builtin_fmaf(qa, lo_f(k1w[c]), s1);
-      s1 = __builtin_fmaf(qb, hi_f(k1w[c]), s1);
-    }
-    s0 += dpp<kQuadXor1>(s0);
-    s0 += dpp<kQuadXor2>(s0);
-    s1 += dpp<kQuadXor1>(s1);
-    s1 += dpp<kQuadXor2>(s1);
-    if (t0 >= nvalid) s0 = -INFINITY;
-    if (t1 >= nvalid) s1 = -INFINITY;
-    float p0, p1;
-    softmax_step<D, G>(st, i, s0, s1, p0, p1);
-    if (Q == 0) *reinterpret_cast<float2*>(&W.pw[i][2 * P]) = make_float2(p0 * kVScale, p1 * kVScale);
-  }
-  wave_sync();
-#pragma unroll
-  for (int i = 0; i < G; ++i) {
-    for (int t = 0; t < nvalid; ++t) {
-      const float a = W.pw[i][t];
-      const __half* vrow = t == tnew ? vn : wv + t * D;
-      if constexpr (E == 2) {
-        const uint32_t vw = reinterpret_cast<const uint32_t*>(vrow)[lane];
-        st.acc[i][0] = __builtin_fmaf(a, lo_f(vw), st.acc[i][0]);
-        st.acc[i][1] = __builtin_fmaf(a, hi_f(vw), st.acc[i][1]);
-      } else {
-        st.acc[i][0] = __builtin_fmaf(a, __half2float(vrow[lane]), st.acc[i][0]);
-      }
-    }
-  }
-  wave_sync();
-}
-
-// Split partials cross workgroups (and XCDs, each with its own L2) inside one launch. They are
-// written and read with device-scope relaxed atomics, which the hardware performs coherently
-// across the XCDs (cache-policy bit sc1) without writing back or invalidating a whole L2, which
-// a device-scope fence would do in every wave.
-__device__ __forceinline__ void put_partial(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float get_partial(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void store_out(void* out, int out_fp32, int64_t idx, float v) {
-  if (out_fp32)
-    static_cast<float*>(out)[idx] = v;
-  else
-    static_cast<__half*>(out)[idx] = __float2half_rn(v);
-}
-
-// Merge the nv split partials (acc[D], m, l) of the G query heads row0 .. row0+G-1 into the
-// output, by one workgroup of 64*kWaves threads: T threads per output element each fold a
-// strided share of the splits (batches of 8 loads in flight), then meet through LDS.
-template <int D, int G>
-__device__ __forceinline__ void merge_splits(const float* __restrict__ ws, int64_t row0, int n_split, int nv,
-                                             float (*mrg)[64 * kWaves], void* out, int out_fp32) {
-  constexpr int NT = 64 * kWaves, NOUT = G * D;
-  constexpr int T = NOUT >= NT ? 1 : NT / NOUT;
-  constexpr int NO = NOUT >= NT ? NT : NOUT;  // output elements per pass
-  const int tid = threadIdx.x, r = tid / NO;
-  for (int oi = tid % NO; oi < NOUT; oi += NO) {
-    const int i = oi / D, ch = oi % D;
-    const float* base = ws + (row0 + i) * n_split * (D + 4);
-    float M = -INFINITY, Ls = 0.f, O = 0.f;
-    for (int s0 = r; s0 < nv; s0 += 8 * T) {
-      float m[8], l[8], o[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int sk = s0 + k * T;
-        const float* p = base + min(sk, nv - 1) * (D + 4);  // clamped: every load in bounds
-        const float mv = get_partial(p + D);
-        m[k] = sk < nv ? mv : -INFINITY;
-        l[k] = get_partial(p + D + 1);
-        o[k] = get_partial(p + ch);
-      }
-      float mx = M;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) mx = fmaxf(mx, m[k]);
-      const float sc = fast_exp2(M - mx);  // 0 while M is still -inf
-      O *= sc;
-      Ls *= sc;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float w = fast_exp2(m[k] - mx);
-        O = __builtin_fmaf(w, o[k], O);
-        Ls = __builtin_fmaf(w, l[k], Ls);
-      }
-      M = mx;
-    }
-    if constexpr (T == 1) {
-      store_out(out, out_fp32, (row0 + i) * D + ch, O / Ls);
-    } else {
-      mrg[0][tid] = M;
-      mrg[1][tid] = Ls;
-      mrg[2][tid] = O;
-    }
-  }
-  if constexpr (T > 1) {
-    __syncthreads();
-    if (tid < NO) {
-      float M = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < T; ++j) M = fmaxf(M, mrg[0][tid + j * NO]);
-      float Ls = 0.f, O = 0.f;
-#pragma unroll
-      for (int j = 0; j < T; ++j) {
-        const float w = fast_exp2(mrg[0][tid + j * NO] - M);  // a share with no split: 0
-        Ls = __builtin_fmaf(w, mrg[1][tid + j * NO], Ls);
-        O = __builtin_fmaf(w, mrg[2][tid + j * NO], O);
-      }
-      store_out(out, out_fp32, (row0 + tid / D) * D + tid % D, O / Ls);
-    }
-  }
-}
-
-template <int D, int BK, int BV, int G>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : (G <= 4 ? 2 : 1))))
-void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape ds, const __half* __restrict__ q,
-                         float* __restrict__ ws, uint32_t* __restrict__ sync, void* __restrict__ out,
-                         const __half* __restrict__ k_app, const __half* __restrict__ v_app, uint8_t* bufw) {
-  constexpr int E = D / 64, DQ = D / 4, NKG = D / 32;
-  using MK = Magic<BK>;
-  using MV = Magic<BV>;
-
-  __shared__ __attribute__((aligned(16))) union {
-    WaveLds<D, G> w[kWaves];
-    float res[kWaves][G][D + 4];
-    float mrg[3][64 * kWaves];
-  } sh;
-  __shared__ int sh_last;
-
-  const int sigma = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int32_t* len = reinterpret_cast<const int32_t*>(buf + L.lengths(b, h));
-  const int nq = max(0, min(len[0], L.max_groups * kGroup));
-  const int nr_old = max(0, min(len[1], L.R));
-  const int nr = min(nr_old + ds.append, L.R);  // with an append: the new token is window slot nr_old
-  const int ngroups = nq / kGroup;
-  const int nunits = ngroups + (nr + kGroup - 1) / kGroup;
-  const int u0 = sigma * ds.chunk;
-  if (u0 >= nunits) return;
-  const int u1 = min(u0 + ds.chunk, nunits);
-  const int uq = min(u1, ngroups);  // end of the quantized units of this split
-
-  WaveLds<D, G>& W = sh.w[wave];
-  const int P = lane >> 2, Q = lane & 3;
-  const int kcons = (lane * E) / 32;
-
-  Unpacker<BK> upk;
-  Unpacker<BV> upv;
-  upk.init();
-  upv.init();
-
-  float qs[G][E], qf[G][E];
-#pragma unroll
-  for (int i = 0; i < G; ++i)
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int ch = lane * E + e;
-      qs[i][e] = __half2float(q[(int64_t(b) * ds.n_q_heads + h * G + i) * D + ch]) * ds.qscale;
-      qf[i][e] = qs[i][e] * MK::fold((ch % DQ) % MK::NC);
-    }
-  const float vf0 = MV::fold((2 * P) % MV::NC) * kVScale, vf1 = MV::fold((2 * P + 1) % MV::NC) * kVScale;
-
-  WaveState<D, G> st;
-#pragma unroll
-  for (int i = 0; i < G; ++i) {
-    st.m[i] = -INFINITY;
-    st.l[i] = 0.f;
-    st.bias[i] = 0.f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) st.acc[i][e] = 0.f;
-  }
-
-  // Quantized records, the next one loaded while the current one is computed. Prefetch loads
-  // are unconditional (their record index is clamped into the buffer: the last one of a
-  // wave re-reads a record it never uses) so that the compiler's memory-counter waits stay
-  // exact: a conditional load at a control-flow merge makes it wait for the prefetch too.
-  const uint8_t* rec0 = buf + L.record(b, h, 0);
-  const uint64_t rb = L.rec_bytes;
-  const int ulast = max(uq - 1, 0);
-  int u = u0 + wave;
-  if constexpr (G == 1) {
-    RecordRegs<D, BK, BV> ra, rbuf;
-    if (u < uq) {
-      load_record<D, BK, BV>(rec0 + u * rb, lane, ra);
-      load_record<D, BK, BV>(rec0 + min(u + kWaves, ulast) * rb, lane, rbuf);
-      while (true) {
-        process_record<D, BK, BV, G>(ra, W, st, upk, upv, qs, qf, vf0, vf1, lane);
-        u += kWaves;
-        if (u >= uq) break;
-        load_record<D, BK, BV>(rec0 + min(u + kWaves, ulast) * rb, lane, ra);
-        process_record<D, BK, BV, G>(rbuf, W, st, upk, upv, qs, qf, vf0, vf1, lane);
-        u += kWaves;
-        if (u >= uq) break;
-        load_record<D, BK, BV>(rec0 + min(u + kWaves, ulast) * rb, lane, rbuf);
-      }
-    }
-  } else {
-    RecordRegs<D, BK, BV> cur, nxt;
-    if (u < uq) {
-      load_record<D, BK, BV>(rec0 + u * rb, lane, cur);
-      for (; u < uq; u += kWaves) {
-        load_record<D, BK, BV>(rec0 + min(u + kWaves, ulast) * rb, lane, nxt);
-        process_record<D, BK, BV, G>(cur, W, st, upk, upv, qs, qf, vf0, vf1, lane);
-        cur = nxt;
-      }
-    }
-  }
-  // window units
-  for (; u < u1; u += kWaves) {
-    const int tbase = (u - ngroups) * kGroup;
-    const int nvalid = min(kGroup, nr - tbase);
-    const __half* wk = reinterpret_cast<const __half*>(buf + L.wk_off + L.window(b, h)) + tbase * D;
-    const __half* wv = reinterpret_cast<const __half*>(buf + L.wv_off + L.window(b, h)) + tbase * D;
-    const int tnew = ds.append ? nr_old - tbase : -1;  // the appended token in this unit, if 0 <= tnew < nvalid
-    const int64_t tok = (int64_t(b) * L.Hkv + h) * D;
-    const __half* kn = ds.append ? k_app + tok : nullptr;
-    const __half* vn = ds.append ? v_app + tok : nullptr;
-    process_window<D, G>(wk, wv, nvalid, tnew, kn, vn, W, st, qs, lane);
-    if (tnew >= 0 && tnew < nvalid) {  // store the appended token in its slot (no read of it here)
-      __half* dk = reinterpret_cast<__half*>(bufw + L.wk_off + L.window(b, h)) + nr_old * D;
-      __half* dv = reinterpret_cast<__half*>(bufw + L.wv_off + L.window(b, h)) + nr_old * D;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        dk[lane * E + e] = kn[lane * E + e];
-        dv[lane * E + e] = vn[lane * E + e];
-      }
-    }
-  }
-
-  // ---- finish the wave: l counted once per quad, bias summed over its producer lanes
-  float lt[G], o[G][E];
-#pragma unroll
-  for (int i = 0; i < G; ++i) {
-    float v = (Q == 0) ? st.l[i] : 0.f;
-#pragma unroll
-    for (int msk = 1; msk < 64; msk <<= 1) v += __shfl_xor(v, msk, 64);
-    lt[i] = v;
-    W.red[i][lane] = st.bias[i];
-  }
-  wave_sync();
-#pragma unroll
-  for (int i = 0; i < G; ++i) {
-    float bsum = 0.f;
-    for (int j = 0; j < 64; ++j)
-      if (((j * E) >> 1) % NKG == kcons) bsum += W.red[i][j];
-#pragma unroll
-    for (int e = 0; e < E; ++e) o[i][e] = (st.acc[i][e] + bsum) * (1.0f / kVScale);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < G; ++i) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) sh.res[wave][i][lane * E + e] = o[i][e];
-    if (lane == 0) {
-      sh.res[wave][i][D] = st.m[i];
-      sh.res[wave][i][D + 1] = lt[i];
-    }
-  }
-  __syncthreads();
-
-  // ---- combine the waves: the partial of each query head, or the output when this
-  // workgroup is the sequence's only split
-  const int nvalid = min(ds.n_split, (nunits + ds.chunk - 1) / ds.chunk);
-  const int64_t row0 = int64_t(b) * ds.n_q_heads + h * G;  // first query head of this KV head
-  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
-    const int i = idx / D, ch = idx % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sh.res[w][i][D]);
-    float O = 0.f, Lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = sh.res[w][i][D];
-      if (mw != -INFINITY) {
-        const float wgt = fast_exp2(mw - M);
-        O += wgt * sh.res[w][i][ch];
-        Lsum += wgt * sh.res[w][i][D + 1];
-      }
-    }
-    if (nvalid == 1) {
-      store_out(out, ds.out_fp32, (row0 + i) * D + ch, O / Lsum);
-      continue;
-    }
-    float* dst = ws + ((row0 + i) * ds.n_split + sigma) * (D + 4);
-    put_partial(dst + ch, O);
-    if (ch == 0) {
-      put_partial(dst + D, M);
-      put_partial(dst + D + 1, Lsum);
-    }
-  }
-  // With an append, the split that finishes (b, h_kv) last advances its device lengths: every
-  // split of (b, h_kv) has read them by then.
-  int32_t* len_w = reinterpret_cast<int32_t*>(bufw + L.lengths(b, h));
-  if (nvalid == 1) {
-    if (ds.append && threadIdx.x == 0) len_w[1] = nr;
-    return;
-  }
-
-  // ---- the last split of (b, h_kv) to finish merges every partial. Each wave waits until its
-  // partial stores are acknowledged at device scope, the workgroup meets, and only then does
-  // one thread move the counter (a device-scope atomic, performed coherently); the workgroup
-  // that brings it to nvalid reads every partial back the same coherent way, then clears the
-  // counter for the next call.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  uint32_t* cnt = sync + (int64_t(b) * L.Hkv + h);
-  if (threadIdx.x == 0) sh_last = atomicAdd(cnt, 1u) + 1u == uint32_t(nvalid);
-  __syncthreads();
-  if (!sh_last) return;
-  merge_splits<D, G>(ws, row0, ds.n_split, nvalid, sh.mrg, out, ds.out_fp32);
-  if (threadIdx.x == 0) {
-    if (ds.append) len_w[1] = nr;
-    atomicExch(cnt, 0u);
-  }
-}
-
-// ------------------------------------------------------------------------------------
-template <int D, int BK, int BV, int G>
-static hipError_t launch_split_t(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q,
-                                 float* ws, void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0,
-                                 hipEvent_t e1) {
-  dim3 grid(ds.n_split, L.Hkv, L.B);
-  uint32_t* sync = reinterpret_cast<uint32_t*>(buf + L.sync_off);
-  const __half* qh = static_cast<const __half*>(q);
-  const __half* kh = static_cast<const __half*>(ka);
-  const __half* vh = static_cast<const __half*>(va);
-  if (e0 || e1)
-    hipExtLaunchKernelGGL((decode_split_kernel<D, BK, BV, G>), grid, dim3(64 * kWaves), 0, s, e0, e1, 0,
-                          static_cast<const uint8_t*>(buf), L, ds, qh, ws, sync, out, kh, vh, buf);
-  else
-    hipLaunchKernelGGL((decode_split_kernel<D, BK, BV, G>), grid, dim3(64 * kWaves), 0, s,
-                       static_cast<const uint8_t*>(buf), L, ds, qh, ws, sync, out, kh, vh, buf);
-  return hipGetLastError();
-}
-
-template <int D, int BK, int BV>
-static hipError_t launch_split_g(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q,
-                                 float* ws, void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0,
-                                 hipEvent_t e1) {
-  switch (ds.G) {
-    case 1: return launch_split_t<D, BK, BV, 1>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 2: return launch_split_t<D, BK, BV, 2>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 4: return launch_split_t<D, BK, BV, 4>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 8: return launch_split_t<D, BK, BV, 8>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-template <int D>
-static hipError_t launch_split_d(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q,
-                                 float* ws, void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0,
-                                 hipEvent_t e1) {
-  switch (L.bk * 16 + L.bv) {
-    case 0x22: return launch_split_g<D, 2, 2>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 0x24: return launch_split_g<D, 2, 4>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 0x28: return launch_split_g<D, 2, 8>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 0x42: return launch_split_g<D, 4, 2>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 0x44: return launch_split_g<D, 4, 4>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 0x48: return launch_split_g<D, 4, 8>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 0x82: return launch_split_g<D, 8, 2>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 0x84: return launch_split_g<D, 8, 4>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 0x88: return launch_split_g<D, 8, 8>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    default: return hipErrorInvalidValue;
-  }
-}
-
 hipError_t launch_decode(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q, float* ws,
                          void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  if (L.D == 128) return launch_split_d<128>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-  if (L.D == 64) return launch_split_d<64>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+  if (L.NS > 0) return launch_decode_sink(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+  if (L.D == 128) return launch_split_d<128, false>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+  if (L.D == 64) return launch_split_d<64, false>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
   return hipErrorInvalidValue;
 }
 

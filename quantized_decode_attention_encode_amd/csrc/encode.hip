@@ -21,6 +21,12 @@
 //     across the 4 chunks of a 32-channel value group;
 //   * codes are packed into the record image in LDS and the record leaves with coalesced
 //     16-byte stores.
+//
+// Sink tokens ("Changelog" v0.9.0, KIVI-Sink): the tokens of largest key L2 norm (squares
+// added in fp32, channel 0 first, earlier token on equal norms), chosen once per
+// (sequence, KV head) among the tokens of the first step that quantizes any. They keep
+// their fp16 rows in the sink regions, are left out of their key groups' min/max, and their
+// value scales are stored with the sign bit set so that decode skips their quantized slots.
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
 #include <stdint.h>
@@ -120,10 +126,12 @@ __device__ __forceinline__ uint32_t code_of(float x, const GroupParams& p) {
 }
 
 // Quantize the 32-token tile (rows ks[0..31], vs[0..31], row stride D elements) into the
-// record at `rec_out`. Called by all 64 lanes of a single-wave workgroup.
+// record at `rec_out`. Called by all 64 lanes of a single-wave workgroup. Bit t of
+// sink_mask (wave-uniform) marks token t as a sink.
 template <int D, int BK, int BV>
 __device__ __forceinline__ void encode_record(const __half* __restrict__ ks, const __half* __restrict__ vs,
-                              uint32_t* __restrict__ rec_out, EncodeLds<D, BK, BV>& lds) {
+                              uint32_t* __restrict__ rec_out, EncodeLds<D, BK, BV>& lds,
+                              uint32_t sink_mask = 0) {
   constexpr int CH = D / 8;      // 16-byte chunks per row
   constexpr int RPI = 64 / CH;   // rows covered by one load instruction
   constexpr int NI = kGroup / RPI;
@@ -159,17 +167,33 @@ __device__ __forceinline__ void encode_record(const __half* __restrict__ ks, con
   // parameters of 8/RPI of its channels, and they meet in LDS.
   constexpr int EK = 8 / RPI;  // key groups whose parameters this lane computes
   float kmn[8], kmx[8];
+  if (sink_mask == 0) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float mn = kx[0][e], mx = kx[0][e];
+    for (int e = 0; e < 8; ++e) {
+      float mn = kx[0][e], mx = kx[0][e];
 #pragma unroll
-    for (int i = 1; i < NI; ++i) {
-      mn = fminf(mn, kx[i][e]);
-      mx = fmaxf(mx, kx[i][e]);
+      for (int i = 1; i < NI; ++i) {
+        mn = fminf(mn, kx[i][e]);
+        mx = fmaxf(mx, kx[i][e]);
+      }
+      column_minmax<CH>(mn, mx);
+      kmn[e] = mn;
+      kmx[e] = mx;
     }
-    column_minmax<CH>(mn, mx);
-    kmn[e] = mn;
-    kmx[e] = mx;
+  } else {  // sinks stay out of the min/max (every group keeps at least 32 - 16 tokens)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const bool skip = (sink_mask >> (r + RPI * i)) & 1u;
+        mn = fminf(mn, skip ? INFINITY : kx[i][e]);
+        mx = fmaxf(mx, skip ? -INFINITY : kx[i][e]);
+      }
+      column_minmax<CH>(mn, mx);
+      kmn[e] = mn;
+      kmx[e] = mx;
+    }
   }
 #pragma unroll
   for (int j = 0; j < EK; ++j) {
@@ -252,7 +276,7 @@ __device__ __forceinline__ void encode_record(const __half* __restrict__ ks, con
     own_lo[j] = g.lo;
     own_inv[j] = g.inv;
     const int t = r + RPI * (q * NQ + j);
-    lds.rec[VP_W + ((t >> 1) * NKG + c8 / 4) * 2 + (t & 1)] = g.packed;
+    lds.rec[VP_W + ((t >> 1) * NKG + c8 / 4) * 2 + (t & 1)] = g.packed | (((sink_mask >> t) & 1u) << 15);
   }
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
@@ -303,7 +327,192 @@ __global__ __launch_bounds__(64) void encode_kernel(uint8_t* __restrict__ buf, L
   const int j = seq.a[b] + jl;
   if (j >= L.max_groups) return;
   const int64_t row0 = ((int64_t(b) * L.Hkv + h) * ld_tok + int64_t(kGroup) * jl) * D;
-  encode_record<D, BK, BV>(K + row0, V + row0, reinterpret_cast<uint32_t*>(buf + L.record(b, h, j)), lds);
+  // sinks of (b, h) inside this record (they are chosen before any record is encoded, and
+  // only the records of that first step can hold them)
+  uint32_t mask = 0;
+  const int32_t* sp = reinterpret_cast<const int32_t*>(buf + L.sink_pos(b, h));
+  for (int k = 0; k < L.NS; ++k) {
+    const int p = sp[k];
+    if ((p >> 5) == j) mask |= 1u << (p & 31);
+  }
+  encode_record<D, BK, BV>(K + row0, V + row0, reinterpret_cast<uint32_t*>(buf + L.record(b, h, j)), lds, mask);
+}
+
+// Squared L2 norm of one fp16 row of D channels: fp32, channel 0 first, each square rounded
+// to fp32 before it is added (this file is built without contraction into fused multiply-adds).
+template <int D>
+__device__ __forceinline__ float row_norm_sq(const __half* __restrict__ row) {
+  float acc = 0.0f;
+#pragma unroll 4
+  for (int c = 0; c < D / 8; ++c) {
+    const uint4 w = reinterpret_cast<const uint4*>(row)[c];
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x0 = __half2float(__ushort_as_half(uint16_t(ww[e] & 0xFFFF)));
+      const float x1 = __half2float(__ushort_as_half(uint16_t(ww[e] >> 16)));
+      acc = acc + x0 * x0;
+      acc = acc + x1 * x1;
+    }
+  }
+  return acc;
+}
+
+// (norm, position) order of the sink choice: the larger norm first, the earlier token on ties.
+__device__ __forceinline__ bool sink_before(float n1, int t1, float n2, int t2) {
+  return n1 > n2 || (n1 == n2 && t1 < t2);
+}
+
+// Sinks of the sequences whose first quantizing step is a prefill or an encode: among
+// tokens 0 .. seq.b[b] - 1 of K[b][h] (0 = the sequence chooses nothing now), which are
+// then also its token positions. Writes sink_pos (ascending) and the sinks' K, V rows.
+template <int D>
+__global__ __launch_bounds__(256) void sink_select_kernel(uint8_t* __restrict__ buf, Layout L,
+                                                          const __half* __restrict__ K,
+                                                          const __half* __restrict__ V, int64_t ld_tok,
+                                                          PerSeq seq) {
+  __shared__ float lnrm[kMaxSinks][256];  // each thread's best candidates, best first
+  __shared__ int lidx[kMaxSinks][256];
+  __shared__ float rn[256];
+  __shared__ int ri[256];
+  __shared__ int win[kMaxSinks];
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int T = seq.b[b], NS = L.NS;
+  if (T <= 0) return;
+  const int tid = threadIdx.x;
+  const int64_t base = (int64_t(b) * L.Hkv + h) * ld_tok * D;
+  int cnt = 0;
+  for (int t = tid; t < T; t += 256) {  // increasing t: an equal norm never displaces an entry
+    const float nrm = row_norm_sq<D>(K + base + int64_t(t) * D);
+    if (cnt < NS || nrm > lnrm[NS - 1][tid]) {
+      int p = cnt < NS ? cnt : NS - 1;
+      while (p > 0 && nrm > lnrm[p - 1][tid]) {
+        lnrm[p][tid] = lnrm[p - 1][tid];
+        lidx[p][tid] = lidx[p - 1][tid];
+        --p;
+      }
+      lnrm[p][tid] = nrm;
+      lidx[p][tid] = t;
+      if (cnt < NS) ++cnt;
+    }
+  }
+  // NS rounds of a block arg-max over the threads' next candidates (norms are >= 0; -1 = none)
+  int head = 0;
+  for (int k = 0; k < NS; ++k) {
+    rn[tid] = head < cnt ? lnrm[head][tid] : -1.0f;
+    ri[tid] = head < cnt ? lidx[head][tid] : 0x7FFFFFFF;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+      if (tid < s && sink_before(rn[tid + s], ri[tid + s], rn[tid], ri[tid])) {
+        rn[tid] = rn[tid + s];
+        ri[tid] = ri[tid + s];
+      }
+      __syncthreads();
+    }
+    const int w = ri[0];
+    if (head < cnt && lidx[head][tid] == w) ++head;
+    if (tid == 0) win[k] = w;
+    __syncthreads();
+  }
+  if (tid == 0) {  // ascending positions
+    for (int i = 1; i < NS; ++i)
+      for (int k = i; k > 0 && win[k - 1] > win[k]; --k) {
+        const int x = win[k];
+        win[k] = win[k - 1];
+        win[k - 1] = x;
+      }
+    int32_t* sp = reinterpret_cast<int32_t*>(buf + L.sink_pos(b, h));
+    for (int k = 0; k < NS; ++k) sp[k] = win[k];
+  }
+  __syncthreads();
+  uint4* sk = reinterpret_cast<uint4*>(buf + L.sink_k(b, h));
+  uint4* sv = reinterpret_cast<uint4*>(buf + L.sink_v(b, h));
+  for (int i = tid; i < NS * (D / 8); i += 256) {
+    const int k = i / (D / 8), c = i % (D / 8);
+    const int64_t row = base + int64_t(win[k]) * D;
+    sk[i] = reinterpret_cast<const uint4*>(K + row)[c];
+    sv[i] = reinterpret_cast<const uint4*>(V + row)[c];
+  }
+}
+
+constexpr int kMaxResidual = 256;  // largest window the host accepts
+
+// masks[m] for a wave-uniform m < R/32, without a dynamically indexed register array
+__device__ __forceinline__ uint32_t pick_mask(const uint32_t (&masks)[kMaxResidual / kGroup], int m) {
+  uint32_t r = masks[0];
+#pragma unroll
+  for (int k = 1; k < kMaxResidual / kGroup; ++k) r = (m == k) ? masks[k] : r;
+  return r;
+}
+
+// A sequence's first flush: choose its sinks among the R window tokens (one wave; R <= 256,
+// so at most 4 candidates per lane), write their positions and fp16 rows, and set the bits
+// of the flushed records' sink masks.
+template <int D>
+__device__ void select_window_sinks(uint8_t* __restrict__ buf, const Layout& L, int b, int h,
+                                    const __half* __restrict__ wk, const __half* __restrict__ wv,
+                                    uint32_t (&masks)[kMaxResidual / kGroup]) {
+  const int lane = threadIdx.x & 63;
+  constexpr int PL = kMaxResidual / 64;
+  float nrm[PL];
+#pragma unroll
+  for (int k = 0; k < PL; ++k) {
+    const int t = lane + 64 * k;
+    nrm[k] = t < L.R ? row_norm_sq<D>(wk + t * D) : -1.0f;  // norms are >= 0; -1 = none
+  }
+  int pos[kMaxSinks];
+#pragma unroll
+  for (int r = 0; r < kMaxSinks; ++r) {
+    pos[r] = 0x7FFFFFFF;
+    if (r >= L.NS) continue;
+    float bn = -1.0f;
+    int bt = 0x7FFFFFFF;
+#pragma unroll
+    for (int k = 0; k < PL; ++k)
+      if (sink_before(nrm[k], lane + 64 * k, bn, bt)) {
+        bn = nrm[k];
+        bt = lane + 64 * k;
+      }
+#pragma unroll
+    for (int msk = 1; msk < 64; msk <<= 1) {
+      const float on = __shfl_xor(bn, msk, 64);
+      const int ot = __shfl_xor(bt, msk, 64);
+      if (sink_before(on, ot, bn, bt)) {
+        bn = on;
+        bt = ot;
+      }
+    }
+    pos[r] = bt;  // the same in every lane
+#pragma unroll
+    for (int k = 0; k < PL; ++k)
+      if (lane + 64 * k == bt) nrm[k] = -2.0f;  // taken
+  }
+  // ascending positions (unused entries hold INT_MAX and stay last)
+#pragma unroll
+  for (int i = 1; i < kMaxSinks; ++i)
+#pragma unroll
+    for (int k = i; k > 0; --k) {
+      const int lo = min(pos[k - 1], pos[k]), hi = max(pos[k - 1], pos[k]);
+      pos[k - 1] = lo;
+      pos[k] = hi;
+    }
+  int32_t* sp = reinterpret_cast<int32_t*>(buf + L.sink_pos(b, h));
+  __half* sk = reinterpret_cast<__half*>(buf + L.sink_k(b, h));
+  __half* sv = reinterpret_cast<__half*>(buf + L.sink_v(b, h));
+  constexpr int HPL = D / 64;
+#pragma unroll
+  for (int r = 0; r < kMaxSinks; ++r) {
+    if (r >= L.NS) break;
+    if (lane == 0) sp[r] = pos[r];
+#pragma unroll
+    for (int e = 0; e < HPL; ++e) {
+      sk[r * D + lane * HPL + e] = wk[pos[r] * D + lane * HPL + e];
+      sv[r * D + lane * HPL + e] = wv[pos[r] * D + lane * HPL + e];
+    }
+#pragma unroll
+    for (int m = 0; m < kMaxResidual / kGroup; ++m)
+      if ((pos[r] >> 5) == m) masks[m] |= 1u << (pos[r] & 31);
+  }
 }
 
 // Append one token per (b, h); a full window is flushed first (R/32 records). seq holds every
@@ -329,10 +538,15 @@ __global__ __launch_bounds__(64) void append_kernel(uint8_t* __restrict__ buf, L
   __half* wv = reinterpret_cast<__half*>(buf + L.wv_off + L.window(b, h));
   if (nr >= L.R) {  // uniform over the workgroup
     const int j0 = nq / kGroup;
+    uint32_t masks[kMaxResidual / kGroup];  // sinks per flushed record
+#pragma unroll
+    for (int m = 0; m < kMaxResidual / kGroup; ++m) masks[m] = 0;
+    if (L.NS > 0 && nq == 0) select_window_sinks<D>(buf, L, b, h, wk, wv, masks);
     for (int m = 0; m < L.R / kGroup; ++m) {
       if (j0 + m < L.max_groups)
         encode_record<D, BK, BV>(wk + m * kGroup * D, wv + m * kGroup * D,
-                                 reinterpret_cast<uint32_t*>(buf + L.record(b, h, j0 + m)), lds);
+                                 reinterpret_cast<uint32_t*>(buf + L.record(b, h, j0 + m)), lds,
+                                 pick_mask(masks, m));
     }
     nq += L.R;
     nr = 0;
@@ -480,6 +694,21 @@ hipError_t launch_window_fill(uint8_t* buf, const Layout& L, const void* K, cons
   else if (L.D == 64)
     hipLaunchKernelGGL(window_fill_kernel<64>, grid, dim3(64), 0, s, buf, L, static_cast<const __half*>(K),
                        static_cast<const __half*>(V), ld_tok, seq);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_sink_select(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,
+                              const PerSeq& seq, hipStream_t s) {
+  dim3 grid(L.Hkv, L.B);
+  const __half* k = static_cast<const __half*>(K);
+  const __half* v = static_cast<const __half*>(V);
+  if (L.NS < 1 || L.NS > kMaxSinks) return hipErrorInvalidValue;
+  if (L.D == 128)
+    hipLaunchKernelGGL(sink_select_kernel<128>, grid, dim3(256), 0, s, buf, L, k, v, ld_tok, seq);
+  else if (L.D == 64)
+    hipLaunchKernelGGL(sink_select_kernel<64>, grid, dim3(256), 0, s, buf, L, k, v, ld_tok, seq);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

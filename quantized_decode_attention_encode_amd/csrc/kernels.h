@@ -34,6 +34,10 @@ hipError_t launch_window_fill(uint8_t* buf, const Layout& L, const void* K, cons
 hipError_t launch_encode_block(const void* X, int n_tok, int D, int bits, int group, int per_channel, void* codes,
                                void* scales, void* zeros, hipStream_t s);
 hipError_t launch_lengths_fill(uint8_t* buf, const Layout& L, const PerSeq& seq, hipStream_t s);
+// Sinks of the sequences with seq.b[b] > 0: chosen among tokens 0 .. seq.b[b]-1 of K[b][h]
+// (the sequence's first quantized tokens), positions and fp16 K, V rows written (L.NS >= 1).
+hipError_t launch_sink_select(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,
+                              const PerSeq& seq, hipStream_t s);
 
 // Decode attention: split-K kernel whose last split per (b, h_kv) merges the partials into
 // `out`. start/stop, when not null, are stamped by the kernel's own dispatch (its execution
@@ -43,5 +47,9 @@ hipError_t launch_lengths_fill(uint8_t* buf, const Layout& L, const PerSeq& seq,
 hipError_t launch_decode(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q, float* ws,
                          void* out, const void* k_tok, const void* v_tok, hipStream_t s,
                          hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
+// The same for caches with sink tokens (L.NS > 0); launch_decode forwards to it.
+hipError_t launch_decode_sink(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q, float* ws,
+                              void* out, const void* k_tok, const void* v_tok, hipStream_t s, hipEvent_t start,
+                              hipEvent_t stop);
 
 }  // namespace kvq

@@ -86,20 +86,26 @@ kvq_status check_config(const kvq_config* c) {
   if (c->max_tokens < kvq::kGroup || c->max_tokens % kvq::kGroup)
     return fail(KVQ_E_INVALID, "max_tokens must be a positive multiple of 32, got %d", c->max_tokens);
   if (c->max_tokens > (1 << 26)) return fail(KVQ_E_INVALID, "max_tokens above 2^26");
+  if (c->n_sink < 0 || c->n_sink > kvq::kMaxSinks)
+    return fail(KVQ_E_INVALID, "n_sink must be in [0, %d], got %d", kvq::kMaxSinks, c->n_sink);
   return ok();
 }
 
 Layout make_layout(const kvq_config* c) {
   Layout L;
-  L.init(c->batch, c->n_kv_heads, c->head_dim, c->key_bits, c->value_bits, c->residual, c->max_tokens);
+  L.init(c->batch, c->n_kv_heads, c->head_dim, c->key_bits, c->value_bits, c->residual, c->max_tokens, c->n_sink);
   return L;
 }
 
-int units_of(int nq, int nr) { return nq / kvq::kGroup + (nr + kvq::kGroup - 1) / kvq::kGroup; }
+// Decode units of a sequence: its records, its window in 32-token pieces, and its sinks (one
+// unit, present once tokens are quantized).
+int units_of(int nq, int nr, int n_sink) {
+  return nq / kvq::kGroup + (nr + kvq::kGroup - 1) / kvq::kGroup + (n_sink > 0 && nq > 0 ? 1 : 0);
+}
 
 // Largest split count the automatic choice can produce.
 int max_auto_splits(const kvq_config* c) {
-  const int units_cap = c->max_tokens / kvq::kGroup + c->residual / kvq::kGroup;
+  const int units_cap = c->max_tokens / kvq::kGroup + c->residual / kvq::kGroup + (c->n_sink > 0 ? 1 : 0);
   return (units_cap + 3) / 4;
 }
 
@@ -176,7 +182,7 @@ kvq_status decode_enqueue(kvq_cache* c, const void* q, void* out, int32_t out_fp
   int64_t total_units = 0;
   for (int b = 0; b < cfg.batch; ++b) {
     if (c->nq[b] + c->nr[b] + add == 0) return fail(KVQ_E_INVALID, "sequence %d is empty", b);
-    const int u = units_of(c->nq[b], c->nr[b] + add);
+    const int u = units_of(c->nq[b], c->nr[b] + add, cfg.n_sink);
     max_units = std::max(max_units, u);
     total_units += int64_t(u) * cfg.n_kv_heads;
   }
@@ -275,6 +281,9 @@ kvq_status kvq_layout(const kvq_config* cfg, kvq_layout_info* out) {
   out->window_v_offset = L.wv_off;
   out->total_bytes = L.total;
   out->sync_offset = L.sync_off;
+  out->sink_pos_offset = L.sp_off;
+  out->sink_k_offset = L.sk_off;
+  out->sink_v_offset = L.sv_off;
   return ok();
 }
 
@@ -362,16 +371,25 @@ kvq_status kvq_encode(kvq_cache* c, const void* K, const void* V, int64_t ld_tok
   hipStream_t s = static_cast<hipStream_t>(stream);
   kvq_status st = ensure_ready(c, s);
   if (st != KVQ_OK) return st;
-  PerSeq enc, len;
+  PerSeq enc, len, sel;
   memset(&enc, 0, sizeof enc);
   memset(&len, 0, sizeof len);
+  memset(&sel, 0, sizeof sel);
+  bool select = false;
   for (int b = 0; b < c->cfg.batch; ++b) {
     enc.a[b] = c->nq[b] / kvq::kGroup;
     enc.b[b] = n_tok[b] / kvq::kGroup;
     len.a[b] = c->nq[b] + n_tok[b];
     len.b[b] = c->nr[b];
+    sel.b[b] = (c->cfg.n_sink > 0 && c->nq[b] == 0) ? n_tok[b] : 0;  // first quantized tokens
+    select = select || sel.b[b] > 0;
   }
-  hipError_t e = kvq::launch_encode(c->buf, c->L, K, V, ld_tok, enc, max_rec, s);
+  hipError_t e;
+  if (select) {
+    e = kvq::launch_sink_select(c->buf, c->L, K, V, ld_tok, sel, s);
+    if (e != hipSuccess) return hip_fail(e, "sink selection launch");
+  }
+  e = kvq::launch_encode(c->buf, c->L, K, V, ld_tok, enc, max_rec, s);
   if (e != hipSuccess) return hip_fail(e, "encode launch");
   e = kvq::launch_lengths_fill(c->buf, c->L, len, s);
   if (e != hipSuccess) return hip_fail(e, "lengths launch");
@@ -404,9 +422,10 @@ kvq_status kvq_prefill(kvq_cache* c, const void* K, const void* V, int64_t ld_to
   if (!seq_len) return fail(KVQ_E_INVALID, "seq_len is NULL");
   const int R = c->cfg.residual;
   int max_rec = 0, max_S = 0;
-  PerSeq enc, win;
+  PerSeq enc, win, sel;
   memset(&enc, 0, sizeof enc);
   memset(&win, 0, sizeof win);
+  memset(&sel, 0, sizeof sel);
   for (int b = 0; b < c->cfg.batch; ++b) {
     const int S = seq_len[b];
     if (S < 0) return fail(KVQ_E_INVALID, "seq_len[%d] = %d is negative", b, S);
@@ -418,6 +437,7 @@ kvq_status kvq_prefill(kvq_cache* c, const void* K, const void* V, int64_t ld_to
     enc.b[b] = nq / kvq::kGroup;
     win.a[b] = nq;
     win.b[b] = nr;
+    sel.b[b] = c->cfg.n_sink > 0 ? nq : 0;  // sinks among the quantized part
     max_rec = std::max(max_rec, nq / kvq::kGroup);
     max_S = std::max(max_S, S);
   }
@@ -429,7 +449,12 @@ kvq_status kvq_prefill(kvq_cache* c, const void* K, const void* V, int64_t ld_to
   kvq_status st = check_device();
   if (st != KVQ_OK) return st;
   if (max_rec) {
-    hipError_t e = kvq::launch_encode(c->buf, c->L, K, V, ld_tok, enc, max_rec, s);
+    hipError_t e;
+    if (c->cfg.n_sink > 0) {
+      e = kvq::launch_sink_select(c->buf, c->L, K, V, ld_tok, sel, s);
+      if (e != hipSuccess) return hip_fail(e, "sink selection launch");
+    }
+    e = kvq::launch_encode(c->buf, c->L, K, V, ld_tok, enc, max_rec, s);
     if (e != hipSuccess) return hip_fail(e, "encode launch");
   }
   hipError_t e = kvq::launch_window_fill(c->buf, c->L, K, V, ld_tok, win, s);  // also writes every length

@@ -6,7 +6,11 @@
 //   records  [B][H_kv][max_tokens/32][record]   one record per group of 32 quantized tokens
 //   window_k fp16  [B][H_kv][R][D]              the newest tokens, unquantized
 //   window_v fp16  [B][H_kv][R][D]
-// Every region but sync starts on a 256-byte boundary (sync follows lengths directly).
+//   sink_pos int32 [B][H_kv][NS]                sink token positions, ascending (NS = n_sink)
+//   sink_k   fp16  [B][H_kv][NS][D]             the sinks' key and value rows, unquantized
+//   sink_v   fp16  [B][H_kv][NS][D]
+// Every region but sync starts on a 256-byte boundary (sync follows lengths directly). With
+// NS = 0 the three sink regions are empty and the buffer is the plain KIVI cache.
 //
 // A record holds everything decode needs for 32 tokens, so one group streams from one
 // contiguous 4*D*(bk+bv+2)-byte block (3 KiB at D=128, 2/2 bits):
@@ -22,7 +26,8 @@
 //   key params   D dwords      [d]: (scale fp16 in bits 0-15, zero fp16 in bits 16-31)
 //                of the key group (32 tokens) of channel d.
 //   value params D dwords      [t/2][k : D/32][t%2]: (scale, zero) of value group k
-//                (channels 32k..32k+31) of token t.
+//                (channels 32k..32k+31) of token t. The scale of a sink token carries the
+//                sign bit: decode skips that slot (the sink's fp16 rows stand in for it).
 #pragma once
 #include <stdint.h>
 
@@ -36,6 +41,7 @@ namespace kvq {
 
 constexpr int kGroup = 32;     // tokens per key group == channels per value group
 constexpr int kMaxBatch = 256;
+constexpr int kMaxSinks = 16;  // sink tokens per (sequence, KV head)
 
 KVQ_HD constexpr uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
@@ -53,11 +59,11 @@ KVQ_HD constexpr uint64_t rec_off_vparams(int D, int bk, int bv) {
 
 // Offsets of the regions of one cache buffer.
 struct Layout {
-  int B, Hkv, D, bk, bv, R, max_groups;
-  uint64_t len_off, sync_off, rec_off, rec_bytes, wk_off, wv_off, total;
+  int B, Hkv, D, bk, bv, R, max_groups, NS;
+  uint64_t len_off, sync_off, rec_off, rec_bytes, wk_off, wv_off, sp_off, sk_off, sv_off, total;
 
-  KVQ_HD void init(int B_, int Hkv_, int D_, int bk_, int bv_, int R_, int max_tokens) {
-    B = B_; Hkv = Hkv_; D = D_; bk = bk_; bv = bv_; R = R_;
+  KVQ_HD void init(int B_, int Hkv_, int D_, int bk_, int bv_, int R_, int max_tokens, int NS_) {
+    B = B_; Hkv = Hkv_; D = D_; bk = bk_; bv = bv_; R = R_; NS = NS_;
     max_groups = max_tokens / kGroup;
     rec_bytes = record_bytes(D, bk, bv);
     len_off = 0;
@@ -66,7 +72,11 @@ struct Layout {
     wk_off = align256(rec_off + uint64_t(B) * Hkv * max_groups * rec_bytes);
     uint64_t wbytes = uint64_t(B) * Hkv * R * D * 2;
     wv_off = align256(wk_off + wbytes);
-    total = align256(wv_off + wbytes);
+    sp_off = align256(wv_off + wbytes);
+    sk_off = align256(sp_off + uint64_t(B) * Hkv * NS * sizeof(int32_t));
+    const uint64_t sbytes = uint64_t(B) * Hkv * NS * D * 2;
+    sv_off = align256(sk_off + sbytes);
+    total = align256(sv_off + sbytes);
   }
   // record j of (b, h)
   KVQ_HD uint64_t record(int b, int h, int j) const {
@@ -76,6 +86,10 @@ struct Layout {
   KVQ_HD uint64_t window(int b, int h) const { return (uint64_t(b) * Hkv + h) * R * D * 2; }
   KVQ_HD uint64_t lengths(int b, int h) const { return len_off + (uint64_t(b) * Hkv + h) * 8; }
   KVQ_HD uint64_t sync(int b, int h) const { return sync_off + (uint64_t(b) * Hkv + h) * 4; }
+  // sinks of (b, h): positions (int32), key rows and value rows (fp16 [NS][D])
+  KVQ_HD uint64_t sink_pos(int b, int h) const { return sp_off + (uint64_t(b) * Hkv + h) * NS * 4; }
+  KVQ_HD uint64_t sink_k(int b, int h) const { return sk_off + (uint64_t(b) * Hkv + h) * NS * D * 2; }
+  KVQ_HD uint64_t sink_v(int b, int h) const { return sv_off + (uint64_t(b) * Hkv + h) * NS * D * 2; }
 };
 
 }  // namespace kvq

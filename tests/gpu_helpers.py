@@ -24,10 +24,10 @@ def say(*a):
 
 def cfg_dict(c):
     return {"B": c.batch, "Hkv": c.n_kv_heads, "D": c.head_dim, "bk": c.key_bits, "bv": c.value_bits,
-            "R": c.residual, "max_tokens": c.max_tokens}
+            "R": c.residual, "max_tokens": c.max_tokens, "NS": c.n_sink}
 
 
-def oracle_prefill(draw, R, pairs=None):
+def oracle_prefill(draw, R, pairs=None, n_sink=0):
     """KiviSequence per (b, h) for the drawn K/V (optionally only the given (b, h) pairs)."""
     wl = draw.wl
     seqs = {}
@@ -35,7 +35,7 @@ def oracle_prefill(draw, R, pairs=None):
         for h in range(wl.n_kv_heads):
             if pairs is not None and (b, h) not in pairs:
                 continue
-            s = kivi.KiviSequence(wl.head_dim, wl.key_bits, wl.value_bits, 32, R)
+            s = kivi.KiviSequence(wl.head_dim, wl.key_bits, wl.value_bits, 32, R, n_sink)
             s.prefill(draw.K[b][h], draw.V[b][h])
             seqs[(b, h)] = s
     return seqs
@@ -52,7 +52,8 @@ def assert_state_equal(buf, c, seqs, what=""):
         got = kvq_unpack.unpack_sequence(buf, cd, b, h)
         assert (got["n_q"], got["n_r"]) == (s.n_q, s.n_r), f"{what} lengths of {(b, h)}"
         for name, ref in (("kc", s.kc), ("vc", s.vc), ("ks", s.ks), ("kz", s.kz), ("vs", s.vs), ("vz", s.vz),
-                          ("wk", s.wk), ("wv", s.wv)):
+                          ("wk", s.wk), ("wv", s.wv), ("sink_pos", s.sink_pos), ("sink_k", s.sink_k),
+                          ("sink_v", s.sink_v)):
             g = got[name]
             assert g.shape == ref.shape, f"{what} {name} shape {g.shape} vs {ref.shape} at {(b, h)}"
             if not np.array_equal(g.view(np.uint8), ref.view(np.uint8)):

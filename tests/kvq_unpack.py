@@ -3,8 +3,9 @@
 Written from the layout description (records of 32 tokens; key codes as
 [P=t/2][quarter][t%2][words] with channel c' of the quarter at bit c'*bk, value codes as
 [channel][words] with token t at bit t*bv, key params [channel], value params
-[t/2][value group][t%2], fp16 (scale, zero) pairs with the scale in the low half). It shares
-no code with the HIP library; parity tests compare its output with the CPU oracle.
+[t/2][value group][t%2], fp16 (scale, zero) pairs with the scale in the low half; then the
+sink regions: positions int32 [B][H_kv][NS], key and value rows fp16 [B][H_kv][NS][D]). It
+shares no code with the HIP library; parity tests compare its output with the CPU oracle.
 """
 from __future__ import annotations
 
@@ -15,7 +16,7 @@ def align256(x: int) -> int:
     return (x + 255) // 256 * 256
 
 
-def offsets(B, Hkv, D, bk, bv, R, max_tokens):
+def offsets(B, Hkv, D, bk, bv, R, max_tokens, NS=0):
     max_groups = max_tokens // 32
     rec = 4 * D * (bk + bv + 2)
     o = {"lengths": 0, "sync": B * Hkv * 2 * 4}
@@ -28,8 +29,12 @@ def offsets(B, Hkv, D, bk, bv, R, max_tokens):
     o["window_k"] = align256(o["records"] + B * Hkv * max_groups * rec)
     wbytes = B * Hkv * R * D * 2
     o["window_v"] = align256(o["window_k"] + wbytes)
-    o["total"] = align256(o["window_v"] + wbytes)
+    o["sink_pos"] = align256(o["window_v"] + wbytes)
+    o["sink_k"] = align256(o["sink_pos"] + B * Hkv * NS * 4)
+    o["sink_v"] = align256(o["sink_k"] + B * Hkv * NS * D * 2)
+    o["total"] = align256(o["sink_v"] + B * Hkv * NS * D * 2)
     o["max_groups"] = max_groups
+    o["NS"] = NS
     return o
 
 
@@ -75,10 +80,12 @@ def unpack_sequence(buf: np.ndarray, cfg: dict, b: int, h: int, n_q: int | None 
     """Logical arrays of (b, h): codes/params of the quantized region plus the window.
 
     ``buf`` is the whole cache buffer as uint8 on the host; cfg has B, Hkv, D, bk, bv, R,
-    max_tokens. Lengths default to the ones stored in the buffer.
+    max_tokens (and NS, default 0). Lengths default to the ones stored in the buffer. The
+    sinks (positions, fp16 rows) are returned when the sequence has quantized tokens.
     """
     B, Hkv, D, bk, bv, R = (cfg[k] for k in ("B", "Hkv", "D", "bk", "bv", "R"))
-    o = offsets(B, Hkv, D, bk, bv, R, cfg["max_tokens"])
+    NS = cfg.get("NS", 0)
+    o = offsets(B, Hkv, D, bk, bv, R, cfg["max_tokens"], NS)
     L = lengths(buf, B, Hkv)
     n_q = int(L[b, h, 0]) if n_q is None else n_q
     n_r = int(L[b, h, 1]) if n_r is None else n_r
@@ -91,5 +98,10 @@ def unpack_sequence(buf: np.ndarray, cfg: dict, b: int, h: int, n_q: int | None 
     wv = buf[o["window_v"] + w0:o["window_v"] + w0 + R * D * 2].view(np.float16).reshape(R, D)[:n_r]
     cat["wk"] = wk.copy()
     cat["wv"] = wv.copy()
+    ns = NS if n_q > 0 else 0
+    i = b * Hkv + h
+    cat["sink_pos"] = buf[o["sink_pos"] + i * NS * 4:o["sink_pos"] + (i * NS + ns) * 4].view("<i4").astype(np.int64)
+    cat["sink_k"] = buf[o["sink_k"] + i * NS * D * 2:o["sink_k"] + (i * NS + ns) * D * 2].view(np.float16).reshape(ns, D).copy()
+    cat["sink_v"] = buf[o["sink_v"] + i * NS * D * 2:o["sink_v"] + (i * NS + ns) * D * 2].view(np.float16).reshape(ns, D).copy()
     cat["n_q"], cat["n_r"] = n_q, n_r
     return cat

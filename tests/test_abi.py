@@ -37,7 +37,7 @@ def declared_functions():
 
 def cfg(**kw):
     base = dict(batch=2, n_kv_heads=4, n_q_heads=8, head_dim=128, key_bits=2, value_bits=4, group=32,
-                residual=32, max_tokens=1024)
+                residual=32, max_tokens=1024, n_sink=0)
     base.update(kw)
     return Config(*(base[f] for f, _ in Config._fields_))
 
@@ -68,6 +68,7 @@ def test_probe_without_gpu_reports_absence():
     ("key_bits", 3, KVQ_E_UNSUPPORTED), ("value_bits", 1, KVQ_E_UNSUPPORTED), ("group", 64, KVQ_E_UNSUPPORTED),
     ("residual", 48, KVQ_E_INVALID), ("residual", 0, KVQ_E_INVALID), ("residual", 288, KVQ_E_INVALID),
     ("max_tokens", 1000, KVQ_E_INVALID), ("max_tokens", 0, KVQ_E_INVALID),
+    ("n_sink", -1, KVQ_E_INVALID), ("n_sink", 17, KVQ_E_INVALID),
 ])
 def test_config_validation(field, value, status):
     c = cfg(**{field: value})
@@ -77,13 +78,15 @@ def test_config_validation(field, value, status):
     assert lib.kvq_workspace_bytes(ctypes.byref(c), 0) == 0
 
 
-@pytest.mark.parametrize("D,bk,bv,R,B,H", [(128, 2, 2, 32, 1, 32), (64, 2, 2, 32, 1, 8), (128, 2, 4, 32, 16, 8),
-                                           (128, 8, 4, 64, 3, 2), (64, 4, 8, 128, 5, 3)])
-def test_layout_matches_independent_formula(D, bk, bv, R, B, H):
-    c = cfg(batch=B, n_kv_heads=H, n_q_heads=H, head_dim=D, key_bits=bk, value_bits=bv, residual=R, max_tokens=2048)
+@pytest.mark.parametrize("D,bk,bv,R,B,H,NS", [(128, 2, 2, 32, 1, 32, 0), (64, 2, 2, 32, 1, 8, 0),
+                                              (128, 2, 4, 32, 16, 8, 0), (128, 8, 4, 64, 3, 2, 5),
+                                              (64, 4, 8, 128, 5, 3, 16), (128, 2, 2, 32, 2, 4, 1)])
+def test_layout_matches_independent_formula(D, bk, bv, R, B, H, NS):
+    c = cfg(batch=B, n_kv_heads=H, n_q_heads=H, head_dim=D, key_bits=bk, value_bits=bv, residual=R, max_tokens=2048,
+            n_sink=NS)
     info = LayoutInfo()
     assert lib.kvq_layout(ctypes.byref(c), ctypes.byref(info)) == KVQ_OK
-    o = kvq_unpack.offsets(B, H, D, bk, bv, R, 2048)
+    o = kvq_unpack.offsets(B, H, D, bk, bv, R, 2048, NS)
     assert info.lengths_offset == o["lengths"] and info.records_offset == o["records"]
     assert info.record_bytes == o["record_bytes"] == 4 * D * (bk + bv + 2)
     assert (info.rec_key_codes, info.rec_value_codes, info.rec_key_params, info.rec_value_params) == (
@@ -91,8 +94,12 @@ def test_layout_matches_independent_formula(D, bk, bv, R, B, H):
     assert info.window_k_offset == o["window_k"] and info.window_v_offset == o["window_v"]
     assert info.total_bytes == o["total"] == lib.kvq_cache_bytes(ctypes.byref(c))
     assert info.sync_offset == o["sync"]
-    for off in (info.records_offset, info.window_k_offset, info.window_v_offset, info.total_bytes):
+    assert (info.sink_pos_offset, info.sink_k_offset, info.sink_v_offset) == (o["sink_pos"], o["sink_k"], o["sink_v"])
+    for off in (info.records_offset, info.window_k_offset, info.window_v_offset, info.sink_pos_offset,
+                info.sink_k_offset, info.sink_v_offset, info.total_bytes):
         assert off % 256 == 0
+    if NS == 0:  # no sink regions: the plain KIVI buffer
+        assert info.sink_pos_offset == info.sink_k_offset == info.sink_v_offset == info.total_bytes
 
 
 def test_record_is_three_kib_at_the_headline_shape():
