@@ -18,7 +18,11 @@ against the 8 TB/s peak (algorithmic bytes / kernel time from HIP events that th
 kernel's own dispatch stamps, on its stream), the prefill-encode rate, and the CPU oracle
 timed on a bounded sample of the same workload.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long] [--no-cpu-baseline]
+With --n-sink N the caches keep N sink tokens per (sequence, KV head) in fp16 (KIVI-Sink,
+"Changelog" v0.9.0): the prefill then also chooses them, and every decode attends them as one
+more fp16 unit and skips their quantized slots.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long] [--n-sink 0] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -35,30 +39,32 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 
-# HBM bytes per decode launch on the long workload from two rocprofv3 --pmc runs
+# HBM bytes per decode launch on the long workload (no sinks) from two rocprofv3 --pmc runs
 # (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, factors from a 1 GiB device copy; see
 # profiles/kvq_long_s64k_counters.md), valid only for the decode kernel and split-plan
 # sources they were taken on (their hash).
-MEASURED_TRAFFIC = {"workload": "long", "src_sha256_16": "168ca50dfe41c89c", "bytes": 202605908}
+MEASURED_TRAFFIC = {"workload": "long", "src_sha256_16": "0d0561a3d36707f9", "bytes": 202621063}
 
 
-def algorithmic_decode_bytes(wl, n_q, n_r):
+def algorithmic_decode_bytes(wl, n_q, n_r, n_sink=0):
     """Bytes one decode launch must move: every record once per KV head (GQA query heads share
-    it), the fp16 window, q and out. n_q, n_r: per-sequence lengths."""
+    it), the fp16 window and sink rows, q and out. n_q, n_r: per-sequence lengths."""
     D = wl.head_dim
     rec = 4 * D * (wl.key_bits + wl.value_bits + 2)  # per 32 quantized tokens
-    kv = sum((nq // 32) * rec + nr * D * 2 * 2 for nq, nr in zip(n_q, n_r)) * wl.n_kv_heads
+    kv = sum((nq // 32) * rec + (nr + (n_sink if nq else 0)) * D * 2 * 2
+             for nq, nr in zip(n_q, n_r)) * wl.n_kv_heads
     return kv + 2 * wl.batch * wl.n_q_heads * D * 2
 
 
-def algorithmic_encode_bytes(wl, n_q_tokens):
-    """Prefill encode: read fp16 K and V once, write codes and parameters once."""
+def algorithmic_encode_bytes(wl, n_q_tokens, n_sink=0):
+    """Prefill encode: read fp16 K and V once, write codes and parameters once (and the sink rows)."""
     D = wl.head_dim
     rec = 4 * D * (wl.key_bits + wl.value_bits + 2)
-    return sum(nq * D * 2 * 2 + (nq // 32) * rec for nq in n_q_tokens) * wl.n_kv_heads
+    return sum(nq * D * 2 * 2 + (nq // 32) * rec + (n_sink * D * 2 * 2 if nq else 0)
+               for nq in n_q_tokens) * wl.n_kv_heads
 
 
-def cpu_baseline(wl, draw, budget_s=12.0):
+def cpu_baseline(wl, draw, budget_s=12.0, n_sink=0):
     """The oracle's decode (reconstruct K_hat/V_hat, fp64 softmax attention) on a sample of the
     KV heads of sequence 0, scaled by tokens to the whole step (every sequence, head and layer)."""
     import numpy as np  # noqa: F401
@@ -78,7 +84,7 @@ def cpu_baseline(wl, draw, budget_s=12.0):
     G = wl.n_q_heads // H
     S0 = draw.seq_lens[0]
     for h in range(H):
-        s = kivi.KiviSequence(wl.head_dim, wl.key_bits, wl.value_bits, 32, wl.residual)
+        s = kivi.KiviSequence(wl.head_dim, wl.key_bits, wl.value_bits, 32, wl.residual, n_sink)
         t0 = time.perf_counter()
         s.prefill(draw.K[0][h], draw.V[0][h])
         t1 = time.perf_counter()
@@ -124,6 +130,7 @@ def main():
     ap.add_argument("--n-split", type=int, default=0, help="splits per sequence (0 = the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--settle-s", type=float, default=0.5, help="seconds of attend-only calls before the warmup")
+    ap.add_argument("--n-sink", type=int, default=0, help="sink tokens per (sequence, KV head), KIVI-Sink (0 = KIVI)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this path shards by "
@@ -155,7 +162,7 @@ def main():
     per_cache = n_steps_total if multi else (n_steps_total + n_caches - 1) // n_caches
     cap = (max(lens) + per_cache + 64 + 31) // 32 * 32
     cfg = make_config(wl.batch, wl.n_kv_heads, wl.n_q_heads, wl.head_dim, wl.key_bits, wl.value_bits, 32,
-                      wl.residual, cap)
+                      wl.residual, cap, n_sink=args.n_sink)
     Kt, Vt = torch.from_numpy(K).to(dev), torch.from_numpy(V).to(dev)
     del K, V
     stream = torch.cuda.current_stream()
@@ -196,7 +203,7 @@ def main():
     enc_t = statistics.median(enc_ms) / 1e3
     n_q0 = [s - ((s - 1) % wl.residual + 1) for s in lens]
     enc_tokens_per_s = sum(lens) / enc_t
-    enc_gbs = algorithmic_encode_bytes(wl, n_q0) / enc_t / 1e9
+    enc_gbs = algorithmic_encode_bytes(wl, n_q0, args.n_sink) / enc_t / 1e9
 
     # ---- device-resident inputs of the decode steps
     toks = [draw.next_token() for _ in range(n_steps_total)]
@@ -271,7 +278,7 @@ def main():
                     nr[b] = 0
                 nr[b] += 1
             if first <= i < last:
-                bytes_per_launch.append(algorithmic_decode_bytes(wl, nq, nr))
+                bytes_per_launch.append(algorithmic_decode_bytes(wl, nq, nr, args.n_sink))
     for r, c in enumerate(caches):
         assert tuple(map(list, lens_now[r])) == tuple(map(list, c.lengths())), "length replay disagrees"
     step_ms = t_ev0.elapsed_time(t_ev1) / args.steps
@@ -301,11 +308,11 @@ def main():
 
     traffic = None
     csrc = os.path.join(ROOT, "quantized_decode_attention_encode_amd", "csrc")
-    if args.workload == MEASURED_TRAFFIC["workload"] and args.n_split == 0:
+    if args.workload == MEASURED_TRAFFIC["workload"] and args.n_split == 0 and args.n_sink == 0:
         import hashlib
 
         h = hashlib.sha256()
-        for name in ("decode.hip", "kvq.cpp"):  # the kernel and the host's split plan
+        for name in ("decode_kernel.h", "decode.hip", "kvq.cpp"):  # the kernel and the host's split plan
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(f.read())
         if h.hexdigest()[:16] == MEASURED_TRAFFIC["src_sha256_16"]:
@@ -331,6 +338,7 @@ def main():
               "flushes a full window, the append kernel runs first)",
             "caches": f"{n_caches} layer caches" if multi else f"{n_caches} replicas of one cache, one per step",
             "codes": f"{wl.key_bits}-bit keys / {wl.value_bits}-bit values, fp16 (scale, zero), fp32 softmax",
+            "sinks": args.n_sink,
         },
         "roofline": {
             "bound": "hbm",
@@ -358,7 +366,7 @@ def main():
         result["encode_all_layers_us"] = round(enc_t * 1e6 * wl.layers, 1)
         result["decode_launches_per_step"] = wl.layers
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, draw)
+        result["cpu_baseline"] = cpu_baseline(wl, draw, n_sink=args.n_sink)
     print(json.dumps(result), flush=True)
 
 
