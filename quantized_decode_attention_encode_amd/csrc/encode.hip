@@ -364,54 +364,104 @@ __device__ __forceinline__ bool sink_before(float n1, int t1, float n2, int t2) 
 }
 
 // Sinks of the sequences whose first quantizing step is a prefill or an encode: among
-// tokens 0 .. seq.b[b] - 1 of K[b][h] (0 = the sequence chooses nothing now), which are
-// then also its token positions. Writes sink_pos (ascending) and the sinks' K, V rows.
+// tokens 0 .. seq.b[b] - 1 of K[b][h] (0 = the sequence chooses nothing now), which are then
+// also its token positions. Two kernels: every workgroup takes a chunk of 2048 tokens and
+// writes its best NS (norm, position) pairs; a second pass per (b, h) picks the best NS of
+// those, writes sink_pos (ascending) and copies the sinks' K, V rows. The chunk lists are
+// staged in the sequence's record area, which the encode that follows overwrites (the
+// first step quantizes every token the lists come from: 8 * NS bytes per chunk of 64
+// records).
+constexpr int kSelTPT = 8;                // tokens per thread
+constexpr int kSelChunk = 256 * kSelTPT;  // tokens per workgroup
+
+// The (norm, position) pair that comes first among the 256 threads' candidates, in every thread.
+__device__ __forceinline__ void block_best(float& n, int& t, float* sn, int* st) {
+#pragma unroll
+  for (int msk = 1; msk < 64; msk <<= 1) {
+    const float on = __shfl_xor(n, msk, 64);
+    const int ot = __shfl_xor(t, msk, 64);
+    if (sink_before(on, ot, n, t)) {
+      n = on;
+      t = ot;
+    }
+  }
+  const int w = threadIdx.x >> 6;
+  __syncthreads();  // the previous round's readers are done
+  if ((threadIdx.x & 63) == 0) {
+    sn[w] = n;
+    st[w] = t;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (sink_before(sn[k], st[k], n, t)) {
+      n = sn[k];
+      t = st[k];
+    }
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void sink_select_kernel(uint8_t* __restrict__ buf, Layout L,
-                                                          const __half* __restrict__ K,
-                                                          const __half* __restrict__ V, int64_t ld_tok,
-                                                          PerSeq seq) {
-  __shared__ float lnrm[kMaxSinks][256];  // each thread's best candidates, best first
-  __shared__ int lidx[kMaxSinks][256];
-  __shared__ float rn[256];
-  __shared__ int ri[256];
+__global__ __launch_bounds__(256) void sink_chunk_kernel(uint8_t* __restrict__ buf, Layout L,
+                                                         const __half* __restrict__ K, int64_t ld_tok, PerSeq seq) {
+  __shared__ float sn[4];
+  __shared__ int st[4];
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int T = seq.b[b], t0 = c * kSelChunk;
+  if (t0 >= T) return;
+  const int tid = threadIdx.x;
+  const int64_t base = (int64_t(b) * L.Hkv + h) * ld_tok * D;
+  float nrm[kSelTPT];  // norms are >= 0; -1 = no token, -2 = already chosen
+#pragma unroll
+  for (int k = 0; k < kSelTPT; ++k) {
+    const int t = t0 + tid + 256 * k;
+    nrm[k] = t < T ? row_norm_sq<D>(K + base + int64_t(t) * D) : -1.0f;
+  }
+  float2* lists = reinterpret_cast<float2*>(buf + L.record(b, h, 0)) + int64_t(c) * L.NS;
+  for (int r = 0; r < L.NS; ++r) {
+    float n = -1.0f;
+    int t = 0x7FFFFFFF;
+#pragma unroll
+    for (int k = 0; k < kSelTPT; ++k)
+      if (nrm[k] >= 0.0f && sink_before(nrm[k], t0 + tid + 256 * k, n, t)) {
+        n = nrm[k];
+        t = t0 + tid + 256 * k;
+      }
+    block_best(n, t, sn, st);
+#pragma unroll
+    for (int k = 0; k < kSelTPT; ++k)
+      if (t0 + tid + 256 * k == t) nrm[k] = -2.0f;
+    if (tid == 0) lists[r] = make_float2(n, __int_as_float(t));
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void sink_merge_kernel(uint8_t* __restrict__ buf, Layout L,
+                                                         const __half* __restrict__ K,
+                                                         const __half* __restrict__ V, int64_t ld_tok, PerSeq seq) {
+  __shared__ float sn[4];
+  __shared__ int st[4];
   __shared__ int win[kMaxSinks];
   const int h = blockIdx.x, b = blockIdx.y;
   const int T = seq.b[b], NS = L.NS;
   if (T <= 0) return;
   const int tid = threadIdx.x;
-  const int64_t base = (int64_t(b) * L.Hkv + h) * ld_tok * D;
-  int cnt = 0;
-  for (int t = tid; t < T; t += 256) {  // increasing t: an equal norm never displaces an entry
-    const float nrm = row_norm_sq<D>(K + base + int64_t(t) * D);
-    if (cnt < NS || nrm > lnrm[NS - 1][tid]) {
-      int p = cnt < NS ? cnt : NS - 1;
-      while (p > 0 && nrm > lnrm[p - 1][tid]) {
-        lnrm[p][tid] = lnrm[p - 1][tid];
-        lidx[p][tid] = lidx[p - 1][tid];
-        --p;
+  const int n_entries = (T + kSelChunk - 1) / kSelChunk * NS;
+  const float2* lists = reinterpret_cast<const float2*>(buf + L.record(b, h, 0));
+  for (int r = 0; r < NS; ++r) {
+    float n = -1.0f;
+    int t = 0x7FFFFFFF;
+    for (int e = tid; e < n_entries; e += 256) {
+      const float2 v = lists[e];
+      const int et = __float_as_int(v.y);
+      bool taken = false;
+      for (int k = 0; k < r; ++k) taken = taken || win[k] == et;
+      if (!taken && v.x >= 0.0f && sink_before(v.x, et, n, t)) {
+        n = v.x;
+        t = et;
       }
-      lnrm[p][tid] = nrm;
-      lidx[p][tid] = t;
-      if (cnt < NS) ++cnt;
     }
-  }
-  // NS rounds of a block arg-max over the threads' next candidates (norms are >= 0; -1 = none)
-  int head = 0;
-  for (int k = 0; k < NS; ++k) {
-    rn[tid] = head < cnt ? lnrm[head][tid] : -1.0f;
-    ri[tid] = head < cnt ? lidx[head][tid] : 0x7FFFFFFF;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-      if (tid < s && sink_before(rn[tid + s], ri[tid + s], rn[tid], ri[tid])) {
-        rn[tid] = rn[tid + s];
-        ri[tid] = ri[tid + s];
-      }
-      __syncthreads();
-    }
-    const int w = ri[0];
-    if (head < cnt && lidx[head][tid] == w) ++head;
-    if (tid == 0) win[k] = w;
+    block_best(n, t, sn, st);
+    if (tid == 0) win[r] = t;
     __syncthreads();
   }
   if (tid == 0) {  // ascending positions
@@ -425,6 +475,7 @@ __global__ __launch_bounds__(256) void sink_select_kernel(uint8_t* __restrict__ 
     for (int k = 0; k < NS; ++k) sp[k] = win[k];
   }
   __syncthreads();
+  const int64_t base = (int64_t(b) * L.Hkv + h) * ld_tok * D;
   uint4* sk = reinterpret_cast<uint4*>(buf + L.sink_k(b, h));
   uint4* sv = reinterpret_cast<uint4*>(buf + L.sink_v(b, h));
   for (int i = tid; i < NS * (D / 8); i += 256) {
@@ -701,16 +752,22 @@ hipError_t launch_window_fill(uint8_t* buf, const Layout& L, const void* K, cons
 
 hipError_t launch_sink_select(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,
                               const PerSeq& seq, hipStream_t s) {
-  dim3 grid(L.Hkv, L.B);
+  if (L.NS < 1 || L.NS > kMaxSinks) return hipErrorInvalidValue;
+  int max_t = 0;
+  for (int b = 0; b < L.B; ++b) max_t = seq.b[b] > max_t ? seq.b[b] : max_t;
+  if (max_t == 0) return hipSuccess;
+  const dim3 g1((max_t + kSelChunk - 1) / kSelChunk, L.Hkv, L.B), g2(L.Hkv, L.B);
   const __half* k = static_cast<const __half*>(K);
   const __half* v = static_cast<const __half*>(V);
-  if (L.NS < 1 || L.NS > kMaxSinks) return hipErrorInvalidValue;
-  if (L.D == 128)
-    hipLaunchKernelGGL(sink_select_kernel<128>, grid, dim3(256), 0, s, buf, L, k, v, ld_tok, seq);
-  else if (L.D == 64)
-    hipLaunchKernelGGL(sink_select_kernel<64>, grid, dim3(256), 0, s, buf, L, k, v, ld_tok, seq);
-  else
+  if (L.D == 128) {
+    hipLaunchKernelGGL(sink_chunk_kernel<128>, g1, dim3(256), 0, s, buf, L, k, ld_tok, seq);
+    hipLaunchKernelGGL(sink_merge_kernel<128>, g2, dim3(256), 0, s, buf, L, k, v, ld_tok, seq);
+  } else if (L.D == 64) {
+    hipLaunchKernelGGL(sink_chunk_kernel<64>, g1, dim3(256), 0, s, buf, L, k, ld_tok, seq);
+    hipLaunchKernelGGL(sink_merge_kernel<64>, g2, dim3(256), 0, s, buf, L, k, v, ld_tok, seq);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
