@@ -11,8 +11,9 @@ Attention is written as explicit sums with ``math.exp``.
 
 Sources are the same passages as ``oracle.kivi``: "Changelog" v0.8.0 (KIVI: per-channel
 keys, per-token values, residual window), v0.42.0 (codes plus per-group (scale, zero),
-softmax attention over the reconstruction), v0.30.0 (lo/scale, fp16 metadata), v0.9.0
-(KIVI-Sink: high key-norm tokens kept in fp16, outside the group statistics).
+softmax attention over the reconstruction), v0.30.0 (lo/scale, fp16 metadata; SKVQ-adapted:
+channel reordering by range, per-group clip search), v0.9.0 (KIVI-Sink: high key-norm tokens
+kept in fp16, outside the group statistics).
 """
 from __future__ import annotations
 
@@ -101,6 +102,42 @@ def select_sinks(K: list[list[float]], n: int) -> list[int]:
             acc = r32(acc + r32(x * x))
         norms.append((-acc, t))
     return sorted(t for _, t in sorted(norms)[:n])
+
+
+def clipped_group_quant(xs: list[float], bits: int, fracs: list[float]):
+    """One group with the clip search: for each clip fraction c (window [lo + d, hi - d],
+    d = (hi - lo) * c), quantize with the stored fp16 step and low end and take the fp32 sum
+    of squared errors in element order; the smallest error wins, the first on ties.
+    Returns (codes, scale16, zero16, index of the chosen fraction)."""
+    L = float(2 ** bits - 1)
+    lo = r32(min(xs) + 0.0)
+    hi = r32(max(xs) + 0.0)
+    best = None
+    for k, c in enumerate(fracs):
+        d = r32(r32(hi - lo) * c)
+        lo_c, hi_c = r32(lo + d), r32(hi - d)
+        scale16 = r16(r32(r32(hi_c - lo_c) / L))
+        zero16 = r16(lo_c)
+        if scale16 == 0.0:
+            codes = [0] * len(xs)
+        else:
+            inv = r32(1.0 / scale16)
+            codes = [int(min(max(round_half_even(r32(r32(x - zero16) * inv)), 0.0), L)) for x in xs]
+        err = 0.0
+        for x, cd in zip(xs, codes):
+            xh = r32(r32(cd * scale16) + zero16)
+            diff = r32(x - xh)
+            err = r32(err + r32(diff * diff))
+        if best is None or err < best[4]:
+            best = (codes, scale16, zero16, k, err)
+    return best[:4]
+
+
+def channel_permutation(rows: list[list[float]]) -> list[int]:
+    """Channels in ascending order of binary32 (max - min) over the rows, stable on ties."""
+    D = len(rows[0])
+    rng = [r32(max(r[d] for r in rows) - min(r[d] for r in rows)) for d in range(D)]
+    return sorted(range(D), key=lambda d: (rng[d], d))
 
 
 def attend(q: list[float], keys: list[list[float]], values: list[list[float]], sm_scale: float = 1.0):
