@@ -72,8 +72,26 @@ typedef struct kvq_config {
                          encode, or the first window flush); they never change afterwards. Their
                          fp16 key and value rows are kept, they take no part in their key
                          groups' min/max, and attention uses their fp16 rows in place of their
-                         quantized slots. */
+                         quantized slots. With method = KVQ_METHOD_SKVQ: the first n_sink tokens
+                         of each sequence, kept in fp16 (the SKVQ sink filter). */
+  int32_t method;           /* KVQ_METHOD_KIVI (0) or KVQ_METHOD_SKVQ (1) */
+  int32_t skvq_reorder;     /* SKVQ: 1 = permute channels by range over the first chunk, 0 = identity */
+  int32_t skvq_clip_search; /* SKVQ: 1 = per-group search over alpha = 1 - k/20 (k = 0..10),
+                               0 = the fixed skvq_clip_alpha */
+  float skvq_clip_alpha;    /* SKVQ with the search off: alpha in (0, 1] (1 = no clipping) */
 } kvq_config;
+
+/* Methods ("Changelog" v0.8.0 KIVI, v0.9.0 KIVI-Sink through n_sink; v0.30.0 SKVQ-adapted):
+ * SKVQ quantizes keys and values in per-token groups of 32 channels taken in the order of a
+ * per-(sequence, KV head) permutation (ascending channel range over the first flushed chunk
+ * of R tokens, fp32 max - min, stable), each group's [min, max] window shrunk around its
+ * centre to [lo + d, hi - d], d = (hi - lo)(1 - alpha)/2, with alpha picked per group by the
+ * smallest fp32 sum of squared reconstruction errors (alpha = 1 on ties, fp32 operations in
+ * group order), and the chosen window stored as its fp16 (scale, zero). The window rule
+ * applies to the tokens after the n_sink sinks; a prefill equals the same tokens appended one
+ * by one. */
+#define KVQ_METHOD_KIVI 0
+#define KVQ_METHOD_SKVQ 1
 
 /* Byte offsets of the regions inside the cache buffer (see the layout description in the
  * design notes; all offsets but sync_offset are multiples of 256). */
@@ -93,9 +111,12 @@ typedef struct kvq_layout_info {
                                counter; every lengths update zeroes them) */
   uint64_t sink_pos_offset; /* int32 [B][H_kv][n_sink]: sink token positions, ascending */
   uint64_t sink_k_offset;   /* fp16 [B][H_kv][n_sink][D]: sink key rows */
-  uint64_t sink_v_offset;   /* fp16 [B][H_kv][n_sink][D]: sink value rows. The sink regions are
-                               valid once the sequence has quantized tokens; in the records a
-                               sink's value scales carry the sign bit (decode skips that slot). */
+  uint64_t sink_v_offset;   /* fp16 [B][H_kv][n_sink][D]: sink value rows. The sinks present are
+                               the leading non-negative positions (-1 = empty slot); in KIVI
+                               records a sink's value scales carry the sign bit (decode skips
+                               that slot). */
+  uint64_t perm_offset;     /* SKVQ: uint8 [B][H_kv][2][D], the K and V channel permutations
+                               (permuted channel j is channel perm[j]); == total_bytes for KIVI */
 } kvq_layout_info;
 
 typedef struct kvq_cache kvq_cache; /* opaque host handle */
@@ -147,7 +168,9 @@ kvq_status kvq_cache_lengths(const kvq_cache* cache, int32_t* n_quantized, int32
  * codes = clamp(rint((x - zero) * (1/scale)), 0, 2^b - 1) with the stored scale, all
  * codes 0 when the stored scale is 0. Results are bit-identical on every run.
  * With n_sink > 0, a sequence that had no quantized token first chooses its sinks among
- * the n_tok[b] tokens (see kvq_config.n_sink); they stay out of their key groups' min/max. */
+ * the n_tok[b] tokens (see kvq_config.n_sink); they stay out of their key groups' min/max.
+ * SKVQ caches (whose sinks and chunks follow from the token stream) return
+ * KVQ_E_UNSUPPORTED: fill them with kvq_prefill and kvq_append. */
 kvq_status kvq_encode(kvq_cache* cache, const void* K, const void* V, int64_t ld_tok,
                       const int32_t* n_tok, void* stream);
 

@@ -28,6 +28,7 @@ PER_FILE = {
     "encode.hip": ["-ffp-contract=off"],
     "decode.hip": [],
     "decode_sink.hip": [],
+    "decode_skvq.hip": [],
     "kvq.cpp": ["-x", "hip"],
 }
 

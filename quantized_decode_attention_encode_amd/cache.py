@@ -13,6 +13,7 @@ import ctypes
 
 import torch
 
+from . import _lib
 from ._lib import KVQ_OK, Config, KVQError, LayoutInfo, check, lib
 
 __all__ = ["KVQCache", "KVQError", "make_config", "kvq_probe", "kvq_cache_bytes", "kvq_layout",
@@ -20,10 +21,17 @@ __all__ = ["KVQCache", "KVQError", "make_config", "kvq_probe", "kvq_cache_bytes"
 
 
 def make_config(batch, n_kv_heads, n_q_heads, head_dim, key_bits=2, value_bits=2, group=32, residual=32,
-                max_tokens=4096, n_sink=0) -> Config:
-    """n_sink > 0: KIVI-Sink, that many high key-norm tokens per (sequence, KV head) kept in fp16."""
+                max_tokens=4096, n_sink=0, method="kivi", skvq_reorder=True, skvq_clip_search=True,
+                skvq_clip_alpha=1.0) -> Config:
+    """method "kivi" (n_sink > 0: KIVI-Sink, that many high key-norm tokens per (sequence, KV head)
+    kept in fp16) or "skvq" (SKVQ-adapted: per-token groups of range-sorted channels with a
+    per-group clip search; n_sink first tokens in fp16; residual is its window, 128 by default
+    on the pages)."""
+    if method not in ("kivi", "skvq"):
+        raise ValueError(f"method must be 'kivi' or 'skvq', got {method!r}")
+    m = _lib.METHOD_SKVQ if method == "skvq" else _lib.METHOD_KIVI
     return Config(batch, n_kv_heads, n_q_heads, head_dim, key_bits, value_bits, group, residual, max_tokens,
-                  n_sink)
+                  n_sink, m, int(bool(skvq_reorder)), int(bool(skvq_clip_search)), float(skvq_clip_alpha))
 
 
 def _stream(stream) -> ctypes.c_void_p:

@@ -172,6 +172,7 @@ template <int D, int G>
 struct WaveLds {
   float qt[G][4][D / 4 + 4];      // scaled, folded query per quarter (padded rows)
   float beta[G][4];               // quarter offsets (q . z minus the fold constant)
+  float qsum[G][4];               // per-token key groups: the query summed over each quarter
   uint32_t A[G][D / 32][16 + 4];  // fp16 value weights per (value group, token pair), see kVScale
   float pw[G][32 + 4];            // window tokens: softmax weights
   float red[G][64];
@@ -181,16 +182,25 @@ template <int D, int BK, int BV>
 struct RecordRegs {
   uint32_t kc[2 * (D * BK / 128)];
   uint32_t vc[(D / 64) * BV];
-  uint32_t kp[D / 64];
+  uint32_t kp[D / 64 < 2 ? 2 : D / 64];  // two words at D = 64 with per-token key groups
   uint32_t vp[D / 64];
 };
 
-template <int D, int BK, int BV>
+// KT (per-token key groups): lane (P, Q) takes the key params of its tokens 2P, 2P+1 for the
+// group of its quarter, two adjacent words at [P][group][t%2].
+template <int D, int BK, int BV, bool KT = false>
 __device__ __forceinline__ void load_record(const uint8_t* __restrict__ rec, int lane, RecordRegs<D, BK, BV>& r) {
   constexpr int E = D / 64, KW = 2 * (D * BK / 128), VW = E * BV;
   load_words<KW>(reinterpret_cast<const uint32_t*>(rec) + lane * KW, r.kc);
   load_words<VW>(reinterpret_cast<const uint32_t*>(rec + rec_off_vcodes(D, BK)) + lane * VW, r.vc);
-  load_words<E>(reinterpret_cast<const uint32_t*>(rec + rec_off_kparams(D, BK, BV)) + lane * E, r.kp);
+  if constexpr (KT) {
+    constexpr int NKG = D / 32;
+    const int kg = ((lane & 3) * (D / 4)) / 32;
+    load_words<2>(reinterpret_cast<const uint32_t*>(rec + rec_off_kparams(D, BK, BV)) + ((lane >> 2) * NKG + kg) * 2,
+                  r.kp);
+  } else {
+    load_words<E>(reinterpret_cast<const uint32_t*>(rec + rec_off_kparams(D, BK, BV)) + lane * E, r.kp);
+  }
   load_words<E>(reinterpret_cast<const uint32_t*>(rec + rec_off_vparams(D, BK, BV)) + lane * E, r.vp);
 }
 
@@ -232,7 +242,7 @@ __device__ __forceinline__ void softmax_step(WaveState<D, G>& st, int i, float s
 
 // One 32-token record of (b, h_kv), all G query heads. With SK, slots whose value scale
 // carries the sign bit (sinks, attended from their fp16 rows instead) get no weight.
-template <int D, int BK, int BV, int G, bool SK>
+template <int D, int BK, int BV, int G, bool SK, bool KT>
 __device__ __forceinline__ void process_record(const RecordRegs<D, BK, BV>& cur, WaveLds<D, G>& W, WaveState<D, G>& st,
                                                const Unpacker<BK>& upk, const Unpacker<BV>& upv,
                                                const float (&qs)[G][D / 64], const float (&qf)[G][D / 64],
@@ -258,9 +268,10 @@ __device__ __forceinline__ void process_record(const RecordRegs<D, BK, BV>& cur,
     }
   }
 
-  // ---- producer: folded scaled query and quarter offsets
+  // ---- producer: folded scaled query and quarter offsets (per-token key groups: set once
+  // per launch, nothing to do per record)
 #pragma unroll
-  for (int i = 0; i < G; ++i) {
+  for (int i = 0; i < G && !KT; ++i) {
     float bp = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -277,7 +288,7 @@ __device__ __forceinline__ void process_record(const RecordRegs<D, BK, BV>& cur,
   // ---- keys
   float s[G][2];
 #pragma unroll
-  for (int i = 0; i < G; ++i) s[i][0] = s[i][1] = W.beta[i][Q];
+  for (int i = 0; i < G; ++i) s[i][0] = s[i][1] = KT ? 0.0f : W.beta[i][Q];
   if constexpr (G == 1) {
     // word by word: few live registers
 #pragma unroll
@@ -330,6 +341,13 @@ __device__ __forceinline__ void process_record(const RecordRegs<D, BK, BV>& cur,
 #pragma unroll
   for (int i = 0; i < G; ++i) {
     float s0 = s[i][0], s1 = s[i][1];
+    if constexpr (KT) {
+      // quarter partial sum_c q~_c (1 + c_code 2^(o-10)) minus the fold constant, times the
+      // token's group scale, plus its zero times the quarter's query sum
+      const float fq = W.beta[i][Q], qsm = W.qsum[i][Q];
+      s0 = __builtin_fmaf(lo_f(cur.kp[0]), s0 - fq, hi_f(cur.kp[0]) * qsm);
+      s1 = __builtin_fmaf(lo_f(cur.kp[1]), s1 - fq, hi_f(cur.kp[1]) * qsm);
+    }
     s0 += dpp<kQuadXor1>(s0);
     s1 += dpp<kQuadXor1>(s1);
     s0 += dpp<kQuadXor2>(s0);
@@ -413,11 +431,14 @@ __device__ __forceinline__ void process_record(const RecordRegs<D, BK, BV>& cur,
 // Up to 32 fp16 window tokens (tokens tbase .. tbase + nvalid - 1 of the window).
 // Token tnew of the unit (when 0 <= tnew < nvalid) is the one this launch appends: its rows
 // come from kn / vn instead of the window.
-template <int D, int G>
+// With KT the query and the accumulators run in permuted channel order: key and value rows
+// (stored in channel order) are read through the permutations pk, pv.
+template <int D, int G, bool KT = false>
 __device__ __forceinline__ void process_window(const __half* __restrict__ wk, const __half* __restrict__ wv, int nvalid,
                                                int tnew, const __half* kn, const __half* vn,
                                                WaveLds<D, G>& W, WaveState<D, G>& st, const float (&qs)[G][D / 64],
-                                               int lane) {
+                                               int lane, const uint8_t* __restrict__ pk = nullptr,
+                                               const uint8_t* __restrict__ pv = nullptr) {
   constexpr int E = D / 64, DQ = D / 4;
   const int P = lane >> 2, Q = lane & 3;
   const int kcons = (lane * E) / 32;
@@ -434,10 +455,21 @@ __device__ __forceinline__ void process_window(const __half* __restrict__ wk, co
   const uint32_t* k0p = reinterpret_cast<const uint32_t*>((t0c == tnew ? kn : wk + t0c * D) + Q * DQ);
   const uint32_t* k1p = reinterpret_cast<const uint32_t*>((t1c == tnew ? kn : wk + t1c * D) + Q * DQ);
   uint32_t k0w[DQ / 2], k1w[DQ / 2];
+  if constexpr (KT) {
+    const uint16_t* r0 = reinterpret_cast<const uint16_t*>(t0c == tnew ? kn : wk + t0c * D);
+    const uint16_t* r1 = reinterpret_cast<const uint16_t*>(t1c == tnew ? kn : wk + t1c * D);
 #pragma unroll
-  for (int c = 0; c < DQ / 2; ++c) {
-    k0w[c] = k0p[c];
-    k1w[c] = k1p[c];
+    for (int c = 0; c < DQ / 2; ++c) {
+      const int ja = pk[Q * DQ + 2 * c], jb = pk[Q * DQ + 2 * c + 1];
+      k0w[c] = uint32_t(r0[ja]) | (uint32_t(r0[jb]) << 16);
+      k1w[c] = uint32_t(r1[ja]) | (uint32_t(r1[jb]) << 16);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < DQ / 2; ++c) {
+      k0w[c] = k0p[c];
+      k1w[c] = k1p[c];
+    }
   }
 #pragma unroll
   for (int i = 0; i < G; ++i) {
@@ -466,7 +498,11 @@ __device__ __forceinline__ void process_window(const __half* __restrict__ wk, co
     for (int t = 0; t < nvalid; ++t) {
       const float a = W.pw[i][t];
       const __half* vrow = t == tnew ? vn : wv + t * D;
-      if constexpr (E == 2) {
+      if constexpr (KT) {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          st.acc[i][e] = __builtin_fmaf(a, __half2float(vrow[pv[lane * E + e]]), st.acc[i][e]);
+      } else if constexpr (E == 2) {
         const uint32_t vw = reinterpret_cast<const uint32_t*>(vrow)[lane];
         st.acc[i][0] = __builtin_fmaf(a, lo_f(vw), st.acc[i][0]);
         st.acc[i][1] = __builtin_fmaf(a, hi_f(vw), st.acc[i][1]);
@@ -499,9 +535,11 @@ __device__ __forceinline__ void store_out(void* out, int out_fp32, int64_t idx, 
 // Merge the nv split partials (acc[D], m, l) of the G query heads row0 .. row0+G-1 into the
 // output, by one workgroup of 64*kWaves threads: T threads per output element each fold a
 // strided share of the splits (batches of 8 loads in flight), then meet through LDS.
+// pv (per-token key groups): partial channel ch is output channel pv[ch].
 template <int D, int G>
 __device__ __forceinline__ void merge_splits(const float* __restrict__ ws, int64_t row0, int n_split, int nv,
-                                             float (*mrg)[64 * kWaves], void* out, int out_fp32) {
+                                             float (*mrg)[64 * kWaves], void* out, int out_fp32,
+                                             const uint8_t* __restrict__ pv = nullptr) {
   constexpr int NT = 64 * kWaves, NOUT = G * D;
   constexpr int T = NOUT >= NT ? 1 : NT / NOUT;
   constexpr int NO = NOUT >= NT ? NT : NOUT;  // output elements per pass
@@ -536,7 +574,7 @@ __device__ __forceinline__ void merge_splits(const float* __restrict__ ws, int64
       M = mx;
     }
     if constexpr (T == 1) {
-      store_out(out, out_fp32, (row0 + i) * D + ch, O / Ls);
+      store_out(out, out_fp32, (row0 + i) * D + (pv ? pv[ch] : ch), O / Ls);
     } else {
       mrg[0][tid] = M;
       mrg[1][tid] = Ls;
@@ -556,12 +594,23 @@ __device__ __forceinline__ void merge_splits(const float* __restrict__ ws, int64
         Ls = __builtin_fmaf(w, mrg[1][tid + j * NO], Ls);
         O = __builtin_fmaf(w, mrg[2][tid + j * NO], O);
       }
-      store_out(out, out_fp32, (row0 + tid / D) * D + tid % D, O / Ls);
+      store_out(out, out_fp32, (row0 + tid / D) * D + (pv ? pv[tid % D] : tid % D), O / Ls);
     }
   }
 }
 
-template <int D, int BK, int BV, int G, bool SK>
+// The identity permutation, used by SKVQ sequences before their first chunk fixes theirs.
+__device__ const uint8_t kIdentityPerm[128] = {
+    0,   1,   2,   3,   4,   5,   6,   7,   8,   9,   10,  11,  12,  13,  14,  15,  16,  17,  18,  19,  20,  21,
+    22,  23,  24,  25,  26,  27,  28,  29,  30,  31,  32,  33,  34,  35,  36,  37,  38,  39,  40,  41,  42,  43,
+    44,  45,  46,  47,  48,  49,  50,  51,  52,  53,  54,  55,  56,  57,  58,  59,  60,  61,  62,  63,  64,  65,
+    66,  67,  68,  69,  70,  71,  72,  73,  74,  75,  76,  77,  78,  79,  80,  81,  82,  83,  84,  85,  86,  87,
+    88,  89,  90,  91,  92,  93,  94,  95,  96,  97,  98,  99,  100, 101, 102, 103, 104, 105, 106, 107, 108, 109,
+    110, 111, 112, 113, 114, 115, 116, 117, 118, 119, 120, 121, 122, 123, 124, 125, 126, 127};
+
+// SK: the cache has sink slots (the sinks present are the leading non-negative positions);
+// KT: SKVQ records (per-token key groups, permuted channels, see layout.h).
+template <int D, int BK, int BV, int G, bool SK, bool KT>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : (G <= 4 ? 2 : 1))))
 void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape ds, const __half* __restrict__ q,
                          float* __restrict__ ws, uint32_t* __restrict__ sync, void* __restrict__ out,
@@ -584,8 +633,13 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
   const int nr_old = max(0, min(len[1], L.R));
   const int nr = min(nr_old + ds.append, L.R);  // with an append: the new token is window slot nr_old
   const int ngroups = nq / kGroup;
-  // with sinks (chosen once tokens are quantized) one more unit, the last: their fp16 rows
-  const bool sinks = SK && nq > 0;
+  // with sinks one more unit, the last: their fp16 rows
+  int nsink = 0;
+  if constexpr (SK) {
+    const int32_t* sp = reinterpret_cast<const int32_t*>(buf + L.sink_pos(b, h));
+    for (int k = 0; k < L.NS && sp[k] >= 0; ++k) nsink = k + 1;
+  }
+  const bool sinks = nsink > 0;
   const int nunits = ngroups + (nr + kGroup - 1) / kGroup + (sinks ? 1 : 0);
   const int u0 = sigma * ds.chunk;
   if (u0 >= nunits) return;
@@ -601,15 +655,42 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
   upk.init();
   upv.init();
 
+  // KT: the query in permuted channel order (channel ch of the records is pk[ch]); a sequence
+  // with no chunk quantized yet has no permutation of its own (any one is consistent for its
+  // fp16 rows): the identity
+  const uint8_t* pk = KT ? (nq > 0 ? buf + L.perm(b, h) : kIdentityPerm) : nullptr;
+  const uint8_t* pv = KT ? (nq > 0 ? pk + D : kIdentityPerm) : nullptr;
   float qs[G][E], qf[G][E];
 #pragma unroll
   for (int i = 0; i < G; ++i)
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int ch = lane * E + e;
-      qs[i][e] = __half2float(q[(int64_t(b) * ds.n_q_heads + h * G + i) * D + ch]) * ds.qscale;
+      qs[i][e] = __half2float(q[(int64_t(b) * ds.n_q_heads + h * G + i) * D + (KT ? pk[ch] : ch)]) * ds.qscale;
       qf[i][e] = qs[i][e] * MK::fold((ch % DQ) % MK::NC);
     }
+  if constexpr (KT) {
+    // no per-channel key scale: the folded query, its fold constant and its plain sum per
+    // quarter are the same for every record
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      float fq = 0.f, qsm = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int ch = lane * E + e;
+        W.qt[i][ch / DQ][ch % DQ] = qf[i][e];
+        fq += qf[i][e];
+        qsm += qs[i][e];
+      }
+      fq = row_sum16(fq);
+      qsm = row_sum16(qsm);
+      if ((lane & 15) == 0) {
+        W.beta[i][lane >> 4] = fq;
+        W.qsum[i][lane >> 4] = qsm;
+      }
+    }
+    wave_sync();
+  }
   const float vf0 = MV::fold((2 * P) % MV::NC) * kVScale, vf1 = MV::fold((2 * P + 1) % MV::NC) * kVScale;
 
   WaveState<D, G> st;
@@ -633,26 +714,26 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
   if constexpr (G == 1) {
     RecordRegs<D, BK, BV> ra, rbuf;
     if (u < uq) {
-      load_record<D, BK, BV>(rec0 + u * rb, lane, ra);
-      load_record<D, BK, BV>(rec0 + min(u + kWaves, ulast) * rb, lane, rbuf);
+      load_record<D, BK, BV, KT>(rec0 + u * rb, lane, ra);
+      load_record<D, BK, BV, KT>(rec0 + min(u + kWaves, ulast) * rb, lane, rbuf);
       while (true) {
-        process_record<D, BK, BV, G, SK>(ra, W, st, upk, upv, qs, qf, vf0, vf1, lane);
+        process_record<D, BK, BV, G, SK, KT>(ra, W, st, upk, upv, qs, qf, vf0, vf1, lane);
         u += kWaves;
         if (u >= uq) break;
-        load_record<D, BK, BV>(rec0 + min(u + kWaves, ulast) * rb, lane, ra);
-        process_record<D, BK, BV, G, SK>(rbuf, W, st, upk, upv, qs, qf, vf0, vf1, lane);
+        load_record<D, BK, BV, KT>(rec0 + min(u + kWaves, ulast) * rb, lane, ra);
+        process_record<D, BK, BV, G, SK, KT>(rbuf, W, st, upk, upv, qs, qf, vf0, vf1, lane);
         u += kWaves;
         if (u >= uq) break;
-        load_record<D, BK, BV>(rec0 + min(u + kWaves, ulast) * rb, lane, rbuf);
+        load_record<D, BK, BV, KT>(rec0 + min(u + kWaves, ulast) * rb, lane, rbuf);
       }
     }
   } else {
     RecordRegs<D, BK, BV> cur, nxt;
     if (u < uq) {
-      load_record<D, BK, BV>(rec0 + u * rb, lane, cur);
+      load_record<D, BK, BV, KT>(rec0 + u * rb, lane, cur);
       for (; u < uq; u += kWaves) {
-        load_record<D, BK, BV>(rec0 + min(u + kWaves, ulast) * rb, lane, nxt);
-        process_record<D, BK, BV, G, SK>(cur, W, st, upk, upv, qs, qf, vf0, vf1, lane);
+        load_record<D, BK, BV, KT>(rec0 + min(u + kWaves, ulast) * rb, lane, nxt);
+        process_record<D, BK, BV, G, SK, KT>(cur, W, st, upk, upv, qs, qf, vf0, vf1, lane);
         cur = nxt;
       }
     }
@@ -661,7 +742,7 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
   for (; u < u1; u += kWaves) {
     const bool sink_unit = sinks && u == nunits - 1;
     const int tbase = (u - ngroups) * kGroup;
-    const int nvalid = sink_unit ? L.NS : min(kGroup, nr - tbase);
+    const int nvalid = sink_unit ? nsink : min(kGroup, nr - tbase);
     const __half* wk = sink_unit ? reinterpret_cast<const __half*>(buf + L.sink_k(b, h))
                                  : reinterpret_cast<const __half*>(buf + L.wk_off + L.window(b, h)) + tbase * D;
     const __half* wv = sink_unit ? reinterpret_cast<const __half*>(buf + L.sink_v(b, h))
@@ -671,7 +752,7 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
     const int64_t tok = (int64_t(b) * L.Hkv + h) * D;
     const __half* kn = ds.append ? k_app + tok : nullptr;
     const __half* vn = ds.append ? v_app + tok : nullptr;
-    process_window<D, G>(wk, wv, nvalid, tnew, kn, vn, W, st, qs, lane);
+    process_window<D, G, KT>(wk, wv, nvalid, tnew, kn, vn, W, st, qs, lane, pk, pv);
     if (tnew >= 0 && tnew < nvalid) {  // store the appended token in its slot (no read of it here)
       __half* dk = reinterpret_cast<__half*>(bufw + L.wk_off + L.window(b, h)) + nr_old * D;
       __half* dv = reinterpret_cast<__half*>(bufw + L.wv_off + L.window(b, h)) + nr_old * D;
@@ -734,7 +815,7 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
       }
     }
     if (nvalid == 1) {
-      store_out(out, ds.out_fp32, (row0 + i) * D + ch, O / Lsum);
+      store_out(out, ds.out_fp32, (row0 + i) * D + (KT ? pv[ch] : ch), O / Lsum);
       continue;
     }
     float* dst = ws + ((row0 + i) * ds.n_split + sigma) * (D + 4);
@@ -763,7 +844,7 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
   if (threadIdx.x == 0) sh_last = atomicAdd(cnt, 1u) + 1u == uint32_t(nvalid);
   __syncthreads();
   if (!sh_last) return;
-  merge_splits<D, G>(ws, row0, ds.n_split, nvalid, sh.mrg, out, ds.out_fp32);
+  merge_splits<D, G>(ws, row0, ds.n_split, nvalid, sh.mrg, out, ds.out_fp32, pv);
   if (threadIdx.x == 0) {
     if (ds.append) len_w[1] = nr;
     atomicExch(cnt, 0u);
@@ -771,7 +852,7 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
 }
 
 // ------------------------------------------------------------------------------------
-template <int D, int BK, int BV, int G, bool SK>
+template <int D, int BK, int BV, int G, bool SK, bool KT>
 static hipError_t launch_split_t(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q,
                                  float* ws, void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0,
                                  hipEvent_t e1) {
@@ -781,41 +862,41 @@ static hipError_t launch_split_t(uint8_t* buf, const Layout& L, const DecodeShap
   const __half* kh = static_cast<const __half*>(ka);
   const __half* vh = static_cast<const __half*>(va);
   if (e0 || e1)
-    hipExtLaunchKernelGGL((decode_split_kernel<D, BK, BV, G, SK>), grid, dim3(64 * kWaves), 0, s, e0, e1, 0,
+    hipExtLaunchKernelGGL((decode_split_kernel<D, BK, BV, G, SK, KT>), grid, dim3(64 * kWaves), 0, s, e0, e1, 0,
                           static_cast<const uint8_t*>(buf), L, ds, qh, ws, sync, out, kh, vh, buf);
   else
-    hipLaunchKernelGGL((decode_split_kernel<D, BK, BV, G, SK>), grid, dim3(64 * kWaves), 0, s,
+    hipLaunchKernelGGL((decode_split_kernel<D, BK, BV, G, SK, KT>), grid, dim3(64 * kWaves), 0, s,
                        static_cast<const uint8_t*>(buf), L, ds, qh, ws, sync, out, kh, vh, buf);
   return hipGetLastError();
 }
 
-template <int D, int BK, int BV, bool SK>
+template <int D, int BK, int BV, bool SK, bool KT>
 static hipError_t launch_split_g(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q,
                                  float* ws, void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0,
                                  hipEvent_t e1) {
   switch (ds.G) {
-    case 1: return launch_split_t<D, BK, BV, 1, SK>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 2: return launch_split_t<D, BK, BV, 2, SK>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 4: return launch_split_t<D, BK, BV, 4, SK>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 8: return launch_split_t<D, BK, BV, 8, SK>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 1: return launch_split_t<D, BK, BV, 1, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 2: return launch_split_t<D, BK, BV, 2, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 4: return launch_split_t<D, BK, BV, 4, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 8: return launch_split_t<D, BK, BV, 8, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int D, bool SK>
+template <int D, bool SK, bool KT>
 static hipError_t launch_split_d(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q,
                                  float* ws, void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0,
                                  hipEvent_t e1) {
   switch (L.bk * 16 + L.bv) {
-    case 0x22: return launch_split_g<D, 2, 2, SK>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 0x24: return launch_split_g<D, 2, 4, SK>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 0x28: return launch_split_g<D, 2, 8, SK>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 0x42: return launch_split_g<D, 4, 2, SK>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 0x44: return launch_split_g<D, 4, 4, SK>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 0x48: return launch_split_g<D, 4, 8, SK>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 0x82: return launch_split_g<D, 8, 2, SK>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 0x84: return launch_split_g<D, 8, 4, SK>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 0x88: return launch_split_g<D, 8, 8, SK>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 0x22: return launch_split_g<D, 2, 2, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 0x24: return launch_split_g<D, 2, 4, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 0x28: return launch_split_g<D, 2, 8, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 0x42: return launch_split_g<D, 4, 2, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 0x44: return launch_split_g<D, 4, 4, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 0x48: return launch_split_g<D, 4, 8, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 0x82: return launch_split_g<D, 8, 2, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 0x84: return launch_split_g<D, 8, 4, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 0x88: return launch_split_g<D, 8, 8, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }

@@ -314,6 +314,199 @@ __device__ __forceinline__ void encode_record(const __half* __restrict__ ks, con
   __syncthreads();
 }
 
+// ------------------------------------------------------------------------------------
+// SKVQ-adapted ("Changelog" v0.30.0): per-token groups of 32 permuted channels for keys and
+// values, each group's window [lo, hi] shrunk to [lo + d, hi - d], d = (hi - lo) * c, with c
+// the fixed fraction (1 - alpha) / 2 or, with the search, the c_k = k / 40 (k = 0..10) whose
+// reconstruction has the smallest fp32 sum of squared errors (taken in group order; the
+// smaller k on ties). Channels are permuted by ascending range over the first chunk (stable).
+// ------------------------------------------------------------------------------------
+constexpr int kClipCandidates = 11;
+
+template <int D, int BK, int BV>
+struct SkvqLds {
+  static constexpr int kRecWords = D * (BK + BV + 2);
+  uint32_t rec[kRecWords];
+  uint8_t vbytes[D * kGroup];      // value codes [permuted channel][token]
+  __half tile[2][kGroup][D + 8];   // K and V rows of the record (padded)
+  uint8_t perm[2][D];
+};
+
+// Codes (packed little-endian, B bits each, 32 of them) and (scale16 | zero16 << 16) of one
+// group with the clip search over `ncand` candidates (fixed fraction `cfix` when ncand = 1).
+template <int B>
+__device__ __forceinline__ void clip_quant_group(const float (&x)[kGroup], int ncand, float cfix,
+                                                 uint32_t (&best_codes)[B], uint32_t& best_params) {
+  constexpr float L = float((1 << B) - 1);
+  float lo = x[0], hi = x[0];
+#pragma unroll
+  for (int i = 1; i < kGroup; ++i) {
+    lo = fminf(lo, x[i]);
+    hi = fmaxf(hi, x[i]);
+  }
+  lo = lo + 0.0f;
+  hi = hi + 0.0f;
+  float best_err = 0.0f;
+  for (int k = 0; k < ncand; ++k) {
+    const float c = ncand > 1 ? float(k) / 40.0f : cfix;
+    const float d = (hi - lo) * c;
+    const float lo_c = lo + d, hi_c = hi - d;
+    const __half s16 = __float2half_rn((hi_c - lo_c) / L);
+    const __half z16 = __float2half_rn(lo_c);
+    const float s = __half2float(s16), z = __half2float(z16);
+    const float inv = (s != 0.0f) ? 1.0f / s : 0.0f;
+    uint32_t cw[B];
+#pragma unroll
+    for (int w = 0; w < B; ++w) cw[w] = 0;
+    float err = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) {
+      const float cf = fminf(fmaxf(rintf((x[i] - z) * inv), 0.0f), L);
+      const float xh = cf * s + z;  // no contraction in this file: a multiply, then an add
+      const float diff = x[i] - xh;
+      err = err + diff * diff;
+      cw[(i * B) / 32] |= uint32_t(cf) << ((i * B) % 32);
+    }
+    if (k == 0 || err < best_err) {
+      best_err = err;
+#pragma unroll
+      for (int w = 0; w < B; ++w) best_codes[w] = cw[w];
+      best_params = uint32_t(__half_as_ushort(s16)) | (uint32_t(__half_as_ushort(z16)) << 16);
+    }
+  }
+}
+
+// Channel permutation of one tile of n rows (row stride D) by ascending range, stable:
+// perm[rank(c)] = c (the identity when `reorder` is 0). Called by `nthreads` threads of the
+// workgroup, each taking channels tid, tid + nthreads, ...; rng is D floats of LDS.
+template <int D>
+__device__ __forceinline__ void range_permutation(const __half* __restrict__ rows, int n, float* rng,
+                                                  uint8_t* __restrict__ perm_out, int tid, int nthreads, int reorder) {
+  if (!reorder) {
+    for (int c = tid; c < D; c += nthreads) perm_out[c] = uint8_t(c);
+    return;
+  }
+  for (int c = tid; c < D; c += nthreads) {
+    float mn = __half2float(rows[c]), mx = mn;
+    for (int t = 1; t < n; ++t) {
+      const float x = __half2float(rows[int64_t(t) * D + c]);
+      mn = fminf(mn, x);
+      mx = fmaxf(mx, x);
+    }
+    rng[c] = mx - mn;
+  }
+  __syncthreads();
+  for (int c = tid; c < D; c += nthreads) {
+    const float r = rng[c];
+    int rank = 0;
+    for (int o = 0; o < D; ++o) rank += (rng[o] < r || (rng[o] == r && o < c)) ? 1 : 0;
+    perm_out[rank] = uint8_t(c);
+  }
+  __syncthreads();
+}
+
+// Quantize 32 tokens (rows ks[0..31], vs[0..31], row stride D) into the SKVQ record at
+// rec_out; perm_k / perm_v are the sequence's permutations (global). One wave.
+template <int D, int BK, int BV>
+__device__ __forceinline__ void skvq_encode_record(const __half* __restrict__ ks, const __half* __restrict__ vs,
+                                                   const uint8_t* __restrict__ perm_k,
+                                                   const uint8_t* __restrict__ perm_v, int ncand, float cfix,
+                                                   uint32_t* __restrict__ rec_out, SkvqLds<D, BK, BV>& lds) {
+  constexpr int NKG = D / kGroup;             // groups per token
+  constexpr int DQ = D / 4;                   // channels per key-code quarter
+  constexpr int QPG = kGroup / DQ;            // quarters per group (1 at D = 128, 2 at D = 64)
+  constexpr int WQ = D * BK / 128;            // key-code words per (token, quarter)
+  constexpr uint32_t VC_W = D * BK;
+  constexpr uint32_t KP_W = D * (BK + BV);
+  constexpr uint32_t VP_W = KP_W + D;
+  constexpr int PAIRS = kGroup * NKG;         // (token, group) pairs per tensor
+  const int lane = threadIdx.x & 63;
+  // rows and permutations into LDS
+  for (int i = lane; i < kGroup * D / 8; i += 64) {
+    const int t = i / (D / 8), c = i % (D / 8);
+    *reinterpret_cast<uint4*>(&lds.tile[0][t][8 * c]) = reinterpret_cast<const uint4*>(ks + t * D)[c];
+    *reinterpret_cast<uint4*>(&lds.tile[1][t][8 * c]) = reinterpret_cast<const uint4*>(vs + t * D)[c];
+  }
+  for (int i = lane; i < D; i += 64) {
+    lds.perm[0][i] = perm_k[i];
+    lds.perm[1][i] = perm_v[i];
+  }
+  __syncthreads();
+  for (int p = lane; p < PAIRS; p += 64) {
+    const int t = p / NKG, k = p % NKG;
+    const int P = t >> 1, tp = t & 1;
+    float x[kGroup];
+    // keys
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) x[i] = __half2float(lds.tile[0][t][lds.perm[0][k * kGroup + i]]);
+    uint32_t cw[BK], par;
+    clip_quant_group<BK>(x, ncand, cfix, cw, par);
+#pragma unroll
+    for (int qq = 0; qq < QPG; ++qq)
+#pragma unroll
+      for (int w = 0; w < WQ; ++w) lds.rec[((P * 4 + k * QPG + qq) * 2 + tp) * WQ + w] = cw[qq * WQ + w];
+    lds.rec[KP_W + (P * NKG + k) * 2 + tp] = par;
+    // values
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) x[i] = __half2float(lds.tile[1][t][lds.perm[1][k * kGroup + i]]);
+    uint32_t vw[BV], vpar;
+    clip_quant_group<BV>(x, ncand, cfix, vw, vpar);
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i)
+      lds.vbytes[(k * kGroup + i) * kGroup + t] = uint8_t((vw[(i * BV) / 32] >> ((i * BV) % 32)) & ((1u << BV) - 1));
+    lds.rec[VP_W + (P * NKG + k) * 2 + tp] = vpar;
+  }
+  __syncthreads();
+  constexpr int PER_WORD = 32 / BV;
+  for (int w = lane; w < D * BV; w += 64) {
+    const int d = w / BV, sw = w % BV;
+    const uint8_t* src = &lds.vbytes[d * kGroup + sw * PER_WORD];
+    uint32_t word = 0;
+#pragma unroll
+    for (int n = 0; n < PER_WORD; ++n) word |= uint32_t(src[n]) << (n * BV);
+    lds.rec[VC_W + w] = word;
+  }
+  __syncthreads();
+  constexpr int NV4 = SkvqLds<D, BK, BV>::kRecWords / 4;
+  const uint4* src4 = reinterpret_cast<const uint4*>(lds.rec);
+  uint4* dst4 = reinterpret_cast<uint4*>(rec_out);
+  for (int v = lane; v < NV4; v += 64) dst4[v] = src4[v];
+  __syncthreads();
+}
+
+__device__ __forceinline__ int clip_candidates(const Layout& L) { return L.clip < 0.0f ? kClipCandidates : 1; }
+
+// SKVQ prefill: record seq.a[b] + blockIdx.x of (b, h) from tokens seq.c[b] + 32 blockIdx.x.
+template <int D, int BK, int BV>
+__global__ __launch_bounds__(64) void skvq_encode_kernel(uint8_t* __restrict__ buf, Layout L,
+                                                         const __half* __restrict__ K,
+                                                         const __half* __restrict__ V, int64_t ld_tok,
+                                                         PerSeq seq) {
+  __shared__ SkvqLds<D, BK, BV> lds;
+  const int jl = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  if (jl >= seq.b[b]) return;
+  const int j = seq.a[b] + jl;
+  if (j >= L.max_groups) return;
+  const int64_t row0 = ((int64_t(b) * L.Hkv + h) * ld_tok + seq.c[b] + int64_t(kGroup) * jl) * D;
+  const uint8_t* pm = buf + L.perm(b, h);
+  skvq_encode_record<D, BK, BV>(K + row0, V + row0, pm, pm + D, clip_candidates(L), L.clip,
+                                reinterpret_cast<uint32_t*>(buf + L.record(b, h, j)), lds);
+}
+
+// SKVQ permutations from the first chunk: R tokens from token seq.c[b] (seq.b[b] > 0 only).
+template <int D>
+__global__ __launch_bounds__(128) void skvq_perm_kernel(uint8_t* __restrict__ buf, Layout L,
+                                                        const __half* __restrict__ K,
+                                                        const __half* __restrict__ V, int64_t ld_tok, PerSeq seq) {
+  __shared__ float rng[D];
+  const int h = blockIdx.x, b = blockIdx.y;
+  if (seq.b[b] <= 0) return;
+  const int64_t row0 = ((int64_t(b) * L.Hkv + h) * ld_tok + seq.c[b]) * D;
+  uint8_t* pm = buf + L.perm(b, h);
+  range_permutation<D>(K + row0, L.R, rng, pm, threadIdx.x, blockDim.x, L.reorder);
+  range_permutation<D>(V + row0, L.R, rng, pm + D, threadIdx.x, blockDim.x, L.reorder);
+}
+
 // Prefill / encode: record (j0[b] + blockIdx.x) of (b = blockIdx.z, h = blockIdx.y) from
 // tokens 32*blockIdx.x .. of the caller's K, V [B][H_kv][ld_tok][D].
 template <int D, int BK, int BV>
@@ -569,11 +762,15 @@ __device__ void select_window_sinks(uint8_t* __restrict__ buf, const Layout& L, 
 // Append one token per (b, h); a full window is flushed first (R/32 records). seq holds every
 // sequence's lengths before the append (the host's mirror of the device lengths), so the
 // token's loads and the flush decision wait for no device read.
+// SKVQ caches: the first NS tokens of a sequence (seq.c = sinks present) go to the sink
+// region; after them the window rule holds, and the first flush also fixes the permutations.
 template <int D, int BK, int BV>
 __global__ __launch_bounds__(64) void append_kernel(uint8_t* __restrict__ buf, Layout L,
                                                     const __half* __restrict__ k_tok,
                                                     const __half* __restrict__ v_tok, PerSeq seq) {
   __shared__ EncodeLds<D, BK, BV> lds;
+  __shared__ SkvqLds<D, BK, BV> slds;
+  __shared__ float rng[D];
   const int h = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x;
   constexpr int HPL = D / 64;  // halves per lane
@@ -587,7 +784,36 @@ __global__ __launch_bounds__(64) void append_kernel(uint8_t* __restrict__ buf, L
   int nq = seq.a[b], nr = seq.b[b];
   __half* wk = reinterpret_cast<__half*>(buf + L.wk_off + L.window(b, h));
   __half* wv = reinterpret_cast<__half*>(buf + L.wv_off + L.window(b, h));
-  if (nr >= L.R) {  // uniform over the workgroup
+  if (L.method == kMethodSkvq) {
+    const int nsp = seq.c[b];
+    if (nsp < L.NS) {  // a sink: lengths unchanged
+      __half* sk = reinterpret_cast<__half*>(buf + L.sink_k(b, h)) + nsp * D;
+      __half* sv = reinterpret_cast<__half*>(buf + L.sink_v(b, h)) + nsp * D;
+#pragma unroll
+      for (int e = 0; e < HPL; ++e) {
+        sk[lane * HPL + e] = kt[e];
+        sv[lane * HPL + e] = vt[e];
+      }
+      if (lane == 0) reinterpret_cast<int32_t*>(buf + L.sink_pos(b, h))[nsp] = nsp;
+      return;
+    }
+    if (nr >= L.R) {  // flush the window as one chunk
+      uint8_t* pm = buf + L.perm(b, h);
+      if (nq == 0) {
+        range_permutation<D>(wk, L.R, rng, pm, lane, 64, L.reorder);
+        range_permutation<D>(wv, L.R, rng, pm + D, lane, 64, L.reorder);
+        __threadfence();  // the permutations are read back just below
+      }
+      const int j0 = nq / kGroup;
+      for (int m = 0; m < L.R / kGroup; ++m)
+        if (j0 + m < L.max_groups)
+          skvq_encode_record<D, BK, BV>(wk + m * kGroup * D, wv + m * kGroup * D, pm, pm + D, clip_candidates(L),
+                                        L.clip, reinterpret_cast<uint32_t*>(buf + L.record(b, h, j0 + m)), slds);
+      nq += L.R;
+      nr = 0;
+      __syncthreads();
+    }
+  } else if (nr >= L.R) {  // uniform over the workgroup
     const int j0 = nq / kGroup;
     uint32_t masks[kMaxResidual / kGroup];  // sinks per flushed record
 #pragma unroll
@@ -615,8 +841,10 @@ __global__ __launch_bounds__(64) void append_kernel(uint8_t* __restrict__ buf, L
   }
 }
 
-// Prefill tail: copy tokens [n_q, n_q + n_r) of K, V into window slots 0.. and set the
-// lengths of (b, h) to (n_q, n_r). seq.a = n_q, seq.b = n_r per sequence.
+// Prefill tail: copy tokens [t0, t0 + n_r) of K, V into window slots 0.. and set the lengths
+// of (b, h) to (n_q, n_r); seq.a = n_q, seq.b = n_r, seq.c = t0 (n_q, or for SKVQ the sinks
+// present plus n_q: its sinks, tokens 0 .. t0 - n_q - 1, are copied too). Sink slots that stay
+// empty are marked -1 (KIVI-Sink: all of them while nothing is quantized).
 template <int D>
 __global__ __launch_bounds__(64) void window_fill_kernel(uint8_t* __restrict__ buf, Layout L,
                                                          const __half* __restrict__ K,
@@ -624,11 +852,28 @@ __global__ __launch_bounds__(64) void window_fill_kernel(uint8_t* __restrict__ b
                                                          int64_t ld_tok, PerSeq seq) {
   const int h = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x;
-  const int nq = seq.a[b], nr = seq.b[b];
+  const int nq = seq.a[b], nr = seq.b[b], t0 = seq.c[b];
   __half* wk = reinterpret_cast<__half*>(buf + L.wk_off + L.window(b, h));
   __half* wv = reinterpret_cast<__half*>(buf + L.wv_off + L.window(b, h));
-  const int64_t row0 = ((int64_t(b) * L.Hkv + h) * ld_tok + nq) * D;
+  const int64_t row0 = ((int64_t(b) * L.Hkv + h) * ld_tok + t0) * D;
   constexpr int HPL = D / 64;
+  if (L.NS > 0) {
+    int32_t* sp = reinterpret_cast<int32_t*>(buf + L.sink_pos(b, h));
+    if (L.method == kMethodSkvq) {
+      const int ns = t0 - nq;
+      const int64_t s0 = (int64_t(b) * L.Hkv + h) * ld_tok * D;
+      __half* sk = reinterpret_cast<__half*>(buf + L.sink_k(b, h));
+      __half* sv = reinterpret_cast<__half*>(buf + L.sink_v(b, h));
+      for (int t = 0; t < ns; ++t)
+        for (int e = 0; e < HPL; ++e) {
+          sk[t * D + lane * HPL + e] = K[s0 + int64_t(t) * D + lane * HPL + e];
+          sv[t * D + lane * HPL + e] = V[s0 + int64_t(t) * D + lane * HPL + e];
+        }
+      if (lane < L.NS) sp[lane] = lane < ns ? lane : -1;
+    } else if (nq == 0 && lane < L.NS) {
+      sp[lane] = -1;
+    }
+  }
   for (int t = 0; t < nr; ++t)
     for (int e = 0; e < HPL; ++e) {
       wk[t * D + lane * HPL + e] = K[row0 + int64_t(t) * D + lane * HPL + e];
@@ -676,8 +921,10 @@ __global__ __launch_bounds__(64) void encode_block_kernel(const __half* __restri
     codes[base + j * stride] = uint8_t(code_of<B>(__half2float(X[base + j * stride]), p));
 }
 
-// Set the lengths of every (b, h) to (seq.a[b], seq.b[b]).
-__global__ __launch_bounds__(64) void lengths_fill_kernel(uint8_t* __restrict__ buf, Layout L, PerSeq seq) {
+// Set the lengths of every (b, h) to (seq.a[b], seq.b[b]); with clear_sinks also mark every
+// sink slot empty (-1).
+__global__ __launch_bounds__(64) void lengths_fill_kernel(uint8_t* __restrict__ buf, Layout L, PerSeq seq,
+                                                          int clear_sinks) {
   const int i = blockIdx.x * 64 + threadIdx.x;
   if (i >= L.B * L.Hkv) return;
   const int b = i / L.Hkv;
@@ -685,6 +932,8 @@ __global__ __launch_bounds__(64) void lengths_fill_kernel(uint8_t* __restrict__ 
   len[0] = seq.a[b];
   len[1] = seq.b[b];
   reinterpret_cast<uint32_t*>(buf + L.sync_off)[i] = 0;  // decode split counters start at zero
+  if (clear_sinks)
+    for (int k = 0; k < L.NS; ++k) reinterpret_cast<int32_t*>(buf + L.sp_off)[int64_t(i) * L.NS + k] = -1;
 }
 
 // ------------------------------------------------------------------------------------
@@ -771,9 +1020,39 @@ hipError_t launch_sink_select(uint8_t* buf, const Layout& L, const void* K, cons
   return hipGetLastError();
 }
 
-hipError_t launch_lengths_fill(uint8_t* buf, const Layout& L, const PerSeq& seq, hipStream_t s) {
+hipError_t launch_lengths_fill(uint8_t* buf, const Layout& L, const PerSeq& seq, hipStream_t s, int clear_sinks) {
   const int n = L.B * L.Hkv;
-  hipLaunchKernelGGL(lengths_fill_kernel, dim3((n + 63) / 64), dim3(64), 0, s, buf, L, seq);
+  hipLaunchKernelGGL(lengths_fill_kernel, dim3((n + 63) / 64), dim3(64), 0, s, buf, L, seq, clear_sinks);
+  return hipGetLastError();
+}
+
+template <int D, int BK, int BV>
+static hipError_t launch_skvq_encode_t(uint8_t* buf, const Layout& L, const void* K, const void* V,
+                                       int64_t ld_tok, const PerSeq& seq, int max_records, hipStream_t s) {
+  dim3 grid(max_records, L.Hkv, L.B);
+  hipLaunchKernelGGL((skvq_encode_kernel<D, BK, BV>), grid, dim3(64), 0, s, buf, L,
+                     static_cast<const __half*>(K), static_cast<const __half*>(V), ld_tok, seq);
+  return hipGetLastError();
+}
+
+hipError_t launch_skvq_encode(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,
+                              const PerSeq& seq, int max_records, hipStream_t s) {
+  if (L.D == 128) { KVQ_DISPATCH_BITS(128, launch_skvq_encode_t, buf, L, K, V, ld_tok, seq, max_records, s) }
+  if (L.D == 64) { KVQ_DISPATCH_BITS(64, launch_skvq_encode_t, buf, L, K, V, ld_tok, seq, max_records, s) }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_skvq_perm(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,
+                            const PerSeq& seq, hipStream_t s) {
+  dim3 grid(L.Hkv, L.B);
+  const __half* k = static_cast<const __half*>(K);
+  const __half* v = static_cast<const __half*>(V);
+  if (L.D == 128)
+    hipLaunchKernelGGL(skvq_perm_kernel<128>, grid, dim3(128), 0, s, buf, L, k, v, ld_tok, seq);
+  else if (L.D == 64)
+    hipLaunchKernelGGL(skvq_perm_kernel<64>, grid, dim3(128), 0, s, buf, L, k, v, ld_tok, seq);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -7,10 +7,11 @@
 
 namespace kvq {
 
-// Two per-sequence int32 arrays passed by value as a kernel argument (2 KiB).
+// Three per-sequence int32 arrays passed by value as a kernel argument (3 KiB).
 struct PerSeq {
   int32_t a[kMaxBatch];
   int32_t b[kMaxBatch];
+  int32_t c[kMaxBatch];
 };
 
 // Decode launch geometry: gridDim.x = n_split workgroups per (b, h_kv), each covering
@@ -33,7 +34,15 @@ hipError_t launch_window_fill(uint8_t* buf, const Layout& L, const void* K, cons
                               const PerSeq& seq, hipStream_t s);
 hipError_t launch_encode_block(const void* X, int n_tok, int D, int bits, int group, int per_channel, void* codes,
                                void* scales, void* zeros, hipStream_t s);
-hipError_t launch_lengths_fill(uint8_t* buf, const Layout& L, const PerSeq& seq, hipStream_t s);
+// clear_sinks: also mark every sink slot empty (a reset, or the first use of a buffer).
+hipError_t launch_lengths_fill(uint8_t* buf, const Layout& L, const PerSeq& seq, hipStream_t s, int clear_sinks);
+// SKVQ permutations of the sequences with seq.b[b] > 0, from the R tokens of K[b][h] and V[b][h]
+// that start at token seq.c[b] (the first chunk).
+hipError_t launch_skvq_perm(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,
+                            const PerSeq& seq, hipStream_t s);
+// SKVQ records seq.a[b] + x (x < seq.b[b]) of every (b, h) from tokens seq.c[b] + 32 x on.
+hipError_t launch_skvq_encode(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,
+                              const PerSeq& seq, int max_records, hipStream_t s);
 // Sinks of the sequences with seq.b[b] > 0: chosen among tokens 0 .. seq.b[b]-1 of K[b][h]
 // (the sequence's first quantized tokens), positions and fp16 K, V rows written (L.NS >= 1).
 hipError_t launch_sink_select(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,
@@ -47,7 +56,11 @@ hipError_t launch_sink_select(uint8_t* buf, const Layout& L, const void* K, cons
 hipError_t launch_decode(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q, float* ws,
                          void* out, const void* k_tok, const void* v_tok, hipStream_t s,
                          hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
-// The same for caches with sink tokens (L.NS > 0); launch_decode forwards to it.
+// The same for SKVQ caches and for KIVI caches with sink tokens (L.NS > 0); launch_decode
+// forwards to them.
+hipError_t launch_decode_skvq(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q, float* ws,
+                              void* out, const void* k_tok, const void* v_tok, hipStream_t s, hipEvent_t start,
+                              hipEvent_t stop);
 hipError_t launch_decode_sink(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q, float* ws,
                               void* out, const void* k_tok, const void* v_tok, hipStream_t s, hipEvent_t start,
                               hipEvent_t stop);

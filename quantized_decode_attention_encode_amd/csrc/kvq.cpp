@@ -31,6 +31,7 @@ struct kvq_cache {
   uint8_t* buf;
   size_t bytes;
   std::vector<int32_t> nq, nr;  // host mirror of the lengths, per sequence
+  std::vector<int32_t> nsp;     // SKVQ: sinks present per sequence (the first tokens)
   bool dev_ready;               // device lengths have been written at least once
   bool profiling;
   std::vector<hipEvent_t> ev;   // begin/end pairs
@@ -88,19 +89,37 @@ kvq_status check_config(const kvq_config* c) {
   if (c->max_tokens > (1 << 26)) return fail(KVQ_E_INVALID, "max_tokens above 2^26");
   if (c->n_sink < 0 || c->n_sink > kvq::kMaxSinks)
     return fail(KVQ_E_INVALID, "n_sink must be in [0, %d], got %d", kvq::kMaxSinks, c->n_sink);
+  if (c->method != KVQ_METHOD_KIVI && c->method != KVQ_METHOD_SKVQ)
+    return fail(KVQ_E_UNSUPPORTED, "method must be KVQ_METHOD_KIVI or KVQ_METHOD_SKVQ, got %d", c->method);
+  if (c->method == KVQ_METHOD_SKVQ) {
+    if ((c->skvq_reorder != 0 && c->skvq_reorder != 1) || (c->skvq_clip_search != 0 && c->skvq_clip_search != 1))
+      return fail(KVQ_E_INVALID, "skvq_reorder and skvq_clip_search must be 0 or 1");
+    if (!c->skvq_clip_search && !(c->skvq_clip_alpha > 0.0f && c->skvq_clip_alpha <= 1.0f))
+      return fail(KVQ_E_INVALID, "skvq_clip_alpha must be in (0, 1], got %g", double(c->skvq_clip_alpha));
+  }
   return ok();
 }
 
+bool is_skvq(const kvq_config& c) { return c.method == KVQ_METHOD_SKVQ; }
+
 Layout make_layout(const kvq_config* c) {
   Layout L;
-  L.init(c->batch, c->n_kv_heads, c->head_dim, c->key_bits, c->value_bits, c->residual, c->max_tokens, c->n_sink);
+  const bool sk = c->method == KVQ_METHOD_SKVQ;
+  // the fixed clip fraction in fp32 operations, or -1 for the search
+  const float clip = (sk && !c->skvq_clip_search) ? (1.0f - c->skvq_clip_alpha) * 0.5f : -1.0f;
+  L.init(c->batch, c->n_kv_heads, c->head_dim, c->key_bits, c->value_bits, c->residual, c->max_tokens, c->n_sink,
+         c->method, clip, sk ? c->skvq_reorder : 1);
   return L;
 }
 
 // Decode units of a sequence: its records, its window in 32-token pieces, and its sinks (one
-// unit, present once tokens are quantized).
-int units_of(int nq, int nr, int n_sink) {
-  return nq / kvq::kGroup + (nr + kvq::kGroup - 1) / kvq::kGroup + (n_sink > 0 && nq > 0 ? 1 : 0);
+// unit, present when any sink is: KIVI-Sink once tokens are quantized, SKVQ from the first token).
+int units_of(int nq, int nr, bool sinks) {
+  return nq / kvq::kGroup + (nr + kvq::kGroup - 1) / kvq::kGroup + (sinks ? 1 : 0);
+}
+
+bool has_sinks(const kvq_cache* c, int b) {
+  return c->cfg.n_sink > 0 && (is_skvq(c->cfg) ? c->nsp[b] > 0 : c->nq[b] > 0);
 }
 
 // Largest split count the automatic choice can produce.
@@ -155,7 +174,7 @@ kvq_status ensure_ready(kvq_cache* c, hipStream_t s) {
   if (!c->dev_ready) {
     PerSeq z;
     memset(&z, 0, sizeof z);
-    hipError_t e = kvq::launch_lengths_fill(c->buf, c->L, z, s);
+    hipError_t e = kvq::launch_lengths_fill(c->buf, c->L, z, s, 1);
     if (e != hipSuccess) return hip_fail(e, "zeroing lengths");
     c->dev_ready = true;
   }
@@ -181,8 +200,8 @@ kvq_status decode_enqueue(kvq_cache* c, const void* q, void* out, int32_t out_fp
   int max_units = 0;
   int64_t total_units = 0;
   for (int b = 0; b < cfg.batch; ++b) {
-    if (c->nq[b] + c->nr[b] + add == 0) return fail(KVQ_E_INVALID, "sequence %d is empty", b);
-    const int u = units_of(c->nq[b], c->nr[b] + add, cfg.n_sink);
+    if (c->nq[b] + c->nr[b] + c->nsp[b] + add == 0) return fail(KVQ_E_INVALID, "sequence %d is empty", b);
+    const int u = units_of(c->nq[b], c->nr[b] + add, has_sinks(c, b));
     max_units = std::max(max_units, u);
     total_units += int64_t(u) * cfg.n_kv_heads;
   }
@@ -284,6 +303,7 @@ kvq_status kvq_layout(const kvq_config* cfg, kvq_layout_info* out) {
   out->sink_pos_offset = L.sp_off;
   out->sink_k_offset = L.sk_off;
   out->sink_v_offset = L.sv_off;
+  out->perm_offset = L.pm_off;
   return ok();
 }
 
@@ -312,6 +332,7 @@ kvq_status kvq_cache_create(const kvq_config* cfg, void* dev_buf, size_t bytes, 
   c->bytes = bytes;
   c->nq.assign(cfg->batch, 0);
   c->nr.assign(cfg->batch, 0);
+  c->nsp.assign(cfg->batch, 0);
   c->dev_ready = false;
   c->profiling = false;
   c->ev_used = 0;
@@ -331,10 +352,11 @@ kvq_status kvq_reset(kvq_cache* c, void* stream) {
   if (st != KVQ_OK) return st;
   PerSeq z;
   memset(&z, 0, sizeof z);
-  hipError_t e = kvq::launch_lengths_fill(c->buf, c->L, z, static_cast<hipStream_t>(stream));
+  hipError_t e = kvq::launch_lengths_fill(c->buf, c->L, z, static_cast<hipStream_t>(stream), 1);
   if (e != hipSuccess) return hip_fail(e, "reset");
   std::fill(c->nq.begin(), c->nq.end(), 0);
   std::fill(c->nr.begin(), c->nr.end(), 0);
+  std::fill(c->nsp.begin(), c->nsp.end(), 0);
   c->dev_ready = true;
   return ok();
 }
@@ -352,6 +374,7 @@ kvq_status kvq_encode(kvq_cache* c, const void* K, const void* V, int64_t ld_tok
                       void* stream) {
   if (!c) return fail(KVQ_E_INVALID, "cache is NULL");
   if (!n_tok) return fail(KVQ_E_INVALID, "n_tok is NULL");
+  if (is_skvq(c->cfg)) return fail(KVQ_E_UNSUPPORTED, "kvq_encode does not apply to SKVQ caches: use kvq_prefill / kvq_append");
   int max_rec = 0, max_tok = 0;
   for (int b = 0; b < c->cfg.batch; ++b) {
     const int n = n_tok[b];
@@ -391,7 +414,7 @@ kvq_status kvq_encode(kvq_cache* c, const void* K, const void* V, int64_t ld_tok
   }
   e = kvq::launch_encode(c->buf, c->L, K, V, ld_tok, enc, max_rec, s);
   if (e != hipSuccess) return hip_fail(e, "encode launch");
-  e = kvq::launch_lengths_fill(c->buf, c->L, len, s);
+  e = kvq::launch_lengths_fill(c->buf, c->L, len, s, 0);
   if (e != hipSuccess) return hip_fail(e, "lengths launch");
   for (int b = 0; b < c->cfg.batch; ++b) c->nq[b] += n_tok[b];
   return ok();
@@ -421,23 +444,37 @@ kvq_status kvq_prefill(kvq_cache* c, const void* K, const void* V, int64_t ld_to
   if (!c) return fail(KVQ_E_INVALID, "cache is NULL");
   if (!seq_len) return fail(KVQ_E_INVALID, "seq_len is NULL");
   const int R = c->cfg.residual;
+  const bool sk = is_skvq(c->cfg);
   int max_rec = 0, max_S = 0;
   PerSeq enc, win, sel;
   memset(&enc, 0, sizeof enc);
   memset(&win, 0, sizeof win);
   memset(&sel, 0, sizeof sel);
+  std::vector<int32_t> nsp(c->cfg.batch, 0);
   for (int b = 0; b < c->cfg.batch; ++b) {
     const int S = seq_len[b];
     if (S < 0) return fail(KVQ_E_INVALID, "seq_len[%d] = %d is negative", b, S);
-    if (c->nq[b] || c->nr[b]) return fail(KVQ_E_INVALID, "sequence %d is not empty; prefill needs an empty cache", b);
-    if (S > c->cfg.max_tokens) return fail(KVQ_E_CAPACITY, "seq_len[%d] = %d exceeds max_tokens %d", b, S, c->cfg.max_tokens);
-    const int nr = S ? (S - 1) % R + 1 : 0;
-    const int nq = S - nr;
+    if (c->nq[b] || c->nr[b] || c->nsp[b])
+      return fail(KVQ_E_INVALID, "sequence %d is not empty; prefill needs an empty cache", b);
+    // SKVQ: the first n_sink tokens are the sinks and the window rule covers the rest
+    const int ns = sk ? std::min(S, c->cfg.n_sink) : 0;
+    if (S - ns > c->cfg.max_tokens)
+      return fail(KVQ_E_CAPACITY, "seq_len[%d] = %d exceeds max_tokens %d", b, S, c->cfg.max_tokens);
+    const int nr = S > ns ? (S - ns - 1) % R + 1 : 0;
+    const int nq = S - ns - nr;
+    nsp[b] = ns;
     enc.a[b] = 0;
     enc.b[b] = nq / kvq::kGroup;
+    enc.c[b] = ns;  // first quantized token
     win.a[b] = nq;
     win.b[b] = nr;
-    sel.b[b] = c->cfg.n_sink > 0 ? nq : 0;  // sinks among the quantized part
+    win.c[b] = ns + nq;  // first window token
+    if (sk) {
+      sel.b[b] = nq > 0 ? 1 : 0;  // permutations from the first chunk, tokens ns .. ns + R - 1
+      sel.c[b] = ns;
+    } else {
+      sel.b[b] = c->cfg.n_sink > 0 ? nq : 0;  // sinks among the quantized part
+    }
     max_rec = std::max(max_rec, nq / kvq::kGroup);
     max_S = std::max(max_S, S);
   }
@@ -448,7 +485,12 @@ kvq_status kvq_prefill(kvq_cache* c, const void* K, const void* V, int64_t ld_to
   hipStream_t s = static_cast<hipStream_t>(stream);
   kvq_status st = check_device();
   if (st != KVQ_OK) return st;
-  if (max_rec) {
+  if (max_rec && sk) {
+    hipError_t e = kvq::launch_skvq_perm(c->buf, c->L, K, V, ld_tok, sel, s);
+    if (e != hipSuccess) return hip_fail(e, "permutation launch");
+    e = kvq::launch_skvq_encode(c->buf, c->L, K, V, ld_tok, enc, max_rec, s);
+    if (e != hipSuccess) return hip_fail(e, "encode launch");
+  } else if (max_rec) {
     hipError_t e;
     if (c->cfg.n_sink > 0) {
       e = kvq::launch_sink_select(c->buf, c->L, K, V, ld_tok, sel, s);
@@ -463,6 +505,7 @@ kvq_status kvq_prefill(kvq_cache* c, const void* K, const void* V, int64_t ld_to
   for (int b = 0; b < c->cfg.batch; ++b) {
     c->nq[b] = win.a[b];
     c->nr[b] = win.b[b];
+    c->nsp[b] = nsp[b];
   }
   return ok();
 }
@@ -480,10 +523,15 @@ kvq_status kvq_append(kvq_cache* c, const void* k_tok, const void* v_tok, void* 
   for (int b = 0; b < c->cfg.batch; ++b) {
     len.a[b] = c->nq[b];
     len.b[b] = c->nr[b];
+    len.c[b] = c->nsp[b];
   }
   hipError_t e = kvq::launch_append(c->buf, c->L, k_tok, v_tok, len, s);
   if (e != hipSuccess) return hip_fail(e, "append launch");
   for (int b = 0; b < c->cfg.batch; ++b) {
+    if (is_skvq(c->cfg) && c->nsp[b] < c->cfg.n_sink) {  // the token became a sink
+      c->nsp[b] += 1;
+      continue;
+    }
     if (c->nr[b] == c->cfg.residual) {
       c->nq[b] += c->cfg.residual;
       c->nr[b] = 0;
@@ -513,6 +561,8 @@ kvq_status kvq_append_decode_attend(kvq_cache* c, const void* k_tok, const void*
     if (int64_t(c->nq[b]) + c->nr[b] + 1 > c->cfg.max_tokens)
       return fail(KVQ_E_CAPACITY, "sequence %d is full (%d tokens)", b, c->cfg.max_tokens);
     flush = flush || c->nr[b] == c->cfg.residual;
+    // an SKVQ token that becomes a sink is the append kernel's work too
+    flush = flush || (is_skvq(c->cfg) && c->nsp[b] < c->cfg.n_sink);
   }
   if (flush) {  // some window is full: the append kernel quantizes it, then a plain decode
     kvq_status st = kvq_append(c, k_tok, v_tok, stream);

@@ -9,8 +9,16 @@
 //   sink_pos int32 [B][H_kv][NS]                sink token positions, ascending (NS = n_sink)
 //   sink_k   fp16  [B][H_kv][NS][D]             the sinks' key and value rows, unquantized
 //   sink_v   fp16  [B][H_kv][NS][D]
+//   perm     uint8 [B][H_kv][2][D]              SKVQ only: channel permutations of K and V
 // Every region but sync starts on a 256-byte boundary (sync follows lengths directly). With
-// NS = 0 the three sink regions are empty and the buffer is the plain KIVI cache.
+// NS = 0 the three sink regions are empty and the buffer is the plain KIVI cache. A sink
+// position of -1 marks an empty slot: the sinks present are the leading non-negative entries.
+//
+// SKVQ-adapted caches ("Changelog" v0.30.0) use the same records with per-token key groups:
+// the key codes hold the permuted channels (channel c' of a quarter is permuted channel
+// Q*D/4 + c'), and the key params use the value-param layout [t/2][k][t%2], group k being
+// the permuted channels 32k .. 32k+31 of token t. Value codes and params hold permuted
+// channels too. Their sinks are the first NS tokens of the sequence.
 //
 // A record holds everything decode needs for 32 tokens, so one group streams from one
 // contiguous 4*D*(bk+bv+2)-byte block (3 KiB at D=128, 2/2 bits):
@@ -42,6 +50,7 @@ namespace kvq {
 constexpr int kGroup = 32;     // tokens per key group == channels per value group
 constexpr int kMaxBatch = 256;
 constexpr int kMaxSinks = 16;  // sink tokens per (sequence, KV head)
+constexpr int kMethodKivi = 0, kMethodSkvq = 1;
 
 KVQ_HD constexpr uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
@@ -59,11 +68,14 @@ KVQ_HD constexpr uint64_t rec_off_vparams(int D, int bk, int bv) {
 
 // Offsets of the regions of one cache buffer.
 struct Layout {
-  int B, Hkv, D, bk, bv, R, max_groups, NS;
-  uint64_t len_off, sync_off, rec_off, rec_bytes, wk_off, wv_off, sp_off, sk_off, sv_off, total;
+  int B, Hkv, D, bk, bv, R, max_groups, NS, method, reorder;
+  float clip;  // SKVQ: the fixed clip fraction (1 - alpha) / 2, or < 0 for the search
+  uint64_t len_off, sync_off, rec_off, rec_bytes, wk_off, wv_off, sp_off, sk_off, sv_off, pm_off, total;
 
-  KVQ_HD void init(int B_, int Hkv_, int D_, int bk_, int bv_, int R_, int max_tokens, int NS_) {
-    B = B_; Hkv = Hkv_; D = D_; bk = bk_; bv = bv_; R = R_; NS = NS_;
+  KVQ_HD void init(int B_, int Hkv_, int D_, int bk_, int bv_, int R_, int max_tokens, int NS_, int method_ = 0,
+                   float clip_ = -1.0f, int reorder_ = 1) {
+    B = B_; Hkv = Hkv_; D = D_; bk = bk_; bv = bv_; R = R_; NS = NS_; method = method_; clip = clip_;
+    reorder = reorder_;
     max_groups = max_tokens / kGroup;
     rec_bytes = record_bytes(D, bk, bv);
     len_off = 0;
@@ -76,7 +88,8 @@ struct Layout {
     sk_off = align256(sp_off + uint64_t(B) * Hkv * NS * sizeof(int32_t));
     const uint64_t sbytes = uint64_t(B) * Hkv * NS * D * 2;
     sv_off = align256(sk_off + sbytes);
-    total = align256(sv_off + sbytes);
+    pm_off = align256(sv_off + sbytes);
+    total = align256(pm_off + (method == kMethodSkvq ? uint64_t(B) * Hkv * 2 * D : 0));
   }
   // record j of (b, h)
   KVQ_HD uint64_t record(int b, int h, int j) const {
@@ -90,6 +103,8 @@ struct Layout {
   KVQ_HD uint64_t sink_pos(int b, int h) const { return sp_off + (uint64_t(b) * Hkv + h) * NS * 4; }
   KVQ_HD uint64_t sink_k(int b, int h) const { return sk_off + (uint64_t(b) * Hkv + h) * NS * D * 2; }
   KVQ_HD uint64_t sink_v(int b, int h) const { return sv_off + (uint64_t(b) * Hkv + h) * NS * D * 2; }
+  // SKVQ: permutation of K (D bytes) then of V: permuted channel j is channel perm[j]
+  KVQ_HD uint64_t perm(int b, int h) const { return pm_off + (uint64_t(b) * Hkv + h) * 2 * D; }
 };
 
 }  // namespace kvq

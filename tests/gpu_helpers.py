@@ -24,7 +24,7 @@ def say(*a):
 
 def cfg_dict(c):
     return {"B": c.batch, "Hkv": c.n_kv_heads, "D": c.head_dim, "bk": c.key_bits, "bv": c.value_bits,
-            "R": c.residual, "max_tokens": c.max_tokens, "NS": c.n_sink}
+            "R": c.residual, "max_tokens": c.max_tokens, "NS": c.n_sink, "method": c.method}
 
 
 def oracle_prefill(draw, R, pairs=None, n_sink=0):
@@ -51,9 +51,15 @@ def assert_state_equal(buf, c, seqs, what=""):
     for (b, h), s in seqs.items():
         got = kvq_unpack.unpack_sequence(buf, cd, b, h)
         assert (got["n_q"], got["n_r"]) == (s.n_q, s.n_r), f"{what} lengths of {(b, h)}"
-        for name, ref in (("kc", s.kc), ("vc", s.vc), ("ks", s.ks), ("kz", s.kz), ("vs", s.vs), ("vz", s.vz),
-                          ("wk", s.wk), ("wv", s.wv), ("sink_pos", s.sink_pos), ("sink_k", s.sink_k),
-                          ("sink_v", s.sink_v)):
+        fields = [("kc", s.kc), ("vc", s.vc), ("ks", s.ks), ("kz", s.kz), ("vs", s.vs), ("vz", s.vz),
+                  ("wk", s.wk), ("wv", s.wv), ("sink_k", s.sink_k), ("sink_v", s.sink_v)]
+        if hasattr(s, "sink_pos"):
+            fields.append(("sink_pos", s.sink_pos))
+        else:  # SKVQ: the first tokens, and the permutations once a chunk is quantized
+            fields.append(("sink_pos", np.arange(s.sink_k.shape[0], dtype=np.int64)))
+            if s.n_q:
+                fields += [("perm_k", np.asarray(s.perm_k, np.int64)), ("perm_v", np.asarray(s.perm_v, np.int64))]
+        for name, ref in fields:
             g = got[name]
             assert g.shape == ref.shape, f"{what} {name} shape {g.shape} vs {ref.shape} at {(b, h)}"
             if not np.array_equal(g.view(np.uint8), ref.view(np.uint8)):

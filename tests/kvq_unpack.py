@@ -4,7 +4,9 @@ Written from the layout description (records of 32 tokens; key codes as
 [P=t/2][quarter][t%2][words] with channel c' of the quarter at bit c'*bk, value codes as
 [channel][words] with token t at bit t*bv, key params [channel], value params
 [t/2][value group][t%2], fp16 (scale, zero) pairs with the scale in the low half; then the
-sink regions: positions int32 [B][H_kv][NS], key and value rows fp16 [B][H_kv][NS][D]). It
+sink regions: positions int32 [B][H_kv][NS], key and value rows fp16 [B][H_kv][NS][D], and for
+SKVQ caches the channel permutations uint8 [B][H_kv][2][D]; SKVQ records keep their key params
+in the value-param layout, one (scale, zero) per token and group of permuted channels). It
 shares no code with the HIP library; parity tests compare its output with the CPU oracle.
 """
 from __future__ import annotations
@@ -16,7 +18,7 @@ def align256(x: int) -> int:
     return (x + 255) // 256 * 256
 
 
-def offsets(B, Hkv, D, bk, bv, R, max_tokens, NS=0):
+def offsets(B, Hkv, D, bk, bv, R, max_tokens, NS=0, skvq=False):
     max_groups = max_tokens // 32
     rec = 4 * D * (bk + bv + 2)
     o = {"lengths": 0, "sync": B * Hkv * 2 * 4}
@@ -32,7 +34,8 @@ def offsets(B, Hkv, D, bk, bv, R, max_tokens, NS=0):
     o["sink_pos"] = align256(o["window_v"] + wbytes)
     o["sink_k"] = align256(o["sink_pos"] + B * Hkv * NS * 4)
     o["sink_v"] = align256(o["sink_k"] + B * Hkv * NS * D * 2)
-    o["total"] = align256(o["sink_v"] + B * Hkv * NS * D * 2)
+    o["perm"] = align256(o["sink_v"] + B * Hkv * NS * D * 2)
+    o["total"] = align256(o["perm"] + (B * Hkv * 2 * D if skvq else 0))
     o["max_groups"] = max_groups
     o["NS"] = NS
     return o
@@ -45,7 +48,7 @@ def _fields(u8: np.ndarray, nbits: int) -> np.ndarray:
     return (bits << np.arange(nbits, dtype=np.uint16)).sum(-1).astype(np.uint8)
 
 
-def unpack_records(recs: np.ndarray, D: int, bk: int, bv: int):
+def unpack_records(recs: np.ndarray, D: int, bk: int, bv: int, skvq: bool = False):
     """Records as bytes [n, record_bytes] -> logical arrays covering their 32*n tokens."""
     n = recs.shape[0]
     o_vc = 4 * D * bk
@@ -56,15 +59,20 @@ def unpack_records(recs: np.ndarray, D: int, bk: int, bv: int):
     kc = kc.transpose(0, 1, 3, 2, 4).reshape(n * 32, D)  # token 2P+tp, channel Q*D/4 + c
     # value codes [d][bytes of 32 tokens] -> [n, d, 32]
     vc = _fields(recs[:, o_vc:o_kp].reshape(n, D, 4 * bv), bv).transpose(0, 2, 1).reshape(n * 32, D)
-    kp = np.ascontiguousarray(recs[:, o_kp:o_vp]).view("<u2").reshape(n, D, 2)
-    ks = kp[..., 0].view(np.float16)
-    kz = kp[..., 1].view(np.float16)
     NKG = D // 32
+    if skvq:  # per-token key groups, value-param layout
+        kp = np.ascontiguousarray(recs[:, o_kp:o_vp]).view("<u2").reshape(n, 16, NKG, 2, 2)
+        kp = kp.transpose(0, 1, 3, 2, 4).reshape(n * 32, NKG, 2)
+        ks, kz = kp[..., 0].view(np.float16), kp[..., 1].view(np.float16)
+    else:
+        kp = np.ascontiguousarray(recs[:, o_kp:o_vp]).view("<u2").reshape(n, D, 2)
+        ks = kp[..., 0].view(np.float16).reshape(n, D)
+        kz = kp[..., 1].view(np.float16).reshape(n, D)
     vp = np.ascontiguousarray(recs[:, o_vp:o_vp + 4 * D]).view("<u2").reshape(n, 16, NKG, 2, 2)
     vp = vp.transpose(0, 1, 3, 2, 4).reshape(n * 32, NKG, 2)  # token 2P+tp
     vs = vp[..., 0].view(np.float16)
     vz = vp[..., 1].view(np.float16)
-    out = {"kc": kc, "ks": ks.reshape(n, D), "kz": kz.reshape(n, D), "vc": vc, "vs": vs, "vz": vz}
+    out = {"kc": kc, "ks": ks, "kz": kz, "vc": vc, "vs": vs, "vz": vz}
     return {k: np.ascontiguousarray(v) for k, v in out.items()}
 
 
@@ -85,21 +93,28 @@ def unpack_sequence(buf: np.ndarray, cfg: dict, b: int, h: int, n_q: int | None 
     """
     B, Hkv, D, bk, bv, R = (cfg[k] for k in ("B", "Hkv", "D", "bk", "bv", "R"))
     NS = cfg.get("NS", 0)
-    o = offsets(B, Hkv, D, bk, bv, R, cfg["max_tokens"], NS)
+    skvq = cfg.get("method", 0) == 1
+    o = offsets(B, Hkv, D, bk, bv, R, cfg["max_tokens"], NS, skvq)
     L = lengths(buf, B, Hkv)
     n_q = int(L[b, h, 0]) if n_q is None else n_q
     n_r = int(L[b, h, 1]) if n_r is None else n_r
     ng = n_q // 32
     start = o["records"] + (b * Hkv + h) * o["max_groups"] * o["record_bytes"]
     recs = buf[start:start + ng * o["record_bytes"]].reshape(ng, o["record_bytes"])
-    cat = unpack_records(recs, D, bk, bv)
+    cat = unpack_records(recs, D, bk, bv, skvq)
     w0 = ((b * Hkv + h) * R) * D * 2
     wk = buf[o["window_k"] + w0:o["window_k"] + w0 + R * D * 2].view(np.float16).reshape(R, D)[:n_r]
     wv = buf[o["window_v"] + w0:o["window_v"] + w0 + R * D * 2].view(np.float16).reshape(R, D)[:n_r]
     cat["wk"] = wk.copy()
     cat["wv"] = wv.copy()
-    ns = NS if n_q > 0 else 0
     i = b * Hkv + h
+    pos = buf[o["sink_pos"] + i * NS * 4:o["sink_pos"] + (i + 1) * NS * 4].view("<i4")
+    ns = 0  # the sinks present: the leading non-negative positions
+    while ns < NS and pos[ns] >= 0:
+        ns += 1
+    if skvq and n_q > 0:  # fixed by the first quantized chunk
+        pm = buf[o["perm"] + i * 2 * D:o["perm"] + (i + 1) * 2 * D]
+        cat["perm_k"], cat["perm_v"] = pm[:D].astype(np.int64), pm[D:].astype(np.int64)
     cat["sink_pos"] = buf[o["sink_pos"] + i * NS * 4:o["sink_pos"] + (i * NS + ns) * 4].view("<i4").astype(np.int64)
     cat["sink_k"] = buf[o["sink_k"] + i * NS * D * 2:o["sink_k"] + (i * NS + ns) * D * 2].view(np.float16).reshape(ns, D).copy()
     cat["sink_v"] = buf[o["sink_v"] + i * NS * D * 2:o["sink_v"] + (i * NS + ns) * D * 2].view(np.float16).reshape(ns, D).copy()

@@ -37,7 +37,8 @@ def declared_functions():
 
 def cfg(**kw):
     base = dict(batch=2, n_kv_heads=4, n_q_heads=8, head_dim=128, key_bits=2, value_bits=4, group=32,
-                residual=32, max_tokens=1024, n_sink=0)
+                residual=32, max_tokens=1024, n_sink=0, method=0, skvq_reorder=1, skvq_clip_search=1,
+                skvq_clip_alpha=1.0)
     base.update(kw)
     return Config(*(base[f] for f, _ in Config._fields_))
 
@@ -68,7 +69,7 @@ def test_probe_without_gpu_reports_absence():
     ("key_bits", 3, KVQ_E_UNSUPPORTED), ("value_bits", 1, KVQ_E_UNSUPPORTED), ("group", 64, KVQ_E_UNSUPPORTED),
     ("residual", 48, KVQ_E_INVALID), ("residual", 0, KVQ_E_INVALID), ("residual", 288, KVQ_E_INVALID),
     ("max_tokens", 1000, KVQ_E_INVALID), ("max_tokens", 0, KVQ_E_INVALID),
-    ("n_sink", -1, KVQ_E_INVALID), ("n_sink", 17, KVQ_E_INVALID),
+    ("n_sink", -1, KVQ_E_INVALID), ("n_sink", 17, KVQ_E_INVALID), ("method", 2, KVQ_E_UNSUPPORTED),
 ])
 def test_config_validation(field, value, status):
     c = cfg(**{field: value})
@@ -100,6 +101,31 @@ def test_layout_matches_independent_formula(D, bk, bv, R, B, H, NS):
         assert off % 256 == 0
     if NS == 0:  # no sink regions: the plain KIVI buffer
         assert info.sink_pos_offset == info.sink_k_offset == info.sink_v_offset == info.total_bytes
+
+
+@pytest.mark.parametrize("alpha,search,reorder,status", [
+    (1.0, 1, 1, KVQ_OK), (0.0, 0, 1, KVQ_E_INVALID), (1.5, 0, 1, KVQ_E_INVALID), (0.8, 0, 0, KVQ_OK),
+    (0.8, 2, 1, KVQ_E_INVALID), (0.8, 1, 3, KVQ_E_INVALID)])
+def test_skvq_config_validation_and_layout(alpha, search, reorder, status):
+    c = cfg(method=1, n_sink=5, residual=128, skvq_clip_alpha=alpha, skvq_clip_search=search, skvq_reorder=reorder)
+    assert lib.kvq_config_check(ctypes.byref(c)) == status
+    if status != KVQ_OK:
+        return
+    info = LayoutInfo()
+    assert lib.kvq_layout(ctypes.byref(c), ctypes.byref(info)) == KVQ_OK
+    o = kvq_unpack.offsets(2, 4, 128, 2, 4, 128, 1024, 5, skvq=True)
+    assert (info.perm_offset, info.total_bytes) == (o["perm"], o["total"])
+    assert info.total_bytes - info.perm_offset >= 2 * 4 * 2 * 128
+
+
+def test_skvq_cache_rejects_encode():
+    c = cfg(method=1, n_sink=5, residual=128)
+    cache = ctypes.c_void_p()
+    buf = ctypes.c_void_p(FAKE)
+    assert lib.kvq_cache_create(ctypes.byref(c), buf, lib.kvq_cache_bytes(ctypes.byref(c)), ctypes.byref(cache)) == KVQ_OK
+    n_tok = (ctypes.c_int32 * 2)(32, 32)
+    assert lib.kvq_encode(cache, buf, buf, 64, n_tok, None) == KVQ_E_UNSUPPORTED
+    lib.kvq_cache_destroy(cache)
 
 
 def test_record_is_three_kib_at_the_headline_shape():
