@@ -20,9 +20,12 @@ timed on a bounded sample of the same workload.
 
 With --n-sink N the caches keep N sink tokens per (sequence, KV head) in fp16 (KIVI-Sink,
 "Changelog" v0.9.0): the prefill then also chooses them, and every decode attends them as one
-more fp16 unit and skips their quantized slots.
+more fp16 unit and skips their quantized slots. With --method skvq the caches are
+SKVQ-adapted ("Changelog" v0.30.0: per-token groups of range-sorted channels, per-group clip
+search, the first --n-sink tokens in fp16; window --window, the pages' defaults 128 and 5).
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long] [--n-sink 0] [--no-cpu-baseline]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long] [--n-sink 0]
+                  [--method kivi|skvq] [--window R] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -64,12 +67,12 @@ def algorithmic_encode_bytes(wl, n_q_tokens, n_sink=0):
                for nq in n_q_tokens) * wl.n_kv_heads
 
 
-def cpu_baseline(wl, draw, budget_s=12.0, n_sink=0):
+def cpu_baseline(wl, draw, budget_s=12.0, n_sink=0, method="kivi", window=32):
     """The oracle's decode (reconstruct K_hat/V_hat, fp64 softmax attention) on a sample of the
     KV heads of sequence 0, scaled by tokens to the whole step (every sequence, head and layer)."""
     import numpy as np  # noqa: F401
 
-    from oracle import kivi
+    from oracle import kivi, skvq
 
     try:
         from threadpoolctl import threadpool_info
@@ -84,7 +87,10 @@ def cpu_baseline(wl, draw, budget_s=12.0, n_sink=0):
     G = wl.n_q_heads // H
     S0 = draw.seq_lens[0]
     for h in range(H):
-        s = kivi.KiviSequence(wl.head_dim, wl.key_bits, wl.value_bits, 32, wl.residual, n_sink)
+        if method == "skvq":
+            s = skvq.SkvqSequence(wl.head_dim, wl.key_bits, wl.value_bits, 32, window, n_sink)
+        else:
+            s = kivi.KiviSequence(wl.head_dim, wl.key_bits, wl.value_bits, 32, window, n_sink)
         t0 = time.perf_counter()
         s.prefill(draw.K[0][h], draw.V[0][h])
         t1 = time.perf_counter()
@@ -130,8 +136,14 @@ def main():
     ap.add_argument("--n-split", type=int, default=0, help="splits per sequence (0 = the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--settle-s", type=float, default=0.5, help="seconds of attend-only calls before the warmup")
-    ap.add_argument("--n-sink", type=int, default=0, help="sink tokens per (sequence, KV head), KIVI-Sink (0 = KIVI)")
+    ap.add_argument("--n-sink", type=int, default=None,
+                    help="sink tokens per (sequence, KV head): KIVI-Sink by key norm (default 0 = KIVI), SKVQ the first "
+                         "tokens (default 5)")
+    ap.add_argument("--method", default="kivi", choices=("kivi", "skvq"))
+    ap.add_argument("--window", type=int, default=None, help="fp16 window (default: the workload's, 128 for skvq)")
     args = ap.parse_args()
+    if args.n_sink is None:
+        args.n_sink = 5 if args.method == "skvq" else 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this path shards by "
               "(sequence, KV head) with no exchange, so N GPUs run N independent copies.", file=sys.stderr)
@@ -148,6 +160,7 @@ def main():
         sys.exit(1)
     dev = "cuda"
     wl = workloads.WORKLOADS[args.workload]
+    R = args.window or (128 if args.method == "skvq" else wl.residual)
     # Single-layer workloads rotate over `replicas` copies of one cache (one cache per step);
     # the multi-layer workload keeps one cache per layer and a step visits every layer.
     multi = wl.layers > 1
@@ -160,9 +173,9 @@ def main():
     # events themselves lengthen a step, so that pass is not the step time)
     n_steps_total = args.warmup + 3 * args.steps
     per_cache = n_steps_total if multi else (n_steps_total + n_caches - 1) // n_caches
-    cap = (max(lens) + per_cache + 64 + 31) // 32 * 32
+    cap = (max(lens) + per_cache + R + 64 + 31) // 32 * 32
     cfg = make_config(wl.batch, wl.n_kv_heads, wl.n_q_heads, wl.head_dim, wl.key_bits, wl.value_bits, 32,
-                      wl.residual, cap, n_sink=args.n_sink)
+                      R, cap, n_sink=args.n_sink, method=args.method)
     Kt, Vt = torch.from_numpy(K).to(dev), torch.from_numpy(V).to(dev)
     del K, V
     stream = torch.cuda.current_stream()
@@ -201,7 +214,7 @@ def main():
         torch.cuda.synchronize()
         enc_ms.append(e0.elapsed_time(e1))
     enc_t = statistics.median(enc_ms) / 1e3
-    n_q0 = [s - ((s - 1) % wl.residual + 1) for s in lens]
+    n_q0 = list(caches[0].lengths()[0])
     enc_tokens_per_s = sum(lens) / enc_t
     enc_gbs = algorithmic_encode_bytes(wl, n_q0, args.n_sink) / enc_t / 1e9
 
@@ -273,8 +286,8 @@ def main():
         for r in visits(i):
             nq, nr = lens_now[r]
             for b in range(wl.batch):
-                if nr[b] == wl.residual:
-                    nq[b] += wl.residual
+                if nr[b] == R:
+                    nq[b] += R
                     nr[b] = 0
                 nr[b] += 1
             if first <= i < last:
@@ -308,7 +321,8 @@ def main():
 
     traffic = None
     csrc = os.path.join(ROOT, "quantized_decode_attention_encode_amd", "csrc")
-    if args.workload == MEASURED_TRAFFIC["workload"] and args.n_split == 0 and args.n_sink == 0:
+    if (args.workload == MEASURED_TRAFFIC["workload"] and args.n_split == 0 and args.n_sink == 0
+            and args.method == "kivi" and R == wl.residual):
         import hashlib
 
         h = hashlib.sha256()
@@ -339,6 +353,8 @@ def main():
             "caches": f"{n_caches} layer caches" if multi else f"{n_caches} replicas of one cache, one per step",
             "codes": f"{wl.key_bits}-bit keys / {wl.value_bits}-bit values, fp16 (scale, zero), fp32 softmax",
             "sinks": args.n_sink,
+            "method": args.method,
+            "window": R,
         },
         "roofline": {
             "bound": "hbm",
@@ -366,7 +382,7 @@ def main():
         result["encode_all_layers_us"] = round(enc_t * 1e6 * wl.layers, 1)
         result["decode_launches_per_step"] = wl.layers
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, draw, n_sink=args.n_sink)
+        result["cpu_baseline"] = cpu_baseline(wl, draw, n_sink=args.n_sink, method=args.method, window=R)
     print(json.dumps(result), flush=True)
 
 

@@ -431,8 +431,9 @@ __device__ __forceinline__ void process_record(const RecordRegs<D, BK, BV>& cur,
 // Up to 32 fp16 window tokens (tokens tbase .. tbase + nvalid - 1 of the window).
 // Token tnew of the unit (when 0 <= tnew < nvalid) is the one this launch appends: its rows
 // come from kn / vn instead of the window.
-// With KT the query and the accumulators run in permuted channel order: key and value rows
-// (stored in channel order) are read through the permutations pk, pv.
+// With KT the query and the accumulators run in permuted channel order, like the stored window
+// and sink rows; only the token this launch appends (kn, vn, in channel order) is read through
+// the permutations pk, pv.
 template <int D, int G, bool KT = false>
 __device__ __forceinline__ void process_window(const __half* __restrict__ wk, const __half* __restrict__ wv, int nvalid,
                                                int tnew, const __half* kn, const __half* vn,
@@ -455,20 +456,18 @@ __device__ __forceinline__ void process_window(const __half* __restrict__ wk, co
   const uint32_t* k0p = reinterpret_cast<const uint32_t*>((t0c == tnew ? kn : wk + t0c * D) + Q * DQ);
   const uint32_t* k1p = reinterpret_cast<const uint32_t*>((t1c == tnew ? kn : wk + t1c * D) + Q * DQ);
   uint32_t k0w[DQ / 2], k1w[DQ / 2];
-  if constexpr (KT) {
-    const uint16_t* r0 = reinterpret_cast<const uint16_t*>(t0c == tnew ? kn : wk + t0c * D);
-    const uint16_t* r1 = reinterpret_cast<const uint16_t*>(t1c == tnew ? kn : wk + t1c * D);
+#pragma unroll
+  for (int c = 0; c < DQ / 2; ++c) {
+    k0w[c] = k0p[c];
+    k1w[c] = k1p[c];
+  }
+  if (KT && (t0c == tnew || t1c == tnew)) {  // the appended token, gathered into permuted order
+    const uint16_t* rn = reinterpret_cast<const uint16_t*>(kn);
 #pragma unroll
     for (int c = 0; c < DQ / 2; ++c) {
-      const int ja = pk[Q * DQ + 2 * c], jb = pk[Q * DQ + 2 * c + 1];
-      k0w[c] = uint32_t(r0[ja]) | (uint32_t(r0[jb]) << 16);
-      k1w[c] = uint32_t(r1[ja]) | (uint32_t(r1[jb]) << 16);
-    }
-  } else {
-#pragma unroll
-    for (int c = 0; c < DQ / 2; ++c) {
-      k0w[c] = k0p[c];
-      k1w[c] = k1p[c];
+      const uint32_t w = uint32_t(rn[pk[Q * DQ + 2 * c]]) | (uint32_t(rn[pk[Q * DQ + 2 * c + 1]]) << 16);
+      if (t0c == tnew) k0w[c] = w;
+      if (t1c == tnew) k1w[c] = w;
     }
   }
 #pragma unroll
@@ -498,7 +497,7 @@ __device__ __forceinline__ void process_window(const __half* __restrict__ wk, co
     for (int t = 0; t < nvalid; ++t) {
       const float a = W.pw[i][t];
       const __half* vrow = t == tnew ? vn : wv + t * D;
-      if constexpr (KT) {
+      if (KT && t == tnew) {  // wave-uniform
 #pragma unroll
         for (int e = 0; e < E; ++e)
           st.acc[i][e] = __builtin_fmaf(a, __half2float(vrow[pv[lane * E + e]]), st.acc[i][e]);
@@ -758,8 +757,9 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
       __half* dv = reinterpret_cast<__half*>(bufw + L.wv_off + L.window(b, h)) + nr_old * D;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        dk[lane * E + e] = kn[lane * E + e];
-        dv[lane * E + e] = vn[lane * E + e];
+        const int c = lane * E + e;
+        dk[c] = kn[KT ? pk[c] : c];
+        dv[c] = vn[KT ? pv[c] : c];
       }
     }
   }

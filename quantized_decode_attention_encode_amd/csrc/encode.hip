@@ -406,7 +406,8 @@ __device__ __forceinline__ void range_permutation(const __half* __restrict__ row
 }
 
 // Quantize 32 tokens (rows ks[0..31], vs[0..31], row stride D) into the SKVQ record at
-// rec_out; perm_k / perm_v are the sequence's permutations (global). One wave.
+// rec_out; perm_k / perm_v are the sequence's permutations (global), or null when the rows
+// are stored permuted already (a window flushed after the first chunk). One wave.
 template <int D, int BK, int BV>
 __device__ __forceinline__ void skvq_encode_record(const __half* __restrict__ ks, const __half* __restrict__ vs,
                                                    const uint8_t* __restrict__ perm_k,
@@ -428,8 +429,8 @@ __device__ __forceinline__ void skvq_encode_record(const __half* __restrict__ ks
     *reinterpret_cast<uint4*>(&lds.tile[1][t][8 * c]) = reinterpret_cast<const uint4*>(vs + t * D)[c];
   }
   for (int i = lane; i < D; i += 64) {
-    lds.perm[0][i] = perm_k[i];
-    lds.perm[1][i] = perm_v[i];
+    lds.perm[0][i] = perm_k ? perm_k[i] : uint8_t(i);
+    lds.perm[1][i] = perm_v ? perm_v[i] : uint8_t(i);
   }
   __syncthreads();
   for (int p = lane; p < PAIRS; p += 64) {
@@ -805,13 +806,37 @@ __global__ __launch_bounds__(64) void append_kernel(uint8_t* __restrict__ buf, L
         __threadfence();  // the permutations are read back just below
       }
       const int j0 = nq / kGroup;
+      // the first chunk's rows are in channel order; later windows are stored permuted
+      const uint8_t* gk = nq == 0 ? pm : nullptr;
+      const uint8_t* gv = nq == 0 ? pm + D : nullptr;
       for (int m = 0; m < L.R / kGroup; ++m)
         if (j0 + m < L.max_groups)
-          skvq_encode_record<D, BK, BV>(wk + m * kGroup * D, wv + m * kGroup * D, pm, pm + D, clip_candidates(L),
+          skvq_encode_record<D, BK, BV>(wk + m * kGroup * D, wv + m * kGroup * D, gk, gv, clip_candidates(L),
                                         L.clip, reinterpret_cast<uint32_t*>(buf + L.record(b, h, j0 + m)), slds);
+      if (nq == 0 && L.NS > 0) {  // the sinks' rows take the permuted order too
+        __half* sk = reinterpret_cast<__half*>(buf + L.sink_k(b, h));
+        __half* sv = reinterpret_cast<__half*>(buf + L.sink_v(b, h));
+        for (int i = lane; i < L.NS * D; i += 64) {
+          slds.tile[0][i / D][i % D] = sk[i];
+          slds.tile[1][i / D][i % D] = sv[i];
+        }
+        __syncthreads();
+        for (int i = lane; i < L.NS * D; i += 64) {
+          sk[i] = slds.tile[0][i / D][pm[i % D]];
+          sv[i] = slds.tile[1][i / D][pm[D + i % D]];
+        }
+      }
       nq += L.R;
       nr = 0;
       __syncthreads();
+    }
+    if (nq > 0) {  // the token in permuted channel order
+      const uint8_t* pm = buf + L.perm(b, h);
+#pragma unroll
+      for (int e = 0; e < HPL; ++e) {
+        kt[e] = k_tok[src + pm[lane * HPL + e]];
+        vt[e] = v_tok[src + pm[D + lane * HPL + e]];
+      }
     }
   } else if (nr >= L.R) {  // uniform over the workgroup
     const int j0 = nq / kGroup;
@@ -857,6 +882,11 @@ __global__ __launch_bounds__(64) void window_fill_kernel(uint8_t* __restrict__ b
   __half* wv = reinterpret_cast<__half*>(buf + L.wv_off + L.window(b, h));
   const int64_t row0 = ((int64_t(b) * L.Hkv + h) * ld_tok + t0) * D;
   constexpr int HPL = D / 64;
+  // SKVQ rows are stored in permuted channel order once the sequence has a permutation
+  // (its first chunk is quantized): slot c of a key row holds channel pk[c]
+  const bool permuted = L.method == kMethodSkvq && nq > 0;
+  const uint8_t* pk = buf + L.perm(b, h);
+  const uint8_t* pv = pk + D;
   if (L.NS > 0) {
     int32_t* sp = reinterpret_cast<int32_t*>(buf + L.sink_pos(b, h));
     if (L.method == kMethodSkvq) {
@@ -866,8 +896,9 @@ __global__ __launch_bounds__(64) void window_fill_kernel(uint8_t* __restrict__ b
       __half* sv = reinterpret_cast<__half*>(buf + L.sink_v(b, h));
       for (int t = 0; t < ns; ++t)
         for (int e = 0; e < HPL; ++e) {
-          sk[t * D + lane * HPL + e] = K[s0 + int64_t(t) * D + lane * HPL + e];
-          sv[t * D + lane * HPL + e] = V[s0 + int64_t(t) * D + lane * HPL + e];
+          const int c = lane * HPL + e;
+          sk[t * D + c] = K[s0 + int64_t(t) * D + (permuted ? pk[c] : c)];
+          sv[t * D + c] = V[s0 + int64_t(t) * D + (permuted ? pv[c] : c)];
         }
       if (lane < L.NS) sp[lane] = lane < ns ? lane : -1;
     } else if (nq == 0 && lane < L.NS) {
@@ -876,8 +907,9 @@ __global__ __launch_bounds__(64) void window_fill_kernel(uint8_t* __restrict__ b
   }
   for (int t = 0; t < nr; ++t)
     for (int e = 0; e < HPL; ++e) {
-      wk[t * D + lane * HPL + e] = K[row0 + int64_t(t) * D + lane * HPL + e];
-      wv[t * D + lane * HPL + e] = V[row0 + int64_t(t) * D + lane * HPL + e];
+      const int c = lane * HPL + e;
+      wk[t * D + c] = K[row0 + int64_t(t) * D + (permuted ? pk[c] : c)];
+      wv[t * D + c] = V[row0 + int64_t(t) * D + (permuted ? pv[c] : c)];
     }
   if (lane == 0) {
     int32_t* len = reinterpret_cast<int32_t*>(buf + L.lengths(b, h));

@@ -18,7 +18,9 @@
 // the key codes hold the permuted channels (channel c' of a quarter is permuted channel
 // Q*D/4 + c'), and the key params use the value-param layout [t/2][k][t%2], group k being
 // the permuted channels 32k .. 32k+31 of token t. Value codes and params hold permuted
-// channels too. Their sinks are the first NS tokens of the sequence.
+// channels too. Their sinks are the first NS tokens of the sequence. Once a sequence has
+// quantized tokens (and so its permutations), its window and sink rows are stored permuted as
+// well: slot c of a key row holds channel perm_k[c], of a value row channel perm_v[c].
 //
 // A record holds everything decode needs for 32 tokens, so one group streams from one
 // contiguous 4*D*(bk+bv+2)-byte block (3 KiB at D=128, 2/2 bits):

@@ -6,7 +6,8 @@ Written from the layout description (records of 32 tokens; key codes as
 [t/2][value group][t%2], fp16 (scale, zero) pairs with the scale in the low half; then the
 sink regions: positions int32 [B][H_kv][NS], key and value rows fp16 [B][H_kv][NS][D], and for
 SKVQ caches the channel permutations uint8 [B][H_kv][2][D]; SKVQ records keep their key params
-in the value-param layout, one (scale, zero) per token and group of permuted channels). It
+in the value-param layout, one (scale, zero) per token and group of permuted channels, and their
+window and sink rows are stored permuted once the permutations exist). It
 shares no code with the HIP library; parity tests compare its output with the CPU oracle.
 """
 from __future__ import annotations
@@ -118,5 +119,10 @@ def unpack_sequence(buf: np.ndarray, cfg: dict, b: int, h: int, n_q: int | None 
     cat["sink_pos"] = buf[o["sink_pos"] + i * NS * 4:o["sink_pos"] + (i * NS + ns) * 4].view("<i4").astype(np.int64)
     cat["sink_k"] = buf[o["sink_k"] + i * NS * D * 2:o["sink_k"] + (i * NS + ns) * D * 2].view(np.float16).reshape(ns, D).copy()
     cat["sink_v"] = buf[o["sink_v"] + i * NS * D * 2:o["sink_v"] + (i * NS + ns) * D * 2].view(np.float16).reshape(ns, D).copy()
+    if "perm_k" in cat:  # SKVQ rows are stored permuted once the permutations exist: back to channel order
+        for key, pm_ in (("wk", cat["perm_k"]), ("sink_k", cat["perm_k"]), ("wv", cat["perm_v"]), ("sink_v", cat["perm_v"])):
+            nat = np.empty_like(cat[key])
+            nat[:, pm_] = cat[key]
+            cat[key] = nat
     cat["n_q"], cat["n_r"] = n_q, n_r
     return cat
