@@ -492,23 +492,34 @@ __device__ __forceinline__ void process_window(const __half* __restrict__ wk, co
     if (Q == 0) *reinterpret_cast<float2*>(&W.pw[i][2 * P]) = make_float2(p0 * kVScale, p1 * kVScale);
   }
   wave_sync();
+  // values: 8 rows in flight at a time, each loaded once for all G heads. Rows past nvalid are
+  // clamped to the last valid one; their weights are 0 (their scores were -inf).
+  constexpr int VB = 8;
+  for (int tb = 0; tb < nvalid; tb += VB) {
+    float v[VB][E];
 #pragma unroll
-  for (int i = 0; i < G; ++i) {
-    for (int t = 0; t < nvalid; ++t) {
-      const float a = W.pw[i][t];
+    for (int k = 0; k < VB; ++k) {
+      const int t = min(tb + k, nvalid - 1);
       const __half* vrow = t == tnew ? vn : wv + t * D;
-      if (KT && t == tnew) {  // wave-uniform
+      if (KT && t == tnew) {  // the appended token, gathered into permuted order
 #pragma unroll
-        for (int e = 0; e < E; ++e)
-          st.acc[i][e] = __builtin_fmaf(a, __half2float(vrow[pv[lane * E + e]]), st.acc[i][e]);
+        for (int e = 0; e < E; ++e) v[k][e] = __half2float(vrow[pv[lane * E + e]]);
       } else if constexpr (E == 2) {
         const uint32_t vw = reinterpret_cast<const uint32_t*>(vrow)[lane];
-        st.acc[i][0] = __builtin_fmaf(a, lo_f(vw), st.acc[i][0]);
-        st.acc[i][1] = __builtin_fmaf(a, hi_f(vw), st.acc[i][1]);
+        v[k][0] = lo_f(vw);
+        v[k][1] = hi_f(vw);
       } else {
-        st.acc[i][0] = __builtin_fmaf(a, __half2float(vrow[lane]), st.acc[i][0]);
+        v[k][0] = __half2float(vrow[lane]);
       }
     }
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+#pragma unroll
+      for (int k = 0; k < VB; ++k) {
+        const float a = W.pw[i][tb + k];
+#pragma unroll
+        for (int e = 0; e < E; ++e) st.acc[i][e] = __builtin_fmaf(a, v[k][e], st.acc[i][e]);
+      }
   }
   wave_sync();
 }
