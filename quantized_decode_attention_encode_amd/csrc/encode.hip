@@ -346,7 +346,8 @@ __device__ __forceinline__ void clip_quant_group(const float (&x)[kGroup], int n
   }
   lo = lo + 0.0f;
   hi = hi + 0.0f;
-  float best_err = 0.0f;
+  // the search keeps the error only; the winner's codes are formed once afterwards
+  float best_err = 0.0f, bs = 0.0f, bz = 0.0f;
   for (int k = 0; k < ncand; ++k) {
     const float c = ncand > 1 ? float(k) / 40.0f : cfix;
     const float d = (hi - lo) * c;
@@ -355,9 +356,6 @@ __device__ __forceinline__ void clip_quant_group(const float (&x)[kGroup], int n
     const __half z16 = __float2half_rn(lo_c);
     const float s = __half2float(s16), z = __half2float(z16);
     const float inv = (s != 0.0f) ? 1.0f / s : 0.0f;
-    uint32_t cw[B];
-#pragma unroll
-    for (int w = 0; w < B; ++w) cw[w] = 0;
     float err = 0.0f;
 #pragma unroll
     for (int i = 0; i < kGroup; ++i) {
@@ -365,14 +363,21 @@ __device__ __forceinline__ void clip_quant_group(const float (&x)[kGroup], int n
       const float xh = cf * s + z;  // no contraction in this file: a multiply, then an add
       const float diff = x[i] - xh;
       err = err + diff * diff;
-      cw[(i * B) / 32] |= uint32_t(cf) << ((i * B) % 32);
     }
     if (k == 0 || err < best_err) {
       best_err = err;
-#pragma unroll
-      for (int w = 0; w < B; ++w) best_codes[w] = cw[w];
+      bs = s;
+      bz = z;
       best_params = uint32_t(__half_as_ushort(s16)) | (uint32_t(__half_as_ushort(z16)) << 16);
     }
+  }
+  const float binv = (bs != 0.0f) ? 1.0f / bs : 0.0f;
+#pragma unroll
+  for (int w = 0; w < B; ++w) best_codes[w] = 0;
+#pragma unroll
+  for (int i = 0; i < kGroup; ++i) {
+    const float cf = fminf(fmaxf(rintf((x[i] - bz) * binv), 0.0f), L);
+    best_codes[(i * B) / 32] |= uint32_t(cf) << ((i * B) % 32);
   }
 }
 
@@ -905,12 +910,34 @@ __global__ __launch_bounds__(64) void window_fill_kernel(uint8_t* __restrict__ b
       sp[lane] = -1;
     }
   }
-  for (int t = 0; t < nr; ++t)
-    for (int e = 0; e < HPL; ++e) {
-      const int c = lane * HPL + e;
-      wk[t * D + c] = K[row0 + int64_t(t) * D + (permuted ? pk[c] : c)];
-      wv[t * D + c] = V[row0 + int64_t(t) * D + (permuted ? pv[c] : c)];
+  int ck[HPL], cv[HPL];  // source channel of each of the lane's slots
+#pragma unroll
+  for (int e = 0; e < HPL; ++e) {
+    const int c = lane * HPL + e;
+    ck[e] = permuted ? pk[c] : c;
+    cv[e] = permuted ? pv[c] : c;
+  }
+  constexpr int TB = 8;  // rows in flight
+  for (int t0 = 0; t0 < nr; t0 += TB) {
+    __half kx[TB][HPL], vx[TB][HPL];
+#pragma unroll
+    for (int k = 0; k < TB; ++k) {
+      const int64_t r = row0 + int64_t(min(t0 + k, nr - 1)) * D;
+#pragma unroll
+      for (int e = 0; e < HPL; ++e) {
+        kx[k][e] = K[r + ck[e]];
+        vx[k][e] = V[r + cv[e]];
+      }
     }
+#pragma unroll
+    for (int k = 0; k < TB; ++k)
+      if (t0 + k < nr)
+#pragma unroll
+        for (int e = 0; e < HPL; ++e) {
+          wk[(t0 + k) * D + lane * HPL + e] = kx[k][e];
+          wv[(t0 + k) * D + lane * HPL + e] = vx[k][e];
+        }
+  }
   if (lane == 0) {
     int32_t* len = reinterpret_cast<int32_t*>(buf + L.lengths(b, h));
     len[0] = nq;
