@@ -482,12 +482,14 @@ __device__ __forceinline__ void skvq_encode_record(const __half* __restrict__ ks
 
 __device__ __forceinline__ int clip_candidates(const Layout& L) { return L.clip < 0.0f ? kClipCandidates : 1; }
 
-// SKVQ prefill: record seq.a[b] + blockIdx.x of (b, h) from tokens seq.c[b] + 32 blockIdx.x.
+// SKVQ records: record seq.a[b] + blockIdx.x of (b, h) from tokens seq.c[b] + 32 blockIdx.x of
+// K, V [B][H_kv][ld_tok][D]: the caller's tokens at a prefill (channel order), or the cache's
+// windows at a flush (rows_permuted: stored in permuted order already).
 template <int D, int BK, int BV>
 __global__ __launch_bounds__(64) void skvq_encode_kernel(uint8_t* __restrict__ buf, Layout L,
                                                          const __half* __restrict__ K,
                                                          const __half* __restrict__ V, int64_t ld_tok,
-                                                         PerSeq seq) {
+                                                         PerSeq seq, int rows_permuted) {
   __shared__ SkvqLds<D, BK, BV> lds;
   const int jl = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   if (jl >= seq.b[b]) return;
@@ -495,8 +497,39 @@ __global__ __launch_bounds__(64) void skvq_encode_kernel(uint8_t* __restrict__ b
   if (j >= L.max_groups) return;
   const int64_t row0 = ((int64_t(b) * L.Hkv + h) * ld_tok + seq.c[b] + int64_t(kGroup) * jl) * D;
   const uint8_t* pm = buf + L.perm(b, h);
-  skvq_encode_record<D, BK, BV>(K + row0, V + row0, pm, pm + D, clip_candidates(L), L.clip,
-                                reinterpret_cast<uint32_t*>(buf + L.record(b, h, j)), lds);
+  skvq_encode_record<D, BK, BV>(K + row0, V + row0, rows_permuted ? nullptr : pm, rows_permuted ? nullptr : pm + D,
+                                clip_candidates(L), L.clip, reinterpret_cast<uint32_t*>(buf + L.record(b, h, j)),
+                                lds);
+}
+
+// SKVQ first flush (seq.b[b] > 0): the window's R rows and the sink rows of (b, h), in channel
+// order so far, are rewritten in permuted order (the permutations have just been computed).
+template <int D>
+__global__ __launch_bounds__(64) void skvq_permute_rows_kernel(uint8_t* __restrict__ buf, Layout L, PerSeq seq) {
+  constexpr int RB = 8;  // rows per pass
+  __shared__ __half rows[2][RB][D];
+  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  if (seq.b[b] <= 0) return;
+  const uint8_t* pk = buf + L.perm(b, h);
+  const uint8_t* pv = pk + D;
+  for (int region = 0; region < 2; ++region) {
+    const int n = region == 0 ? L.R : L.NS;
+    __half* rk = reinterpret_cast<__half*>(buf + (region == 0 ? L.wk_off + L.window(b, h) : L.sink_k(b, h)));
+    __half* rv = reinterpret_cast<__half*>(buf + (region == 0 ? L.wv_off + L.window(b, h) : L.sink_v(b, h)));
+    for (int r0 = 0; r0 < n; r0 += RB) {
+      const int nb = min(RB, n - r0);
+      for (int i = lane; i < nb * D; i += 64) {
+        rows[0][i / D][i % D] = rk[r0 * D + i];
+        rows[1][i / D][i % D] = rv[r0 * D + i];
+      }
+      __syncthreads();
+      for (int i = lane; i < nb * D; i += 64) {
+        rk[r0 * D + i] = rows[0][i / D][pk[i % D]];
+        rv[r0 * D + i] = rows[1][i / D][pv[i % D]];
+      }
+      __syncthreads();
+    }
+  }
 }
 
 // SKVQ permutations from the first chunk: R tokens from token seq.c[b] (seq.b[b] > 0 only).
@@ -769,14 +802,13 @@ __device__ void select_window_sinks(uint8_t* __restrict__ buf, const Layout& L, 
 // sequence's lengths before the append (the host's mirror of the device lengths), so the
 // token's loads and the flush decision wait for no device read.
 // SKVQ caches: the first NS tokens of a sequence (seq.c = sinks present) go to the sink
-// region; after them the window rule holds, and the first flush also fixes the permutations.
+// region; after them the window rule holds. Their full windows are flushed by the host's
+// launches before this kernel (seq then holds the lengths after the flush).
 template <int D, int BK, int BV>
 __global__ __launch_bounds__(64) void append_kernel(uint8_t* __restrict__ buf, Layout L,
                                                     const __half* __restrict__ k_tok,
                                                     const __half* __restrict__ v_tok, PerSeq seq) {
   __shared__ EncodeLds<D, BK, BV> lds;
-  __shared__ SkvqLds<D, BK, BV> slds;
-  __shared__ float rng[D];
   const int h = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x;
   constexpr int HPL = D / 64;  // halves per lane
@@ -802,38 +834,6 @@ __global__ __launch_bounds__(64) void append_kernel(uint8_t* __restrict__ buf, L
       }
       if (lane == 0) reinterpret_cast<int32_t*>(buf + L.sink_pos(b, h))[nsp] = nsp;
       return;
-    }
-    if (nr >= L.R) {  // flush the window as one chunk
-      uint8_t* pm = buf + L.perm(b, h);
-      if (nq == 0) {
-        range_permutation<D>(wk, L.R, rng, pm, lane, 64, L.reorder);
-        range_permutation<D>(wv, L.R, rng, pm + D, lane, 64, L.reorder);
-        __threadfence();  // the permutations are read back just below
-      }
-      const int j0 = nq / kGroup;
-      // the first chunk's rows are in channel order; later windows are stored permuted
-      const uint8_t* gk = nq == 0 ? pm : nullptr;
-      const uint8_t* gv = nq == 0 ? pm + D : nullptr;
-      for (int m = 0; m < L.R / kGroup; ++m)
-        if (j0 + m < L.max_groups)
-          skvq_encode_record<D, BK, BV>(wk + m * kGroup * D, wv + m * kGroup * D, gk, gv, clip_candidates(L),
-                                        L.clip, reinterpret_cast<uint32_t*>(buf + L.record(b, h, j0 + m)), slds);
-      if (nq == 0 && L.NS > 0) {  // the sinks' rows take the permuted order too
-        __half* sk = reinterpret_cast<__half*>(buf + L.sink_k(b, h));
-        __half* sv = reinterpret_cast<__half*>(buf + L.sink_v(b, h));
-        for (int i = lane; i < L.NS * D; i += 64) {
-          slds.tile[0][i / D][i % D] = sk[i];
-          slds.tile[1][i / D][i % D] = sv[i];
-        }
-        __syncthreads();
-        for (int i = lane; i < L.NS * D; i += 64) {
-          sk[i] = slds.tile[0][i / D][pm[i % D]];
-          sv[i] = slds.tile[1][i / D][pm[D + i % D]];
-        }
-      }
-      nq += L.R;
-      nr = 0;
-      __syncthreads();
     }
     if (nq > 0) {  // the token in permuted channel order
       const uint8_t* pm = buf + L.perm(b, h);
@@ -1087,18 +1087,34 @@ hipError_t launch_lengths_fill(uint8_t* buf, const Layout& L, const PerSeq& seq,
 
 template <int D, int BK, int BV>
 static hipError_t launch_skvq_encode_t(uint8_t* buf, const Layout& L, const void* K, const void* V,
-                                       int64_t ld_tok, const PerSeq& seq, int max_records, hipStream_t s) {
+                                       int64_t ld_tok, const PerSeq& seq, int max_records, int rows_permuted,
+                                       hipStream_t s) {
   dim3 grid(max_records, L.Hkv, L.B);
   hipLaunchKernelGGL((skvq_encode_kernel<D, BK, BV>), grid, dim3(64), 0, s, buf, L,
-                     static_cast<const __half*>(K), static_cast<const __half*>(V), ld_tok, seq);
+                     static_cast<const __half*>(K), static_cast<const __half*>(V), ld_tok, seq, rows_permuted);
   return hipGetLastError();
 }
 
 hipError_t launch_skvq_encode(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,
-                              const PerSeq& seq, int max_records, hipStream_t s) {
-  if (L.D == 128) { KVQ_DISPATCH_BITS(128, launch_skvq_encode_t, buf, L, K, V, ld_tok, seq, max_records, s) }
-  if (L.D == 64) { KVQ_DISPATCH_BITS(64, launch_skvq_encode_t, buf, L, K, V, ld_tok, seq, max_records, s) }
+                              const PerSeq& seq, int max_records, int rows_permuted, hipStream_t s) {
+  if (L.D == 128) {
+    KVQ_DISPATCH_BITS(128, launch_skvq_encode_t, buf, L, K, V, ld_tok, seq, max_records, rows_permuted, s)
+  }
+  if (L.D == 64) {
+    KVQ_DISPATCH_BITS(64, launch_skvq_encode_t, buf, L, K, V, ld_tok, seq, max_records, rows_permuted, s)
+  }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_skvq_permute_rows(uint8_t* buf, const Layout& L, const PerSeq& seq, hipStream_t s) {
+  dim3 grid(L.Hkv, L.B);
+  if (L.D == 128)
+    hipLaunchKernelGGL(skvq_permute_rows_kernel<128>, grid, dim3(64), 0, s, buf, L, seq);
+  else if (L.D == 64)
+    hipLaunchKernelGGL(skvq_permute_rows_kernel<64>, grid, dim3(64), 0, s, buf, L, seq);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_skvq_perm(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,

@@ -40,9 +40,13 @@ hipError_t launch_lengths_fill(uint8_t* buf, const Layout& L, const PerSeq& seq,
 // that start at token seq.c[b] (the first chunk).
 hipError_t launch_skvq_perm(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,
                             const PerSeq& seq, hipStream_t s);
-// SKVQ records seq.a[b] + x (x < seq.b[b]) of every (b, h) from tokens seq.c[b] + 32 x on.
+// SKVQ records seq.a[b] + x (x < seq.b[b]) of every (b, h) from tokens seq.c[b] + 32 x on;
+// rows_permuted: the rows are stored in permuted channel order (a window flush).
 hipError_t launch_skvq_encode(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,
-                              const PerSeq& seq, int max_records, hipStream_t s);
+                              const PerSeq& seq, int max_records, int rows_permuted, hipStream_t s);
+// SKVQ first flush of the sequences with seq.b[b] > 0: their window and sink rows rewritten in
+// permuted order.
+hipError_t launch_skvq_permute_rows(uint8_t* buf, const Layout& L, const PerSeq& seq, hipStream_t s);
 // Sinks of the sequences with seq.b[b] > 0: chosen among tokens 0 .. seq.b[b]-1 of K[b][h]
 // (the sequence's first quantized tokens), positions and fp16 K, V rows written (L.NS >= 1).
 hipError_t launch_sink_select(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,

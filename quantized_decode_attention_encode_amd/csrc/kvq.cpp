@@ -488,7 +488,7 @@ kvq_status kvq_prefill(kvq_cache* c, const void* K, const void* V, int64_t ld_to
   if (max_rec && sk) {
     hipError_t e = kvq::launch_skvq_perm(c->buf, c->L, K, V, ld_tok, sel, s);
     if (e != hipSuccess) return hip_fail(e, "permutation launch");
-    e = kvq::launch_skvq_encode(c->buf, c->L, K, V, ld_tok, enc, max_rec, s);
+    e = kvq::launch_skvq_encode(c->buf, c->L, K, V, ld_tok, enc, max_rec, 0, s);
     if (e != hipSuccess) return hip_fail(e, "encode launch");
   } else if (max_rec) {
     hipError_t e;
@@ -524,6 +524,40 @@ kvq_status kvq_append(kvq_cache* c, const void* k_tok, const void* v_tok, void* 
     len.a[b] = c->nq[b];
     len.b[b] = c->nr[b];
     len.c[b] = c->nsp[b];
+  }
+  if (is_skvq(c->cfg)) {
+    // SKVQ windows are flushed here, one wave per record (the clip search is the costly part):
+    // a first flush computes the permutations from the window and rewrites the window and sink
+    // rows in permuted order; every flush then encodes the (permuted) window rows
+    PerSeq first, fl;
+    memset(&first, 0, sizeof first);
+    memset(&fl, 0, sizeof fl);
+    bool any = false, any_first = false;
+    for (int b = 0; b < c->cfg.batch; ++b) {
+      if (c->nsp[b] < c->cfg.n_sink || c->nr[b] < c->cfg.residual) continue;
+      any = true;
+      fl.a[b] = c->nq[b] / kvq::kGroup;
+      fl.b[b] = c->cfg.residual / kvq::kGroup;
+      if (c->nq[b] == 0) {
+        first.b[b] = 1;
+        any_first = true;
+      }
+      len.a[b] = c->nq[b] + c->cfg.residual;  // the append kernel then sees an empty window
+      len.b[b] = 0;
+    }
+    const void* wk = c->buf + c->L.wk_off;
+    const void* wv = c->buf + c->L.wv_off;
+    hipError_t e;
+    if (any_first) {
+      e = kvq::launch_skvq_perm(c->buf, c->L, wk, wv, c->cfg.residual, first, s);
+      if (e != hipSuccess) return hip_fail(e, "permutation launch");
+      e = kvq::launch_skvq_permute_rows(c->buf, c->L, first, s);
+      if (e != hipSuccess) return hip_fail(e, "row permutation launch");
+    }
+    if (any) {
+      e = kvq::launch_skvq_encode(c->buf, c->L, wk, wv, c->cfg.residual, fl, c->cfg.residual / kvq::kGroup, 1, s);
+      if (e != hipSuccess) return hip_fail(e, "flush launch");
+    }
   }
   hipError_t e = kvq::launch_append(c->buf, c->L, k_tok, v_tok, len, s);
   if (e != hipSuccess) return hip_fail(e, "append launch");
