@@ -46,7 +46,7 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 # (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, factors from a 1 GiB device copy; see
 # profiles/kvq_long_s64k_counters.md), valid only for the decode kernel and split-plan
 # sources they were taken on (their hash).
-MEASURED_TRAFFIC = {"workload": "long", "src_sha256_16": "0d0561a3d36707f9", "bytes": 202621063}
+MEASURED_TRAFFIC = {"workload": "long", "src_sha256_16": "e642750159ff07c6", "bytes": 202616468}
 
 
 def algorithmic_decode_bytes(wl, n_q, n_r, n_sink=0):
