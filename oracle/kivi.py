@@ -304,6 +304,24 @@ def attend(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray, sm_scale: float 
     return (p @ v_hat) / p.sum()
 
 
+def attend_causal(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray, sm_scale: float = 1.0) -> np.ndarray:
+    """S_q queries ``q[S_q, D]`` that are the cache's newest S_q tokens (rows in token order):
+    query j sees the first T - (S_q - 1 - j) rows, so its own token and everything before it.
+
+    Multi-query attend over the quantized cache (speculative decode; the pages pair the fused
+    decode kernel with multi-token work in "Changelog" v0.40.0 "Added", RaBitQ): each query is
+    the plain decode attention of ``attend`` over its causal prefix.
+    """
+    S_q, T = q.shape[0], k_hat.shape[0]
+    if S_q > T:
+        raise ValueError("more queries than cached tokens")
+    out = np.zeros((S_q, v_hat.shape[1]), F64)
+    for j in range(S_q):
+        lim = T - (S_q - 1 - j)
+        out[j] = attend(q[j], k_hat[:lim], v_hat[:lim], sm_scale)
+    return out
+
+
 def kv_head_of(h_q: int, n_q_heads: int, n_kv_heads: int) -> int:
     """Query head h_q reads KV head floor(h_q * H_kv / H_q) (contiguous GQA blocks)."""
     return (h_q * n_kv_heads) // n_q_heads

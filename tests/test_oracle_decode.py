@@ -176,3 +176,27 @@ def test_eight_bits_near_lossless_and_error_shrinks_with_step():
     r48 = np.median(err[4]) / np.median(err[8])
     assert 5 / 2 <= r24 <= 5 * 2, r24
     assert 17 / 2 <= r48 <= 17 * 2, r48
+
+
+# ---------------------------------------------------------------------------------------
+# Multi-query (causal) attend: query j of S_q sees the cache up to its own token
+# ---------------------------------------------------------------------------------------
+def test_causal_multi_query_against_brute_force_prefixes():
+    rng = np.random.default_rng(21)
+    T, D, S_q = 45, 32, 4
+    k = rng.standard_normal((T, D))
+    v = rng.standard_normal((T, D))
+    q = rng.standard_normal((S_q, D)).astype(np.float16)
+    out = kivi.attend_causal(q, k, v, 0.7)
+    for j in range(S_q):
+        n = T - (S_q - 1 - j)
+        ref = brute.attend([float(x) for x in q[j]], k[:n].tolist(), v[:n].tolist(), 0.7)
+        assert np.allclose(out[j], ref, rtol=0, atol=1e-12)
+    # one query: plain decode attention; the newest query sees every row
+    assert np.allclose(kivi.attend_causal(q[-1:], k, v), kivi.attend(q[-1], k, v), rtol=0, atol=0)
+    assert np.allclose(out[-1], kivi.attend(q[-1], k, v, 0.7), rtol=0, atol=0)
+    # a key that only the last query can see changes only the last output
+    k2 = k.copy()
+    k2[-1] *= 50
+    out2 = kivi.attend_causal(q, k2, v, 0.7)
+    assert np.array_equal(out2[:-1], out[:-1]) and not np.allclose(out2[-1], out[-1])
