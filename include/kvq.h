@@ -223,6 +223,22 @@ kvq_status kvq_decode_attend(kvq_cache* cache, const void* q, void* out, int32_t
                              float sm_scale, void* workspace, size_t ws_bytes, int32_t n_split,
                              void* stream);
 
+/* Multi-query attend (speculative decoding: several new tokens scored at once). The newest
+ * n_query tokens of every sequence (already appended) each attend, causally, over the cache up
+ * to and including themselves: query j (0-based) of head h of sequence b sees the first
+ * S_b - (n_query - 1 - j) tokens, S_b being all the tokens the sequence holds (sinks, quantized
+ * and window, in token order). n_query = 1 is kvq_decode_attend.
+ *   q:   fp16 [B][H_q][n_query][D];  out: fp16 (or fp32) [B][H_q][n_query][D].
+ *   n_query: a power of two with n_query x (H_q / H_kv) <= 8 (KVQ_E_UNSUPPORTED otherwise);
+ *   every sequence holds at least n_query tokens (KVQ_E_INVALID otherwise).
+ *   workspace: at least n_query x kvq_workspace_bytes(cfg, n_split) bytes.
+ * The same kernel as kvq_decode_attend, with the query rows of each KV head (heads x queries)
+ * sharing every code it unpacks; masked scores take a large negative finite value, so a split
+ * that sees only a query's future contributes nothing to it. */
+kvq_status kvq_decode_attend_multi(kvq_cache* cache, const void* q, void* out, int32_t n_query, int32_t out_fp32,
+                                   float sm_scale, void* workspace, size_t ws_bytes, int32_t n_split,
+                                   void* stream);
+
 /* North-star calls 2 and 3 in one: exactly kvq_append(cache, k_tok, v_tok) followed by
  * kvq_decode_attend(cache, q, ...) on the same stream, same arguments and errors, same cache
  * state and output. When no window is full (31 appends in 32 at R = 32) it is one kernel

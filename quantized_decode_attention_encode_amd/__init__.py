@@ -10,6 +10,7 @@ from .cache import (  # noqa: F401
     kvq_append_decode_attend,
     kvq_cache_bytes,
     kvq_decode_attend,
+    kvq_decode_attend_multi,
     kvq_encode,
     kvq_encode_block,
     kvq_layout,

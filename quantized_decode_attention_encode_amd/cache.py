@@ -17,7 +17,8 @@ from . import _lib
 from ._lib import KVQ_OK, Config, KVQError, LayoutInfo, check, lib
 
 __all__ = ["KVQCache", "KVQError", "make_config", "kvq_probe", "kvq_cache_bytes", "kvq_layout",
-           "kvq_workspace_bytes", "kvq_encode", "kvq_prefill", "kvq_append", "kvq_decode_attend"]
+           "kvq_workspace_bytes", "kvq_encode", "kvq_prefill", "kvq_append", "kvq_decode_attend",
+           "kvq_decode_attend_multi"]
 
 
 def make_config(batch, n_kv_heads, n_q_heads, head_dim, key_bits=2, value_bits=2, group=32, residual=32,
@@ -115,8 +116,8 @@ class KVQCache:
     def reset(self, stream=None):
         check(lib.kvq_reset(self.handle, _stream(stream)))
 
-    def workspace(self, n_split: int = 0) -> torch.Tensor:
-        need = kvq_workspace_bytes(self.cfg, n_split)
+    def workspace(self, n_split: int = 0, n_query: int = 1) -> torch.Tensor:
+        need = kvq_workspace_bytes(self.cfg, n_split) * n_query
         if self._ws is None or self._ws.numel() < need:
             self._ws = torch.empty(need, dtype=torch.uint8, device=self.buffer.device)
         return self._ws
@@ -196,6 +197,30 @@ def kvq_decode_attend(cache: KVQCache, q: torch.Tensor, out: torch.Tensor | None
     st = lib.kvq_decode_attend(cache.handle, _dev(q, "q"), _dev(out, "out", odt), 1 if out_fp32 else 0,
                                float(sm_scale), _dev(workspace, "workspace", torch.uint8), workspace.numel(),
                                int(n_split), _stream(stream))
+    if st != KVQ_OK:
+        check(st)
+    return out
+
+
+def kvq_decode_attend_multi(cache: KVQCache, q: torch.Tensor, out: torch.Tensor | None = None, sm_scale: float = 1.0,
+                            n_split: int = 0, out_fp32: bool = False, workspace: torch.Tensor | None = None,
+                            stream=None) -> torch.Tensor:
+    """Causal attention of the newest n_query tokens' queries q [B, H_q, n_query, D] fp16 over the
+    cache (query j sees the tokens up to and including its own); returns out of q's shape."""
+    c = cache.cfg
+    if q.dim() != 4 or tuple(q.shape[:2]) != (c.batch, c.n_q_heads) or q.shape[3] != c.head_dim:
+        raise KVQError(-1, f"q must be [B, H_q, n_query, D] with B, H_q, D = {(c.batch, c.n_q_heads, c.head_dim)}")
+    n_query = int(q.shape[2])
+    odt = torch.float32 if out_fp32 else torch.float16
+    if out is None:
+        out = torch.empty(tuple(q.shape), dtype=odt, device=q.device)
+    if tuple(out.shape) != tuple(q.shape):
+        raise KVQError(-1, "out must have q's shape")
+    if workspace is None:
+        workspace = cache.workspace(n_split, n_query)
+    st = lib.kvq_decode_attend_multi(cache.handle, _dev(q, "q"), _dev(out, "out", odt), n_query, 1 if out_fp32 else 0,
+                                     float(sm_scale), _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+                                     int(n_split), _stream(stream))
     if st != KVQ_OK:
         check(st)
     return out

@@ -240,13 +240,25 @@ __device__ __forceinline__ void softmax_step(WaveState<D, G>& st, int i, float s
   st.l[i] += p0 + p1;
 }
 
+// Multi-query decode: virtual head i sees the positions below lim[i] (query i % S_q of its
+// head is the cache's token S - S_q + i % S_q). A masked score becomes kMaskScore, a finite
+// value so far below any real score that its weight vanishes once a visible token is seen
+// (in the same wave, across waves and across splits alike); -inf could leave a running max
+// of -inf, and exp2(-inf - -inf) is not 0.
+constexpr float kMaskScore = -1.0e30f;
+template <int G>
+struct Causal {
+  int lim[G];
+  int lim_min;  // no position below it is masked for any head
+};
+
 // One 32-token record of (b, h_kv), all G query heads. With SK, slots whose value scale
 // carries the sign bit (sinks, attended from their fp16 rows instead) get no weight.
 template <int D, int BK, int BV, int G, bool SK, bool KT>
 __device__ __forceinline__ void process_record(const RecordRegs<D, BK, BV>& cur, WaveLds<D, G>& W, WaveState<D, G>& st,
                                                const Unpacker<BK>& upk, const Unpacker<BV>& upv,
                                                const float (&qs)[G][D / 64], const float (&qf)[G][D / 64],
-                                               float vf0, float vf1, int lane) {
+                                               float vf0, float vf1, int lane, const Causal<G>& cz, int tok0) {
   constexpr int E = D / 64, DQ = D / 4, WQ = D * BK / 128, NKG = D / 32;
   using MK = Magic<BK>;
   using MV = Magic<BV>;
@@ -338,16 +350,29 @@ __device__ __forceinline__ void process_record(const RecordRegs<D, BK, BV>& cur,
     }
   }
 
+  if constexpr (KT) {
 #pragma unroll
-  for (int i = 0; i < G; ++i) {
-    float s0 = s[i][0], s1 = s[i][1];
-    if constexpr (KT) {
+    for (int i = 0; i < G; ++i) {
       // quarter partial sum_c q~_c (1 + c_code 2^(o-10)) minus the fold constant, times the
       // token's group scale, plus its zero times the quarter's query sum
       const float fq = W.beta[i][Q], qsm = W.qsum[i][Q];
-      s0 = __builtin_fmaf(lo_f(cur.kp[0]), s0 - fq, hi_f(cur.kp[0]) * qsm);
-      s1 = __builtin_fmaf(lo_f(cur.kp[1]), s1 - fq, hi_f(cur.kp[1]) * qsm);
+      s[i][0] = __builtin_fmaf(lo_f(cur.kp[0]), s[i][0] - fq, hi_f(cur.kp[0]) * qsm);
+      s[i][1] = __builtin_fmaf(lo_f(cur.kp[1]), s[i][1] - fq, hi_f(cur.kp[1]) * qsm);
     }
+  }
+  // one query row per KV head (G = 1) means one query: nothing is ever masked
+  if (G > 1 && tok0 + kGroup > cz.lim_min) {  // wave-uniform: a record holding some query's future
+    // a masked quarter partial makes the whole score at least this far below any real one
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (tok0 + 2 * P >= cz.lim[i]) s[i][0] = kMaskScore;
+      if (tok0 + 2 * P + 1 >= cz.lim[i]) s[i][1] = kMaskScore;
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    float s0 = s[i][0], s1 = s[i][1];
     s0 += dpp<kQuadXor1>(s0);
     s1 += dpp<kQuadXor1>(s1);
     s0 += dpp<kQuadXor2>(s0);
@@ -438,8 +463,10 @@ template <int D, int G, bool KT = false>
 __device__ __forceinline__ void process_window(const __half* __restrict__ wk, const __half* __restrict__ wv, int nvalid,
                                                int tnew, const __half* kn, const __half* vn,
                                                WaveLds<D, G>& W, WaveState<D, G>& st, const float (&qs)[G][D / 64],
-                                               int lane, const uint8_t* __restrict__ pk = nullptr,
+                                               int lane, const Causal<G>& cz, int tok0,
+                                               const int32_t* __restrict__ pos, const uint8_t* __restrict__ pk = nullptr,
                                                const uint8_t* __restrict__ pv = nullptr) {
+  // token t of the unit is at position pos[t] (sinks chosen by norm), else tok0 + t
   constexpr int E = D / 64, DQ = D / 4;
   const int P = lane >> 2, Q = lane & 3;
   const int kcons = (lane * E) / 32;
@@ -485,6 +512,11 @@ __device__ __forceinline__ void process_window(const __half* __restrict__ wk, co
     s0 += dpp<kQuadXor2>(s0);
     s1 += dpp<kQuadXor1>(s1);
     s1 += dpp<kQuadXor2>(s1);
+    if constexpr (G > 1) {
+      const int a0 = pos ? pos[t0c] : tok0 + t0, a1 = pos ? pos[t1c] : tok0 + t1;
+      if (a0 >= cz.lim[i]) s0 = kMaskScore;
+      if (a1 >= cz.lim[i]) s1 = kMaskScore;
+    }
     if (t0 >= nvalid) s0 = -INFINITY;
     if (t1 >= nvalid) s1 = -INFINITY;
     float p0, p1;
@@ -650,6 +682,15 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
     for (int k = 0; k < L.NS && sp[k] >= 0; ++k) nsink = k + 1;
   }
   const bool sinks = nsink > 0;
+  // positions: SKVQ sinks are tokens 0 .. nsink - 1 and its records start after them
+  const int pos0 = KT ? nsink : 0;
+  Causal<G> cz;
+  {
+    const int S = pos0 + nq + nr;
+#pragma unroll
+    for (int i = 0; i < G; ++i) cz.lim[i] = S - (ds.nqry - 1 - i % ds.nqry);
+    cz.lim_min = S - (ds.nqry - 1);
+  }
   const int nunits = ngroups + (nr + kGroup - 1) / kGroup + (sinks ? 1 : 0);
   const int u0 = sigma * ds.chunk;
   if (u0 >= nunits) return;
@@ -727,11 +768,11 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
       load_record<D, BK, BV, KT>(rec0 + u * rb, lane, ra);
       load_record<D, BK, BV, KT>(rec0 + min(u + kWaves, ulast) * rb, lane, rbuf);
       while (true) {
-        process_record<D, BK, BV, G, SK, KT>(ra, W, st, upk, upv, qs, qf, vf0, vf1, lane);
+        process_record<D, BK, BV, G, SK, KT>(ra, W, st, upk, upv, qs, qf, vf0, vf1, lane, cz, pos0 + u * kGroup);
         u += kWaves;
         if (u >= uq) break;
         load_record<D, BK, BV, KT>(rec0 + min(u + kWaves, ulast) * rb, lane, ra);
-        process_record<D, BK, BV, G, SK, KT>(rbuf, W, st, upk, upv, qs, qf, vf0, vf1, lane);
+        process_record<D, BK, BV, G, SK, KT>(rbuf, W, st, upk, upv, qs, qf, vf0, vf1, lane, cz, pos0 + u * kGroup);
         u += kWaves;
         if (u >= uq) break;
         load_record<D, BK, BV, KT>(rec0 + min(u + kWaves, ulast) * rb, lane, rbuf);
@@ -743,7 +784,7 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
       load_record<D, BK, BV, KT>(rec0 + u * rb, lane, cur);
       for (; u < uq; u += kWaves) {
         load_record<D, BK, BV, KT>(rec0 + min(u + kWaves, ulast) * rb, lane, nxt);
-        process_record<D, BK, BV, G, SK, KT>(cur, W, st, upk, upv, qs, qf, vf0, vf1, lane);
+        process_record<D, BK, BV, G, SK, KT>(cur, W, st, upk, upv, qs, qf, vf0, vf1, lane, cz, pos0 + u * kGroup);
         cur = nxt;
       }
     }
@@ -762,7 +803,9 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
     const int64_t tok = (int64_t(b) * L.Hkv + h) * D;
     const __half* kn = ds.append ? k_app + tok : nullptr;
     const __half* vn = ds.append ? v_app + tok : nullptr;
-    process_window<D, G, KT>(wk, wv, nvalid, tnew, kn, vn, W, st, qs, lane, pk, pv);
+    const int32_t* sink_pos = (sink_unit && !KT) ? reinterpret_cast<const int32_t*>(buf + L.sink_pos(b, h)) : nullptr;
+    process_window<D, G, KT>(wk, wv, nvalid, tnew, kn, vn, W, st, qs, lane, cz,
+                             sink_unit ? 0 : pos0 + nq + tbase, sink_pos, pk, pv);
     if (tnew >= 0 && tnew < nvalid) {  // store the appended token in its slot (no read of it here)
       __half* dk = reinterpret_cast<__half*>(bufw + L.wk_off + L.window(b, h)) + nr_old * D;
       __half* dv = reinterpret_cast<__half*>(bufw + L.wv_off + L.window(b, h)) + nr_old * D;

@@ -24,6 +24,8 @@ struct DecodeShape {
   float qscale;     // sm_scale * log2(e): scores are kept in base-2 units
   int out_fp32;
   int append;       // 1: the launch also appends one token per (b, h) (no window is full)
+  int nqry;         // queries per head: the newest nqry tokens, causal among themselves (G
+                    // and n_q_heads count query rows: heads x nqry)
 };
 
 hipError_t launch_encode(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,

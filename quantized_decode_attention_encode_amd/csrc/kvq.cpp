@@ -188,19 +188,27 @@ namespace {
 // Plan and enqueue one decode launch. With k_tok / v_tok set, the launch also appends one token
 // per sequence (the caller has checked that no window is full): it attends over the window
 // plus that token, stores the token in its slot and advances the device lengths.
+// n_query > 1: that many queries per head, the cache's newest tokens (causal among themselves).
 kvq_status decode_enqueue(kvq_cache* c, const void* q, void* out, int32_t out_fp32, float sm_scale,
                           void* workspace, size_t ws_bytes, int32_t n_split, void* stream,
-                          const void* k_tok, const void* v_tok) {
+                          const void* k_tok, const void* v_tok, int32_t n_query = 1) {
   if (!q || !out) return fail(KVQ_E_INVALID, "q or out is NULL");
   if (!workspace) return fail(KVQ_E_WORKSPACE, "workspace is NULL");
   if (n_split < 0) return fail(KVQ_E_INVALID, "n_split must be >= 0");
   if (!std::isfinite(sm_scale)) return fail(KVQ_E_INVALID, "sm_scale is not finite");
   const kvq_config& cfg = c->cfg;
   const int add = k_tok ? 1 : 0;  // window tokens the launch appends
+  const int G = cfg.n_q_heads / cfg.n_kv_heads;
+  if (n_query < 1 || (n_query & (n_query - 1)) || G * n_query > 8)
+    return fail(KVQ_E_UNSUPPORTED, "n_query = %d: it must be a power of two with n_query x (query heads per KV head = %d) <= 8",
+                n_query, G);
   int max_units = 0;
   int64_t total_units = 0;
   for (int b = 0; b < cfg.batch; ++b) {
-    if (c->nq[b] + c->nr[b] + c->nsp[b] + add == 0) return fail(KVQ_E_INVALID, "sequence %d is empty", b);
+    const int held = c->nq[b] + c->nr[b] + c->nsp[b] + add;
+    if (held == 0) return fail(KVQ_E_INVALID, "sequence %d is empty", b);
+    if (held < n_query)
+      return fail(KVQ_E_INVALID, "sequence %d holds %d tokens, fewer than the %d queries", b, held, n_query);
     const int u = units_of(c->nq[b], c->nr[b] + add, has_sinks(c, b));
     max_units = std::max(max_units, u);
     total_units += int64_t(u) * cfg.n_kv_heads;
@@ -217,7 +225,7 @@ kvq_status decode_enqueue(kvq_cache* c, const void* q, void* out, int32_t out_fp
     chunk = std::max(4, (chunk + 3) / 4 * 4);
   }
   const int ns = (max_units + chunk - 1) / chunk;
-  const size_t need = size_t(cfg.batch) * cfg.n_q_heads * ns * (cfg.head_dim + 4) * sizeof(float);
+  const size_t need = size_t(cfg.batch) * cfg.n_q_heads * n_query * ns * (cfg.head_dim + 4) * sizeof(float);
   if (ws_bytes < need) return fail(KVQ_E_WORKSPACE, "workspace holds %zu bytes, this call needs %zu", ws_bytes, need);
   hipStream_t s = static_cast<hipStream_t>(stream);
   kvq_status st = ensure_ready(c, s);
@@ -225,8 +233,9 @@ kvq_status decode_enqueue(kvq_cache* c, const void* q, void* out, int32_t out_fp
   kvq::DecodeShape ds;
   ds.n_split = ns;
   ds.chunk = chunk;
-  ds.G = cfg.n_q_heads / cfg.n_kv_heads;
-  ds.n_q_heads = cfg.n_q_heads;
+  ds.G = G * n_query;  // query rows per KV head
+  ds.n_q_heads = cfg.n_q_heads * n_query;
+  ds.nqry = n_query;
   ds.qscale = sm_scale * 1.4426950408889634f;
   ds.out_fp32 = out_fp32 ? 1 : 0;
   ds.append = add;
@@ -579,6 +588,13 @@ kvq_status kvq_decode_attend(kvq_cache* c, const void* q, void* out, int32_t out
                              void* workspace, size_t ws_bytes, int32_t n_split, void* stream) {
   if (!c) return fail(KVQ_E_INVALID, "cache is NULL");
   return decode_enqueue(c, q, out, out_fp32, sm_scale, workspace, ws_bytes, n_split, stream, nullptr, nullptr);
+}
+
+kvq_status kvq_decode_attend_multi(kvq_cache* c, const void* q, void* out, int32_t n_query, int32_t out_fp32,
+                                   float sm_scale, void* workspace, size_t ws_bytes, int32_t n_split, void* stream) {
+  if (!c) return fail(KVQ_E_INVALID, "cache is NULL");
+  return decode_enqueue(c, q, out, out_fp32, sm_scale, workspace, ws_bytes, n_split, stream, nullptr, nullptr,
+                        n_query);
 }
 
 kvq_status kvq_append_decode_attend(kvq_cache* c, const void* k_tok, const void* v_tok, const void* q, void* out,

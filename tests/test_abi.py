@@ -187,6 +187,10 @@ def test_host_side_errors_before_any_launch():
         ws = ctypes.c_void_p(FAKE)
         assert lib.kvq_decode_attend(h, P, P, 0, 1.0, ws, 1 << 30, 0, None) == KVQ_E_INVALID
         assert b"empty" in lib.kvq_last_error()
+        # multi-query: n_query a power of two with G * n_query <= 8 (G = 2 here)
+        for nq_bad in (3, 8, 0):
+            assert lib.kvq_decode_attend_multi(h, P, P, nq_bad, 0, 1.0, ws, 1 << 30, 0, None) == KVQ_E_UNSUPPORTED
+        assert lib.kvq_decode_attend_multi(h, P, P, 4, 0, 1.0, ws, 1 << 30, 0, None) == KVQ_E_INVALID
         assert lib.kvq_decode_attend(h, P, P, 0, 1.0, None, 1 << 30, 0, None) == KVQ_E_WORKSPACE
         assert lib.kvq_decode_attend(h, P, P, 0, float("nan"), ws, 1 << 30, 0, None) == KVQ_E_INVALID
         assert lib.kvq_decode_attend(h, P, P, 0, 1.0, ws, 1 << 30, -2, None) == KVQ_E_INVALID
