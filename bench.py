@@ -24,8 +24,11 @@ more fp16 unit and skips their quantized slots. With --method skvq the caches ar
 SKVQ-adapted ("Changelog" v0.30.0: per-token groups of range-sorted channels, per-group clip
 search, the first --n-sink tokens in fp16; window --window, the pages' defaults 128 and 5).
 
+With --n-query N > 1 a step appends N tokens per sequence and then scores them with one causal
+multi-query attend (kvq_decode_attend_multi: speculative decoding's verification step).
+
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long] [--n-sink 0]
-                  [--method kivi|skvq] [--window R] [--no-cpu-baseline]
+                  [--method kivi|skvq] [--window R] [--n-query 1] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -141,6 +144,7 @@ def main():
                          "tokens (default 5)")
     ap.add_argument("--method", default="kivi", choices=("kivi", "skvq"))
     ap.add_argument("--window", type=int, default=None, help="fp16 window (default: the workload's, 128 for skvq)")
+    ap.add_argument("--n-query", type=int, default=1, help="queries per head per step (causal multi-query attend)")
     args = ap.parse_args()
     if args.n_sink is None:
         args.n_sink = 5 if args.method == "skvq" else 0
@@ -173,7 +177,8 @@ def main():
     # events themselves lengthen a step, so that pass is not the step time)
     n_steps_total = args.warmup + 3 * args.steps
     per_cache = n_steps_total if multi else (n_steps_total + n_caches - 1) // n_caches
-    cap = (max(lens) + per_cache + R + 64 + 31) // 32 * 32
+    NQ = args.n_query
+    cap = (max(lens) + per_cache * NQ + R + 64 + 31) // 32 * 32
     cfg = make_config(wl.batch, wl.n_kv_heads, wl.n_q_heads, wl.head_dim, wl.key_bits, wl.value_bits, 32,
                       R, cap, n_sink=args.n_sink, method=args.method)
     Kt, Vt = torch.from_numpy(K).to(dev), torch.from_numpy(V).to(dev)
@@ -219,7 +224,7 @@ def main():
     enc_gbs = algorithmic_encode_bytes(wl, n_q0, args.n_sink) / enc_t / 1e9
 
     # ---- device-resident inputs of the decode steps
-    toks = [draw.next_token() for _ in range(n_steps_total)]
+    toks = [draw.next_token() for _ in range(n_steps_total * NQ)]
     kt = torch.from_numpy(np.stack([t[0] for t in toks])).to(dev)
     vt = torch.from_numpy(np.stack([t[1] for t in toks])).to(dev)
     del Kt, Vt
@@ -231,22 +236,37 @@ def main():
     import ctypes
     lib = _lib.lib
     sp = ctypes.c_void_p(stream.cuda_stream)
-    kp = [ctypes.c_void_p(kt[i].data_ptr()) for i in range(n_steps_total)]
-    vp = [ctypes.c_void_p(vt[i].data_ptr()) for i in range(n_steps_total)]
+    kp = [ctypes.c_void_p(kt[i].data_ptr()) for i in range(n_steps_total * NQ)]
+    vp = [ctypes.c_void_p(vt[i].data_ptr()) for i in range(n_steps_total * NQ)]
     dec_args = [(c.handle, ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(o.data_ptr()), 0, 1.0,
                  ctypes.c_void_p(w.data_ptr()), w.numel(), args.n_split, sp) for c, o, w in zip(caches, outs, wss)]
     visits = (lambda i: range(n_caches)) if multi else (lambda i: (i % n_caches,))
 
     fused_args = [(c.handle, None, None) + a[1:] for c, a in zip(caches, dec_args)]
+    if NQ > 1:  # q [B, H_q, NQ, D] for the multi-query steps
+        qm = torch.from_numpy((np.random.default_rng(wl.seed + 1000).standard_normal(
+            (wl.batch, wl.n_q_heads, NQ, wl.head_dim)) / math.sqrt(wl.head_dim)).astype(np.float16)).to(dev)
+        outm = [torch.empty(tuple(qm.shape), dtype=torch.float16, device=dev) for _ in caches]
+        wsm = [c.workspace(args.n_split, NQ).clone() for c in caches]
+        multi_args = [(c.handle, ctypes.c_void_p(qm.data_ptr()), ctypes.c_void_p(o.data_ptr()), NQ, 0, 1.0,
+                       ctypes.c_void_p(w.data_ptr()), w.numel(), args.n_split, sp) for c, o, w in zip(caches, outm, wsm)]
 
     def step(i):  # one decode step of the hot path: append + attend, one call
         for r in visits(i):
-            a = fused_args[r]
-            st = lib.kvq_append_decode_attend(a[0], kp[i], vp[i], *a[3:])
+            if NQ > 1:
+                st = 0
+                for k in range(NQ):
+                    st = st or lib.kvq_append(caches[r].handle, kp[i * NQ + k], vp[i * NQ + k], sp)
+                st = st or lib.kvq_decode_attend_multi(*multi_args[r])
+            else:
+                a = fused_args[r]
+                st = lib.kvq_append_decode_attend(a[0], kp[i], vp[i], *a[3:])
             if st:
                 _lib.check(st)
 
     def step_separate(i):  # the same step through kvq_append, then kvq_decode_attend
+        if NQ > 1:
+            return step(i)
         for r in visits(i):
             st = lib.kvq_append(caches[r].handle, kp[i], vp[i], sp)
             st = st or lib.kvq_decode_attend(*dec_args[r])
@@ -285,13 +305,15 @@ def main():
     for i in range(n_steps_total):
         for r in visits(i):
             nq, nr = lens_now[r]
-            for b in range(wl.batch):
-                if nr[b] == R:
-                    nq[b] += R
-                    nr[b] = 0
-                nr[b] += 1
-            if first <= i < last:
-                bytes_per_launch.append(algorithmic_decode_bytes(wl, nq, nr, args.n_sink))
+            for _ in range(NQ):
+                for b in range(wl.batch):
+                    if nr[b] == R:
+                        nq[b] += R
+                        nr[b] = 0
+                    nr[b] += 1
+            if first <= i < last:  # (the extra queries add their q and out rows)
+                bytes_per_launch.append(algorithmic_decode_bytes(wl, nq, nr, args.n_sink)
+                                        + (NQ - 1) * 2 * wl.batch * wl.n_q_heads * wl.head_dim * 2)
     for r, c in enumerate(caches):
         assert tuple(map(list, lens_now[r])) == tuple(map(list, c.lengths())), "length replay disagrees"
     step_ms = t_ev0.elapsed_time(t_ev1) / args.steps
@@ -322,7 +344,7 @@ def main():
     traffic = None
     csrc = os.path.join(ROOT, "quantized_decode_attention_encode_amd", "csrc")
     if (args.workload == MEASURED_TRAFFIC["workload"] and args.n_split == 0 and args.n_sink == 0
-            and args.method == "kivi" and R == wl.residual):
+            and args.method == "kivi" and R == wl.residual and NQ == 1):
         import hashlib
 
         h = hashlib.sha256()
@@ -348,13 +370,15 @@ def main():
         "config": {
             "workload": f"{wl.name}: {wl.describe()}",
             "step": ("every layer: " if multi else "")
-            + "kvq_append_decode_attend (append + attend in one decode kernel; on the 1 step in 32 that "
-              "flushes a full window, the append kernel runs first)",
+            + ("kvq_append_decode_attend (append + attend in one decode kernel; on the 1 step in 32 that "
+               "flushes a full window, the append kernel runs first)" if NQ == 1 else
+               f"{NQ} x kvq_append, then kvq_decode_attend_multi over the {NQ} new tokens (causal)"),
             "caches": f"{n_caches} layer caches" if multi else f"{n_caches} replicas of one cache, one per step",
             "codes": f"{wl.key_bits}-bit keys / {wl.value_bits}-bit values, fp16 (scale, zero), fp32 softmax",
             "sinks": args.n_sink,
             "method": args.method,
             "window": R,
+            "n_query": NQ,
         },
         "roofline": {
             "bound": "hbm",
