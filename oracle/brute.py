@@ -148,3 +148,36 @@ def attend(q: list[float], keys: list[list[float]], values: list[list[float]], s
     tot = sum(w)
     D = len(values[0])
     return [sum(w[t] * values[t][d] for t in range(len(values))) / tot for d in range(D)]
+
+
+def kitty_encode_keys(K: list[list[float]], n_hi: int, hi_bits: int, lo_bits: int, g: int):
+    """Kitty keys ("Changelog" v0.11.0) by brute force: for key group j, each channel's
+    population variance over tokens 0 .. (j+1)g - 1, recomputed from scratch in exact
+    rational arithmetic (mean first, then the mean squared deviation); the n_hi channels of
+    largest variance (lower index first on ties) are quantized at hi_bits, the rest at lo_bits.
+    Returns codes[t][d], scale[j][d], zero[j][d], hi[j][d]."""
+    from fractions import Fraction
+
+    T, D = len(K), len(K[0])
+    codes = [[0] * D for _ in range(T)]
+    scale, zero, hi = [], [], []
+    for j in range(T // g):
+        n = (j + 1) * g
+        var = []
+        for d in range(D):
+            xs = [Fraction(K[t][d]) for t in range(n)]
+            mean = sum(xs) / n
+            var.append(sum((x - mean) ** 2 for x in xs) / n)
+        order = sorted(range(D), key=lambda d: (-var[d], d))
+        top = set(order[:n_hi])
+        srow, zrow, hrow = [0.0] * D, [0.0] * D, [False] * D
+        for d in range(D):
+            col = [K[j * g + i][d] for i in range(g)]
+            c, s, z = quantize_group(col, hi_bits if d in top else lo_bits)
+            srow[d], zrow[d], hrow[d] = s, z, d in top
+            for i in range(g):
+                codes[j * g + i][d] = c[i]
+        scale.append(srow)
+        zero.append(zrow)
+        hi.append(hrow)
+    return codes, scale, zero, hi
