@@ -79,6 +79,9 @@ typedef struct kvq_config {
   int32_t skvq_clip_search; /* SKVQ: 1 = per-group search over alpha = 1 - k/20 (k = 0..10),
                                0 = the fixed skvq_clip_alpha */
   float skvq_clip_alpha;    /* SKVQ with the search off: alpha in (0, 1] (1 = no clipping) */
+  int32_t kitty_n_hi;       /* KITTY: key channels at the high width, a multiple of 16 in [0, head_dim]
+                               (32 of 128 at the pages' quarter) */
+  int32_t kitty_hi_bits;    /* KITTY: the high key width, 4 (key_bits is the low width, 2) */
 } kvq_config;
 
 /* Methods ("Changelog" v0.8.0 KIVI, v0.9.0 KIVI-Sink through n_sink; v0.30.0 SKVQ-adapted):
@@ -92,6 +95,15 @@ typedef struct kvq_config {
  * by one. */
 #define KVQ_METHOD_KIVI 0
 #define KVQ_METHOD_SKVQ 1
+/* Kitty ("Changelog" v0.11.0; "Algorithm Overview", Kitty: values in fp16): every key group
+ * (32 tokens of a channel) is quantized by KIVI's min/max rule at kitty_hi_bits when its channel
+ * is among the kitty_n_hi channels of largest variance over all key tokens of the sequence up to
+ * the end of that group (the exact population variance of the fp16 values, computed from integer
+ * running sums; the lower channel index first on equal variances), else at key_bits. Values are
+ * stored as their fp16 inputs (value_bits = 16). The window rule is KIVI's; a flush ranks each of
+ * its groups with the sums at its own end, so a prefill equals the same tokens appended one by
+ * one. n_sink must be 0; decode takes one query per head (kvq_decode_attend_multi: n_query = 1). */
+#define KVQ_METHOD_KITTY 2
 
 /* Byte offsets of the regions inside the cache buffer (see the layout description in the
  * design notes; all offsets but sync_offset are multiples of 256). */
@@ -117,6 +129,16 @@ typedef struct kvq_layout_info {
                                that slot). */
   uint64_t perm_offset;     /* SKVQ: uint8 [B][H_kv][2][D], the K and V channel permutations
                                (permuted channel j is channel perm[j]); == total_bytes for KIVI */
+  uint64_t rec_slot_table;  /* KITTY records: uint8 [D], the channel of each key slot (slots
+                               0 .. n_hi-1 the high-width channels, ascending, then the others);
+                               rec_key_codes: per token (D + n_hi)/16 u32 words, 16-slot chunks,
+                               chunk k at word k + min(k, n_hi/16), a high chunk two words of
+                               4-bit codes, a low one a word of 2-bit codes; rec_key_params:
+                               (scale, zero) per slot; rec_value_codes: fp16 values [32][D];
+                               rec_value_params: unused (0). 0 for other methods */
+  uint64_t kstats_offset;   /* KITTY: per (b, h_kv) the running key sums over the quantized
+                               tokens, int64 s1[D] then uint64 s2_lo[D], s2_hi[D] (X = x * 2^24);
+                               == total_bytes for other methods */
 } kvq_layout_info;
 
 typedef struct kvq_cache kvq_cache; /* opaque host handle */

@@ -32,17 +32,19 @@ class KVQError(RuntimeError):
 class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_kv_heads", "n_q_heads", "head_dim", "key_bits", "value_bits", "group", "residual",
-        "max_tokens", "n_sink", "method", "skvq_reorder", "skvq_clip_search")] + [("skvq_clip_alpha", ctypes.c_float)]
+        "max_tokens", "n_sink", "method", "skvq_reorder", "skvq_clip_search")] + [("skvq_clip_alpha", ctypes.c_float)] + [
+        (n, ctypes.c_int32) for n in ("kitty_n_hi", "kitty_hi_bits")]
 
 
-METHOD_KIVI, METHOD_SKVQ = 0, 1
+METHOD_KIVI, METHOD_SKVQ, METHOD_KITTY = 0, 1, 2
 
 
 class LayoutInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "lengths_offset", "records_offset", "record_bytes", "rec_key_codes", "rec_value_codes",
         "rec_key_params", "rec_value_params", "window_k_offset", "window_v_offset", "total_bytes",
-        "sync_offset", "sink_pos_offset", "sink_k_offset", "sink_v_offset", "perm_offset")]
+        "sync_offset", "sink_pos_offset", "sink_k_offset", "sink_v_offset", "perm_offset", "rec_slot_table",
+        "kstats_offset")]
 
 
 def _load():

@@ -23,16 +23,25 @@ __all__ = ["KVQCache", "KVQError", "make_config", "kvq_probe", "kvq_cache_bytes"
 
 def make_config(batch, n_kv_heads, n_q_heads, head_dim, key_bits=2, value_bits=2, group=32, residual=32,
                 max_tokens=4096, n_sink=0, method="kivi", skvq_reorder=True, skvq_clip_search=True,
-                skvq_clip_alpha=1.0) -> Config:
+                skvq_clip_alpha=1.0, kitty_hi_fraction=0.25, kitty_hi_bits=4) -> Config:
     """method "kivi" (n_sink > 0: KIVI-Sink, that many high key-norm tokens per (sequence, KV head)
-    kept in fp16) or "skvq" (SKVQ-adapted: per-token groups of range-sorted channels with a
+    kept in fp16), "skvq" (SKVQ-adapted: per-token groups of range-sorted channels with a
     per-group clip search; n_sink first tokens in fp16; residual is its window, 128 by default
-    on the pages)."""
-    if method not in ("kivi", "skvq"):
-        raise ValueError(f"method must be 'kivi' or 'skvq', got {method!r}")
-    m = _lib.METHOD_SKVQ if method == "skvq" else _lib.METHOD_KIVI
+    on the pages) or "kitty" (the round(kitty_hi_fraction * head_dim) key channels of largest
+    running variance at kitty_hi_bits, the rest at key_bits; values in fp16, so value_bits is
+    16 whatever is passed)."""
+    methods = {"kivi": _lib.METHOD_KIVI, "skvq": _lib.METHOD_SKVQ, "kitty": _lib.METHOD_KITTY}
+    if method not in methods:
+        raise ValueError(f"method must be one of {sorted(methods)}, got {method!r}")
+    n_hi = 0
+    if method == "kitty":
+        if not 0.0 <= kitty_hi_fraction <= 1.0:
+            raise ValueError("kitty_hi_fraction must be in [0, 1]")
+        n_hi = int(kitty_hi_fraction * head_dim + 0.5)
+        value_bits = 16
     return Config(batch, n_kv_heads, n_q_heads, head_dim, key_bits, value_bits, group, residual, max_tokens,
-                  n_sink, m, int(bool(skvq_reorder)), int(bool(skvq_clip_search)), float(skvq_clip_alpha))
+                  n_sink, methods[method], int(bool(skvq_reorder)), int(bool(skvq_clip_search)),
+                  float(skvq_clip_alpha), n_hi, int(kitty_hi_bits))
 
 
 def _stream(stream) -> ctypes.c_void_p:

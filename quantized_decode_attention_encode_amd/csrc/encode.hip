@@ -33,6 +33,7 @@
 
 #include "kernels.h"
 #include "layout.h"
+#include "quant.h"
 
 namespace kvq {
 
@@ -93,36 +94,6 @@ __device__ __forceinline__ float pick(const float (&v)[N], int sel) {
     for (int k = 0; k < n / 2; ++k) level[k] = hi ? level[2 * k + 1] : level[2 * k];
   }
   return level[0];
-}
-
-struct GroupParams {
-  float lo, inv;
-  uint32_t packed;  // scale16 | zero16 << 16
-};
-
-// Parameters of one group from its exact min and max.
-template <int B>
-__device__ __forceinline__ GroupParams group_params(float mn, float mx) {
-  constexpr float L = float((1 << B) - 1);
-  GroupParams p;
-  const float lo = mn + 0.0f;
-  const float hi = mx + 0.0f;
-  const float s32 = (hi - lo) / L;
-  const __half sc16 = __float2half_rn(s32);
-  const float s = __half2float(sc16);
-  p.lo = lo;
-  p.inv = (s != 0.0f) ? 1.0f / s : 0.0f;
-  const uint32_t zb = __half_as_ushort(__float2half_rn(lo));  // exact: lo is an fp16 value
-  p.packed = uint32_t(__half_as_ushort(sc16)) | (zb << 16);
-  return p;
-}
-
-template <int B>
-__device__ __forceinline__ uint32_t code_of(float x, const GroupParams& p) {
-  constexpr float L = float((1 << B) - 1);
-  const float t = (x - p.lo) * p.inv;  // with inv = 0 this is 0, so a zero scale gives code 0
-  const float c = fminf(fmaxf(rintf(t), 0.0f), L);
-  return uint32_t(c);
 }
 
 // Quantize the 32-token tile (rows ks[0..31], vs[0..31], row stride D elements) into the

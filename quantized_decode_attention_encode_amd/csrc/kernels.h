@@ -71,4 +71,14 @@ hipError_t launch_decode_sink(uint8_t* buf, const Layout& L, const DecodeShape& 
                               void* out, const void* k_tok, const void* v_tok, hipStream_t s, hipEvent_t start,
                               hipEvent_t stop);
 
+// Kitty records seq.a[b] + x (x < seq.b[b]) of every (b, h) from tokens seq.c[b] + 32 x on of
+// K[b][h], V[b][h] (row stride D, ld_tok rows per (b, h)): group sums, running sums (those of
+// record 0 start from zero, later ones from the sequence's stored sums, which end updated), then
+// ranking and encoding.
+hipError_t launch_kitty_encode(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,
+                               const PerSeq& seq, int max_records, hipStream_t s);
+// Kitty decode: split kernel (partials in ws) and merge kernel (out). start/stop as above.
+hipError_t launch_kitty_decode(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q, float* ws,
+                               void* out, hipStream_t s, hipEvent_t start, hipEvent_t stop);
+
 }  // namespace kvq

@@ -1,0 +1,602 @@
+// kitty.hip - Kitty caches ("Changelog" v0.11.0, Kitty): key channels ranked by their running
+// variance, the top n_hi quantized at 4 bits and the rest at 2 bits in KIVI's per-channel
+// groups of 32 tokens, values kept in fp16 ("Algorithm Overview": Kitty stores fp16 values).
+//
+// Encode (three launches over the records a prefill, encode or window flush adds):
+//   kitty_stats_kernel   one wave per record: each channel's exact sums over the record's
+//                        32 tokens, s1 = sum X and s2 = sum X^2 with X = x * 2^24 (an integer
+//                        for every finite fp16 x; |X| < 2^40, so s1 fits int64 and s2 uint128),
+//                        staged in the record's value area.
+//   kitty_scan_kernel    one workgroup per (b, h): running sums up to each record's end (the
+//                        sequence's stored sums plus every earlier group), written back over the
+//                        staged group sums, and the new totals into the sequence's state. Integer
+//                        sums are exact in any order, so the 16 waves scan segments in parallel.
+//   kitty_encode_kernel  one wave per record: n * s2 - s1^2 (n^2 times the variance, exact in
+//                        128 bits) ranks the channels (the larger first, the lower index on
+//                        ties); the top n_hi take 4-bit groups, the rest 2-bit ones, by KIVI's
+//                        min/max rule (quant.h); codes, params and the slot table are written,
+//                        then the fp16 value rows over the staging.
+// Decode: kitty_decode_kernel, split-K over the records and window units of each (b, h_kv) with
+// an fp32 online softmax in base-2 units; kitty_merge_kernel combines the splits' partials.
+//   key lanes   lane (t = l/2, half = l%2): token t, the code chunks k = 2j + half; each code
+//               multiplies q~[slot] = q[channel] * scale[slot] (formed once per record in LDS);
+//               the zero terms add up to beta = q . zero, one number per record and head.
+//   value lanes lane (octet o, token subset): 16-byte loads of 8 fp16 values of the tokens
+//               tg, tg + 64/(D/8), ...; the subsets meet at the end of the wave.
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
+#include <stdint.h>
+
+#include "kernels.h"
+#include "layout.h"
+#include "quant.h"
+
+namespace kvq {
+namespace {
+
+typedef unsigned __int128 u128;
+constexpr int kHB = 4, kLB = 2;  // high and low key widths
+constexpr int kScanWaves = 16;
+constexpr int kDecWaves = 4;
+
+// x * 2^24 for the finite fp16 x with bits hb, exactly
+__device__ __forceinline__ int64_t fp16_fixed(uint32_t hb) {
+  const int ex = (hb >> 10) & 31;
+  const int64_t man = hb & 1023;
+  const int64_t mag = ex ? ((man | 1024) << (ex - 1)) : man;
+  return (hb & 0x8000) ? -mag : mag;
+}
+
+__device__ __forceinline__ u128 square(int64_t x) {
+  const uint64_t a = uint64_t(x < 0 ? -x : x);
+  return u128(a) * a;
+}
+
+__device__ __forceinline__ uint64_t* staging(uint8_t* buf, const Layout& L, int b, int h, int j) {
+  return reinterpret_cast<uint64_t*>(buf + L.record(b, h, j) + kitty_off_values(L.D, L.nhi));
+}
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+__device__ __forceinline__ float half_lo(uint32_t w) { return float(__builtin_bit_cast(_Float16, uint16_t(w & 0xFFFF))); }
+__device__ __forceinline__ float half_hi(uint32_t w) { return float(__builtin_bit_cast(_Float16, uint16_t(w >> 16))); }
+
+// ---------------------------------------------------------------------------------------
+// encode
+// ---------------------------------------------------------------------------------------
+// seq.a = first record, seq.b = records, seq.c = token of K[b][h] where the first one starts.
+template <int D>
+__global__ __launch_bounds__(64) void kitty_stats_kernel(uint8_t* __restrict__ buf, Layout L,
+                                                         const __half* __restrict__ K, int64_t ld_tok, PerSeq seq) {
+  const int x = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  if (x >= seq.b[b]) return;
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x;
+  const uint16_t* src = reinterpret_cast<const uint16_t*>(K) +
+                        ((int64_t(b) * L.Hkv + h) * ld_tok + seq.c[b] + int64_t(x) * kGroup) * D + lane * E;
+  int64_t s1[E];
+  u128 s2[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    s1[e] = 0;
+    s2[e] = 0;
+  }
+#pragma unroll 8
+  for (int t = 0; t < kGroup; ++t)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int64_t X = fp16_fixed(src[t * D + e]);
+      s1[e] += X;
+      s2[e] += square(X);
+    }
+  uint64_t* st = staging(buf, L, b, h, seq.a[b] + x);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int c = lane * E + e;
+    st[c] = uint64_t(s1[e]);
+    st[D + c] = uint64_t(s2[e]);
+    st[2 * D + c] = uint64_t(s2[e] >> 64);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kScanWaves) void kitty_scan_kernel(uint8_t* __restrict__ buf, Layout L, PerSeq seq) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int n = seq.b[b];
+  if (n == 0) return;  // uniform over the workgroup
+  constexpr int E = D / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ int64_t seg1[kScanWaves][D];
+  __shared__ u128 seg2[kScanWaves][D];
+  const int per = (n + kScanWaves - 1) / kScanWaves;
+  const int x0 = min(n, wave * per), x1 = min(n, x0 + per);
+  const int j0 = seq.a[b];
+  int64_t r1[E];
+  u128 r2[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    r1[e] = 0;
+    r2[e] = 0;
+  }
+#pragma unroll 4
+  for (int x = x0; x < x1; ++x) {
+    const uint64_t* p = staging(buf, L, b, h, j0 + x);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int c = lane * E + e;
+      r1[e] += int64_t(p[c]);
+      r2[e] += u128(p[D + c]) | (u128(p[2 * D + c]) << 64);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    seg1[wave][lane * E + e] = r1[e];
+    seg2[wave][lane * E + e] = r2[e];
+  }
+  __syncthreads();
+  // sums before this wave's segment: the sequence's stored sums (none before its first
+  // record: a sequence's first encode starts from zero, whatever the buffer held) plus the
+  // earlier segments
+  uint64_t* base = reinterpret_cast<uint64_t*>(buf + L.kstats(b, h));
+  const bool fresh = j0 == 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int c = lane * E + e;
+    r1[e] = fresh ? 0 : int64_t(base[c]);
+    r2[e] = fresh ? u128(0) : (u128(base[D + c]) | (u128(base[2 * D + c]) << 64));
+    for (int w = 0; w < wave; ++w) {
+      r1[e] += seg1[w][c];
+      r2[e] += seg2[w][c];
+    }
+  }
+  for (int x = x0; x < x1; ++x) {
+    uint64_t* p = staging(buf, L, b, h, j0 + x);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int c = lane * E + e;
+      r1[e] += int64_t(p[c]);
+      r2[e] += u128(p[D + c]) | (u128(p[2 * D + c]) << 64);
+      p[c] = uint64_t(r1[e]);
+      p[D + c] = uint64_t(r2[e]);
+      p[2 * D + c] = uint64_t(r2[e] >> 64);
+    }
+  }
+  __syncthreads();  // every wave has read the stored sums
+  if (wave == kScanWaves - 1) {  // its running sums now cover every group: the new totals
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int c = lane * E + e;
+      base[c] = uint64_t(r1[e]);
+      base[D + c] = uint64_t(r2[e]);
+      base[2 * D + c] = uint64_t(r2[e] >> 64);
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void kitty_encode_kernel(uint8_t* __restrict__ buf, Layout L,
+                                                          const __half* __restrict__ K, const __half* __restrict__ V,
+                                                          int64_t ld_tok, PerSeq seq) {
+  const int x = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  if (x >= seq.b[b]) return;
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x;
+  const int j = seq.a[b] + x;
+  const int nhi = L.nhi, nhc = nhi / 16, W = kitty_words(D, nhi);
+  uint8_t* rec = buf + L.record(b, h, j);
+  const int64_t row0 = ((int64_t(b) * L.Hkv + h) * ld_tok + seq.c[b] + int64_t(x) * kGroup) * D;
+  __shared__ u128 key[D];
+  __shared__ uint8_t hiflag[D];
+  __shared__ uint8_t cb[kGroup][D];  // codes by (token, slot)
+
+  // the key tile: the lane's channels over the 32 tokens
+  float kx[kGroup][E];
+#pragma unroll
+  for (int t = 0; t < kGroup; ++t)
+#pragma unroll
+    for (int e = 0; e < E; ++e) kx[t][e] = __half2float(K[row0 + int64_t(t) * D + lane * E + e]);
+  // n * s2 - s1^2 from the running sums at the group's end (staged in the value area)
+  const uint64_t* st = reinterpret_cast<const uint64_t*>(rec + kitty_off_values(D, nhi));
+  const uint64_t n = uint64_t(j + 1) * kGroup;
+  u128 my[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int c = lane * E + e;
+    const int64_t s1 = int64_t(st[c]);
+    const u128 s2 = u128(st[D + c]) | (u128(st[2 * D + c]) << 64);
+    my[e] = s2 * n - square(s1);
+    key[c] = my[e];
+  }
+  __syncthreads();
+  // rank: channels of larger spread, or of equal spread and lower index, come first
+  bool hi[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int c = lane * E + e;
+    int r = 0;
+    for (int c2 = 0; c2 < D; ++c2) {
+      const u128 k2 = key[c2];
+      r += (k2 > my[e] || (k2 == my[e] && c2 < c)) ? 1 : 0;
+    }
+    hi[e] = r < nhi;
+    hiflag[c] = hi[e] ? 1 : 0;
+  }
+  __syncthreads();
+  // slots: the high channels first, each set in ascending channel order
+  uint32_t* params = reinterpret_cast<uint32_t*>(rec + kitty_off_params(D, nhi));
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int c = lane * E + e;
+    int below = 0;
+    for (int c2 = 0; c2 < c; ++c2) below += hiflag[c2];
+    const int slot = hi[e] ? below : nhi + (c - below);
+    rec[kitty_off_table(D, nhi) + slot] = uint8_t(c);
+    float mn = kx[0][e], mx = kx[0][e];
+#pragma unroll
+    for (int t = 1; t < kGroup; ++t) {
+      mn = fminf(mn, kx[t][e]);
+      mx = fmaxf(mx, kx[t][e]);
+    }
+    if (hi[e]) {
+      const GroupParams p = group_params<kHB>(mn, mx);
+      params[slot] = p.packed;
+#pragma unroll
+      for (int t = 0; t < kGroup; ++t) cb[t][slot] = uint8_t(code_of<kHB>(kx[t][e], p));
+    } else {
+      const GroupParams p = group_params<kLB>(mn, mx);
+      params[slot] = p.packed;
+#pragma unroll
+      for (int t = 0; t < kGroup; ++t) cb[t][slot] = uint8_t(code_of<kLB>(kx[t][e], p));
+    }
+  }
+  __syncthreads();
+  // code words: token t, word w: a high chunk's half (8 slots x 4 bits) or a low chunk
+  // (16 slots x 2 bits)
+  uint32_t* cw = reinterpret_cast<uint32_t*>(rec);
+  for (int w = lane; w < kGroup * W; w += 64) {
+    const int t = w / W, wt = w % W;
+    uint32_t v = 0;
+    if (wt < 2 * nhc) {
+      const int s0 = (wt >> 1) * 16 + (wt & 1) * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v |= uint32_t(cb[t][s0 + i]) << (kHB * i);
+    } else {
+      const int s0 = (wt - nhc) * 16;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v |= uint32_t(cb[t][s0 + i]) << (kLB * i);
+    }
+    cw[w] = v;
+  }
+  // value rows, over the staging (read above, before the barriers)
+  const uint4* vs = reinterpret_cast<const uint4*>(V + row0);
+  uint4* vd = reinterpret_cast<uint4*>(rec + kitty_off_values(D, nhi));
+  for (int i = lane; i < kGroup * D / 8; i += 64) vd[i] = vs[i];
+}
+
+// ---------------------------------------------------------------------------------------
+// decode
+// ---------------------------------------------------------------------------------------
+template <int D, int G>
+struct KittyLds {
+  float qc[G][D];       // query by channel (base-2 units)
+  float qt[G][D];       // query times key scale, by slot
+  float p[G][kGroup];   // softmax weights of the unit's tokens
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(64 * kDecWaves) void kitty_decode_kernel(const uint8_t* __restrict__ buf, Layout L,
+                                                                       DecodeShape ds, const __half* __restrict__ q,
+                                                                       float* __restrict__ ws) {
+  constexpr int E = D / 64, NO = D / 8, NTG = 64 / NO, TPL = kGroup / NTG, NJ = D / 32;
+  __shared__ KittyLds<D, G> lw[kDecWaves];
+  __shared__ float res[kDecWaves][G][D + 2];
+  const int sigma = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int32_t* len = reinterpret_cast<const int32_t*>(buf + L.lengths(b, h));
+  const int nq = max(0, min(len[0], L.max_groups * kGroup));
+  const int nr = max(0, min(len[1], L.R));
+  const int ngroups = nq / kGroup;
+  const int nunits = ngroups + (nr + kGroup - 1) / kGroup;
+  const int u0 = sigma * ds.chunk;
+  if (u0 >= nunits) return;  // uniform over the workgroup
+  const int u1 = min(u0 + ds.chunk, nunits);
+  KittyLds<D, G>& W = lw[wave];
+  const int nhi = L.nhi, nhc = nhi / 16, Wd = kitty_words(D, nhi);
+  const int tk = lane >> 1, hh = lane & 1;  // key lanes
+  const int o = lane % NO, tg = lane / NO;  // value lanes
+#pragma unroll
+  for (int i = 0; i < G; ++i)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int c = lane * E + e;
+      W.qc[i][c] = __half2float(q[(int64_t(b) * ds.n_q_heads + h * G + i) * D + c]) * ds.qscale;
+    }
+  float m[G], l[G], acc[G][8];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    m[i] = -INFINITY;
+    l[i] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[i][c] = 0.f;
+  }
+  wave_sync();
+  for (int u = u0 + wave; u < u1; u += kDecWaves) {
+    float s[G];
+    const uint4* vsrc;
+    int nvalid;
+    if (u < ngroups) {
+      const uint8_t* rec = buf + L.record(b, h, u);
+      const uint32_t* cw = reinterpret_cast<const uint32_t*>(rec) + tk * Wd;
+      uint32_t w0[NJ], w1[NJ];
+#pragma unroll
+      for (int jj = 0; jj < NJ; ++jj) {
+        const int k = 2 * jj + hh;
+        const int a = k + min(k, nhc);
+        w0[jj] = cw[a];
+        w1[jj] = cw[a + 1];  // the second word of a high chunk (unused otherwise; inside the record)
+      }
+      uint32_t pr[E];
+      int tb[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        pr[e] = reinterpret_cast<const uint32_t*>(rec + kitty_off_params(D, nhi))[lane * E + e];
+        tb[e] = rec[kitty_off_table(D, nhi) + lane * E + e];
+      }
+      vsrc = reinterpret_cast<const uint4*>(rec + kitty_off_values(D, nhi));
+      nvalid = kGroup;
+      float beta[G];
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        float bp = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float qv = W.qc[i][tb[e]];
+          W.qt[i][lane * E + e] = qv * half_lo(pr[e]);
+          bp = __builtin_fmaf(qv, half_hi(pr[e]), bp);
+        }
+        beta[i] = wave_sum(bp);
+      }
+      wave_sync();
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        float a = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj) {
+          const int k = 2 * jj + hh;
+          const float* qk = &W.qt[i][16 * k];
+          if (k < nhc) {
+#pragma unroll
+            for (int ii = 0; ii < 8; ++ii) {
+              a = __builtin_fmaf(qk[ii], float((w0[jj] >> (kHB * ii)) & 15u), a);
+              a = __builtin_fmaf(qk[8 + ii], float((w1[jj] >> (kHB * ii)) & 15u), a);
+            }
+          } else {
+#pragma unroll
+            for (int ii = 0; ii < 16; ++ii) a = __builtin_fmaf(qk[ii], float((w0[jj] >> (kLB * ii)) & 3u), a);
+          }
+        }
+        s[i] = a + __shfl_xor(a, 1, 64) + beta[i];
+      }
+    } else {
+      const int tbase = (u - ngroups) * kGroup;
+      nvalid = min(kGroup, nr - tbase);
+      const __half* wk = reinterpret_cast<const __half*>(buf + L.wk_off + L.window(b, h)) + tbase * D;
+      vsrc = reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(buf + L.wv_off + L.window(b, h)) + tbase * D);
+      const int tc = min(tk, nvalid - 1);
+      const uint4* kr = reinterpret_cast<const uint4*>(wk + tc * D + hh * (D / 2));
+      uint4 kk[D / 16];
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) kk[i] = kr[i];
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        const float* qh = &W.qc[i][hh * (D / 2)];
+        float a = 0.f;
+#pragma unroll
+        for (int r = 0; r < D / 16; ++r) {
+          const uint32_t wv[4] = {kk[r].x, kk[r].y, kk[r].z, kk[r].w};
+#pragma unroll
+          for (int z = 0; z < 4; ++z) {
+            a = __builtin_fmaf(qh[8 * r + 2 * z], half_lo(wv[z]), a);
+            a = __builtin_fmaf(qh[8 * r + 2 * z + 1], half_hi(wv[z]), a);
+          }
+        }
+        s[i] = a + __shfl_xor(a, 1, 64);
+        if (tk >= nvalid) s[i] = -INFINITY;
+      }
+    }
+    // the unit's value rows (rows past nvalid clamped; their weights are 0)
+    uint4 vv[TPL];
+#pragma unroll
+    for (int k = 0; k < TPL; ++k) vv[k] = vsrc[min(tg + NTG * k, nvalid - 1) * NO + o];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const float mx = wave_max(s[i]);
+      if (mx > m[i]) {  // uniform
+        const float alpha = __builtin_amdgcn_exp2f(m[i] - mx);
+        l[i] *= alpha;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[i][c] *= alpha;
+        m[i] = mx;
+      }
+      const float p = __builtin_amdgcn_exp2f(s[i] - m[i]);
+      if (hh == 0) {
+        l[i] += p;
+        W.p[i][tk] = p;
+      }
+    }
+    wave_sync();
+#pragma unroll
+    for (int k = 0; k < TPL; ++k) {
+      const uint32_t wv[4] = {vv[k].x, vv[k].y, vv[k].z, vv[k].w};
+      float vf[8];
+#pragma unroll
+      for (int z = 0; z < 4; ++z) {
+        vf[2 * z] = half_lo(wv[z]);
+        vf[2 * z + 1] = half_hi(wv[z]);
+      }
+      const int t = tg + NTG * k;
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        const float a = W.p[i][t];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[i][c] = __builtin_fmaf(a, vf[c], acc[i][c]);
+      }
+    }
+    wave_sync();
+  }
+  // the wave's partial: l over its lanes, acc over the token subsets of each octet
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    l[i] = wave_sum(l[i]);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int msk = NO; msk < 64; msk <<= 1) acc[i][c] += __shfl_xor(acc[i][c], msk, 64);
+    if (lane < NO)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) res[wave][i][8 * o + c] = acc[i][c];
+    if (lane == 0) {
+      res[wave][i][D] = m[i];
+      res[wave][i][D + 1] = l[i];
+    }
+  }
+  __syncthreads();
+  // the workgroup's partial per query head: (acc[D], m, l) in the split's workspace slot
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kDecWaves) {
+    const int i = idx / D, c = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, res[w][i][D]);
+    float A = 0.f, Ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float mw = res[w][i][D];
+      if (mw == -INFINITY) continue;  // a wave with no unit
+      const float f = __builtin_amdgcn_exp2f(mw - M);
+      A = __builtin_fmaf(f, res[w][i][c], A);
+      Ls = __builtin_fmaf(f, res[w][i][D + 1], Ls);
+    }
+    float* p = ws + ((int64_t(b) * ds.n_q_heads + h * G + i) * ds.n_split + sigma) * (D + 4);
+    p[c] = A;
+    if (c == 0) {
+      p[D] = M;
+      p[D + 1] = Ls;
+    }
+  }
+}
+
+// One wave per (query head, sequence): the splits' partials merged into the output.
+template <int D>
+__global__ __launch_bounds__(64) void kitty_merge_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape ds,
+                                                         const float* __restrict__ ws, void* __restrict__ out) {
+  constexpr int E = D / 64;
+  const int hq = blockIdx.x, b = blockIdx.y;
+  const int h = hq / ds.G;
+  const int lane = threadIdx.x;
+  const int32_t* len = reinterpret_cast<const int32_t*>(buf + L.lengths(b, h));
+  const int nq = max(0, min(len[0], L.max_groups * kGroup));
+  const int nr = max(0, min(len[1], L.R));
+  const int nunits = nq / kGroup + (nr + kGroup - 1) / kGroup;
+  const int nv = min(ds.n_split, (nunits + ds.chunk - 1) / ds.chunk);
+  const float* p0 = ws + (int64_t(b) * ds.n_q_heads + hq) * ds.n_split * (D + 4);
+  float M = -INFINITY;
+  for (int sg = 0; sg < nv; ++sg) M = fmaxf(M, p0[sg * (D + 4) + D]);
+  float A[E], Ls = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) A[e] = 0.f;
+  for (int sg = 0; sg < nv; ++sg) {
+    const float* p = p0 + sg * (D + 4);
+    const float f = __builtin_amdgcn_exp2f(p[D] - M);
+    Ls = __builtin_fmaf(f, p[D + 1], Ls);
+#pragma unroll
+    for (int e = 0; e < E; ++e) A[e] = __builtin_fmaf(f, p[lane * E + e], A[e]);
+  }
+  const float inv = 1.0f / Ls;
+  const int64_t o0 = (int64_t(b) * ds.n_q_heads + hq) * D;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const float v = A[e] * inv;
+    if (ds.out_fp32)
+      static_cast<float*>(out)[o0 + lane * E + e] = v;
+    else
+      static_cast<__half*>(out)[o0 + lane * E + e] = __float2half_rn(v);
+  }
+}
+
+template <int D>
+hipError_t kitty_encode_d(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,
+                          const PerSeq& seq, int max_records, hipStream_t s) {
+  const dim3 grid(max_records, L.Hkv, L.B);
+  const __half* kh = static_cast<const __half*>(K);
+  const __half* vh = static_cast<const __half*>(V);
+  hipLaunchKernelGGL(kitty_stats_kernel<D>, grid, dim3(64), 0, s, buf, L, kh, ld_tok, seq);
+  hipLaunchKernelGGL(kitty_scan_kernel<D>, dim3(L.Hkv, L.B), dim3(64 * kScanWaves), 0, s, buf, L, seq);
+  hipLaunchKernelGGL(kitty_encode_kernel<D>, grid, dim3(64), 0, s, buf, L, kh, vh, ld_tok, seq);
+  return hipGetLastError();
+}
+
+template <int D, int G>
+hipError_t kitty_decode_t(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q, float* ws, void* out,
+                          hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  const dim3 grid(ds.n_split, L.Hkv, L.B);
+  const uint8_t* cb = buf;
+  const __half* qh = static_cast<const __half*>(q);
+  if (e0 || e1) {
+    hipExtLaunchKernelGGL((kitty_decode_kernel<D, G>), grid, dim3(64 * kDecWaves), 0, s, e0, nullptr, 0, cb, L, ds,
+                          qh, ws);
+    hipExtLaunchKernelGGL((kitty_merge_kernel<D>), dim3(ds.n_q_heads, L.B), dim3(64), 0, s, nullptr, e1, 0, cb, L,
+                          ds, static_cast<const float*>(ws), out);
+  } else {
+    hipLaunchKernelGGL((kitty_decode_kernel<D, G>), grid, dim3(64 * kDecWaves), 0, s, cb, L, ds, qh, ws);
+    hipLaunchKernelGGL((kitty_merge_kernel<D>), dim3(ds.n_q_heads, L.B), dim3(64), 0, s, cb, L, ds,
+                       static_cast<const float*>(ws), out);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t kitty_decode_d(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q, float* ws, void* out,
+                          hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  switch (ds.G) {
+    case 1: return kitty_decode_t<D, 1>(buf, L, ds, q, ws, out, s, e0, e1);
+    case 2: return kitty_decode_t<D, 2>(buf, L, ds, q, ws, out, s, e0, e1);
+    case 4: return kitty_decode_t<D, 4>(buf, L, ds, q, ws, out, s, e0, e1);
+    case 8: return kitty_decode_t<D, 8>(buf, L, ds, q, ws, out, s, e0, e1);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kitty_encode(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,
+                               const PerSeq& seq, int max_records, hipStream_t s) {
+  if (max_records <= 0) return hipSuccess;
+  if (L.D == 128) return kitty_encode_d<128>(buf, L, K, V, ld_tok, seq, max_records, s);
+  if (L.D == 64) return kitty_encode_d<64>(buf, L, K, V, ld_tok, seq, max_records, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_kitty_decode(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q, float* ws,
+                               void* out, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (L.D == 128) return kitty_decode_d<128>(buf, L, ds, q, ws, out, s, e0, e1);
+  if (L.D == 64) return kitty_decode_d<64>(buf, L, ds, q, ws, out, s, e0, e1);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvq

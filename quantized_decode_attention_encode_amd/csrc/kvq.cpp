@@ -78,9 +78,19 @@ kvq_status check_config(const kvq_config* c) {
     return fail(KVQ_E_UNSUPPORTED, "query heads per KV head must be 1, 2, 4 or 8, got %d", G);
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(KVQ_E_UNSUPPORTED, "head_dim must be 64 or 128, got %d", c->head_dim);
-  for (int bits : {c->key_bits, c->value_bits})
-    if (bits != 2 && bits != 4 && bits != 8)
-      return fail(KVQ_E_UNSUPPORTED, "bit widths must be 2, 4 or 8, got %d", bits);
+  if (c->method == KVQ_METHOD_KITTY) {
+    if (c->key_bits != 2 || c->kitty_hi_bits != 4)
+      return fail(KVQ_E_UNSUPPORTED, "Kitty key widths must be 2 (key_bits) and 4 (kitty_hi_bits), got %d and %d",
+                  c->key_bits, c->kitty_hi_bits);
+    if (c->value_bits != 16) return fail(KVQ_E_INVALID, "Kitty keeps values in fp16: value_bits must be 16, got %d", c->value_bits);
+    if (c->kitty_n_hi < 0 || c->kitty_n_hi > c->head_dim || c->kitty_n_hi % 16)
+      return fail(KVQ_E_UNSUPPORTED, "kitty_n_hi must be a multiple of 16 in [0, head_dim], got %d", c->kitty_n_hi);
+    if (c->n_sink != 0) return fail(KVQ_E_UNSUPPORTED, "Kitty caches take no sink tokens (n_sink = %d)", c->n_sink);
+  } else {
+    for (int bits : {c->key_bits, c->value_bits})
+      if (bits != 2 && bits != 4 && bits != 8)
+        return fail(KVQ_E_UNSUPPORTED, "bit widths must be 2, 4 or 8, got %d", bits);
+  }
   if (c->group != kvq::kGroup) return fail(KVQ_E_UNSUPPORTED, "group size must be 32, got %d", c->group);
   if (c->residual < kvq::kGroup || c->residual > kMaxResidual || c->residual % kvq::kGroup)
     return fail(KVQ_E_INVALID, "residual must be a multiple of 32 in [32, %d], got %d", kMaxResidual, c->residual);
@@ -89,8 +99,9 @@ kvq_status check_config(const kvq_config* c) {
   if (c->max_tokens > (1 << 26)) return fail(KVQ_E_INVALID, "max_tokens above 2^26");
   if (c->n_sink < 0 || c->n_sink > kvq::kMaxSinks)
     return fail(KVQ_E_INVALID, "n_sink must be in [0, %d], got %d", kvq::kMaxSinks, c->n_sink);
-  if (c->method != KVQ_METHOD_KIVI && c->method != KVQ_METHOD_SKVQ)
-    return fail(KVQ_E_UNSUPPORTED, "method must be KVQ_METHOD_KIVI or KVQ_METHOD_SKVQ, got %d", c->method);
+  if (c->method != KVQ_METHOD_KIVI && c->method != KVQ_METHOD_SKVQ && c->method != KVQ_METHOD_KITTY)
+    return fail(KVQ_E_UNSUPPORTED, "method must be KVQ_METHOD_KIVI, KVQ_METHOD_SKVQ or KVQ_METHOD_KITTY, got %d",
+                c->method);
   if (c->method == KVQ_METHOD_SKVQ) {
     if ((c->skvq_reorder != 0 && c->skvq_reorder != 1) || (c->skvq_clip_search != 0 && c->skvq_clip_search != 1))
       return fail(KVQ_E_INVALID, "skvq_reorder and skvq_clip_search must be 0 or 1");
@@ -101,14 +112,18 @@ kvq_status check_config(const kvq_config* c) {
 }
 
 bool is_skvq(const kvq_config& c) { return c.method == KVQ_METHOD_SKVQ; }
+bool is_kitty(const kvq_config& c) { return c.method == KVQ_METHOD_KITTY; }
 
 Layout make_layout(const kvq_config* c) {
   Layout L;
   const bool sk = c->method == KVQ_METHOD_SKVQ;
+  const bool kt = c->method == KVQ_METHOD_KITTY;
   // the fixed clip fraction in fp32 operations, or -1 for the search
   const float clip = (sk && !c->skvq_clip_search) ? (1.0f - c->skvq_clip_alpha) * 0.5f : -1.0f;
-  L.init(c->batch, c->n_kv_heads, c->head_dim, c->key_bits, c->value_bits, c->residual, c->max_tokens, c->n_sink,
-         c->method, clip, sk ? c->skvq_reorder : 1);
+  // Kitty: (bk, bv) = (2, 2) selects the append kernel instance, which only stores tokens for
+  // these caches (their windows are flushed by the Kitty encode launches)
+  L.init(c->batch, c->n_kv_heads, c->head_dim, c->key_bits, kt ? c->key_bits : c->value_bits, c->residual,
+         c->max_tokens, c->n_sink, c->method, clip, sk ? c->skvq_reorder : 1, kt ? c->kitty_n_hi : 0);
   return L;
 }
 
@@ -199,6 +214,8 @@ kvq_status decode_enqueue(kvq_cache* c, const void* q, void* out, int32_t out_fp
   const kvq_config& cfg = c->cfg;
   const int add = k_tok ? 1 : 0;  // window tokens the launch appends
   const int G = cfg.n_q_heads / cfg.n_kv_heads;
+  if (is_kitty(cfg) && (n_query != 1 || k_tok))
+    return fail(KVQ_E_UNSUPPORTED, "Kitty caches attend one query per head, after a separate append");
   if (n_query < 1 || (n_query & (n_query - 1)) || G * n_query > 8)
     return fail(KVQ_E_UNSUPPORTED, "n_query = %d: it must be a power of two with n_query x (query heads per KV head = %d) <= 8",
                 n_query, G);
@@ -255,8 +272,12 @@ kvq_status decode_enqueue(kvq_cache* c, const void* q, void* out, int32_t out_fp
   }
   // With profiling on, the events are stamped by the kernel's own dispatch packet, so their
   // interval is its execution time (no queue or launch latency).
-  e = kvq::launch_decode(c->buf, c->L, ds, q, ws, out, k_tok, v_tok, s, prof ? c->ev[c->ev_used] : nullptr,
-                         prof ? c->ev[c->ev_used + 1] : nullptr);
+  if (is_kitty(cfg))
+    e = kvq::launch_kitty_decode(c->buf, c->L, ds, q, ws, out, s, prof ? c->ev[c->ev_used] : nullptr,
+                                 prof ? c->ev[c->ev_used + 1] : nullptr);
+  else
+    e = kvq::launch_decode(c->buf, c->L, ds, q, ws, out, k_tok, v_tok, s, prof ? c->ev[c->ev_used] : nullptr,
+                           prof ? c->ev[c->ev_used + 1] : nullptr);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (prof) c->ev_used += 2;
   if (add)
@@ -313,6 +334,15 @@ kvq_status kvq_layout(const kvq_config* cfg, kvq_layout_info* out) {
   out->sink_k_offset = L.sk_off;
   out->sink_v_offset = L.sv_off;
   out->perm_offset = L.pm_off;
+  out->rec_slot_table = 0;
+  out->kstats_offset = L.ks_off;
+  if (is_kitty(*cfg)) {
+    out->rec_key_codes = 0;
+    out->rec_key_params = kvq::kitty_off_params(L.D, L.nhi);
+    out->rec_slot_table = kvq::kitty_off_table(L.D, L.nhi);
+    out->rec_value_codes = kvq::kitty_off_values(L.D, L.nhi);
+    out->rec_value_params = 0;
+  }
   return ok();
 }
 
@@ -421,7 +451,10 @@ kvq_status kvq_encode(kvq_cache* c, const void* K, const void* V, int64_t ld_tok
     e = kvq::launch_sink_select(c->buf, c->L, K, V, ld_tok, sel, s);
     if (e != hipSuccess) return hip_fail(e, "sink selection launch");
   }
-  e = kvq::launch_encode(c->buf, c->L, K, V, ld_tok, enc, max_rec, s);
+  if (is_kitty(c->cfg))
+    e = kvq::launch_kitty_encode(c->buf, c->L, K, V, ld_tok, enc, max_rec, s);  // enc.c = 0: blocks start at token 0
+  else
+    e = kvq::launch_encode(c->buf, c->L, K, V, ld_tok, enc, max_rec, s);
   if (e != hipSuccess) return hip_fail(e, "encode launch");
   e = kvq::launch_lengths_fill(c->buf, c->L, len, s, 0);
   if (e != hipSuccess) return hip_fail(e, "lengths launch");
@@ -499,6 +532,9 @@ kvq_status kvq_prefill(kvq_cache* c, const void* K, const void* V, int64_t ld_to
     if (e != hipSuccess) return hip_fail(e, "permutation launch");
     e = kvq::launch_skvq_encode(c->buf, c->L, K, V, ld_tok, enc, max_rec, 0, s);
     if (e != hipSuccess) return hip_fail(e, "encode launch");
+  } else if (max_rec && is_kitty(c->cfg)) {
+    hipError_t e = kvq::launch_kitty_encode(c->buf, c->L, K, V, ld_tok, enc, max_rec, s);
+    if (e != hipSuccess) return hip_fail(e, "encode launch");
   } else if (max_rec) {
     hipError_t e;
     if (c->cfg.n_sink > 0) {
@@ -568,6 +604,26 @@ kvq_status kvq_append(kvq_cache* c, const void* k_tok, const void* v_tok, void* 
       if (e != hipSuccess) return hip_fail(e, "flush launch");
     }
   }
+  if (is_kitty(c->cfg)) {
+    // full windows are quantized by the Kitty encode launches (their window rows are the source);
+    // the append kernel then sees an empty window
+    PerSeq fl;
+    memset(&fl, 0, sizeof fl);
+    bool any = false;
+    for (int b = 0; b < c->cfg.batch; ++b) {
+      if (c->nr[b] < c->cfg.residual) continue;
+      any = true;
+      fl.a[b] = c->nq[b] / kvq::kGroup;
+      fl.b[b] = c->cfg.residual / kvq::kGroup;
+      len.a[b] = c->nq[b] + c->cfg.residual;
+      len.b[b] = 0;
+    }
+    if (any) {
+      hipError_t e = kvq::launch_kitty_encode(c->buf, c->L, c->buf + c->L.wk_off, c->buf + c->L.wv_off,
+                                              c->cfg.residual, fl, c->cfg.residual / kvq::kGroup, s);
+      if (e != hipSuccess) return hip_fail(e, "flush launch");
+    }
+  }
   hipError_t e = kvq::launch_append(c->buf, c->L, k_tok, v_tok, len, s);
   if (e != hipSuccess) return hip_fail(e, "append launch");
   for (int b = 0; b < c->cfg.batch; ++b) {
@@ -614,6 +670,7 @@ kvq_status kvq_append_decode_attend(kvq_cache* c, const void* k_tok, const void*
     // an SKVQ token that becomes a sink is the append kernel's work too
     flush = flush || (is_skvq(c->cfg) && c->nsp[b] < c->cfg.n_sink);
   }
+  flush = flush || is_kitty(c->cfg);  // Kitty decode reads no appended token: append first
   if (flush) {  // some window is full: the append kernel quantizes it, then a plain decode
     kvq_status st = kvq_append(c, k_tok, v_tok, stream);
     if (st != KVQ_OK) return st;

@@ -10,6 +10,8 @@
 //   sink_k   fp16  [B][H_kv][NS][D]             the sinks' key and value rows, unquantized
 //   sink_v   fp16  [B][H_kv][NS][D]
 //   perm     uint8 [B][H_kv][2][D]              SKVQ only: channel permutations of K and V
+//   kstats   [B][H_kv] x (int64 s1[D], uint64 s2lo[D], uint64 s2hi[D])
+//                                               Kitty only: exact running key sums per channel
 // Every region but sync starts on a 256-byte boundary (sync follows lengths directly). With
 // NS = 0 the three sink regions are empty and the buffer is the plain KIVI cache. A sink
 // position of -1 marks an empty slot: the sinks present are the leading non-negative entries.
@@ -21,6 +23,16 @@
 // channels too. Their sinks are the first NS tokens of the sequence. Once a sequence has
 // quantized tokens (and so its permutations), its window and sink rows are stored permuted as
 // well: slot c of a key row holds channel perm_k[c], of a value row channel perm_v[c].
+//
+// Kitty caches ("Changelog" v0.11.0) use records of their own (kitty_* below): per token the
+// key codes of the slots, slot s holding channel table[s]: slots 0 .. nhi-1 are the high-width
+// channels in ascending order at HB = 4 bits, the rest the low-width ones at LB = 2 bits; in
+// chunks of 16 slots, a high chunk taking two u32 words and a low chunk one, chunk k at word
+// k + min(k, nhi/16) of the token, slot 16k+i at bit i*bits of its chunk (little-endian across a
+// high chunk's two words); then the key params [slot] (scale | zero << 16), the slot table
+// (uint8 [D]) and the fp16 value rows [32][D] (values are not quantized). Before a record is
+// encoded its value area stages the key sums of its group (s1[D] int64, s2 lo[D], s2 hi[D]
+// uint64), and then the running sums up to the group's end.
 //
 // A record holds everything decode needs for 32 tokens, so one group streams from one
 // contiguous 4*D*(bk+bv+2)-byte block (3 KiB at D=128, 2/2 bits):
@@ -52,7 +64,7 @@ namespace kvq {
 constexpr int kGroup = 32;     // tokens per key group == channels per value group
 constexpr int kMaxBatch = 256;
 constexpr int kMaxSinks = 16;  // sink tokens per (sequence, KV head)
-constexpr int kMethodKivi = 0, kMethodSkvq = 1;
+constexpr int kMethodKivi = 0, kMethodSkvq = 1, kMethodKitty = 2;
 
 KVQ_HD constexpr uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
@@ -68,18 +80,29 @@ KVQ_HD constexpr uint64_t rec_off_vparams(int D, int bk, int bv) {
   return rec_off_kparams(D, bk, bv) + param_bytes(D);
 }
 
+// Kitty records (HB = 4, LB = 2): u32 code words per token, and the offsets inside a record.
+KVQ_HD constexpr int kitty_words(int D, int nhi) { return D / 16 + nhi / 16; }
+KVQ_HD constexpr uint64_t kitty_off_params(int D, int nhi) { return 128ull * kitty_words(D, nhi); }
+KVQ_HD constexpr uint64_t kitty_off_table(int D, int nhi) { return kitty_off_params(D, nhi) + 4ull * D; }
+KVQ_HD constexpr uint64_t kitty_off_values(int D, int nhi) { return (kitty_off_table(D, nhi) + D + 15) & ~15ull; }
+KVQ_HD constexpr uint64_t kitty_record_bytes(int D, int nhi) {
+  return (kitty_off_values(D, nhi) + 64ull * D + 127) & ~127ull;
+}
+
 // Offsets of the regions of one cache buffer.
 struct Layout {
   int B, Hkv, D, bk, bv, R, max_groups, NS, method, reorder;
   float clip;  // SKVQ: the fixed clip fraction (1 - alpha) / 2, or < 0 for the search
-  uint64_t len_off, sync_off, rec_off, rec_bytes, wk_off, wv_off, sp_off, sk_off, sv_off, pm_off, total;
+  int nhi;     // Kitty: high-width key channels (a multiple of 16)
+  uint64_t len_off, sync_off, rec_off, rec_bytes, wk_off, wv_off, sp_off, sk_off, sv_off, pm_off, ks_off, total;
 
   KVQ_HD void init(int B_, int Hkv_, int D_, int bk_, int bv_, int R_, int max_tokens, int NS_, int method_ = 0,
-                   float clip_ = -1.0f, int reorder_ = 1) {
+                   float clip_ = -1.0f, int reorder_ = 1, int nhi_ = 0) {
     B = B_; Hkv = Hkv_; D = D_; bk = bk_; bv = bv_; R = R_; NS = NS_; method = method_; clip = clip_;
     reorder = reorder_;
+    nhi = nhi_;
     max_groups = max_tokens / kGroup;
-    rec_bytes = record_bytes(D, bk, bv);
+    rec_bytes = method == kMethodKitty ? kitty_record_bytes(D, nhi) : record_bytes(D, bk, bv);
     len_off = 0;
     sync_off = uint64_t(B) * Hkv * 2 * sizeof(int32_t);
     rec_off = align256(sync_off + uint64_t(B) * Hkv * sizeof(uint32_t));
@@ -91,7 +114,8 @@ struct Layout {
     const uint64_t sbytes = uint64_t(B) * Hkv * NS * D * 2;
     sv_off = align256(sk_off + sbytes);
     pm_off = align256(sv_off + sbytes);
-    total = align256(pm_off + (method == kMethodSkvq ? uint64_t(B) * Hkv * 2 * D : 0));
+    ks_off = align256(pm_off + (method == kMethodSkvq ? uint64_t(B) * Hkv * 2 * D : 0));
+    total = align256(ks_off + (method == kMethodKitty ? uint64_t(B) * Hkv * 24 * D : 0));
   }
   // record j of (b, h)
   KVQ_HD uint64_t record(int b, int h, int j) const {
@@ -107,6 +131,8 @@ struct Layout {
   KVQ_HD uint64_t sink_v(int b, int h) const { return sv_off + (uint64_t(b) * Hkv + h) * NS * D * 2; }
   // SKVQ: permutation of K (D bytes) then of V: permuted channel j is channel perm[j]
   KVQ_HD uint64_t perm(int b, int h) const { return pm_off + (uint64_t(b) * Hkv + h) * 2 * D; }
+  // Kitty: running key sums of (b, h): s1 int64 [D], s2 low words uint64 [D], s2 high words [D]
+  KVQ_HD uint64_t kstats(int b, int h) const { return ks_off + (uint64_t(b) * Hkv + h) * 24 * D; }
 };
 
 }  // namespace kvq

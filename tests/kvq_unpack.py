@@ -19,9 +19,20 @@ def align256(x: int) -> int:
     return (x + 255) // 256 * 256
 
 
-def offsets(B, Hkv, D, bk, bv, R, max_tokens, NS=0, skvq=False):
+def kitty_record(D: int, n_hi: int) -> dict:
+    """Offsets inside a Kitty record: (D + n_hi)/16 code words per token, then (scale, zero) per
+    slot, the slot table, and the fp16 value rows [32][D] (16-byte aligned); 128-byte records."""
+    W = D // 16 + n_hi // 16
+    o = {"words": W, "params": 128 * W}
+    o["table"] = o["params"] + 4 * D
+    o["values"] = (o["table"] + D + 15) // 16 * 16
+    o["bytes"] = (o["values"] + 64 * D + 127) // 128 * 128
+    return o
+
+
+def offsets(B, Hkv, D, bk, bv, R, max_tokens, NS=0, skvq=False, kitty_n_hi=None):
     max_groups = max_tokens // 32
-    rec = 4 * D * (bk + bv + 2)
+    rec = 4 * D * (bk + bv + 2) if kitty_n_hi is None else kitty_record(D, kitty_n_hi)["bytes"]
     o = {"lengths": 0, "sync": B * Hkv * 2 * 4}
     o["records"] = align256(o["sync"] + B * Hkv * 4)
     o["record_bytes"] = rec
@@ -36,7 +47,8 @@ def offsets(B, Hkv, D, bk, bv, R, max_tokens, NS=0, skvq=False):
     o["sink_k"] = align256(o["sink_pos"] + B * Hkv * NS * 4)
     o["sink_v"] = align256(o["sink_k"] + B * Hkv * NS * D * 2)
     o["perm"] = align256(o["sink_v"] + B * Hkv * NS * D * 2)
-    o["total"] = align256(o["perm"] + (B * Hkv * 2 * D if skvq else 0))
+    o["kstats"] = align256(o["perm"] + (B * Hkv * 2 * D if skvq else 0))
+    o["total"] = align256(o["kstats"] + (B * Hkv * 24 * D if kitty_n_hi is not None else 0))
     o["max_groups"] = max_groups
     o["NS"] = NS
     return o
@@ -75,6 +87,62 @@ def unpack_records(recs: np.ndarray, D: int, bk: int, bv: int, skvq: bool = Fals
     vz = vp[..., 1].view(np.float16)
     out = {"kc": kc, "ks": ks, "kz": kz, "vc": vc, "vs": vs, "vz": vz}
     return {k: np.ascontiguousarray(v) for k, v in out.items()}
+
+
+def unpack_kitty_records(recs: np.ndarray, D: int, n_hi: int):
+    """Kitty records as bytes [n, record_bytes] -> channel-order logical arrays: key codes
+    [32n, D], scale / zero [n, D] (fp16), the high-width mask [n, D] and the fp16 values [32n, D]."""
+    n = recs.shape[0]
+    o = kitty_record(D, n_hi)
+    W, nhc = o["words"], n_hi // 16
+    words = np.ascontiguousarray(recs[:, :128 * W]).view("<u4").reshape(n, 32, W).astype(np.uint64)
+    slot = np.zeros((n, 32, D), np.uint8)
+    for k in range(D // 16):
+        if k < nhc:  # 16 4-bit codes over words 2k, 2k+1
+            w = words[..., 2 * k] | (words[..., 2 * k + 1] << np.uint64(32))
+            bits = 4
+        else:  # 16 2-bit codes in word k + nhc
+            w = words[..., k + nhc]
+            bits = 2
+        for i in range(16):
+            slot[..., 16 * k + i] = ((w >> np.uint64(bits * i)) & np.uint64((1 << bits) - 1)).astype(np.uint8)
+    table = recs[:, o["table"]:o["table"] + D].astype(np.int64)
+    prm = np.ascontiguousarray(recs[:, o["params"]:o["params"] + 4 * D]).view("<u2").reshape(n, D, 2)
+    kc = np.zeros((n, 32, D), np.uint8)
+    ks = np.zeros((n, D), np.uint16)
+    kz = np.zeros((n, D), np.uint16)
+    hi = np.zeros((n, D), bool)
+    for r in range(n):
+        kc[r][:, table[r]] = slot[r]
+        ks[r, table[r]] = prm[r, :, 0]
+        kz[r, table[r]] = prm[r, :, 1]
+        hi[r, table[r]] = np.arange(D) < n_hi
+    vq = np.ascontiguousarray(recs[:, o["values"]:o["values"] + 64 * D]).view(np.float16).reshape(n * 32, D)
+    return {"kc": kc.reshape(n * 32, D), "ks": ks.view(np.float16), "kz": kz.view(np.float16), "khi": hi,
+            "vq": vq.copy(), "table": table}
+
+
+def unpack_kitty_sequence(buf: np.ndarray, cfg: dict, b: int, h: int):
+    """Kitty (b, h): records, window and the running key sums (Python ints) from the buffer."""
+    B, Hkv, D, R, n_hi = (cfg[k] for k in ("B", "Hkv", "D", "R", "n_hi"))
+    o = offsets(B, Hkv, D, 2, 2, R, cfg["max_tokens"], 0, False, n_hi)
+    L = lengths(buf, B, Hkv)
+    n_q, n_r = int(L[b, h, 0]), int(L[b, h, 1])
+    ng = n_q // 32
+    start = o["records"] + (b * Hkv + h) * o["max_groups"] * o["record_bytes"]
+    recs = buf[start:start + ng * o["record_bytes"]].reshape(ng, o["record_bytes"])
+    cat = unpack_kitty_records(recs, D, n_hi)
+    w0 = ((b * Hkv + h) * R) * D * 2
+    cat["wk"] = buf[o["window_k"] + w0:o["window_k"] + w0 + R * D * 2].view(np.float16).reshape(R, D)[:n_r].copy()
+    cat["wv"] = buf[o["window_v"] + w0:o["window_v"] + w0 + R * D * 2].view(np.float16).reshape(R, D)[:n_r].copy()
+    st = buf[o["kstats"] + (b * Hkv + h) * 24 * D:o["kstats"] + (b * Hkv + h + 1) * 24 * D]
+    s1 = st[:8 * D].view("<i8")
+    lo = st[8 * D:16 * D].view("<u8")
+    hi = st[16 * D:].view("<u8")
+    cat["s1"] = [int(v) for v in s1]
+    cat["s2"] = [int(a) + (int(c) << 64) for a, c in zip(lo, hi)]
+    cat["n_q"], cat["n_r"] = n_q, n_r
+    return cat
 
 
 def unpack_record(rec: np.ndarray, D: int, bk: int, bv: int):

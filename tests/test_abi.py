@@ -38,7 +38,7 @@ def declared_functions():
 def cfg(**kw):
     base = dict(batch=2, n_kv_heads=4, n_q_heads=8, head_dim=128, key_bits=2, value_bits=4, group=32,
                 residual=32, max_tokens=1024, n_sink=0, method=0, skvq_reorder=1, skvq_clip_search=1,
-                skvq_clip_alpha=1.0)
+                skvq_clip_alpha=1.0, kitty_n_hi=0, kitty_hi_bits=4)
     base.update(kw)
     return Config(*(base[f] for f, _ in Config._fields_))
 
@@ -69,7 +69,7 @@ def test_probe_without_gpu_reports_absence():
     ("key_bits", 3, KVQ_E_UNSUPPORTED), ("value_bits", 1, KVQ_E_UNSUPPORTED), ("group", 64, KVQ_E_UNSUPPORTED),
     ("residual", 48, KVQ_E_INVALID), ("residual", 0, KVQ_E_INVALID), ("residual", 288, KVQ_E_INVALID),
     ("max_tokens", 1000, KVQ_E_INVALID), ("max_tokens", 0, KVQ_E_INVALID),
-    ("n_sink", -1, KVQ_E_INVALID), ("n_sink", 17, KVQ_E_INVALID), ("method", 2, KVQ_E_UNSUPPORTED),
+    ("n_sink", -1, KVQ_E_INVALID), ("n_sink", 17, KVQ_E_INVALID), ("method", 3, KVQ_E_UNSUPPORTED),
 ])
 def test_config_validation(field, value, status):
     c = cfg(**{field: value})
@@ -116,6 +116,54 @@ def test_skvq_config_validation_and_layout(alpha, search, reorder, status):
     o = kvq_unpack.offsets(2, 4, 128, 2, 4, 128, 1024, 5, skvq=True)
     assert (info.perm_offset, info.total_bytes) == (o["perm"], o["total"])
     assert info.total_bytes - info.perm_offset >= 2 * 4 * 2 * 128
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), KVQ_OK), (dict(kitty_n_hi=0), KVQ_OK), (dict(kitty_n_hi=128), KVQ_OK),
+    (dict(kitty_n_hi=24), KVQ_E_UNSUPPORTED), (dict(kitty_n_hi=144), KVQ_E_UNSUPPORTED),
+    (dict(kitty_n_hi=-16), KVQ_E_UNSUPPORTED), (dict(value_bits=2), KVQ_E_INVALID),
+    (dict(key_bits=4), KVQ_E_UNSUPPORTED), (dict(kitty_hi_bits=8), KVQ_E_UNSUPPORTED),
+    (dict(n_sink=2), KVQ_E_UNSUPPORTED)])
+def test_kitty_config_validation(kw, status):
+    base = dict(method=2, value_bits=16, kitty_n_hi=32)
+    base.update(kw)
+    c = cfg(**base)
+    assert lib.kvq_config_check(ctypes.byref(c)) == status
+
+
+@pytest.mark.parametrize("D,n_hi,B,H,R", [(128, 32, 1, 32, 32), (64, 16, 3, 2, 64), (128, 0, 2, 4, 32),
+                                          (128, 128, 2, 1, 32)])
+def test_kitty_layout_matches_independent_formula(D, n_hi, B, H, R):
+    c = cfg(method=2, value_bits=16, kitty_n_hi=n_hi, head_dim=D, batch=B, n_kv_heads=H, n_q_heads=H, residual=R,
+            max_tokens=2048)
+    info = LayoutInfo()
+    assert lib.kvq_layout(ctypes.byref(c), ctypes.byref(info)) == KVQ_OK
+    o = kvq_unpack.offsets(B, H, D, 2, 2, R, 2048, 0, False, n_hi)
+    r = kvq_unpack.kitty_record(D, n_hi)
+    assert info.record_bytes == o["record_bytes"] == r["bytes"]
+    assert (info.rec_key_codes, info.rec_key_params, info.rec_slot_table, info.rec_value_codes) == (
+        0, r["params"], r["table"], r["values"])
+    assert (info.kstats_offset, info.total_bytes) == (o["kstats"], o["total"])
+    assert info.total_bytes == lib.kvq_cache_bytes(ctypes.byref(c))
+    assert info.total_bytes - info.kstats_offset >= B * H * 24 * D
+
+
+def test_kitty_record_at_the_headline_shape():
+    # D = 128, 32 channels at 4 bits: 40 B of key codes per token (2.5 bits a channel), 512 B of
+    # key params, 128 B of slot table, 8 KiB of fp16 values
+    r = kvq_unpack.kitty_record(128, 32)
+    assert (r["words"] * 4, r["params"], r["table"], r["values"], r["bytes"]) == (40, 1280, 1792, 1920, 10112)
+
+
+def test_kitty_rejects_multi_query():
+    c = cfg(method=2, value_bits=16, kitty_n_hi=32)
+    cache = ctypes.c_void_p()
+    buf = ctypes.c_void_p(FAKE)
+    assert lib.kvq_cache_create(ctypes.byref(c), buf, lib.kvq_cache_bytes(ctypes.byref(c)), ctypes.byref(cache)) == KVQ_OK
+    ws = ctypes.c_void_p(FAKE)
+    st = lib.kvq_decode_attend_multi(cache, buf, buf, 2, 0, ctypes.c_float(1.0), ws, 1 << 30, 0, None)
+    assert st == KVQ_E_UNSUPPORTED
+    lib.kvq_cache_destroy(cache)
 
 
 def test_skvq_cache_rejects_encode():

@@ -1,0 +1,172 @@
+"""GPU parity for Kitty caches ("Changelog" v0.11.0, Kitty) through the C ABI.
+
+The cache state (per key group the high-width channel set, the 4- and 2-bit codes and their
+fp16 (scale, zero), the fp16 values, the window and the exact running key sums) must equal the
+oracle's bit for bit after prefill, after encode calls and after appends across window flushes;
+attention must be within the tolerance of the fp64 oracle for several split counts. Cases cover
+D = 64 and 128, no / a quarter / half / all channels at 4 bits, query-head groups 1..8, empty,
+one-token and window-only sequences.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import kitty
+from quantized_decode_attention_encode_amd import (KVQCache, kvq_append, kvq_append_decode_attend, kvq_decode_attend,
+                                                   kvq_encode, kvq_prefill, make_config, workloads)
+from tests import kvq_unpack
+from tests.gpu_helpers import assert_close, host_buffer, oracle_attend, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+CASES = [
+    # name, B, Hq, Hkv, D, hi_fraction, lengths, R
+    ("d128-quarter-mha", 2, 4, 4, 128, 0.25, [700, 133], 32),
+    ("d64-quarter-gqa2", 3, 4, 2, 64, 0.25, [300, 1, 36], 32),
+    ("d128-none-gqa4-R64", 2, 8, 2, 128, 0.0, [400, 64], 64),
+    ("d128-all-gqa8", 2, 8, 1, 128, 1.0, [330, 90], 32),
+    ("d128-half-R64", 2, 2, 2, 128, 0.5, [250, 17], 64),
+]
+
+
+def make(case, seed=41, lens=None):
+    name, B, Hq, Hkv, D, frac, lengths, R = case
+    wl = workloads.custom(name=name, batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, key_bits=2, value_bits=2,
+                          n_outlier=3, seed=seed, residual=R, ragged=(1, 2))
+    draw = workloads.Draw(wl, seq_lens=lens if lens is not None else lengths)
+    cfg = make_config(B, Hkv, Hq, D, 2, 16, 32, R, 1024, method="kitty", kitty_hi_fraction=frac)
+    return wl, draw, cfg
+
+
+def oracle_seq(wl, cfg):
+    return kitty.KittySequence(wl.head_dim, cfg.kitty_n_hi, 4, 2, 32, cfg.residual)
+
+
+def assert_kitty_state(buf, cfg, seqs, what=""):
+    cd = {"B": cfg.batch, "Hkv": cfg.n_kv_heads, "D": cfg.head_dim, "R": cfg.residual, "max_tokens": cfg.max_tokens,
+          "n_hi": cfg.kitty_n_hi}
+    for (b, h), s in seqs.items():
+        got = kvq_unpack.unpack_kitty_sequence(buf, cd, b, h)
+        assert (got["n_q"], got["n_r"]) == (s.n_q, s.n_r), f"{what} lengths of {(b, h)}"
+        for name, ref in (("kc", s.kc), ("ks", s.ks), ("kz", s.kz), ("khi", s.khi), ("vq", s.vq), ("wk", s.wk),
+                          ("wv", s.wv)):
+            g = got[name]
+            assert g.shape == ref.shape, f"{what} {name} shape {g.shape} vs {ref.shape} at {(b, h)}"
+            if not np.array_equal(g.view(np.uint8), ref.view(np.uint8)):
+                bad = np.argwhere(g.view(np.uint8).reshape(g.shape[0], -1) != ref.view(np.uint8).reshape(ref.shape[0], -1))
+                raise AssertionError(f"{what} {name} differs at {(b, h)}: first mismatches {bad[:5].tolist()}")
+        if s.n_q:  # the running sums exist once a group is quantized
+            assert got["s1"] == s.mom.s1 and got["s2"] == s.mom.s2, f"{what} running sums of {(b, h)}"
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_kitty_prefill_state_and_decode(case):
+    wl, draw, cfg = make(case)
+    say("case", case[0], "lens", draw.seq_lens, "n_hi", cfg.kitty_n_hi)
+    cache = KVQCache(cfg, device=DEV)
+    K, V, lens = draw.padded()
+    kvq_prefill(cache, torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV), lens)
+    torch.cuda.synchronize()
+    seqs = {}
+    for b in range(wl.batch):
+        for h in range(wl.n_kv_heads):
+            s = oracle_seq(wl, cfg)
+            s.prefill(draw.K[b][h], draw.V[b][h])
+            seqs[(b, h)] = s
+    assert_kitty_state(host_buffer(cache), cfg, seqs, case[0])
+    if 0 < cfg.kitty_n_hi < cfg.head_dim:  # the ranking moves between groups on this data
+        assert any(len({tuple(r) for r in s.khi}) > 1 for s in seqs.values() if s.n_q > 32)
+    ref = oracle_attend(draw.q.astype(np.float64), seqs, wl)
+    q = torch.from_numpy(draw.q).to(DEV)
+    for n_split in (0, 1, 3, 40):
+        out = kvq_decode_attend(cache, q, out_fp32=True, n_split=n_split)
+        err = assert_close(out.cpu().numpy(), ref, f"{case[0]} n_split={n_split}")
+        say("  n_split", n_split, "err", err)
+    out16 = kvq_decode_attend(cache, q).float().cpu().numpy()  # fp16 output
+    assert_close(out16, ref, f"{case[0]} fp16 out")
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_kitty_appends_through_flushes(fused):
+    case = CASES[1]
+    n_steps = 80
+    lens0 = [0, 5, 40]  # empty, window only, a group and a window
+    wl, draw, cfg = make(case, seed=42, lens=[s + n_steps for s in lens0])
+    K, V, _ = draw.padded()
+    Kt, Vt = torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV)
+    cache = KVQCache(cfg, device=DEV)
+    kvq_prefill(cache, Kt, Vt, lens0)
+    seqs = {}
+    for b in range(wl.batch):
+        for h in range(wl.n_kv_heads):
+            s = oracle_seq(wl, cfg)
+            s.prefill(draw.K[b][h][:lens0[b]], draw.V[b][h][:lens0[b]])
+            seqs[(b, h)] = s
+    q = torch.from_numpy(draw.q).to(DEV)
+    for t in range(n_steps):
+        k = torch.stack([Kt[b, :, lens0[b] + t] for b in range(wl.batch)]).contiguous()
+        v = torch.stack([Vt[b, :, lens0[b] + t] for b in range(wl.batch)]).contiguous()
+        for b in range(wl.batch):
+            for h in range(wl.n_kv_heads):
+                seqs[(b, h)].append(draw.K[b][h][lens0[b] + t], draw.V[b][h][lens0[b] + t])
+        if fused:
+            out = kvq_append_decode_attend(cache, k, v, q, out_fp32=True, n_split=2)
+        else:
+            kvq_append(cache, k, v)
+            out = kvq_decode_attend(cache, q, out_fp32=True, n_split=2)
+        if t % 11 == 0 or t == n_steps - 1:
+            torch.cuda.synchronize()
+            assert_kitty_state(host_buffer(cache), cfg, seqs, f"step {t}")
+            ref = oracle_attend(draw.q.astype(np.float64), seqs, wl)
+            assert_close(out.cpu().numpy(), ref, f"step {t}")
+
+
+def test_kitty_prefill_equals_appends_on_the_device():
+    case = CASES[0]
+    wl, draw, cfg = make(case, seed=43, lens=[200, 131])
+    K, V, lens = draw.padded()
+    Kt, Vt = torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV)
+    a = KVQCache(cfg, device=DEV)
+    kvq_prefill(a, Kt, Vt, lens)
+    b_ = KVQCache(cfg, device=DEV)
+    lens0 = [70, 33]
+    kvq_prefill(b_, Kt, Vt, lens0)
+    for t in range(max(x - y for x, y in zip(lens, lens0))):
+        # both sequences take the same number of appends here: pad the shorter one's source
+        k = torch.stack([Kt[b, :, min(lens0[b] + t, Kt.shape[2] - 1)] for b in range(2)]).contiguous()
+        v = torch.stack([Vt[b, :, min(lens0[b] + t, Vt.shape[2] - 1)] for b in range(2)]).contiguous()
+        kvq_append(b_, k, v)
+    torch.cuda.synchronize()
+    cd = {"B": 2, "Hkv": wl.n_kv_heads, "D": wl.head_dim, "R": cfg.residual, "max_tokens": cfg.max_tokens,
+          "n_hi": cfg.kitty_n_hi}
+    ba, bb = host_buffer(a), host_buffer(b_)
+    # sequence 0 took exactly 130 appends (200 - 70), the same tokens as the prefill
+    for h in range(wl.n_kv_heads):
+        x = kvq_unpack.unpack_kitty_sequence(ba, cd, 0, h)
+        y = kvq_unpack.unpack_kitty_sequence(bb, cd, 0, h)
+        for name in ("kc", "ks", "kz", "khi", "vq", "wk", "wv"):
+            assert np.array_equal(x[name].view(np.uint8), y[name].view(np.uint8)), (name, h)
+        assert x["s1"] == y["s1"] and x["s2"] == y["s2"]
+
+
+def test_kitty_encode_calls():
+    case = CASES[3]
+    wl, draw, cfg = make(case, seed=44, lens=[160, 160])
+    K, V, _ = draw.padded()
+    Kt, Vt = torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV)
+    cache = KVQCache(cfg, device=DEV)
+    kvq_encode(cache, Kt[:, :, :64].contiguous(), Vt[:, :, :64].contiguous(), [64, 32])
+    kvq_encode(cache, Kt[:, :, 64:160].contiguous(), Vt[:, :, 64:160].contiguous(), [96, 64])
+    torch.cuda.synchronize()
+    seqs = {}
+    for b, (n0, n1) in enumerate([(64, 96), (32, 64)]):
+        for h in range(wl.n_kv_heads):
+            s = oracle_seq(wl, cfg)
+            s.encode(draw.K[b][h][:n0], draw.V[b][h][:n0])
+            s.encode(draw.K[b][h][64:64 + n1], draw.V[b][h][64:64 + n1])
+            seqs[(b, h)] = s
+    assert_kitty_state(host_buffer(cache), cfg, seqs, "encode")
+    ref = oracle_attend(draw.q.astype(np.float64), seqs, wl)
+    out = kvq_decode_attend(cache, torch.from_numpy(draw.q).to(DEV), out_fp32=True)
+    assert_close(out.cpu().numpy(), ref, "after encode")
