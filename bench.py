@@ -24,11 +24,16 @@ more fp16 unit and skips their quantized slots. With --method skvq the caches ar
 SKVQ-adapted ("Changelog" v0.30.0: per-token groups of range-sorted channels, per-group clip
 search, the first --n-sink tokens in fp16; window --window, the pages' defaults 128 and 5).
 
+With --method kitty the caches are Kitty ("Changelog" v0.11.0: per key group, the
+--kitty-hi-fraction of channels with the largest running variance at 4 bits, the rest at 2 bits;
+values in fp16): the step is kvq_append then the Kitty decode kernel (split-K, merged in-kernel).
+
 With --n-query N > 1 a step appends N tokens per sequence and then scores them with one causal
 multi-query attend (kvq_decode_attend_multi: speculative decoding's verification step).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long] [--n-sink 0]
-                  [--method kivi|skvq] [--window R] [--n-query 1] [--no-cpu-baseline]
+                  [--method kivi|skvq|kitty] [--window R] [--n-query 1] [--kitty-hi-fraction 0.25]
+                  [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -52,30 +57,40 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 MEASURED_TRAFFIC = {"workload": "long", "src_sha256_16": "e642750159ff07c6", "bytes": 202616468}
 
 
-def algorithmic_decode_bytes(wl, n_q, n_r, n_sink=0):
+def kitty_record_bytes(D, n_hi):
+    """Algorithmic bytes of a Kitty record (32 tokens): 4-bit codes of n_hi channels and 2-bit
+    codes of the rest, an fp16 (scale, zero) and a slot-table byte per channel, fp16 values."""
+    return 32 * (4 * n_hi + 2 * (D - n_hi)) // 8 + 4 * D + D + 32 * D * 2
+
+
+def algorithmic_decode_bytes(wl, n_q, n_r, n_sink=0, kitty_n_hi=None):
     """Bytes one decode launch must move: every record once per KV head (GQA query heads share
     it), the fp16 window and sink rows, q and out. n_q, n_r: per-sequence lengths."""
     D = wl.head_dim
     rec = 4 * D * (wl.key_bits + wl.value_bits + 2)  # per 32 quantized tokens
+    if kitty_n_hi is not None:
+        rec = kitty_record_bytes(D, kitty_n_hi)
     kv = sum((nq // 32) * rec + (nr + (n_sink if nq else 0)) * D * 2 * 2
              for nq, nr in zip(n_q, n_r)) * wl.n_kv_heads
     return kv + 2 * wl.batch * wl.n_q_heads * D * 2
 
 
-def algorithmic_encode_bytes(wl, n_q_tokens, n_sink=0):
+def algorithmic_encode_bytes(wl, n_q_tokens, n_sink=0, kitty_n_hi=None):
     """Prefill encode: read fp16 K and V once, write codes and parameters once (and the sink rows)."""
     D = wl.head_dim
     rec = 4 * D * (wl.key_bits + wl.value_bits + 2)
+    if kitty_n_hi is not None:
+        rec = kitty_record_bytes(D, kitty_n_hi)
     return sum(nq * D * 2 * 2 + (nq // 32) * rec + (n_sink * D * 2 * 2 if nq else 0)
                for nq in n_q_tokens) * wl.n_kv_heads
 
 
-def cpu_baseline(wl, draw, budget_s=12.0, n_sink=0, method="kivi", window=32):
+def cpu_baseline(wl, draw, budget_s=12.0, n_sink=0, method="kivi", window=32, kitty_n_hi=0):
     """The oracle's decode (reconstruct K_hat/V_hat, fp64 softmax attention) on a sample of the
     KV heads of sequence 0, scaled by tokens to the whole step (every sequence, head and layer)."""
     import numpy as np  # noqa: F401
 
-    from oracle import kivi, skvq
+    from oracle import kitty, kivi, skvq
 
     try:
         from threadpoolctl import threadpool_info
@@ -92,6 +107,8 @@ def cpu_baseline(wl, draw, budget_s=12.0, n_sink=0, method="kivi", window=32):
     for h in range(H):
         if method == "skvq":
             s = skvq.SkvqSequence(wl.head_dim, wl.key_bits, wl.value_bits, 32, window, n_sink)
+        elif method == "kitty":
+            s = kitty.KittySequence(wl.head_dim, kitty_n_hi, 4, wl.key_bits, 32, window)
         else:
             s = kivi.KiviSequence(wl.head_dim, wl.key_bits, wl.value_bits, 32, window, n_sink)
         t0 = time.perf_counter()
@@ -142,7 +159,8 @@ def main():
     ap.add_argument("--n-sink", type=int, default=None,
                     help="sink tokens per (sequence, KV head): KIVI-Sink by key norm (default 0 = KIVI), SKVQ the first "
                          "tokens (default 5)")
-    ap.add_argument("--method", default="kivi", choices=("kivi", "skvq"))
+    ap.add_argument("--method", default="kivi", choices=("kivi", "skvq", "kitty"))
+    ap.add_argument("--kitty-hi-fraction", type=float, default=0.25, help="Kitty: key channels at 4 bits")
     ap.add_argument("--window", type=int, default=None, help="fp16 window (default: the workload's, 128 for skvq)")
     ap.add_argument("--n-query", type=int, default=1, help="queries per head per step (causal multi-query attend)")
     args = ap.parse_args()
@@ -180,7 +198,8 @@ def main():
     NQ = args.n_query
     cap = (max(lens) + per_cache * NQ + R + 64 + 31) // 32 * 32
     cfg = make_config(wl.batch, wl.n_kv_heads, wl.n_q_heads, wl.head_dim, wl.key_bits, wl.value_bits, 32,
-                      R, cap, n_sink=args.n_sink, method=args.method)
+                      R, cap, n_sink=args.n_sink, method=args.method, kitty_hi_fraction=args.kitty_hi_fraction)
+    kitty_n_hi = cfg.kitty_n_hi if args.method == "kitty" else None
     Kt, Vt = torch.from_numpy(K).to(dev), torch.from_numpy(V).to(dev)
     del K, V
     stream = torch.cuda.current_stream()
@@ -221,7 +240,7 @@ def main():
     enc_t = statistics.median(enc_ms) / 1e3
     n_q0 = list(caches[0].lengths()[0])
     enc_tokens_per_s = sum(lens) / enc_t
-    enc_gbs = algorithmic_encode_bytes(wl, n_q0, args.n_sink) / enc_t / 1e9
+    enc_gbs = algorithmic_encode_bytes(wl, n_q0, args.n_sink, kitty_n_hi) / enc_t / 1e9
 
     # ---- device-resident inputs of the decode steps
     toks = [draw.next_token() for _ in range(n_steps_total * NQ)]
@@ -312,7 +331,7 @@ def main():
                         nr[b] = 0
                     nr[b] += 1
             if first <= i < last:  # (the extra queries add their q and out rows)
-                bytes_per_launch.append(algorithmic_decode_bytes(wl, nq, nr, args.n_sink)
+                bytes_per_launch.append(algorithmic_decode_bytes(wl, nq, nr, args.n_sink, kitty_n_hi)
                                         + (NQ - 1) * 2 * wl.batch * wl.n_q_heads * wl.head_dim * 2)
     for r, c in enumerate(caches):
         assert tuple(map(list, lens_now[r])) == tuple(map(list, c.lengths())), "length replay disagrees"
@@ -370,11 +389,17 @@ def main():
         "config": {
             "workload": f"{wl.name}: {wl.describe()}",
             "step": ("every layer: " if multi else "")
-            + ("kvq_append_decode_attend (append + attend in one decode kernel; on the 1 step in 32 that "
+            + ("kvq_append_decode_attend (Kitty: the append kernel, then the decode kernel; the "
+               "1 step in 32 that flushes a full window runs the Kitty encode launches first)"
+               if kitty_n_hi is not None else
+               "kvq_append_decode_attend (append + attend in one decode kernel; on the 1 step in 32 that "
                "flushes a full window, the append kernel runs first)" if NQ == 1 else
                f"{NQ} x kvq_append, then kvq_decode_attend_multi over the {NQ} new tokens (causal)"),
             "caches": f"{n_caches} layer caches" if multi else f"{n_caches} replicas of one cache, one per step",
-            "codes": f"{wl.key_bits}-bit keys / {wl.value_bits}-bit values, fp16 (scale, zero), fp32 softmax",
+            "codes": (f"{wl.key_bits}-bit keys / {wl.value_bits}-bit values, fp16 (scale, zero), fp32 softmax"
+                      if kitty_n_hi is None else
+                      f"{kitty_n_hi} of {wl.head_dim} key channels at 4 bits (running variance), the rest at "
+                      f"{wl.key_bits} bits, fp16 (scale, zero); fp16 values; fp32 softmax"),
             "sinks": args.n_sink,
             "method": args.method,
             "window": R,
@@ -387,7 +412,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "kernel": "decode_split_kernel",
+            "kernel": "decode_split_kernel" if kitty_n_hi is None else "kitty_decode_kernel",
             "kernel_avg_us": round(split_avg_ms * 1e3, 3),
             "algorithmic_bytes_per_launch": int(alg_bytes),
         },
@@ -406,7 +431,8 @@ def main():
         result["encode_all_layers_us"] = round(enc_t * 1e6 * wl.layers, 1)
         result["decode_launches_per_step"] = wl.layers
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, draw, n_sink=args.n_sink, method=args.method, window=R)
+        result["cpu_baseline"] = cpu_baseline(wl, draw, n_sink=args.n_sink, method=args.method, window=R,
+                                              kitty_n_hi=kitty_n_hi or 0)
     print(json.dumps(result), flush=True)
 
 

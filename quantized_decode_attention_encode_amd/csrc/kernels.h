@@ -77,7 +77,8 @@ hipError_t launch_decode_sink(uint8_t* buf, const Layout& L, const DecodeShape& 
 // ranking and encoding.
 hipError_t launch_kitty_encode(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,
                                const PerSeq& seq, int max_records, hipStream_t s);
-// Kitty decode: split kernel (partials in ws) and merge kernel (out). start/stop as above.
+// Kitty decode: split kernel whose last split per (b, h_kv) merges the partials (ws) into out.
+// start/stop as above.
 hipError_t launch_kitty_decode(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q, float* ws,
                                void* out, hipStream_t s, hipEvent_t start, hipEvent_t stop);
 

@@ -17,7 +17,8 @@
 //                        min/max rule (quant.h); codes, params and the slot table are written,
 //                        then the fp16 value rows over the staging.
 // Decode: kitty_decode_kernel, split-K over the records and window units of each (b, h_kv) with
-// an fp32 online softmax in base-2 units; kitty_merge_kernel combines the splits' partials.
+// an fp32 online softmax in base-2 units; the last split of each (b, h_kv) to finish merges the
+// splits' partials (merge_splits of the KIVI decode).
 //   key lanes   lane (t = l/2, half = l%2): token t, the code chunks k = 2j + half; each code
 //               multiplies q~[slot] = q[channel] * scale[slot] (formed once per record in LDS);
 //               the zero terms add up to beta = q . zero, one number per record and head.
@@ -28,6 +29,7 @@
 #include <hip/hip_ext.h>
 #include <stdint.h>
 
+#include "decode_kernel.h"  // dpp, wave_sync, split-partial stores and the in-kernel merge
 #include "kernels.h"
 #include "layout.h"
 #include "quant.h"
@@ -57,25 +59,31 @@ __device__ __forceinline__ uint64_t* staging(uint8_t* buf, const Layout& L, int 
   return reinterpret_cast<uint64_t*>(buf + L.record(b, h, j) + kitty_off_values(L.D, L.nhi));
 }
 
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  __builtin_amdgcn_wave_barrier();
+// Reductions over the wave in every lane, without LDS: DPP inside each 16-lane row, then the
+// gfx950 row swaps (with both operands equal, permlane32_swap yields rows (0,1,0,1) and
+// (2,3,2,3), permlane16_swap rows (0,0,2,2) and (1,1,3,3)).
+__device__ __forceinline__ float wave_sum_all(float v) {
+  v += dpp<kQuadXor1>(v);
+  v += dpp<kQuadXor2>(v);
+  v += dpp<kRowRor4>(v);
+  v += dpp<kRowRor8>(v);
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
-  return v;
+__device__ __forceinline__ float wave_max_all(float v) {
+  v = fmaxf(v, dpp<kQuadXor1>(v));
+  v = fmaxf(v, dpp<kQuadXor2>(v));
+  v = fmaxf(v, dpp<kRowRor4>(v));
+  v = fmaxf(v, dpp<kRowRor8>(v));
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
-}
-
-__device__ __forceinline__ float half_lo(uint32_t w) { return float(__builtin_bit_cast(_Float16, uint16_t(w & 0xFFFF))); }
-__device__ __forceinline__ float half_hi(uint32_t w) { return float(__builtin_bit_cast(_Float16, uint16_t(w >> 16))); }
 
 // ---------------------------------------------------------------------------------------
 // encode
@@ -299,13 +307,48 @@ struct KittyLds {
   float p[G][kGroup];   // softmax weights of the unit's tokens
 };
 
+// One record's loads for one lane: its token's code words (key lanes), its slots' params and
+// table entries, and its value octet of its tokens (value lanes; rows past the window's valid
+// ones are clamped, their weights are 0).
+template <int D>
+struct RecRegs {
+  uint32_t w0[D / 32], w1[D / 32], pr[D / 64];
+  int tb[D / 64];
+  uint4 vv[kGroup / (64 / (D / 8))];
+};
+
+template <int D>
+__device__ __forceinline__ void load_rec(const uint8_t* __restrict__ rec, int nhc, int Wd, int nhi, int tk, int hh,
+                                         int lane, int o, RecRegs<D>& r) {
+  constexpr int E = D / 64, NO = D / 8, NTG = 64 / NO, TPL = kGroup / NTG, NJ = D / 32;
+  const uint32_t* cw = reinterpret_cast<const uint32_t*>(rec) + tk * Wd;
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) {
+    const int k = 2 * jj + hh;
+    const int a = k + min(k, nhc);
+    r.w0[jj] = cw[a];
+    r.w1[jj] = cw[a + 1];  // the second word of a high chunk (unused otherwise; inside the record)
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    r.pr[e] = reinterpret_cast<const uint32_t*>(rec + kitty_off_params(D, nhi))[lane * E + e];
+    r.tb[e] = rec[kitty_off_table(D, nhi) + lane * E + e];
+  }
+  const uint4* vs = reinterpret_cast<const uint4*>(rec + kitty_off_values(D, nhi));
+#pragma unroll
+  for (int k = 0; k < TPL; ++k) r.vv[k] = vs[(lane / NO + NTG * k) * NO + lane % NO];
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(64 * kDecWaves) void kitty_decode_kernel(const uint8_t* __restrict__ buf, Layout L,
                                                                        DecodeShape ds, const __half* __restrict__ q,
-                                                                       float* __restrict__ ws) {
+                                                                       float* __restrict__ ws, uint32_t* __restrict__ sync,
+                                                                       void* __restrict__ out) {
   constexpr int E = D / 64, NO = D / 8, NTG = 64 / NO, TPL = kGroup / NTG, NJ = D / 32;
   __shared__ KittyLds<D, G> lw[kDecWaves];
   __shared__ float res[kDecWaves][G][D + 2];
+  __shared__ float mrg[3][64 * kDecWaves];
+  __shared__ int sh_last;
   const int sigma = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int32_t* len = reinterpret_cast<const int32_t*>(buf + L.lengths(b, h));
@@ -336,63 +379,66 @@ __global__ __launch_bounds__(64 * kDecWaves) void kitty_decode_kernel(const uint
     for (int c = 0; c < 8; ++c) acc[i][c] = 0.f;
   }
   wave_sync();
+  // One record ahead is requested while the current one is computed (G <= 2; wider query-head
+  // groups have no registers to spare). The prefetch index is clamped into the wave's records,
+  // so the load is unconditional (the last one re-reads a record).
+  constexpr bool kPrefetch = G <= 2;
+  const int ulast = max(min(u1, ngroups) - 1, 0);
+  RecRegs<D> cur, nxt;
+  if (u0 + wave < min(u1, ngroups)) load_rec<D>(buf + L.record(b, h, u0 + wave), nhc, Wd, nhi, tk, hh, lane, o, cur);
   for (int u = u0 + wave; u < u1; u += kDecWaves) {
     float s[G];
-    const uint4* vsrc;
+    const uint4* vsrc = nullptr;
     int nvalid;
+    uint4 vv[TPL];
     if (u < ngroups) {
-      const uint8_t* rec = buf + L.record(b, h, u);
-      const uint32_t* cw = reinterpret_cast<const uint32_t*>(rec) + tk * Wd;
-      uint32_t w0[NJ], w1[NJ];
-#pragma unroll
-      for (int jj = 0; jj < NJ; ++jj) {
-        const int k = 2 * jj + hh;
-        const int a = k + min(k, nhc);
-        w0[jj] = cw[a];
-        w1[jj] = cw[a + 1];  // the second word of a high chunk (unused otherwise; inside the record)
-      }
-      uint32_t pr[E];
-      int tb[E];
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        pr[e] = reinterpret_cast<const uint32_t*>(rec + kitty_off_params(D, nhi))[lane * E + e];
-        tb[e] = rec[kitty_off_table(D, nhi) + lane * E + e];
-      }
-      vsrc = reinterpret_cast<const uint4*>(rec + kitty_off_values(D, nhi));
+      if constexpr (kPrefetch)
+        load_rec<D>(buf + L.record(b, h, min(u + kDecWaves, ulast)), nhc, Wd, nhi, tk, hh, lane, o, nxt);
+      else if (u != u0 + wave)
+        load_rec<D>(buf + L.record(b, h, u), nhc, Wd, nhi, tk, hh, lane, o, cur);
       nvalid = kGroup;
+#pragma unroll
+      for (int k = 0; k < TPL; ++k) vv[k] = cur.vv[k];
       float beta[G];
 #pragma unroll
       for (int i = 0; i < G; ++i) {
         float bp = 0.f;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const float qv = W.qc[i][tb[e]];
-          W.qt[i][lane * E + e] = qv * half_lo(pr[e]);
-          bp = __builtin_fmaf(qv, half_hi(pr[e]), bp);
+          const float qv = W.qc[i][cur.tb[e]];
+          W.qt[i][lane * E + e] = qv * lo_f(cur.pr[e]);
+          bp = __builtin_fmaf(qv, hi_f(cur.pr[e]), bp);
         }
-        beta[i] = wave_sum(bp);
+        beta[i] = wave_sum_all(bp);
       }
       wave_sync();
+      // each code is converted once and serves every query head
+      float a[G];
 #pragma unroll
-      for (int i = 0; i < G; ++i) {
-        float a = 0.f;
+      for (int i = 0; i < G; ++i) a[i] = 0.f;
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj) {
-          const int k = 2 * jj + hh;
-          const float* qk = &W.qt[i][16 * k];
-          if (k < nhc) {
+      for (int jj = 0; jj < NJ; ++jj) {
+        const int k = 2 * jj + hh;
+        if (k < nhc) {
 #pragma unroll
-            for (int ii = 0; ii < 8; ++ii) {
-              a = __builtin_fmaf(qk[ii], float((w0[jj] >> (kHB * ii)) & 15u), a);
-              a = __builtin_fmaf(qk[8 + ii], float((w1[jj] >> (kHB * ii)) & 15u), a);
-            }
-          } else {
+          for (int ii = 0; ii < 16; ++ii) {
+            const uint32_t w = ii < 8 ? cur.w0[jj] : cur.w1[jj];
+            const float c = float((w >> (kHB * (ii & 7))) & 15u);
 #pragma unroll
-            for (int ii = 0; ii < 16; ++ii) a = __builtin_fmaf(qk[ii], float((w0[jj] >> (kLB * ii)) & 3u), a);
+            for (int i = 0; i < G; ++i) a[i] = __builtin_fmaf(W.qt[i][16 * k + ii], c, a[i]);
+          }
+        } else {
+#pragma unroll
+          for (int ii = 0; ii < 16; ++ii) {
+            const float c = float((cur.w0[jj] >> (kLB * ii)) & 3u);
+#pragma unroll
+            for (int i = 0; i < G; ++i) a[i] = __builtin_fmaf(W.qt[i][16 * k + ii], c, a[i]);
           }
         }
-        s[i] = a + __shfl_xor(a, 1, 64) + beta[i];
       }
+#pragma unroll
+      for (int i = 0; i < G; ++i) s[i] = a[i] + dpp<kQuadXor1>(a[i]) + beta[i];  // lanes (t, 0), (t, 1) are adjacent
+      if constexpr (kPrefetch) cur = nxt;
     } else {
       const int tbase = (u - ngroups) * kGroup;
       nvalid = min(kGroup, nr - tbase);
@@ -404,6 +450,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void kitty_decode_kernel(const uint
 #pragma unroll
       for (int i = 0; i < D / 16; ++i) kk[i] = kr[i];
 #pragma unroll
+      for (int k = 0; k < TPL; ++k) vv[k] = vsrc[min(tg + NTG * k, nvalid - 1) * NO + o];
+#pragma unroll
       for (int i = 0; i < G; ++i) {
         const float* qh = &W.qc[i][hh * (D / 2)];
         float a = 0.f;
@@ -412,21 +460,17 @@ __global__ __launch_bounds__(64 * kDecWaves) void kitty_decode_kernel(const uint
           const uint32_t wv[4] = {kk[r].x, kk[r].y, kk[r].z, kk[r].w};
 #pragma unroll
           for (int z = 0; z < 4; ++z) {
-            a = __builtin_fmaf(qh[8 * r + 2 * z], half_lo(wv[z]), a);
-            a = __builtin_fmaf(qh[8 * r + 2 * z + 1], half_hi(wv[z]), a);
+            a = __builtin_fmaf(qh[8 * r + 2 * z], lo_f(wv[z]), a);
+            a = __builtin_fmaf(qh[8 * r + 2 * z + 1], hi_f(wv[z]), a);
           }
         }
-        s[i] = a + __shfl_xor(a, 1, 64);
+        s[i] = a + dpp<kQuadXor1>(a);
         if (tk >= nvalid) s[i] = -INFINITY;
       }
     }
-    // the unit's value rows (rows past nvalid clamped; their weights are 0)
-    uint4 vv[TPL];
-#pragma unroll
-    for (int k = 0; k < TPL; ++k) vv[k] = vsrc[min(tg + NTG * k, nvalid - 1) * NO + o];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
-      const float mx = wave_max(s[i]);
+      const float mx = wave_max_all(s[i]);
       if (mx > m[i]) {  // uniform
         const float alpha = __builtin_amdgcn_exp2f(m[i] - mx);
         l[i] *= alpha;
@@ -447,8 +491,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void kitty_decode_kernel(const uint
       float vf[8];
 #pragma unroll
       for (int z = 0; z < 4; ++z) {
-        vf[2 * z] = half_lo(wv[z]);
-        vf[2 * z + 1] = half_hi(wv[z]);
+        vf[2 * z] = lo_f(wv[z]);
+        vf[2 * z + 1] = hi_f(wv[z]);
       }
       const int t = tg + NTG * k;
 #pragma unroll
@@ -463,7 +507,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void kitty_decode_kernel(const uint
   // the wave's partial: l over its lanes, acc over the token subsets of each octet
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    l[i] = wave_sum(l[i]);
+    l[i] = wave_sum_all(l[i]);
 #pragma unroll
     for (int c = 0; c < 8; ++c)
 #pragma unroll
@@ -477,7 +521,11 @@ __global__ __launch_bounds__(64 * kDecWaves) void kitty_decode_kernel(const uint
     }
   }
   __syncthreads();
-  // the workgroup's partial per query head: (acc[D], m, l) in the split's workspace slot
+  // the workgroup's partial per query head (acc[D], m, l), or the output when it is the
+  // sequence's only split; the last split of (b, h_kv) to finish merges the partials (the
+  // protocol of the KIVI decode: device-scope partial stores, a device-scope counter)
+  const int nvalid = min(ds.n_split, (nunits + ds.chunk - 1) / ds.chunk);
+  const int64_t row0 = int64_t(b) * ds.n_q_heads + h * G;
   for (int idx = threadIdx.x; idx < G * D; idx += 64 * kDecWaves) {
     const int i = idx / D, c = idx % D;
     float M = -INFINITY;
@@ -492,51 +540,26 @@ __global__ __launch_bounds__(64 * kDecWaves) void kitty_decode_kernel(const uint
       A = __builtin_fmaf(f, res[w][i][c], A);
       Ls = __builtin_fmaf(f, res[w][i][D + 1], Ls);
     }
-    float* p = ws + ((int64_t(b) * ds.n_q_heads + h * G + i) * ds.n_split + sigma) * (D + 4);
-    p[c] = A;
+    if (nvalid == 1) {
+      store_out(out, ds.out_fp32, (row0 + i) * D + c, A / Ls);
+      continue;
+    }
+    float* p = ws + ((row0 + i) * ds.n_split + sigma) * (D + 4);
+    put_partial(p + c, A);
     if (c == 0) {
-      p[D] = M;
-      p[D + 1] = Ls;
+      put_partial(p + D, M);
+      put_partial(p + D + 1, Ls);
     }
   }
-}
-
-// One wave per (query head, sequence): the splits' partials merged into the output.
-template <int D>
-__global__ __launch_bounds__(64) void kitty_merge_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape ds,
-                                                         const float* __restrict__ ws, void* __restrict__ out) {
-  constexpr int E = D / 64;
-  const int hq = blockIdx.x, b = blockIdx.y;
-  const int h = hq / ds.G;
-  const int lane = threadIdx.x;
-  const int32_t* len = reinterpret_cast<const int32_t*>(buf + L.lengths(b, h));
-  const int nq = max(0, min(len[0], L.max_groups * kGroup));
-  const int nr = max(0, min(len[1], L.R));
-  const int nunits = nq / kGroup + (nr + kGroup - 1) / kGroup;
-  const int nv = min(ds.n_split, (nunits + ds.chunk - 1) / ds.chunk);
-  const float* p0 = ws + (int64_t(b) * ds.n_q_heads + hq) * ds.n_split * (D + 4);
-  float M = -INFINITY;
-  for (int sg = 0; sg < nv; ++sg) M = fmaxf(M, p0[sg * (D + 4) + D]);
-  float A[E], Ls = 0.f;
-#pragma unroll
-  for (int e = 0; e < E; ++e) A[e] = 0.f;
-  for (int sg = 0; sg < nv; ++sg) {
-    const float* p = p0 + sg * (D + 4);
-    const float f = __builtin_amdgcn_exp2f(p[D] - M);
-    Ls = __builtin_fmaf(f, p[D + 1], Ls);
-#pragma unroll
-    for (int e = 0; e < E; ++e) A[e] = __builtin_fmaf(f, p[lane * E + e], A[e]);
-  }
-  const float inv = 1.0f / Ls;
-  const int64_t o0 = (int64_t(b) * ds.n_q_heads + hq) * D;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const float v = A[e] * inv;
-    if (ds.out_fp32)
-      static_cast<float*>(out)[o0 + lane * E + e] = v;
-    else
-      static_cast<__half*>(out)[o0 + lane * E + e] = __float2half_rn(v);
-  }
+  if (nvalid == 1) return;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  uint32_t* cnt = sync + (int64_t(b) * L.Hkv + h);
+  if (threadIdx.x == 0) sh_last = atomicAdd(cnt, 1u) + 1u == uint32_t(nvalid);
+  __syncthreads();
+  if (!sh_last) return;
+  merge_splits<D, G>(ws, row0, ds.n_split, nvalid, mrg, out, ds.out_fp32);
+  if (threadIdx.x == 0) atomicExch(cnt, 0u);
 }
 
 template <int D>
@@ -556,17 +579,13 @@ hipError_t kitty_decode_t(uint8_t* buf, const Layout& L, const DecodeShape& ds, 
                           hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const dim3 grid(ds.n_split, L.Hkv, L.B);
   const uint8_t* cb = buf;
+  uint32_t* sync = reinterpret_cast<uint32_t*>(buf + L.sync_off);
   const __half* qh = static_cast<const __half*>(q);
-  if (e0 || e1) {
-    hipExtLaunchKernelGGL((kitty_decode_kernel<D, G>), grid, dim3(64 * kDecWaves), 0, s, e0, nullptr, 0, cb, L, ds,
-                          qh, ws);
-    hipExtLaunchKernelGGL((kitty_merge_kernel<D>), dim3(ds.n_q_heads, L.B), dim3(64), 0, s, nullptr, e1, 0, cb, L,
-                          ds, static_cast<const float*>(ws), out);
-  } else {
-    hipLaunchKernelGGL((kitty_decode_kernel<D, G>), grid, dim3(64 * kDecWaves), 0, s, cb, L, ds, qh, ws);
-    hipLaunchKernelGGL((kitty_merge_kernel<D>), dim3(ds.n_q_heads, L.B), dim3(64), 0, s, cb, L, ds,
-                       static_cast<const float*>(ws), out);
-  }
+  if (e0 || e1)
+    hipExtLaunchKernelGGL((kitty_decode_kernel<D, G>), grid, dim3(64 * kDecWaves), 0, s, e0, e1, 0, cb, L, ds, qh, ws,
+                          sync, out);
+  else
+    hipLaunchKernelGGL((kitty_decode_kernel<D, G>), grid, dim3(64 * kDecWaves), 0, s, cb, L, ds, qh, ws, sync, out);
   return hipGetLastError();
 }
 
