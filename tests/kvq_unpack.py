@@ -7,8 +7,11 @@ Written from the layout description (records of 32 tokens; key codes as
 sink regions: positions int32 [B][H_kv][NS], key and value rows fp16 [B][H_kv][NS][D], and for
 SKVQ caches the channel permutations uint8 [B][H_kv][2][D]; SKVQ records keep their key params
 in the value-param layout, one (scale, zero) per token and group of permuted channels, and their
-window and sink rows are stored permuted once the permutations exist). It
-shares no code with the HIP library; parity tests compare its output with the CPU oracle.
+window and sink rows are stored permuted once the permutations exist; Kitty records hold per
+token the key codes of the slots in 16-slot chunks, two words for a 4-bit chunk and one for a
+2-bit chunk, then the (scale, zero) per slot, the slot-to-channel table and the fp16 values,
+and a Kitty buffer ends with the running key sums per (b, h)). It shares no code with the HIP
+library; parity tests compare its output with the CPU oracle.
 """
 from __future__ import annotations
 
