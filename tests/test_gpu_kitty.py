@@ -27,6 +27,8 @@ CASES = [
     ("d128-none-gqa4-R64", 2, 8, 2, 128, 0.0, [400, 64], 64),
     ("d128-all-gqa8", 2, 8, 1, 128, 1.0, [330, 90], 32),
     ("d128-half-R64", 2, 2, 2, 128, 0.5, [250, 17], 64),
+    ("d64-quarter-gqa8-R128", 2, 8, 1, 64, 0.25, [500, 140], 128),
+    ("d128-eighth-gqa2-long", 1, 2, 1, 128, 0.125, [1000], 32),
 ]
 
 
@@ -120,6 +122,35 @@ def test_kitty_appends_through_flushes(fused):
             assert_kitty_state(host_buffer(cache), cfg, seqs, f"step {t}")
             ref = oracle_attend(draw.q.astype(np.float64), seqs, wl)
             assert_close(out.cpu().numpy(), ref, f"step {t}")
+
+
+def test_kitty_flush_of_a_long_window():
+    case = CASES[5]  # R = 128: each flush quantizes 4 groups, each ranked with its own sums
+    n_steps = 140
+    lens0 = [130, 3]
+    wl, draw, cfg = make(case, seed=45, lens=[s + n_steps for s in lens0])
+    K, V, _ = draw.padded()
+    Kt, Vt = torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV)
+    cache = KVQCache(cfg, device=DEV)
+    kvq_prefill(cache, Kt, Vt, lens0)
+    seqs = {}
+    for b in range(wl.batch):
+        s = oracle_seq(wl, cfg)
+        s.prefill(draw.K[b][0][:lens0[b]], draw.V[b][0][:lens0[b]])
+        seqs[(b, 0)] = s
+    q = torch.from_numpy(draw.q).to(DEV)
+    for t in range(n_steps):
+        k = torch.stack([Kt[b, :, lens0[b] + t] for b in range(wl.batch)]).contiguous()
+        v = torch.stack([Vt[b, :, lens0[b] + t] for b in range(wl.batch)]).contiguous()
+        for b in range(wl.batch):
+            seqs[(b, 0)].append(draw.K[b][0][lens0[b] + t], draw.V[b][0][lens0[b] + t])
+        kvq_append(cache, k, v)
+    torch.cuda.synchronize()
+    assert seqs[(0, 0)].n_q == 256 and seqs[(1, 0)].n_q == 128  # flushes happened
+    assert_kitty_state(host_buffer(cache), cfg, seqs, "after the flushes")
+    ref = oracle_attend(draw.q.astype(np.float64), seqs, wl)
+    out = kvq_decode_attend(cache, q, out_fp32=True, n_split=3)
+    assert_close(out.cpu().numpy(), ref, "after the flushes")
 
 
 def test_kitty_prefill_equals_appends_on_the_device():
