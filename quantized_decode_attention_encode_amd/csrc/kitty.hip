@@ -7,10 +7,11 @@
 //                        32 tokens, s1 = sum X and s2 = sum X^2 with X = x * 2^24 (an integer
 //                        for every finite fp16 x; |X| < 2^40, so s1 fits int64 and s2 uint128),
 //                        staged in the record's value area.
-//   kitty_scan_kernel    one workgroup per (b, h): running sums up to each record's end (the
-//                        sequence's stored sums plus every earlier group), written back over the
-//                        staged group sums, and the new totals into the sequence's state. Integer
-//                        sums are exact in any order, so the 16 waves scan segments in parallel.
+//   kitty_seg/top/fix    running sums up to each record's end (the sequence's stored sums plus
+//                        every earlier group) written back over the staged group sums, and the
+//                        new totals into the sequence's state: segment totals, one walk over
+//                        them per (b, h), then every segment's records (a two-level scan; the
+//                        integer sums are exact in any order).
 //   kitty_encode_kernel  one wave per record: n * s2 - s1^2 (n^2 times the variance, exact in
 //                        128 bits) ranks the channels (the larger first, the lower index on
 //                        ties); the top n_hi take 4-bit groups, the rest 2-bit ones, by KIVI's
@@ -39,7 +40,6 @@ namespace {
 
 typedef unsigned __int128 u128;
 constexpr int kHB = 4, kLB = 2;  // high and low key widths
-constexpr int kScanWaves = 16;
 constexpr int kDecWaves = 4;
 
 // x * 2^24 for the finite fp16 x with bits hb, exactly
@@ -53,6 +53,17 @@ __device__ __forceinline__ int64_t fp16_fixed(uint32_t hb) {
 __device__ __forceinline__ u128 square(int64_t x) {
   const uint64_t a = uint64_t(x < 0 ? -x : x);
   return u128(a) * a;
+}
+
+// An fp32 image of a non-negative 128-bit integer that keeps its order: the leading 24 bits,
+// truncated, at the leading bit's power of two. x < y gives f(x) <= f(y), so f(x) < f(y) decides
+// x < y, and only equal images need the exact comparison.
+__device__ __forceinline__ float order_image(u128 x) {
+  const uint64_t hi = uint64_t(x >> 64), lo = uint64_t(x);
+  if ((hi | lo) == 0) return 0.0f;
+  const int top = hi ? 127 - __clzll(hi) : 63 - __clzll(lo);  // the leading one's bit
+  const uint32_t m = uint32_t(top >= 23 ? (x >> (top - 23)) : (x << (23 - top)));  // 24 bits, bit 23 set
+  return __uint_as_float((uint32_t(top + 127) << 23) | (m & 0x7FFFFFu));
 }
 
 __device__ __forceinline__ uint64_t* staging(uint8_t* buf, const Layout& L, int b, int h, int j) {
@@ -123,76 +134,115 @@ __global__ __launch_bounds__(64) void kitty_stats_kernel(uint8_t* __restrict__ b
   }
 }
 
+// Running sums, in three launches (integer sums are exact in any order): each segment of
+// kSeg records sums its records' group sums (kitty_seg_kernel, the total staged after the group
+// sums of the segment's first record); one wave per (b, h) turns the totals into exclusive
+// prefixes, starting from the sequence's stored sums (none before its first record: a
+// sequence's first encode starts from zero, whatever the buffer held), and stores the new
+// totals (kitty_top_kernel); each segment then rewrites its records' staged group sums as
+// running sums up to their ends (kitty_fix_kernel).
+constexpr int kSeg = 16;
+
+__device__ __forceinline__ void load_sums(const uint64_t* p, int c, int D, int64_t& s1, u128& s2) {
+  s1 = int64_t(p[c]);
+  s2 = u128(p[D + c]) | (u128(p[2 * D + c]) << 64);
+}
+__device__ __forceinline__ void store_sums(uint64_t* p, int c, int D, int64_t s1, u128 s2) {
+  p[c] = uint64_t(s1);
+  p[D + c] = uint64_t(s2);
+  p[2 * D + c] = uint64_t(s2 >> 64);
+}
+
 template <int D>
-__global__ __launch_bounds__(64 * kScanWaves) void kitty_scan_kernel(uint8_t* __restrict__ buf, Layout L, PerSeq seq) {
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int n = seq.b[b];
-  if (n == 0) return;  // uniform over the workgroup
+__global__ __launch_bounds__(64) void kitty_seg_kernel(uint8_t* __restrict__ buf, Layout L, PerSeq seq) {
+  const int sg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int n = seq.b[b], x0 = sg * kSeg;
+  if (x0 >= n) return;
   constexpr int E = D / 64;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __shared__ int64_t seg1[kScanWaves][D];
-  __shared__ u128 seg2[kScanWaves][D];
-  const int per = (n + kScanWaves - 1) / kScanWaves;
-  const int x0 = min(n, wave * per), x1 = min(n, x0 + per);
-  const int j0 = seq.a[b];
-  int64_t r1[E];
-  u128 r2[E];
+  const int lane = threadIdx.x, j0 = seq.a[b], x1 = min(n, x0 + kSeg);
+  int64_t t1[E];
+  u128 t2[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    r1[e] = 0;
-    r2[e] = 0;
+    t1[e] = 0;
+    t2[e] = 0;
   }
 #pragma unroll 4
   for (int x = x0; x < x1; ++x) {
     const uint64_t* p = staging(buf, L, b, h, j0 + x);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int c = lane * E + e;
-      r1[e] += int64_t(p[c]);
-      r2[e] += u128(p[D + c]) | (u128(p[2 * D + c]) << 64);
+      int64_t a1;
+      u128 a2;
+      load_sums(p, lane * E + e, D, a1, a2);
+      t1[e] += a1;
+      t2[e] += a2;
     }
   }
+  uint64_t* tot = staging(buf, L, b, h, j0 + x0) + 3 * D;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    seg1[wave][lane * E + e] = r1[e];
-    seg2[wave][lane * E + e] = r2[e];
-  }
-  __syncthreads();
-  // sums before this wave's segment: the sequence's stored sums (none before its first
-  // record: a sequence's first encode starts from zero, whatever the buffer held) plus the
-  // earlier segments
+  for (int e = 0; e < E; ++e) store_sums(tot, lane * E + e, D, t1[e], t2[e]);
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void kitty_top_kernel(uint8_t* __restrict__ buf, Layout L, PerSeq seq) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int n = seq.b[b];
+  if (n == 0) return;
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x, j0 = seq.a[b];
   uint64_t* base = reinterpret_cast<uint64_t*>(buf + L.kstats(b, h));
-  const bool fresh = j0 == 0;
+  int64_t r1[E];
+  u128 r2[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int c = lane * E + e;
-    r1[e] = fresh ? 0 : int64_t(base[c]);
-    r2[e] = fresh ? u128(0) : (u128(base[D + c]) | (u128(base[2 * D + c]) << 64));
-    for (int w = 0; w < wave; ++w) {
-      r1[e] += seg1[w][c];
-      r2[e] += seg2[w][c];
+    if (j0 == 0) {
+      r1[e] = 0;
+      r2[e] = 0;
+    } else {
+      load_sums(base, lane * E + e, D, r1[e], r2[e]);
     }
   }
+#pragma unroll 4
+  for (int x0 = 0; x0 < n; x0 += kSeg) {
+    uint64_t* tot = staging(buf, L, b, h, j0 + x0) + 3 * D;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      int64_t a1;
+      u128 a2;
+      load_sums(tot, lane * E + e, D, a1, a2);
+      store_sums(tot, lane * E + e, D, r1[e], r2[e]);  // the segment's exclusive prefix
+      r1[e] += a1;
+      r2[e] += a2;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) store_sums(base, lane * E + e, D, r1[e], r2[e]);
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void kitty_fix_kernel(uint8_t* __restrict__ buf, Layout L, PerSeq seq) {
+  const int sg = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int n = seq.b[b], x0 = sg * kSeg;
+  if (x0 >= n) return;
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x, j0 = seq.a[b], x1 = min(n, x0 + kSeg);
+  const uint64_t* pre = staging(buf, L, b, h, j0 + x0) + 3 * D;
+  int64_t r1[E];
+  u128 r2[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) load_sums(pre, lane * E + e, D, r1[e], r2[e]);
+#pragma unroll 4
   for (int x = x0; x < x1; ++x) {
     uint64_t* p = staging(buf, L, b, h, j0 + x);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int c = lane * E + e;
-      r1[e] += int64_t(p[c]);
-      r2[e] += u128(p[D + c]) | (u128(p[2 * D + c]) << 64);
-      p[c] = uint64_t(r1[e]);
-      p[D + c] = uint64_t(r2[e]);
-      p[2 * D + c] = uint64_t(r2[e] >> 64);
-    }
-  }
-  __syncthreads();  // every wave has read the stored sums
-  if (wave == kScanWaves - 1) {  // its running sums now cover every group: the new totals
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int c = lane * E + e;
-      base[c] = uint64_t(r1[e]);
-      base[D + c] = uint64_t(r2[e]);
-      base[2 * D + c] = uint64_t(r2[e] >> 64);
+      int64_t a1;
+      u128 a2;
+      load_sums(p, lane * E + e, D, a1, a2);
+      r1[e] += a1;
+      r2[e] += a2;
+      store_sums(p, lane * E + e, D, r1[e], r2[e]);
     }
   }
 }
@@ -210,7 +260,7 @@ __global__ __launch_bounds__(64) void kitty_encode_kernel(uint8_t* __restrict__ 
   uint8_t* rec = buf + L.record(b, h, j);
   const int64_t row0 = ((int64_t(b) * L.Hkv + h) * ld_tok + seq.c[b] + int64_t(x) * kGroup) * D;
   __shared__ u128 key[D];
-  __shared__ uint8_t hiflag[D];
+  __shared__ float fkey[D];
   __shared__ uint8_t cb[kGroup][D];  // codes by (token, slot)
 
   // the key tile: the lane's channels over the 32 tokens
@@ -223,36 +273,54 @@ __global__ __launch_bounds__(64) void kitty_encode_kernel(uint8_t* __restrict__ 
   const uint64_t* st = reinterpret_cast<const uint64_t*>(rec + kitty_off_values(D, nhi));
   const uint64_t n = uint64_t(j + 1) * kGroup;
   u128 my[E];
+  float myf[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int c = lane * E + e;
     const int64_t s1 = int64_t(st[c]);
     const u128 s2 = u128(st[D + c]) | (u128(st[2 * D + c]) << 64);
     my[e] = s2 * n - square(s1);
+    myf[e] = order_image(my[e]);
     key[c] = my[e];
+    fkey[c] = myf[e];
   }
   __syncthreads();
-  // rank: channels of larger spread, or of equal spread and lower index, come first
+  // rank: channels of larger spread, or of equal spread and lower index, come first (the fp32
+  // images decide unless they are equal)
   bool hi[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int c = lane * E + e;
     int r = 0;
+    bool tie = false;
     for (int c2 = 0; c2 < D; ++c2) {
-      const u128 k2 = key[c2];
-      r += (k2 > my[e] || (k2 == my[e] && c2 < c)) ? 1 : 0;
+      const float f2 = fkey[c2];
+      r += f2 > myf[e] ? 1 : 0;
+      tie = tie || (f2 == myf[e] && c2 != c);
+    }
+    if (tie) {
+      for (int c2 = 0; c2 < D; ++c2) {
+        if (fkey[c2] != myf[e]) continue;
+        const u128 k2 = key[c2];
+        r += (k2 > my[e] || (k2 == my[e] && c2 < c)) ? 1 : 0;
+      }
     }
     hi[e] = r < nhi;
-    hiflag[c] = hi[e] ? 1 : 0;
   }
-  __syncthreads();
+  // high channels below each of the lane's channels, from the wave's votes (channel
+  // lane*E + e votes in mask e)
+  uint64_t vote[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) vote[e] = __ballot(hi[e]);
+  const uint64_t below_lane = lane ? (~0ull >> (64 - lane)) : 0ull;
   // slots: the high channels first, each set in ascending channel order
   uint32_t* params = reinterpret_cast<uint32_t*>(rec + kitty_off_params(D, nhi));
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int c = lane * E + e;
-    int below = 0;
-    for (int c2 = 0; c2 < c; ++c2) below += hiflag[c2];
+    int below = 0;  // high channels c2 < c: c2 = lane' * E + e' with lane' < lane, or lane' = lane and e' < e
+#pragma unroll
+    for (int e2 = 0; e2 < E; ++e2) below += __popcll(vote[e2] & (e2 < e ? (below_lane | (1ull << lane)) : below_lane));
     const int slot = hi[e] ? below : nhi + (c - below);
     rec[kitty_off_table(D, nhi) + slot] = uint8_t(c);
     float mn = kx[0][e], mx = kx[0][e];
@@ -568,8 +636,11 @@ hipError_t kitty_encode_d(uint8_t* buf, const Layout& L, const void* K, const vo
   const dim3 grid(max_records, L.Hkv, L.B);
   const __half* kh = static_cast<const __half*>(K);
   const __half* vh = static_cast<const __half*>(V);
+  const dim3 segs((max_records + kSeg - 1) / kSeg, L.Hkv, L.B);
   hipLaunchKernelGGL(kitty_stats_kernel<D>, grid, dim3(64), 0, s, buf, L, kh, ld_tok, seq);
-  hipLaunchKernelGGL(kitty_scan_kernel<D>, dim3(L.Hkv, L.B), dim3(64 * kScanWaves), 0, s, buf, L, seq);
+  hipLaunchKernelGGL(kitty_seg_kernel<D>, segs, dim3(64), 0, s, buf, L, seq);
+  hipLaunchKernelGGL(kitty_top_kernel<D>, dim3(L.Hkv, L.B), dim3(64), 0, s, buf, L, seq);
+  hipLaunchKernelGGL(kitty_fix_kernel<D>, segs, dim3(64), 0, s, buf, L, seq);
   hipLaunchKernelGGL(kitty_encode_kernel<D>, grid, dim3(64), 0, s, buf, L, kh, vh, ld_tok, seq);
   return hipGetLastError();
 }
