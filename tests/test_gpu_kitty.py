@@ -201,3 +201,40 @@ def test_kitty_encode_calls():
     ref = oracle_attend(draw.q.astype(np.float64), seqs, wl)
     out = kvq_decode_attend(cache, torch.from_numpy(draw.q).to(DEV), out_fp32=True)
     assert_close(out.cpu().numpy(), ref, "after encode")
+
+
+def test_kitty_ranking_ties_on_the_device():
+    """Spreads that tie exactly at the top-n_hi boundary (copies of a channel, and a copy
+    shifted by an exactly representable constant; 17 constant channels) are decided by the
+    lower channel index (equal fp32 images, then the exact 128-bit comparison and the index), and
+    a near-tie (one value moved by 2^-6) by the spreads, on the device as in the oracle."""
+    D, R, T = 128, 32, 244
+    sign = np.where(np.arange(T) % 2 == 0, 1.0, -1.0)
+    K = np.zeros((T, D))
+    for d in range(D):
+        K[:, d] = sign * (1.0 + d / 256.0)  # small distinct spreads
+    for d in range(98, 128):
+        K[:, d] = sign * (10.0 + d - 98)  # the 30 largest spreads
+    for d in (5, 9, 50):
+        K[:, d] = sign * 5.0  # tied for ranks 32..35 with channel 70
+    K[:, 70] = sign * 5.0 + 8.0  # the same values shifted: the same spread, exactly
+    K[:, 7] = sign * 5.0
+    K[3, 7] += 2.0 ** -6  # a near-tie just below them (token 3 holds -5: its magnitude shrinks)
+    const = [0, 1, 2, 3, 4, 6, 8, 10, 11, 12, 13, 14, 15, 16, 17, 18, 19]
+    K[:, const] = 0.75  # spread 0: 17 channels tied at the bottom
+    K = K.astype(np.float16)
+    rng = np.random.default_rng(46)
+    V = rng.standard_normal((T, D)).astype(np.float16)
+    expect = {0.25: [5, 9] + list(range(98, 128)), 0.875: None}  # 5 and 9: the lower indices of the tie
+    for frac in (0.25, 0.875):
+        cfg = make_config(1, 1, 1, D, 2, 16, 32, R, 1024, method="kitty", kitty_hi_fraction=frac)
+        cache = KVQCache(cfg, device=DEV)
+        kvq_prefill(cache, torch.from_numpy(K[None, None]).to(DEV), torch.from_numpy(V[None, None]).to(DEV), [T])
+        torch.cuda.synchronize()
+        s = kitty.KittySequence(D, cfg.kitty_n_hi, 4, 2, 32, R)
+        s.prefill(K, V)
+        if expect[frac] is not None:
+            assert all(np.flatnonzero(r).tolist() == expect[frac] for r in s.khi)
+        else:  # every channel but 16 of the constants: the lowest-index constant gets in
+            assert all(r[0] and not r[1:20][[c - 1 for c in const[1:]]].any() for r in s.khi)
+        assert_kitty_state(host_buffer(cache), cfg, {(0, 0): s}, f"ties, fraction {frac}")
