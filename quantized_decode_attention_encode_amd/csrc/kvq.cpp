@@ -86,6 +86,10 @@ kvq_status check_config(const kvq_config* c) {
     if (c->kitty_n_hi < 0 || c->kitty_n_hi > c->head_dim || c->kitty_n_hi % 16)
       return fail(KVQ_E_UNSUPPORTED, "kitty_n_hi must be a multiple of 16 in [0, head_dim], got %d", c->kitty_n_hi);
     if (c->n_sink != 0) return fail(KVQ_E_UNSUPPORTED, "Kitty caches take no sink tokens (n_sink = %d)", c->n_sink);
+    // the running key sums stay exact for every finite fp16 key up to 2^22 tokens: |sum X| <
+    // 2^22 * 2^40 fits int64, and n * sum X^2 < 2^44 * 2^80 fits 128 bits
+    if (c->max_tokens > (1 << 22))
+      return fail(KVQ_E_UNSUPPORTED, "Kitty caches hold at most 2^22 tokens per sequence, got max_tokens %d", c->max_tokens);
   } else {
     for (int bits : {c->key_bits, c->value_bits})
       if (bits != 2 && bits != 4 && bits != 8)

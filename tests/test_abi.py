@@ -123,7 +123,8 @@ def test_skvq_config_validation_and_layout(alpha, search, reorder, status):
     (dict(kitty_n_hi=24), KVQ_E_UNSUPPORTED), (dict(kitty_n_hi=144), KVQ_E_UNSUPPORTED),
     (dict(kitty_n_hi=-16), KVQ_E_UNSUPPORTED), (dict(value_bits=2), KVQ_E_INVALID),
     (dict(key_bits=4), KVQ_E_UNSUPPORTED), (dict(kitty_hi_bits=8), KVQ_E_UNSUPPORTED),
-    (dict(n_sink=2), KVQ_E_UNSUPPORTED)])
+    (dict(n_sink=2), KVQ_E_UNSUPPORTED), (dict(max_tokens=1 << 22), KVQ_OK),
+    (dict(max_tokens=(1 << 22) + 32), KVQ_E_UNSUPPORTED)])
 def test_kitty_config_validation(kw, status):
     base = dict(method=2, value_bits=16, kitty_n_hi=32)
     base.update(kw)
