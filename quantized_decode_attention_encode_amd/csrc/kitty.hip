@@ -2,11 +2,12 @@
 // variance, the top n_hi quantized at 4 bits and the rest at 2 bits in KIVI's per-channel
 // groups of 32 tokens, values kept in fp16 ("Algorithm Overview": Kitty stores fp16 values).
 //
-// Encode (three launches over the records a prefill, encode or window flush adds):
+// Encode (five launches over the records a prefill, encode or window flush adds):
 //   kitty_stats_kernel   one wave per record: each channel's exact sums over the record's
 //                        32 tokens, s1 = sum X and s2 = sum X^2 with X = x * 2^24 (an integer
-//                        for every finite fp16 x; |X| < 2^40, so s1 fits int64 and s2 uint128),
-//                        staged in the record's value area.
+//                        for every finite fp16 x; |X| < 2^40, so over the at most 2^22 tokens
+//                        of a Kitty sequence s1 fits int64, s2 and n * s2 uint128), staged in
+//                        the record's value area.
 //   kitty_seg/top/fix    running sums up to each record's end (the sequence's stored sums plus
 //                        every earlier group) written back over the staged group sums, and the
 //                        new totals into the sequence's state: segment totals, one walk over
@@ -14,7 +15,8 @@
 //                        integer sums are exact in any order).
 //   kitty_encode_kernel  one wave per record: n * s2 - s1^2 (n^2 times the variance, exact in
 //                        128 bits) ranks the channels (the larger first, the lower index on
-//                        ties); the top n_hi take 4-bit groups, the rest 2-bit ones, by KIVI's
+//                        ties; compared through order-preserving fp32 images, exactly where the
+//                        images are equal); the top n_hi take 4-bit groups, the rest 2-bit ones, by KIVI's
 //                        min/max rule (quant.h); codes, params and the slot table are written,
 //                        then the fp16 value rows over the staging.
 // Decode: kitty_decode_kernel, split-K over the records and window units of each (b, h_kv) with
@@ -448,8 +450,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void kitty_decode_kernel(const uint
   }
   wave_sync();
   // One record ahead is requested while the current one is computed (G <= 2; wider query-head
-  // groups have no registers to spare). The prefetch index is clamped into the wave's records,
-  // so the load is unconditional (the last one re-reads a record).
+  // groups have no registers to spare). The prefetch index is clamped to the split's last
+  // record, so the load is unconditional (a wave's last prefetch re-reads a record).
   constexpr bool kPrefetch = G <= 2;
   const int ulast = max(min(u1, ngroups) - 1, 0);
   RecRegs<D> cur, nxt;
