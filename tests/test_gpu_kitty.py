@@ -238,3 +238,35 @@ def test_kitty_ranking_ties_on_the_device():
         else:  # every channel but 16 of the constants: the lowest-index constant gets in
             assert all(r[0] and not r[1:20][[c - 1 for c in const[1:]]].any() for r in s.khi)
         assert_kitty_state(host_buffer(cache), cfg, {(0, 0): s}, f"ties, fraction {frac}")
+
+
+@pytest.mark.parametrize("name,pairs", [("long", {(0, 0), (0, 13), (0, 31)}), ("gqa", {(0, 0), (5, 3), (15, 7)})])
+def test_kitty_full_size(name, pairs):
+    """The long (64K tokens, 32 heads) and ragged GQA-batch workloads as Kitty caches, in the
+    launch configuration bench.py times (automatic split count, fp16 output): sampled (b, h)
+    pairs bit-exact against the oracle and their query heads' outputs within tolerance."""
+    wl = workloads.WORKLOADS[name]
+    draw = workloads.Draw(wl)
+    cap = (max(draw.seq_lens) + 31) // 32 * 32
+    cfg = make_config(wl.batch, wl.n_kv_heads, wl.n_q_heads, wl.head_dim, wl.key_bits, 16, 32, wl.residual, cap,
+                      method="kitty", kitty_hi_fraction=0.25)
+    say(f"kitty {name}: {wl.describe()}, n_hi {cfg.kitty_n_hi}")
+    cache = KVQCache(cfg, device=DEV)
+    K, V, lens = draw.padded()
+    Kt, Vt = torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV)
+    del K, V
+    kvq_prefill(cache, Kt, Vt, lens)
+    out = kvq_decode_attend(cache, torch.from_numpy(draw.q).to(DEV)).float().cpu().numpy()
+    buf = host_buffer(cache)
+    del Kt, Vt
+    seqs = {}
+    for (b, h) in pairs:
+        s = oracle_seq(wl, cfg)
+        s.prefill(draw.K[b][h], draw.V[b][h])
+        seqs[(b, h)] = s
+    assert_kitty_state(buf, cfg, seqs, name)
+    G = wl.n_q_heads // wl.n_kv_heads
+    heads = {(b, hq) for (b, h) in pairs for hq in range(G * h, G * h + G)}
+    ref = oracle_attend(draw.q.astype(np.float64), seqs, wl, heads=heads)
+    err = assert_close(out, ref, f"kitty {name}")
+    say(f"  kitty {name}: state bit-exact on {len(pairs)} (b, h); attention max abs {err[0]:.2e}")
