@@ -4,4 +4,4 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``b
 may import this package. It shares no code with the HIP library or its Python binding, and
 imports neither of them.
 """
-from . import brute, kivi  # noqa: F401
+from . import brute, kitty, kivi, skvq  # noqa: F401
