@@ -449,10 +449,10 @@ __global__ __launch_bounds__(64 * kDecWaves) void kitty_decode_kernel(const uint
     for (int c = 0; c < 8; ++c) acc[i][c] = 0.f;
   }
   wave_sync();
-  // One record ahead is requested while the current one is computed (G <= 2; wider query-head
-  // groups have no registers to spare). The prefetch index is clamped to the split's last
+  // One record ahead is requested while the current one is computed (G <= 4; at G = 8 the
+  // registers would spill). The prefetch index is clamped to the split's last
   // record, so the load is unconditional (a wave's last prefetch re-reads a record).
-  constexpr bool kPrefetch = G <= 2;
+  constexpr bool kPrefetch = G <= 4;
   const int ulast = max(min(u1, ngroups) - 1, 0);
   RecRegs<D> cur, nxt;
   if (u0 + wave < min(u1, ngroups)) load_rec<D>(buf + L.record(b, h, u0 + wave), nhc, Wd, nhi, tk, hh, lane, o, cur);
