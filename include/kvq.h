@@ -102,8 +102,8 @@ typedef struct kvq_config {
  * running sums; the lower channel index first on equal variances), else at key_bits. Values are
  * stored as their fp16 inputs (value_bits = 16). The window rule is KIVI's; a flush ranks each of
  * its groups with the sums at its own end, so a prefill equals the same tokens appended one by
- * one. n_sink must be 0; decode takes one query per head (kvq_decode_attend_multi: n_query = 1);
- * max_tokens is at most 2^22, which keeps the integer sums exact for every finite fp16 key. */
+ * one. n_sink must be 0; max_tokens is at most 2^22, which keeps the integer sums exact for every
+ * finite fp16 key. */
 #define KVQ_METHOD_KITTY 2
 
 /* Byte offsets of the regions inside the cache buffer (see the layout description in the

@@ -431,6 +431,12 @@ __global__ __launch_bounds__(64 * kDecWaves) void kitty_decode_kernel(const uint
   const int u1 = min(u0 + ds.chunk, nunits);
   KittyLds<D, G>& W = lw[wave];
   const int nhi = L.nhi, nhc = nhi / 16, Wd = kitty_words(D, nhi);
+  // Multi-query attend (ds.nqry > 1): row i is query i % nqry of its head, the cache's token
+  // S - nqry + i % nqry; it sees the positions below lim[i] (kMaskScore above, as in the KIVI
+  // decode: a wave or split that sees only a row's future merges with weight 0).
+  int lim[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) lim[i] = nq + nr - (ds.nqry - 1 - i % ds.nqry);
   const int tk = lane >> 1, hh = lane & 1;  // key lanes
   const int o = lane % NO, tg = lane / NO;  // value lanes
 #pragma unroll
@@ -508,6 +514,11 @@ __global__ __launch_bounds__(64 * kDecWaves) void kitty_decode_kernel(const uint
       }
 #pragma unroll
       for (int i = 0; i < G; ++i) s[i] = a[i] + dpp<kQuadXor1>(a[i]) + beta[i];  // lanes (t, 0), (t, 1) are adjacent
+      if (ds.nqry > 1 && u * kGroup + kGroup > lim[0]) {  // wave-uniform: a record that reaches a query
+#pragma unroll
+        for (int i = 0; i < G; ++i)
+          if (u * kGroup + tk >= lim[i]) s[i] = kMaskScore;
+      }
       if constexpr (kPrefetch) cur = nxt;
     } else {
       const int tbase = (u - ngroups) * kGroup;
@@ -535,6 +546,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void kitty_decode_kernel(const uint
           }
         }
         s[i] = a + dpp<kQuadXor1>(a);
+        if (nq + tbase + tk >= lim[i]) s[i] = kMaskScore;
         if (tk >= nvalid) s[i] = -INFINITY;
       }
     }

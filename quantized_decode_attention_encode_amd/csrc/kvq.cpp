@@ -218,8 +218,7 @@ kvq_status decode_enqueue(kvq_cache* c, const void* q, void* out, int32_t out_fp
   const kvq_config& cfg = c->cfg;
   const int add = k_tok ? 1 : 0;  // window tokens the launch appends
   const int G = cfg.n_q_heads / cfg.n_kv_heads;
-  if (is_kitty(cfg) && (n_query != 1 || k_tok))
-    return fail(KVQ_E_UNSUPPORTED, "Kitty caches attend one query per head, after a separate append");
+  if (is_kitty(cfg) && k_tok) return fail(KVQ_E_UNSUPPORTED, "Kitty caches append before the decode launch");
   if (n_query < 1 || (n_query & (n_query - 1)) || G * n_query > 8)
     return fail(KVQ_E_UNSUPPORTED, "n_query = %d: it must be a power of two with n_query x (query heads per KV head = %d) <= 8",
                 n_query, G);

@@ -156,17 +156,6 @@ def test_kitty_record_at_the_headline_shape():
     assert (r["words"] * 4, r["params"], r["table"], r["values"], r["bytes"]) == (40, 1280, 1792, 1920, 10112)
 
 
-def test_kitty_rejects_multi_query():
-    c = cfg(method=2, value_bits=16, kitty_n_hi=32)
-    cache = ctypes.c_void_p()
-    buf = ctypes.c_void_p(FAKE)
-    assert lib.kvq_cache_create(ctypes.byref(c), buf, lib.kvq_cache_bytes(ctypes.byref(c)), ctypes.byref(cache)) == KVQ_OK
-    ws = ctypes.c_void_p(FAKE)
-    st = lib.kvq_decode_attend_multi(cache, buf, buf, 2, 0, ctypes.c_float(1.0), ws, 1 << 30, 0, None)
-    assert st == KVQ_E_UNSUPPORTED
-    lib.kvq_cache_destroy(cache)
-
-
 def test_skvq_cache_rejects_encode():
     c = cfg(method=1, n_sink=5, residual=128)
     cache = ctypes.c_void_p()

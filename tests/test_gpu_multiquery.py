@@ -1,14 +1,14 @@
 """GPU parity for multi-query attend (kvq_decode_attend_multi): the newest n_query tokens of each
 sequence attend causally over the quantized cache, against the fp64 oracle's causal prefix
 attention. Lengths are chosen so that masked tokens fall in the window, in the last record
-(a window of 1..2 tokens) and among the sinks (short sequences), for KIVI, KIVI-Sink and
-SKVQ caches, every split count; n_query = 1 must equal kvq_decode_attend bit for bit.
+(a window of 1..2 tokens) and among the sinks (short sequences), for KIVI, KIVI-Sink, SKVQ and
+Kitty caches, every split count; n_query = 1 must equal kvq_decode_attend bit for bit.
 """
 import numpy as np
 import pytest
 import torch
 
-from oracle import kivi, skvq
+from oracle import kitty, kivi, skvq
 from quantized_decode_attention_encode_amd import (KVQCache, kvq_decode_attend, kvq_decode_attend_multi,
                                                    kvq_prefill, make_config, workloads)
 from tests.gpu_helpers import assert_close, oracle_prefill, say
@@ -24,6 +24,9 @@ CASES = [
     ("sink-d128-g1-q8", 3, 2, 2, 128, 2, 2, [40, 300, 8], 8, "kivi", 5, 32),
     ("skvq-d64-g2-q2", 3, 4, 2, 64, 2, 2, [3, 140, 6], 2, "skvq", 3, 64),
     ("skvq-d128-g1-q4", 2, 2, 2, 128, 4, 4, [133, 4], 4, "skvq", 2, 128),
+    ("kitty-d128-g1-q4", 3, 2, 2, 128, 2, 16, [321, 96, 4], 4, "kitty", 0, 32),
+    ("kitty-d64-g2-q4", 2, 4, 2, 64, 2, 16, [200, 7], 4, "kitty", 0, 64),
+    ("kitty-d128-g4-q2", 2, 8, 2, 128, 2, 16, [129, 33], 2, "kitty", 0, 32),
 ]
 
 
@@ -36,11 +39,14 @@ def setup(case, seed=41):
     cache = KVQCache(cfg, device=DEV)
     K, V, _ = draw.padded()
     kvq_prefill(cache, torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV), lens)
-    if method == "skvq":
+    if method in ("skvq", "kitty"):
         seqs = {}
         for b in range(B):
             for h in range(Hkv):
-                s = skvq.SkvqSequence(D, bk, bv, 32, R, ns)
+                if method == "skvq":
+                    s = skvq.SkvqSequence(D, bk, bv, 32, R, ns)
+                else:
+                    s = kitty.KittySequence(D, cfg.kitty_n_hi, 4, bk, 32, R)
                 s.prefill(draw.K[b][h], draw.V[b][h])
                 seqs[(b, h)] = s
     else:
