@@ -17,7 +17,7 @@ What it follows (VeloxQuant-MLX documentation pages):
   with codes plus a per-group (scale, zero); attention is the plain softmax over the
   reconstructed keys (``oracle.kivi.attend``).
 
-Readings taken where the pages leave a step open (each is listed in the design doc):
+Readings taken where the pages leave a step open:
 
 * a key group is g = 32 consecutive tokens of one channel (KIVI's per-channel key groups);
   it is quantized by KIVI's min/max rule (``oracle.kivi.quantize_groups``) at the bit width

@@ -27,7 +27,7 @@ What it follows (VeloxQuant-MLX documentation pages):
   fp16 and left out of the statistics the quantization parameters come from;
   ``n_sink_tokens = 0`` is plain KIVI.
 
-Readings taken where the pages leave a step open (each is listed in the design doc):
+Readings taken where the pages leave a step open:
 
 * zero = group minimum, stored fp16 (exact, it is an fp16 input value);
 * scale = (max - min) / (2**b - 1), fp32 subtract then fp32 divide, rounded once to fp16;

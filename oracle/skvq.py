@@ -22,7 +22,7 @@ What it follows (VeloxQuant-MLX documentation pages):
   skvq_group_size 32, skvq_window 128, skvq_n_sink 5, skvq_reorder True, skvq_clip_search
   True, skvq_clip_alpha 1.0.
 
-Readings taken where the pages leave a step open (each is listed in the design doc):
+Readings taken where the pages leave a step open:
 
 * sinks are the first n_sink tokens of the sequence; the window rule applies to the tokens
   after them: with S' = S - n_sink >= 1 of those, the window holds ((S' - 1) mod R) + 1 and
