@@ -284,3 +284,19 @@ def test_status_strings():
     for st, name in [(KVQ_OK, "KVQ_OK"), (KVQ_E_INVALID, "KVQ_E_INVALID"), (KVQ_E_CAPACITY, "KVQ_E_CAPACITY"),
                      (KVQ_E_NODEVICE, "KVQ_E_NODEVICE"), (-99, "KVQ_E_UNKNOWN")]:
         assert lib.kvq_status_string(st).decode() == name
+
+
+def test_kitty_config_from_python():
+    from quantized_decode_attention_encode_amd import make_config
+
+    c = make_config(1, 2, 2, 128, 2, 2, 32, 32, 1024, method="kitty")  # the pages' quarter
+    assert (c.method, c.kitty_n_hi, c.kitty_hi_bits, c.value_bits) == (2, 32, 4, 16)
+    assert lib.kvq_config_check(ctypes.byref(c)) == KVQ_OK
+    assert make_config(1, 1, 1, 64, method="kitty", kitty_hi_fraction=0.25).kitty_n_hi == 16
+    assert make_config(1, 1, 1, 128, method="kitty", kitty_hi_fraction=1.0).kitty_n_hi == 128
+    odd = make_config(1, 1, 1, 128, method="kitty", kitty_hi_fraction=0.3)  # 38 channels: not built
+    assert odd.kitty_n_hi == 38 and lib.kvq_config_check(ctypes.byref(odd)) == KVQ_E_UNSUPPORTED
+    with pytest.raises(ValueError):
+        make_config(1, 1, 1, 128, method="kitty", kitty_hi_fraction=1.5)
+    with pytest.raises(ValueError):
+        make_config(1, 1, 1, 128, method="polar")
