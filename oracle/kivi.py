@@ -44,9 +44,11 @@ Readings taken where the pages leave a step open:
   by the first step that quantizes tokens of it (a prefill or encode with a quantized part,
   or the first window flush), among the tokens that step quantizes; the squared norm is an
   fp32 sum of fp32 squares taken channel by channel in order; equal norms go to the earlier
-  token. A sink keeps its fp16 key and value rows; its quantized slot stays in its record
-  (codes from the group parameters, clamped) but is skipped by attention, and the stored
-  scale of each of its value groups carries the sign bit as the marker of that.
+  token. A sink keeps its fp16 key and value rows; its quantized slot stays in the cache
+  (codes from the group parameters, clamped) but attention uses the fp16 rows in its place.
+  How a device marks that slot is a storage choice of the device layout, not part of what
+  the method computes: the oracle's value parameters are the plain ones, and the sinks are
+  its list of positions.
 """
 from __future__ import annotations
 
@@ -130,20 +132,17 @@ def encode_keys(K: np.ndarray, bits: int, g: int = 32, sinks=()):
     return np.ascontiguousarray(c.transpose(0, 2, 1).reshape(T, D)), s, z
 
 
-def encode_values(V: np.ndarray, bits: int, g: int = 32, sinks=()):
+def encode_values(V: np.ndarray, bits: int, g: int = 32):
     """Per-token value quantization of an fp16 block ``V[T, D]`` with D a multiple of g.
 
-    A group is g consecutive channels of one token. Returns ``codes[T, D]`` (uint8),
-    ``scale[T, D/g]`` and ``zero[T, D/g]`` (fp16). The scales of the rows listed in
-    ``sinks`` are stored with their sign bit set: the marker that attention skips that slot.
+    A group is g consecutive channels of one token, so a sink token ("Changelog" v0.9.0,
+    KIVI-Sink) changes no value group's statistics: its own groups are quantized like any
+    other row. Returns ``codes[T, D]`` (uint8), ``scale[T, D/g]`` and ``zero[T, D/g]`` (fp16).
     """
     T, D = V.shape
     if D % g:
         raise ValueError("head dim must be a multiple of the group size")
     c, s, z = quantize_groups(V.reshape(T, D // g, g), bits)
-    if len(sinks):
-        bits16 = s.view(np.uint16)
-        bits16[np.asarray(sinks)] |= np.uint16(0x8000)
     return c.reshape(T, D), s, z
 
 
@@ -248,7 +247,7 @@ class KiviSequence:
         self.kc = np.concatenate([self.kc, c])
         self.ks = np.concatenate([self.ks, s])
         self.kz = np.concatenate([self.kz, z])
-        c, s, z = encode_values(V, self.bv, self.g, local)
+        c, s, z = encode_values(V, self.bv, self.g)
         self.vc = np.concatenate([self.vc, c])
         self.vs = np.concatenate([self.vs, s])
         self.vz = np.concatenate([self.vz, z])
@@ -282,7 +281,7 @@ class KiviSequence:
         return np.concatenate([kq, self.wk.astype(F64)])
 
     def values_hat(self) -> np.ndarray:
-        vq = dequantize_values(self.vc, np.abs(self.vs), self.vz, self.g) if self.n_q else np.zeros((0, self.D))
+        vq = dequantize_values(self.vc, self.vs, self.vz, self.g) if self.n_q else np.zeros((0, self.D))
         vq[self.sink_pos] = self.sink_v.astype(F64)
         return np.concatenate([vq, self.wv.astype(F64)])
 

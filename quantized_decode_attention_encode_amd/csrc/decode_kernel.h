@@ -654,9 +654,10 @@ __device__ const uint8_t kIdentityPerm[128] = {
 // KT: SKVQ records (per-token key groups, permuted channels, see layout.h).
 template <int D, int BK, int BV, int G, bool SK, bool KT>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(G == 1 ? 4 : (G <= 4 ? 2 : 1))))
-void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape ds, const __half* __restrict__ q,
-                         float* __restrict__ ws, uint32_t* __restrict__ sync, void* __restrict__ out,
-                         const __half* __restrict__ k_app, const __half* __restrict__ v_app, uint8_t* bufw) {
+void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape ds, PerSeq seq,
+                         const __half* __restrict__ q, float* __restrict__ ws, uint32_t* __restrict__ sync,
+                         void* __restrict__ out, const __half* __restrict__ k_app, const __half* __restrict__ v_app,
+                         uint8_t* bufw) {
   constexpr int E = D / 64, DQ = D / 4, NKG = D / 32;
   using MK = Magic<BK>;
   using MV = Magic<BV>;
@@ -670,17 +671,16 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
 
   const int sigma = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int32_t* len = reinterpret_cast<const int32_t*>(buf + L.lengths(b, h));
-  const int nq = max(0, min(len[0], L.max_groups * kGroup));
-  const int nr_old = max(0, min(len[1], L.R));
+  // The plan comes from the host's lengths (seq: quantized tokens, window tokens before this
+  // launch's append, sinks present), never from the device copy: with an append, the split that
+  // finishes last rewrites the device window length inside this launch, and a split that read
+  // it afterwards would see a different number of units than its siblings.
+  const int nq = max(0, min(seq.a[b], L.max_groups * kGroup));
+  const int nr_old = max(0, min(seq.b[b], L.R));
   const int nr = min(nr_old + ds.append, L.R);  // with an append: the new token is window slot nr_old
   const int ngroups = nq / kGroup;
   // with sinks one more unit, the last: their fp16 rows
-  int nsink = 0;
-  if constexpr (SK) {
-    const int32_t* sp = reinterpret_cast<const int32_t*>(buf + L.sink_pos(b, h));
-    for (int k = 0; k < L.NS && sp[k] >= 0; ++k) nsink = k + 1;
-  }
+  const int nsink = SK ? max(0, min(seq.c[b], L.NS)) : 0;
   const bool sinks = nsink > 0;
   // positions: SKVQ sinks are tokens 0 .. nsink - 1 and its records start after them
   const int pos0 = KT ? nsink : 0;
@@ -907,9 +907,9 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
 
 // ------------------------------------------------------------------------------------
 template <int D, int BK, int BV, int G, bool SK, bool KT>
-static hipError_t launch_split_t(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q,
-                                 float* ws, void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0,
-                                 hipEvent_t e1) {
+static hipError_t launch_split_t(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq,
+                                 const void* q, float* ws, void* out, const void* ka, const void* va, hipStream_t s,
+                                 hipEvent_t e0, hipEvent_t e1) {
   dim3 grid(ds.n_split, L.Hkv, L.B);
   uint32_t* sync = reinterpret_cast<uint32_t*>(buf + L.sync_off);
   const __half* qh = static_cast<const __half*>(q);
@@ -917,40 +917,40 @@ static hipError_t launch_split_t(uint8_t* buf, const Layout& L, const DecodeShap
   const __half* vh = static_cast<const __half*>(va);
   if (e0 || e1)
     hipExtLaunchKernelGGL((decode_split_kernel<D, BK, BV, G, SK, KT>), grid, dim3(64 * kWaves), 0, s, e0, e1, 0,
-                          static_cast<const uint8_t*>(buf), L, ds, qh, ws, sync, out, kh, vh, buf);
+                          static_cast<const uint8_t*>(buf), L, ds, seq, qh, ws, sync, out, kh, vh, buf);
   else
     hipLaunchKernelGGL((decode_split_kernel<D, BK, BV, G, SK, KT>), grid, dim3(64 * kWaves), 0, s,
-                       static_cast<const uint8_t*>(buf), L, ds, qh, ws, sync, out, kh, vh, buf);
+                       static_cast<const uint8_t*>(buf), L, ds, seq, qh, ws, sync, out, kh, vh, buf);
   return hipGetLastError();
 }
 
 template <int D, int BK, int BV, bool SK, bool KT>
-static hipError_t launch_split_g(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q,
-                                 float* ws, void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0,
-                                 hipEvent_t e1) {
+static hipError_t launch_split_g(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq,
+                                 const void* q, float* ws, void* out, const void* ka, const void* va, hipStream_t s,
+                                 hipEvent_t e0, hipEvent_t e1) {
   switch (ds.G) {
-    case 1: return launch_split_t<D, BK, BV, 1, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 2: return launch_split_t<D, BK, BV, 2, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 4: return launch_split_t<D, BK, BV, 4, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 8: return launch_split_t<D, BK, BV, 8, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 1: return launch_split_t<D, BK, BV, 1, SK, KT>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+    case 2: return launch_split_t<D, BK, BV, 2, SK, KT>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+    case 4: return launch_split_t<D, BK, BV, 4, SK, KT>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+    case 8: return launch_split_t<D, BK, BV, 8, SK, KT>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int D, bool SK, bool KT>
-static hipError_t launch_split_d(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q,
-                                 float* ws, void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0,
-                                 hipEvent_t e1) {
+static hipError_t launch_split_d(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq,
+                                 const void* q, float* ws, void* out, const void* ka, const void* va, hipStream_t s,
+                                 hipEvent_t e0, hipEvent_t e1) {
   switch (L.bk * 16 + L.bv) {
-    case 0x22: return launch_split_g<D, 2, 2, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 0x24: return launch_split_g<D, 2, 4, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 0x28: return launch_split_g<D, 2, 8, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 0x42: return launch_split_g<D, 4, 2, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 0x44: return launch_split_g<D, 4, 4, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 0x48: return launch_split_g<D, 4, 8, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 0x82: return launch_split_g<D, 8, 2, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 0x84: return launch_split_g<D, 8, 4, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-    case 0x88: return launch_split_g<D, 8, 8, SK, KT>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+    case 0x22: return launch_split_g<D, 2, 2, SK, KT>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+    case 0x24: return launch_split_g<D, 2, 4, SK, KT>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+    case 0x28: return launch_split_g<D, 2, 8, SK, KT>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+    case 0x42: return launch_split_g<D, 4, 2, SK, KT>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+    case 0x44: return launch_split_g<D, 4, 4, SK, KT>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+    case 0x48: return launch_split_g<D, 4, 8, SK, KT>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+    case 0x82: return launch_split_g<D, 8, 2, SK, KT>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+    case 0x84: return launch_split_g<D, 8, 4, SK, KT>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+    case 0x88: return launch_split_g<D, 8, 8, SK, KT>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }

@@ -5,10 +5,10 @@
 
 namespace kvq {
 
-hipError_t launch_decode_sink(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q, float* ws,
+hipError_t launch_decode_sink(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq, const void* q, float* ws,
                               void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  if (L.D == 128) return launch_split_d<128, true, false>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
-  if (L.D == 64) return launch_split_d<64, true, false>(buf, L, ds, q, ws, out, ka, va, s, e0, e1);
+  if (L.D == 128) return launch_split_d<128, true, false>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+  if (L.D == 64) return launch_split_d<64, true, false>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
   return hipErrorInvalidValue;
 }
 

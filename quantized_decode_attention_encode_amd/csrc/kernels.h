@@ -57,17 +57,19 @@ hipError_t launch_sink_select(uint8_t* buf, const Layout& L, const void* K, cons
 // Decode attention: split-K kernel whose last split per (b, h_kv) merges the partials into
 // `out`. start/stop, when not null, are stamped by the kernel's own dispatch (its execution
 // time).
+// seq: the host's lengths of every sequence (a = quantized tokens, b = window tokens before the
+// launch's append, c = sinks present); the launch is planned from them, not from the device copy.
 // With ds.append, k_tok / v_tok (fp16 [B][H_kv][D]) are the appended tokens: the launch attends
 // over the window plus them, stores them in their window slots and advances the device lengths.
-hipError_t launch_decode(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q, float* ws,
+hipError_t launch_decode(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq, const void* q, float* ws,
                          void* out, const void* k_tok, const void* v_tok, hipStream_t s,
                          hipEvent_t start = nullptr, hipEvent_t stop = nullptr);
 // The same for SKVQ caches and for KIVI caches with sink tokens (L.NS > 0); launch_decode
 // forwards to them.
-hipError_t launch_decode_skvq(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q, float* ws,
+hipError_t launch_decode_skvq(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq, const void* q, float* ws,
                               void* out, const void* k_tok, const void* v_tok, hipStream_t s, hipEvent_t start,
                               hipEvent_t stop);
-hipError_t launch_decode_sink(uint8_t* buf, const Layout& L, const DecodeShape& ds, const void* q, float* ws,
+hipError_t launch_decode_sink(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq, const void* q, float* ws,
                               void* out, const void* k_tok, const void* v_tok, hipStream_t s, hipEvent_t start,
                               hipEvent_t stop);
 

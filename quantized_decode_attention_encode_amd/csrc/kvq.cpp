@@ -2,8 +2,9 @@
 //
 // Validation happens here, on the host, before any launch; lengths are mirrored on the
 // host (every change is decided here) so capacity checks and decode geometry never need a
-// device synchronisation. The decode kernels read the device copy of the lengths; append
-// takes the mirror as kernel arguments (its token loads then wait for nothing). Each call
+// device synchronisation. The decode and append kernels take the mirror as kernel arguments
+// (their loads then wait for nothing, and a decode that also appends never plans from lengths
+// it rewrites itself); the device copy is kept for the other kernels and readers. Each call
 // is planned from the mirror at enqueue time, so a captured graph of these calls replays
 // that plan: it is valid only for the lengths it was captured at.
 #include <hip/hip_runtime.h>
@@ -259,6 +260,13 @@ kvq_status decode_enqueue(kvq_cache* c, const void* q, void* out, int32_t out_fp
   ds.qscale = sm_scale * 1.4426950408889634f;
   ds.out_fp32 = out_fp32 ? 1 : 0;
   ds.append = add;
+  PerSeq seq;  // the plan's lengths: the host mirror before this launch's append
+  memset(&seq, 0, sizeof seq);
+  for (int b = 0; b < cfg.batch; ++b) {
+    seq.a[b] = c->nq[b];
+    seq.b[b] = c->nr[b];
+    seq.c[b] = is_skvq(cfg) ? c->nsp[b] : (has_sinks(c, b) ? cfg.n_sink : 0);
+  }
   float* ws = static_cast<float*>(workspace);
   hipError_t e;
   const bool prof = c->profiling;
@@ -279,7 +287,7 @@ kvq_status decode_enqueue(kvq_cache* c, const void* q, void* out, int32_t out_fp
     e = kvq::launch_kitty_decode(c->buf, c->L, ds, q, ws, out, s, prof ? c->ev[c->ev_used] : nullptr,
                                  prof ? c->ev[c->ev_used + 1] : nullptr);
   else
-    e = kvq::launch_decode(c->buf, c->L, ds, q, ws, out, k_tok, v_tok, s, prof ? c->ev[c->ev_used] : nullptr,
+    e = kvq::launch_decode(c->buf, c->L, ds, seq, q, ws, out, k_tok, v_tok, s, prof ? c->ev[c->ev_used] : nullptr,
                            prof ? c->ev[c->ev_used + 1] : nullptr);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   if (prof) c->ev_used += 2;

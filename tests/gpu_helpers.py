@@ -55,8 +55,13 @@ def assert_state_equal(buf, c, seqs, what=""):
                   ("wk", s.wk), ("wv", s.wv), ("sink_k", s.sink_k), ("sink_v", s.sink_v)]
         if hasattr(s, "sink_pos"):
             fields.append(("sink_pos", s.sink_pos))
+            # the device's slot marker: exactly the sinks' quantized slots
+            mark = np.zeros(s.n_q, bool)
+            mark[s.sink_pos] = True
+            fields.append(("vmark", mark))
         else:  # SKVQ: the first tokens, and the permutations once a chunk is quantized
             fields.append(("sink_pos", np.arange(s.sink_k.shape[0], dtype=np.int64)))
+            fields.append(("vmark", np.zeros(s.n_q, bool)))  # its sinks have no quantized slot
             if s.n_q:
                 fields += [("perm_k", np.asarray(s.perm_k, np.int64)), ("perm_v", np.asarray(s.perm_v, np.int64))]
         for name, ref in fields:

@@ -3,7 +3,8 @@
 Written from the layout description (records of 32 tokens; key codes as
 [P=t/2][quarter][t%2][words] with channel c' of the quarter at bit c'*bk, value codes as
 [channel][words] with token t at bit t*bv, key params [channel], value params
-[t/2][value group][t%2], fp16 (scale, zero) pairs with the scale in the low half; then the
+[t/2][value group][t%2], fp16 (scale, zero) pairs with the scale in the low half, whose sign
+bit marks a sink's quantized slot (stripped here and returned as "vmark"); then the
 sink regions: positions int32 [B][H_kv][NS], key and value rows fp16 [B][H_kv][NS][D], and for
 SKVQ caches the channel permutations uint8 [B][H_kv][2][D]; SKVQ records keep their key params
 in the value-param layout, one (scale, zero) per token and group of permuted channels, and their
@@ -86,9 +87,17 @@ def unpack_records(recs: np.ndarray, D: int, bk: int, bv: int, skvq: bool = Fals
         kz = kp[..., 1].view(np.float16).reshape(n, D)
     vp = np.ascontiguousarray(recs[:, o_vp:o_vp + 4 * D]).view("<u2").reshape(n, 16, NKG, 2, 2)
     vp = vp.transpose(0, 1, 3, 2, 4).reshape(n * 32, NKG, 2)  # token 2P+tp
-    vs = vp[..., 0].view(np.float16)
+    # The device marks the quantized slot of a KIVI-Sink token (attended from its fp16 rows
+    # instead) with the sign bit of each of its value scales; a stored scale is never negative.
+    # The marker is stripped here and returned on its own: "vmark" per token (every group of
+    # the token agrees, or the record is malformed).
+    sign = (vp[..., 0] & 0x8000) != 0
+    vmark = sign.any(axis=-1)
+    if np.any(sign.any(axis=-1) != sign.all(axis=-1)):
+        raise ValueError("a token's value groups disagree on the sink marker")
+    vs = (vp[..., 0] & 0x7FFF).view(np.float16)
     vz = vp[..., 1].view(np.float16)
-    out = {"kc": kc, "ks": ks, "kz": kz, "vc": vc, "vs": vs, "vz": vz}
+    out = {"kc": kc, "ks": ks, "kz": kz, "vc": vc, "vs": vs, "vz": vz, "vmark": vmark}
     return {k: np.ascontiguousarray(v) for k, v in out.items()}
 
 

@@ -321,16 +321,21 @@ def test_largest_batch_and_more_splits_than_units():
         assert_close(out.cpu().numpy(), ref, f"maxb n_split={n_split}")
 
 
+@pytest.mark.parametrize("residual", [32, 64, 128])
 @pytest.mark.parametrize("n_split", [0, 1, 3])
 @pytest.mark.parametrize("start", ["prefill", "encode", "window-only"])
-def test_fused_append_decode_equals_append_then_decode(start, n_split):
+def test_fused_append_decode_equals_append_then_decode(start, n_split, residual):
     # kvq_append_decode_attend must leave the same cache bytes and give the same outputs as
     # kvq_append followed by kvq_decode_attend, step after step, across window flushes (ragged
-    # lengths: some sequences flush while others append in one launch)
+    # lengths: some sequences flush while others append in one launch). Windows of 64 and 128
+    # tokens hold several 32-token units, so appends cross unit boundaries inside the window:
+    # the step whose token opens a new unit changes the unit count of its sequence in the
+    # same launch that appends it.
     case = ("fused", 3, 8, 2, 128, 2, 4, None)
     lens = {"prefill": [200, 97, 64], "encode": [192, 64, 96], "window-only": [5, 31, 1]}[start]
     n_steps = 70
-    wl, draw, cfg = make(case, seed=60, seq_lens=[s + n_steps for s in lens], max_tokens=512)
+    wl, draw, cfg = make(case, seed=60, residual=residual, seq_lens=[s + n_steps for s in lens], max_tokens=512)
+    say("fused", start, "n_split", n_split, "R", residual)
     K, V, _ = draw.padded()
     Kt, Vt = torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV)
     caches = [KVQCache(cfg, device=DEV) for _ in range(2)]
@@ -349,7 +354,16 @@ def test_fused_append_decode_equals_append_then_decode(start, n_split):
         assert torch.equal(o0, o1), f"{start} step {t}"
         assert caches[0].lengths() == caches[1].lengths()
     b0, b1 = host_buffer(caches[0]), host_buffer(caches[1])
-    seqs = oracle_prefill(draw, cfg.residual)  # every drawn token = the prefill plus the appends
+    # the oracle takes the same path (an encode leaves the window empty, so with R > 32 its state
+    # differs from a straight prefill of the same tokens)
+    seqs = {}
+    for b in range(3):
+        for h in range(wl.n_kv_heads):
+            s = kivi.KiviSequence(wl.head_dim, wl.key_bits, wl.value_bits, 32, residual)
+            (s.encode if start == "encode" else s.prefill)(draw.K[b][h][:lens[b]], draw.V[b][h][:lens[b]])
+            for t in range(n_steps):
+                s.append(draw.K[b][h][lens[b] + t], draw.V[b][h][lens[b] + t])
+            seqs[(b, h)] = s
     assert_state_equal(b1, cfg, seqs, f"{start} fused")
     assert_state_equal(b0, cfg, seqs, f"{start} separate")
     ref = oracle_attend(draw.q.astype(np.float64), seqs, wl)

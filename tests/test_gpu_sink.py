@@ -133,3 +133,112 @@ def test_sinks_chosen_by_the_first_flush(fused):
             ref = oracle_attend(draw.q.astype(np.float64), seqs, wl)
             assert_close(out.cpu().numpy(), ref, f"step {t}")
     assert seqs[(0, 0)].sink_pos.size == cfg.n_sink and np.all(seqs[(0, 0)].sink_pos < 32)
+
+
+# ---------------------------------------------------------------------------------------------
+# Long prefills: the sink choice runs over several 2048-token chunks whose candidate lists are
+# merged, so the winners can come from any chunk and ties can straddle a chunk boundary.
+TIE = (2047, 2048, 4095, 4096)  # one identical key row: an exact norm tie across two boundaries
+
+MULTI = [
+    # name, B, Hq, Hkv, D, bk, bv, sequence lengths, n_sink
+    ("d128-b22-s1", 3, 4, 4, 128, 2, 2, (5000, 9000, 6150), 1),
+    ("d64-b24-gqa2-s5", 3, 4, 2, 64, 2, 4, (8999, 5031, 7000), 5),
+    ("d128-b44-gqa4-s16", 2, 8, 2, 128, 4, 4, (6400, 9000), 16),
+]
+
+
+def plant_multichunk(draw, n_sink, seed):
+    """Per (b, h): n_sink - 1 keys of distinct, large norms at random positions of the quantized
+    part (spread over its chunks), and the TIE tokens sharing one key row whose norm ranks just
+    below them; so the sinks are those n_sink - 1 tokens and token 2047, the earliest of the tie.
+    Returns the expected sink positions per (b, h)."""
+    rng = np.random.default_rng(seed)
+    D, R = draw.wl.head_dim, draw.wl.residual
+    expect = {}
+    for b, Kb in enumerate(draw.K):
+        n_q, _ = kivi.window_split(Kb.shape[1], R)
+        assert n_q > max(TIE)
+        for h in range(Kb.shape[0]):
+            u = rng.standard_normal(D, np.float32).astype(np.float16)
+            tie = (u.astype(np.float32) * 8).astype(np.float16)  # a power of two: exact, norm 64 |u|^2
+            for t in TIE:
+                Kb[h, t] = tie
+            top = rng.choice(np.setdiff1d(np.arange(n_q), TIE), n_sink - 1, replace=False)
+            for t in top:  # norms ~ 256 * chi2(128): far above the tie, distinct from each other
+                Kb[h, t] = (rng.standard_normal(D, np.float32) * 16).astype(np.float16)
+            expect[(b, h)] = sorted(int(t) for t in top) + [2047]
+            expect[(b, h)].sort()
+    return expect
+
+
+@pytest.mark.parametrize("start", ["prefill", "encode"])
+@pytest.mark.parametrize("case", MULTI, ids=[c[0] for c in MULTI])
+def test_sink_choice_over_many_chunks(case, start):
+    name, B, Hq, Hkv, D, bk, bv, lens, ns = case
+    if start == "encode":  # kvq_encode takes whole groups and leaves the window empty
+        lens = tuple(s // 32 * 32 for s in lens)
+    wl = workloads.custom(name=name, batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, key_bits=bk, value_bits=bv,
+                          n_outlier=2, seed=70 + ns, ragged=(1, 2))
+    draw = workloads.Draw(wl, seq_lens=list(lens))
+    expect = plant_multichunk(draw, ns, 80 + ns)
+    say("case", name, start, "lens", draw.seq_lens)
+    cfg = make_config(B, Hkv, Hq, D, bk, bv, 32, 32, 9216, n_sink=ns)
+    cache = KVQCache(cfg, device=DEV)
+    K, V, _ = draw.padded()
+    Kt, Vt = torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV)
+    if start == "prefill":
+        kvq_prefill(cache, Kt, Vt, list(lens))
+    else:
+        kvq_encode(cache, Kt, Vt, list(lens))
+    torch.cuda.synchronize()
+    seqs = {}
+    for b in range(B):
+        for h in range(Hkv):
+            s = kivi.KiviSequence(D, bk, bv, 32, 32, ns)
+            (s.prefill if start == "prefill" else s.encode)(draw.K[b][h], draw.V[b][h])
+            assert s.sink_pos.tolist() == expect[(b, h)], (b, h)  # the oracle picks the planted ones
+            seqs[(b, h)] = s
+    assert_state_equal(host_buffer(cache), cfg, seqs, f"{name} {start}")
+    ref = oracle_attend(draw.q.astype(np.float64), seqs, wl)
+    q = torch.from_numpy(draw.q).to(DEV)
+    for n_split in (0, 5):
+        out = kvq_decode_attend(cache, q, out_fp32=True, n_split=n_split)
+        err = assert_close(out.cpu().numpy(), ref, f"{name} {start} n_split={n_split}")
+        say("  n_split", n_split, "err", err)
+    # appends across a window flush keep the sinks, fused with the decode
+    for t in range(40):
+        k, v = draw.next_token()
+        kt, vt = torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV)
+        for (b, h), s in seqs.items():
+            s.append(k[b, h], v[b, h])
+        out = kvq_append_decode_attend(cache, kt, vt, q, out_fp32=True)
+    torch.cuda.synchronize()
+    assert_state_equal(host_buffer(cache), cfg, seqs, f"{name} {start} appended")
+    assert_close(out.cpu().numpy(), oracle_attend(draw.q.astype(np.float64), seqs, wl), f"{name} {start} appended")
+
+
+def test_long_workload_with_five_sinks():
+    # the bench's sink configuration at full size (65504 quantized tokens: 32 chunks per head),
+    # bit-exact state and attention on sampled heads
+    wl = workloads.WORKLOADS["long"]
+    say(f"long with 5 sinks: {wl.describe()}")
+    draw = workloads.Draw(wl)
+    cfg = make_config(wl.batch, wl.n_kv_heads, wl.n_q_heads, wl.head_dim, wl.key_bits, wl.value_bits, 32,
+                      wl.residual, 65536, n_sink=5)
+    cache = KVQCache(cfg, device=DEV)
+    K, V, lens = draw.padded()
+    Kt, Vt = torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV)
+    del K, V
+    kvq_prefill(cache, Kt, Vt, lens)
+    out = kvq_decode_attend(cache, torch.from_numpy(draw.q).to(DEV)).float().cpu().numpy()
+    buf = host_buffer(cache)
+    del Kt, Vt
+    pairs = {(0, 0), (0, 17), (0, 31)}
+    seqs = oracle_prefill(draw, wl.residual, pairs=pairs, n_sink=5)
+    chunks = {(b, h): sorted({int(p) // 2048 for p in s.sink_pos}) for (b, h), s in seqs.items()}
+    say("  sink chunks per sampled head", chunks)
+    assert_state_equal(buf, cfg, seqs, "long n_sink=5")
+    ref = oracle_attend(draw.q.astype(np.float64), seqs, wl, heads=pairs)
+    err = assert_close(out, ref, "long n_sink=5")
+    say("  long n_sink=5: attention max abs / row rel", err)

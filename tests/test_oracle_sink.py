@@ -6,7 +6,7 @@ other than the oracle itself:
 * the brute-force twin (pure Python, explicit binary32 rounding) for the selection and for
   the key groups with sinks left out, bit for bit;
 * invariants: sink rows are reproduced exactly, the remaining rows' groups take their range
-  from the remaining rows only, the value-scale marker, the first-step rule;
+  from the remaining rows only, plain value parameters, the first-step rule;
 * the page's own claims: n_sink_tokens = 0 is plain KIVI, and keeping a high-norm token out
   of the statistics lowers the other tokens' key error.
 """
@@ -74,15 +74,24 @@ def test_group_range_comes_from_the_other_tokens():
     assert np.array_equal(s[1], s0[1]) and np.array_equal(c[32:], c0[32:])  # group 1 untouched
 
 
-def test_value_scale_marker():
+def test_sink_values_are_quantized_like_any_row():
+    # a value group is one token's channels: choosing sinks changes no value parameter, and the
+    # sink's own value rows reach attention exact (fp16) in place of their quantized slot
     rng = np.random.default_rng(4)
-    V = rng.standard_normal((32, 64)).astype(F16)
-    _, s_plain, _ = kivi.encode_values(V, 4, 32)
-    c, s, z = kivi.encode_values(V, 4, 32, [2, 9])
-    u, up = s.view(np.uint16), s_plain.view(np.uint16)
-    assert np.all(u[[2, 9]] == up[[2, 9]] | 0x8000)
-    others = np.setdiff1d(np.arange(32), [2, 9])
-    assert np.array_equal(u[others], up[others])
+    K = rng.standard_normal((64, 64)).astype(F16)
+    K[[2, 40]] = (K[[2, 40]].astype(np.float32) * 8).astype(F16)
+    V = rng.standard_normal((64, 64)).astype(F16)
+    plain, sink = kivi.KiviSequence(64, 2, 4, n_sink=0), kivi.KiviSequence(64, 2, 4, n_sink=2)
+    plain.encode(K, V)
+    sink.encode(K, V)
+    assert sink.sink_pos.tolist() == [2, 40]
+    for f in ("vc", "vs", "vz"):
+        assert np.array_equal(getattr(plain, f).view(np.uint8), getattr(sink, f).view(np.uint8)), f
+    assert np.all(sink.vs.view(np.uint16) < 0x8000)  # plain non-negative scales
+    vh = sink.values_hat()
+    assert np.array_equal(vh[[2, 40]], V[[2, 40]].astype(np.float64))
+    others = np.setdiff1d(np.arange(64), [2, 40])
+    assert np.array_equal(vh[others], plain.values_hat()[others])
 
 
 def _sink_seq(K, V, n_sink, R=32, bits=(2, 2)):
