@@ -246,6 +246,22 @@ kvq_status kvq_decode_attend(kvq_cache* cache, const void* q, void* out, int32_t
                              float sm_scale, void* workspace, size_t ws_bytes, int32_t n_split,
                              void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): kvq_decode_attend without a caller workspace. The
+ * split partials go to a file-scope device array of KVQ_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends; nothing is allocated or freed by this
+ * call (no hipMalloc / hipFree, no allocating library routine), and no profiling events are
+ * created or recorded.
+ *   Arguments, layout, ordering and errors as kvq_decode_attend; a call whose partials
+ *   (B * H_q * n_splits * (D + 4) * 4 bytes for the split count the call uses) exceed
+ *   KVQ_NOALLOC_SCRATCH_BYTES is KVQ_E_WORKSPACE, with nothing enqueued.
+ * All calls on one GPU share that GPU's array, and it keeps the last call's contents (nothing
+ * in it needs to start at zero: every partial a call reads, the same call wrote). Calls that
+ * overlap on one GPU (unordered streams, or several host threads) race on it: order them. */
+#define KVQ_NOALLOC_SCRATCH_BYTES (8u << 20)
+kvq_status kvq_decode_attend_noalloc(kvq_cache* cache, const void* q, void* out, int32_t out_fp32,
+                                     float sm_scale, int32_t n_split, void* stream);
+
 /* Multi-query attend (speculative decoding: several new tokens scored at once). The newest
  * n_query tokens of every sequence (already appended) each attend, causally, over the cache up
  * to and including themselves: query j (0-based) of head h of sequence b sees the first

@@ -11,6 +11,7 @@ from .cache import (  # noqa: F401
     kvq_cache_bytes,
     kvq_decode_attend,
     kvq_decode_attend_multi,
+    kvq_decode_attend_noalloc,
     kvq_encode,
     kvq_encode_block,
     kvq_layout,

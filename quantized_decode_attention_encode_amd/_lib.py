@@ -20,6 +20,7 @@ KVQ_E_WORKSPACE = -4
 KVQ_E_NODEVICE = -5
 KVQ_E_HIP = -6
 KVQ_MAX_BATCH = 256
+KVQ_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class KVQError(RuntimeError):
@@ -72,6 +73,7 @@ def _load():
         "kvq_decode_attend": (I32, [P, P, P, I32, F32, P, SZ, I32, P]),
         "kvq_append_decode_attend": (I32, [P, P, P, P, P, I32, F32, P, SZ, I32, P]),
         "kvq_decode_attend_multi": (I32, [P, P, P, I32, I32, F32, P, SZ, I32, P]),
+        "kvq_decode_attend_noalloc": (I32, [P, P, P, I32, F32, I32, P]),
         "kvq_profile_enable": (I32, [P, I32]),
         "kvq_profile_read": (I32, [P, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
         "kvq_last_error": (ctypes.c_char_p, []),
@@ -87,7 +89,8 @@ def _load():
 lib = _load()
 EXPORTED = ("kvq_probe", "kvq_config_check", "kvq_cache_bytes", "kvq_layout", "kvq_workspace_bytes",
             "kvq_cache_create", "kvq_cache_destroy", "kvq_reset", "kvq_cache_lengths", "kvq_encode", "kvq_encode_block",
-            "kvq_prefill", "kvq_append", "kvq_decode_attend", "kvq_append_decode_attend", "kvq_decode_attend_multi", "kvq_profile_enable", "kvq_profile_read",
+            "kvq_prefill", "kvq_append", "kvq_decode_attend", "kvq_append_decode_attend", "kvq_decode_attend_multi", "kvq_decode_attend_noalloc",
+            "kvq_profile_enable", "kvq_profile_read",
             "kvq_last_error", "kvq_status_string")
 
 

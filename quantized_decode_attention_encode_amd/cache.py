@@ -18,7 +18,7 @@ from ._lib import KVQ_OK, Config, KVQError, LayoutInfo, check, lib
 
 __all__ = ["KVQCache", "KVQError", "make_config", "kvq_probe", "kvq_cache_bytes", "kvq_layout",
            "kvq_workspace_bytes", "kvq_encode", "kvq_prefill", "kvq_append", "kvq_decode_attend",
-           "kvq_decode_attend_multi"]
+           "kvq_decode_attend_multi", "kvq_decode_attend_noalloc"]
 
 
 def make_config(batch, n_kv_heads, n_q_heads, head_dim, key_bits=2, value_bits=2, group=32, residual=32,
@@ -206,6 +206,23 @@ def kvq_decode_attend(cache: KVQCache, q: torch.Tensor, out: torch.Tensor | None
     st = lib.kvq_decode_attend(cache.handle, _dev(q, "q"), _dev(out, "out", odt), 1 if out_fp32 else 0,
                                float(sm_scale), _dev(workspace, "workspace", torch.uint8), workspace.numel(),
                                int(n_split), _stream(stream))
+    if st != KVQ_OK:
+        check(st)
+    return out
+
+
+def kvq_decode_attend_noalloc(cache: KVQCache, q: torch.Tensor, out: torch.Tensor, sm_scale: float = 1.0,
+                              n_split: int = 0, out_fp32: bool = False, stream=None) -> torch.Tensor:
+    """kvq_decode_attend with no workspace: the split partials live in the library's static
+    device scratch. The caller passes q [B, H_q, D] fp16 and a preallocated out of q's shape."""
+    c = cache.cfg
+    if tuple(q.shape) != (c.batch, c.n_q_heads, c.head_dim):
+        raise KVQError(-1, f"q must be [B, H_q, D] = {(c.batch, c.n_q_heads, c.head_dim)}")
+    odt = torch.float32 if out_fp32 else torch.float16
+    if out is None or tuple(out.shape) != tuple(q.shape):
+        raise KVQError(-1, "out must be a preallocated tensor of q's shape")
+    st = lib.kvq_decode_attend_noalloc(cache.handle, _dev(q, "q"), _dev(out, "out", odt), 1 if out_fp32 else 0,
+                                       float(sm_scale), int(n_split), _stream(stream))
     if st != KVQ_OK:
         check(st)
     return out

@@ -15,6 +15,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -211,7 +212,7 @@ namespace {
 // n_query > 1: that many queries per head, the cache's newest tokens (causal among themselves).
 kvq_status decode_enqueue(kvq_cache* c, const void* q, void* out, int32_t out_fp32, float sm_scale,
                           void* workspace, size_t ws_bytes, int32_t n_split, void* stream,
-                          const void* k_tok, const void* v_tok, int32_t n_query = 1) {
+                          const void* k_tok, const void* v_tok, int32_t n_query = 1, bool allow_profile = true) {
   if (!q || !out) return fail(KVQ_E_INVALID, "q or out is NULL");
   if (!workspace) return fail(KVQ_E_WORKSPACE, "workspace is NULL");
   if (n_split < 0) return fail(KVQ_E_INVALID, "n_split must be >= 0");
@@ -269,7 +270,7 @@ kvq_status decode_enqueue(kvq_cache* c, const void* q, void* out, int32_t out_fp
   }
   float* ws = static_cast<float*>(workspace);
   hipError_t e;
-  const bool prof = c->profiling;
+  const bool prof = c->profiling && allow_profile;
   if (prof) {
     if (c->ev_used + 2 > c->ev.size()) {
       if (c->ev.size() >= size_t(2 * kMaxProfilePairs)) return fail(KVQ_E_INVALID, "profile buffer full; call kvq_profile_read");
@@ -293,6 +294,36 @@ kvq_status decode_enqueue(kvq_cache* c, const void* q, void* out, int32_t out_fp
   if (prof) c->ev_used += 2;
   if (add)
     for (int b = 0; b < cfg.batch; ++b) c->nr[b] += 1;
+  return ok();
+}
+
+}  // namespace
+
+// Split partials of kvq_decode_attend_noalloc: a file-scope device array, so that the call needs
+// no caller workspace and allocates nothing. Every GPU the library runs on holds its own copy
+// (KVQ_NOALLOC_SCRATCH_BYTES) until the process ends; in host code `scratch` only names the
+// symbol, and its device address is looked up once per device and kept in g_scratch.
+static __device__ __align__(256) uint8_t scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // device address of `scratch` on each device, once looked up
+
+kvq_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KVQ_E_NODEVICE, "no HIP device: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_E_NODEVICE, "device %d is beyond the %d this library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with device `dev` current
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(KVQ_E_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
   return ok();
 }
 
@@ -655,6 +686,22 @@ kvq_status kvq_decode_attend(kvq_cache* c, const void* q, void* out, int32_t out
                              void* workspace, size_t ws_bytes, int32_t n_split, void* stream) {
   if (!c) return fail(KVQ_E_INVALID, "cache is NULL");
   return decode_enqueue(c, q, out, out_fp32, sm_scale, workspace, ws_bytes, n_split, stream, nullptr, nullptr);
+}
+
+kvq_status kvq_decode_attend_noalloc(kvq_cache* c, const void* q, void* out, int32_t out_fp32, float sm_scale,
+                                     int32_t n_split, void* stream) {
+  if (!c) return fail(KVQ_E_INVALID, "cache is NULL");
+  kvq_status st = check_device();
+  if (st != KVQ_OK) return st;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != KVQ_OK) return st;
+  st = decode_enqueue(c, q, out, out_fp32, sm_scale, ws, KVQ_NOALLOC_SCRATCH_BYTES, n_split, stream, nullptr,
+                      nullptr, 1, false);
+  if (st == KVQ_E_WORKSPACE)
+    return fail(KVQ_E_WORKSPACE, "kvq_decode_attend_noalloc: %s (the static scratch holds %u bytes; pass a smaller "
+                "n_split, or use kvq_decode_attend with a workspace)", kvq_last_error(), unsigned(KVQ_NOALLOC_SCRATCH_BYTES));
+  return st;
 }
 
 kvq_status kvq_decode_attend_multi(kvq_cache* c, const void* q, void* out, int32_t n_query, int32_t out_fp32,
