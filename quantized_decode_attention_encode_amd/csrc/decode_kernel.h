@@ -163,10 +163,21 @@ struct Unpacker {
   }
 };
 
-// Value weights travel as fp16: A_t = fp16(p_t * s_t * 2^(10-o_t) * 2^-6). With p <= 1, an
-// fp16 scale s <= 43669 (2-bit) / 8734 (4-bit) / 514 (8-bit) and a fold factor 2^(10-o) <= 64
-// (2/4-bit) or 256 (8-bit), A never exceeds the fp16 range; accumulators then carry 2^-6 units.
-constexpr float kVScale = 1.0f / 64.0f;
+// Value weights travel as fp16: A_t = fp16(p_t * s_t * 2^(10-o_t) * kVScale), with p <= 1 the
+// softmax weight relative to the running max, s the token's value-group scale and 2^(10-o) <= F
+// the fold factor (F = 64 at 2/4 bits, 256 at 8 bits). kVScale = 2^6 keeps the weights of a long
+// context normal fp16 (relative rounding <= 2^-11) down to p ~ 2^-23 at unit-sized scales; it is
+// safe while s * F * 2^6 <= 65504, i.e. every value scale of the record is at most kBigScale<B>.
+// A record holding a larger scale (a wave vote decides) forms its weights at 2^-6 instead (safe
+// for every fp16 scale: s <= 43669 at 2 bits), sums them on their own and adds that sum times
+// 2^12, so the accumulators always carry kVScale units.
+constexpr float kVScale = 64.0f;
+constexpr float kVScaleBig = 1.0f / 64.0f;
+constexpr float kVBigRatio = kVScale / kVScaleBig;  // 2^12
+// fp16 bit pattern of the largest value scale a record may hold for the kVScale weights: 15.5
+// (15.5 * 64 * 64 < 65504) at 2/4 bits, 3.875 (3.875 * 256 * 64 < 65504) at 8 bits
+template <int BV>
+__device__ __forceinline__ constexpr uint32_t big_scale_bits() { return BV == 8 ? 0x43C0u : 0x4BC0u; }
 
 template <int D, int G>
 struct WaveLds {
@@ -280,6 +291,18 @@ __device__ __forceinline__ void process_record(const RecordRegs<D, BK, BV>& cur,
     }
   }
 
+  // value scales beyond big_scale_bits (the sign bit is the sink marker, not the scale's):
+  // this record's weights are formed at kVScaleBig (wave-uniform)
+  bool bigv;
+  {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) mx = max(mx, cur.vp[e] & 0x7FFFu);
+    bigv = __any(mx > big_scale_bits<BV>());
+  }
+  const float vw0 = bigv ? vf0 * (1.0f / kVBigRatio) : vf0, vw1 = bigv ? vf1 * (1.0f / kVBigRatio) : vf1;
+  const float amul = bigv ? kVBigRatio : 1.0f;
+
   // ---- producer: folded scaled query and quarter offsets (per-token key groups: set once
   // per launch, nothing to do per record)
 #pragma unroll
@@ -379,76 +402,93 @@ __device__ __forceinline__ void process_record(const RecordRegs<D, BK, BV>& cur,
     s1 += dpp<kQuadXor2>(s1);
     float p0, p1;
     softmax_step<D, G, SK>(st, i, s0, s1, p0, p1, keep0, keep1);
-    // ---- producer: fp16 folded value weights and the zero-term bias (in kVScale units)
+    // ---- producer: fp16 folded value weights and the zero-term bias (in kVScale units), the
+    // record's part summed on its own first
+    float br = 0.0f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       // entry e of this lane: token t, value group k (the value-param dword lane*E + e)
       const int idx = lane * E + e;
       const int tp = idx & 1, k = (idx >> 1) % NKG, t = 2 * P + tp;
       const float p = tp ? p1 : p0;
-      const float vfold = (tp ? vf1 : vf0);  // 2^(10-o_t) * kVScale
+      const float vfold = (tp ? vw1 : vw0);  // 2^(10-o_t) * kVScale, or * kVScaleBig
       const __half a16 = __float2half_rn((p * vfold) * lo_f(cur.vp[e]));
-      st.bias[i] += (p * kVScale) * hi_f(cur.vp[e]) - __half2float(a16);
+      br = __builtin_fmaf(-__half2float(a16), amul, __builtin_fmaf(p * kVScale, hi_f(cur.vp[e]), br));
       const int dw = (t / MV::NC) * MV::NH + (t % MV::NC) % MV::NH, hf = (t % MV::NC) / MV::NH;
       reinterpret_cast<__half*>(&W.A[i][k][dw])[hf] = a16;
     }
+    st.bias[i] += br;
   }
   wave_sync();
 
   // ---- values: v_dot2_f32_f16 of (weight pair) x (code pair); a word = NC tokens of a channel
+  // (x: the chains' accumulators, st.acc itself, or zeros for a record with kVScaleBig weights)
   using h2 = _Float16 __attribute__((ext_vector_type(2)));
-  if constexpr (G == 1) {
+  auto values = [&](float (&x)[G][E]) {
+    if constexpr (G == 1) {
 #pragma unroll
-    for (int w = 0; w < BV; ++w) {
-      uint32_t vr[E][MV::NH];
+      for (int w = 0; w < BV; ++w) {
+        uint32_t vr[E][MV::NH];
 #pragma unroll
-      for (int e = 0; e < E; ++e) upv.run(cur.vc[e * BV + w], vr[e]);
-      uint32_t av[MV::NH];
+        for (int e = 0; e < E; ++e) upv.run(cur.vc[e * BV + w], vr[e]);
+        uint32_t av[MV::NH];
 #pragma unroll
-      for (int j = 0; j < MV::NH; j += (MV::NH >= 4 ? 4 : 2)) {
-        if constexpr (MV::NH >= 4) {
-          const uint4 t4 = *reinterpret_cast<const uint4*>(&W.A[0][kcons][w * MV::NH + j]);
-          av[j] = t4.x; av[j + 1] = t4.y; av[j + 2] = t4.z; av[j + 3] = t4.w;
-        } else {
-          const uint2 t2 = *reinterpret_cast<const uint2*>(&W.A[0][kcons][w * MV::NH + j]);
-          av[j] = t2.x; av[j + 1] = t2.y;
+        for (int j = 0; j < MV::NH; j += (MV::NH >= 4 ? 4 : 2)) {
+          if constexpr (MV::NH >= 4) {
+            const uint4 t4 = *reinterpret_cast<const uint4*>(&W.A[0][kcons][w * MV::NH + j]);
+            av[j] = t4.x; av[j + 1] = t4.y; av[j + 2] = t4.z; av[j + 3] = t4.w;
+          } else {
+            const uint2 t2 = *reinterpret_cast<const uint2*>(&W.A[0][kcons][w * MV::NH + j]);
+            av[j] = t2.x; av[j + 1] = t2.y;
+          }
         }
-      }
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        float x = st.acc[0][e];
-#pragma unroll
-        for (int j = 0; j < MV::NH; ++j)
-          x = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, av[j]), __builtin_bit_cast(h2, vr[e][j]), x, false);
-        st.acc[0][e] = x;
-      }
-    }
-  } else {
-    uint32_t vr[E][BV][MV::NH];
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-#pragma unroll
-      for (int w = 0; w < BV; ++w) upv.run(cur.vc[e * BV + w], vr[e][w]);
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-      uint32_t av[16];
-#pragma unroll
-      for (int j = 0; j < 16; j += 4) {
-        const uint4 t4 = *reinterpret_cast<const uint4*>(&W.A[i][kcons][j]);
-        av[j] = t4.x; av[j + 1] = t4.y; av[j + 2] = t4.z; av[j + 3] = t4.w;
-      }
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        float x = st.acc[i][e];
-#pragma unroll
-        for (int w = 0; w < BV; ++w)
+        for (int e = 0; e < E; ++e)
 #pragma unroll
           for (int j = 0; j < MV::NH; ++j)
-            x = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, av[w * MV::NH + j]), __builtin_bit_cast(h2, vr[e][w][j]),
-                                       x, false);
-        st.acc[i][e] = x;
+            x[0][e] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, av[j]), __builtin_bit_cast(h2, vr[e][j]), x[0][e],
+                                             false);
+      }
+    } else {
+      uint32_t vr[E][BV][MV::NH];
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+#pragma unroll
+        for (int w = 0; w < BV; ++w) upv.run(cur.vc[e * BV + w], vr[e][w]);
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        uint32_t av[16];
+#pragma unroll
+        for (int j = 0; j < 16; j += 4) {
+          const uint4 t4 = *reinterpret_cast<const uint4*>(&W.A[i][kcons][j]);
+          av[j] = t4.x; av[j + 1] = t4.y; av[j + 2] = t4.z; av[j + 3] = t4.w;
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+#pragma unroll
+          for (int w = 0; w < BV; ++w)
+#pragma unroll
+            for (int j = 0; j < MV::NH; ++j)
+              x[i][e] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, av[w * MV::NH + j]),
+                                               __builtin_bit_cast(h2, vr[e][w][j]), x[i][e], false);
       }
     }
+  };
+  // Each record is summed from zero and joins the running sums once: the converted codes carry
+  // their constant 1 (up to 64 times the code's own part, removed only at the end through the
+  // bias), so a running sum is much larger than the value it stands for, and adding every code
+  // pair to it directly would round away the low bits of small weights.
+  {
+    float x[G][E];
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[i][e] = 0.0f;
+    values(x);
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+#pragma unroll
+      for (int e = 0; e < E; ++e) st.acc[i][e] = __builtin_fmaf(x[i][e], amul, st.acc[i][e]);
   }
   wave_sync();
 }

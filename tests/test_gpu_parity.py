@@ -369,3 +369,81 @@ def test_fused_append_decode_equals_append_then_decode(start, n_split, residual)
     ref = oracle_attend(draw.q.astype(np.float64), seqs, wl)
     o = kvq_decode_attend(caches[1], q, out_fp32=True, n_split=n_split)
     assert_close(o.cpu().numpy(), ref, f"{start} fused end state")
+
+
+def test_tiny_softmax_weights_keep_their_precision():
+    # One planted key dominates; the other ~24K tokens' weights sit near 2^-22.5 of the maximum
+    # (nearly all within [2^-24, 2^-14]) and together carry ~0.4% of the softmax mass, with value
+    # rows centred at +2 against the top token's -2. Value weights formed at a fixed 2^-6 scale
+    # would round a quarter of those weights (the fold-4 code positions) to zero in fp16: a numpy
+    # model of that rounding puts the output 1.8e-3 off. At the 2^6 scale they stay normal fp16
+    # (model: 4e-8; the kernel's own fp32 floor is a few 1e-5). Bound: 2e-4 of the fp64 oracle.
+    rng = np.random.default_rng(77)
+    B, H, D, S = 1, 2, 128, 24576
+    K = rng.standard_normal((B, H, S, D), np.float32)
+    V = rng.standard_normal((B, H, S, D), np.float32) + 2.0
+    u = rng.standard_normal((B, H, D)).astype(np.float32)
+    u /= np.linalg.norm(u, axis=-1, keepdims=True)
+    alpha = 0.35  # typical scores ~ N(0, 0.35^2); the planted one 15.6 (22.5 in log2 units) above
+    K[:, :, 1000] = (15.6 / alpha) * u
+    V[:, :, 1000] -= 4.0
+    K, V = K.astype(np.float16), V.astype(np.float16)
+    q = (alpha * u).astype(np.float16)
+    cfg = make_config(B, H, H, D, 2, 2, 32, 32, S)
+    c = KVQCache(cfg, device=DEV)
+    kvq_prefill(c, torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV), [S])
+    seqs = {}
+    for h in range(H):
+        s = kivi.KiviSequence(D, 2, 2, 32, 32)
+        s.prefill(K[0, h], V[0, h])
+        seqs[(0, h)] = s
+        sc = (s.keys_hat() @ q[0, h].astype(np.float64)) * np.log2(np.e)
+        x = sc.max() - sc  # log2 of max weight / weight
+        frac = np.mean((x >= 14) & (x <= 24))
+        mass = np.sum(np.exp2(-x)) - 1.0  # every token but the top one, relative to it
+        say(f"head {h}: {frac:.3f} of the weights in [2^-24, 2^-14] of the max; their mass {mass:.3e}")
+        assert frac > 0.9 and mass > 2e-3
+    ref = np.stack([kivi.attend(q[0, h], seqs[(0, h)].keys_hat(), seqs[(0, h)].values_hat()) for h in range(H)])[None]
+    qt = torch.from_numpy(q).to(DEV)
+    for n_split in (0, 1, 9):
+        out = kvq_decode_attend(c, qt, out_fp32=True, n_split=n_split).cpu().numpy()
+        err = np.abs(out - ref).max()
+        say(f"  n_split={n_split}: max abs err {err:.2e}")
+        assert err <= 2e-4, f"n_split={n_split}: {err:.3e}"
+
+
+@pytest.mark.parametrize("D,bv,G,boost", [(128, 2, 1, 12.0), (64, 2, 4, 12.0), (128, 8, 1, 300.0), (128, 4, 2, 80.0)])
+def test_records_with_large_value_scales(D, bv, G, boost):
+    # Value rows of a few tokens scaled up so that their groups' scales exceed what the 2^6 weight
+    # scale can hold (15.5 at 2/4 bits, 3.875 at 8 bits): those records form their weights at
+    # 2^-6 and fold them back, next to ordinary records in the same splits. Each weight is then
+    # a normal fp16 (relative rounding <= 2^-11), so the output is within 2^-11 max|v_hat|.
+    rng = np.random.default_rng(78 + D + bv + G)
+    B, Hkv, S = 2, 2, 700
+    Hq = Hkv * G
+    K = rng.standard_normal((B, Hkv, S, D), np.float32).astype(np.float16)
+    V = rng.standard_normal((B, Hkv, S, D), np.float32)
+    big = rng.choice(S, S // 20, replace=False)
+    V[:, :, big] *= boost
+    V = V.astype(np.float16)
+    q = (rng.standard_normal((B, Hq, D), np.float32) / np.sqrt(D)).astype(np.float16)
+    cfg = make_config(B, Hkv, Hq, D, 2, bv, 32, 32, 1024)
+    c = KVQCache(cfg, device=DEV)
+    kvq_prefill(c, torch.from_numpy(K).to(DEV), torch.from_numpy(V).to(DEV), [S, S - 77])
+    seqs = {}
+    for b, n in ((0, S), (1, S - 77)):
+        for h in range(Hkv):
+            s = kivi.KiviSequence(D, 2, bv, 32, 32)
+            s.prefill(K[b, h, :n], V[b, h, :n])
+            seqs[(b, h)] = s
+    vmax = max(np.abs(s.values_hat()).max() for s in seqs.values())
+    thr = 3.875 if bv == 8 else 15.5
+    assert max(s.vs.astype(np.float32).max() for s in seqs.values()) > thr  # some records take the 2^-6 path
+    wl = workloads.custom(name="bigv", batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=D, key_bits=2, value_bits=bv)
+    ref = oracle_attend(q.astype(np.float64), seqs, wl)
+    for n_split in (0, 1, 4):
+        out = kvq_decode_attend(c, torch.from_numpy(q).to(DEV), out_fp32=True, n_split=n_split).cpu().numpy()
+        err = np.abs(out - ref).max()
+        rel = (np.linalg.norm(out - ref, axis=-1) / np.linalg.norm(ref, axis=-1)).max()
+        say(f"D={D} bv={bv} G={G} n_split={n_split}: max abs {err:.3e} (vmax {vmax:.1f}), row rel {rel:.2e}")
+        assert err <= 2.0 ** -11 * vmax + 2e-5 and rel <= 1e-2
