@@ -49,6 +49,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+PEAK_FP16_MFMA_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak (no sparsity)
 
 # HBM bytes per decode launch on the long workload (no sinks) from two rocprofv3 --pmc runs
 # (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, factors from a 1 GiB device copy; see
@@ -73,6 +74,17 @@ def algorithmic_decode_bytes(wl, n_q, n_r, n_sink=0, kitty_n_hi=None):
     kv = sum((nq // 32) * rec + (nr + (n_sink if nq else 0)) * D * 2 * 2
              for nq, nr in zip(n_q, n_r)) * wl.n_kv_heads
     return kv + 2 * wl.batch * wl.n_q_heads * D * 2
+
+
+def attend_flops(wl, n_q, n_r, n_query):
+    """Useful flops of one causal multi-query attend: per query head and query j, a dot product
+    and a weighted sum over its visible tokens (S - (n_query - 1 - j)), 2 flops per element each."""
+    total = 0
+    for b in range(wl.batch):
+        S = n_q[b] + n_r[b]
+        visible = sum(S - (n_query - 1 - j) for j in range(n_query))
+        total += 4 * wl.head_dim * wl.n_q_heads * visible
+    return total
 
 
 def algorithmic_encode_bytes(wl, n_q_tokens, n_sink=0, kitty_n_hi=None):
@@ -320,7 +332,7 @@ def main():
     for i in range(first, last):
         step(i)
     torch.cuda.synchronize()
-    bytes_per_launch = []
+    bytes_per_launch, flops_per_launch = [], []
     for i in range(n_steps_total):
         for r in visits(i):
             nq, nr = lens_now[r]
@@ -333,6 +345,7 @@ def main():
             if first <= i < last:  # (the extra queries add their q and out rows)
                 bytes_per_launch.append(algorithmic_decode_bytes(wl, nq, nr, args.n_sink, kitty_n_hi)
                                         + (NQ - 1) * 2 * wl.batch * wl.n_q_heads * wl.head_dim * 2)
+                flops_per_launch.append(attend_flops(wl, nq, nr, NQ))
     for r, c in enumerate(caches):
         assert tuple(map(list, lens_now[r])) == tuple(map(list, c.lengths())), "length replay disagrees"
     step_ms = t_ev0.elapsed_time(t_ev1) / args.steps
@@ -345,6 +358,12 @@ def main():
     split_avg_ms = split_ms / split_n
     alg_bytes = statistics.mean(bytes_per_launch)
     achieved = alg_bytes / (split_avg_ms / 1e3) / 1e9
+    # more query rows per KV head than the decode kernel holds: the matrix-core kernel, whose
+    # bound is its fp16 MFMA rate (useful flops; the fp16 high + low operands cost 2.5x that)
+    G_rows = (wl.n_q_heads // wl.n_kv_heads) * NQ
+    tiles = NQ > 1 and (G_rows > 8 or (NQ & (NQ - 1)))
+    alg_flops = statistics.mean(flops_per_launch)
+    tflops = alg_flops / (split_avg_ms / 1e3) / 1e12
 
     # ---- achievable HBM bandwidth for context: a plain device copy, 1 GiB each way
     a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -415,6 +434,18 @@ def main():
             "kernel": "decode_split_kernel" if kitty_n_hi is None else "kitty_decode_kernel",
             "kernel_avg_us": round(split_avg_ms * 1e3, 3),
             "algorithmic_bytes_per_launch": int(alg_bytes),
+        } if not tiles else {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_FP16_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_FP16_MFMA_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "attend_tiles_kernel (+ tiles_merge_kernel when split)",
+            "kernel_avg_us": round(split_avg_ms * 1e3, 3),
+            "algorithmic_flops_per_launch": int(alg_flops),
+            "hbm": {"achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_HBM_GBS, 4), "algorithmic_bytes_per_launch": int(alg_bytes)},
         },
         "decode_split_us": round(split_avg_ms * 1e3, 3),
         "decode_gbps": round(achieved, 1),

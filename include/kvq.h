@@ -153,7 +153,10 @@ kvq_status kvq_probe(int32_t* has_gfx950);
 /* Validate a configuration (the pages' QuantizerConfigError checks). */
 kvq_status kvq_config_check(const kvq_config* cfg);
 
-/* Device bytes the caller allocates for one cache (0 if cfg is invalid). */
+/* Device bytes the caller allocates for one cache (0 if cfg is invalid). The counterpart of the
+ * standalone caches' memory_bytes() ("veloxquant_mlx.cache package", e.g.
+ * PolarQuantKVCache.memory_bytes: bytes held for the cached tokens), taken here at full
+ * capacity (max_tokens per sequence) plus the lengths, window and sink regions. */
 size_t kvq_cache_bytes(const kvq_config* cfg);
 
 /* Region offsets of the cache buffer. */
@@ -262,23 +265,32 @@ kvq_status kvq_decode_attend(kvq_cache* cache, const void* q, void* out, int32_t
 kvq_status kvq_decode_attend_noalloc(kvq_cache* cache, const void* q, void* out, int32_t out_fp32,
                                      float sm_scale, int32_t n_split, void* stream);
 
-/* Multi-query attend (speculative decoding: several new tokens scored at once). The newest
- * n_query tokens of every sequence (already appended) each attend, causally, over the cache up
- * to and including themselves: query j (0-based) of head h of sequence b sees the first
- * S_b - (n_query - 1 - j) tokens, S_b being all the tokens the sequence holds (sinks, quantized
- * and window, in token order). n_query = 1 is kvq_decode_attend.
+/* Multi-query attend: speculative decoding (a few new tokens scored at once) and chunked prefill
+ * (hundreds), the multi-token work the pages pair with their fused decode ("Changelog" v0.40.0
+ * "Added": a matrix-tiled prefill / cross-attention companion for large S_q; v0.42.0 "Added" for
+ * the decode attention itself). The newest n_query tokens of every sequence (already appended)
+ * each attend, causally, over the cache up to and including themselves: query j (0-based) of
+ * head h of sequence b sees the first S_b - (n_query - 1 - j) tokens, S_b being all the tokens
+ * the sequence holds (sinks, quantized and window, in token order). n_query = 1 is
+ * kvq_decode_attend.
  *   q:   fp16 [B][H_q][n_query][D];  out: fp16 (or fp32) [B][H_q][n_query][D].
- *   n_query: a power of two with n_query x (H_q / H_kv) <= 8 (KVQ_E_UNSUPPORTED otherwise);
- *   every sequence holds at least n_query tokens (KVQ_E_INVALID otherwise).
+ *   n_query: 1 .. max_tokens; every sequence holds at least n_query tokens (KVQ_E_INVALID).
  *   workspace: at least n_query x kvq_workspace_bytes(cfg, n_split) bytes.
- * The same kernel as kvq_decode_attend, with the query rows of each KV head (heads x queries)
- * sharing every code it unpacks; masked scores take a large negative finite value, so a split
- * that sees only a query's future contributes nothing to it. */
+ * Two kernels serve it, by the query rows per KV head (G x n_query, G = H_q / H_kv):
+ *  - at most 8 rows and n_query a power of two: the decode kernel of kvq_decode_attend, the rows
+ *    sharing every code it unpacks; every method and sink setting;
+ *  - otherwise the matrix-core kernel (KIVI caches without sinks; KVQ_E_UNSUPPORTED for others):
+ *    64 rows per workgroup, k_hat / v_hat rebuilt once per 32 tokens as fp16 high + low pairs
+ *    (22 significant bits) and multiplied on v_mfma_f32_16x16x32_f16 tiles with fp32
+ *    accumulation; splits along the tokens are merged by a second kernel.
+ * Masked scores take a large negative finite value, so a split that sees only a query's future
+ * contributes nothing to it. */
 kvq_status kvq_decode_attend_multi(kvq_cache* cache, const void* q, void* out, int32_t n_query, int32_t out_fp32,
                                    float sm_scale, void* workspace, size_t ws_bytes, int32_t n_split,
                                    void* stream);
 
-/* North-star calls 2 and 3 in one: exactly kvq_append(cache, k_tok, v_tok) followed by
+/* North-star calls 2 and 3 in one ("Changelog" v0.8.0 / v0.28.0 window and chunk flush, v0.42.0
+ * fused decode): exactly kvq_append(cache, k_tok, v_tok) followed by
  * kvq_decode_attend(cache, q, ...) on the same stream, same arguments and errors, same cache
  * state and output. When no window is full (31 appends in 32 at R = 32) it is one kernel
  * launch: the decode reads each new token from k_tok / v_tok, stores it in its window slot and

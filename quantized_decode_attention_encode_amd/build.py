@@ -29,6 +29,8 @@ PER_FILE = {
     "decode.hip": [],
     "decode_sink.hip": [],
     "decode_skvq.hip": [],
+    # multi-query attend on the matrix cores
+    "attend_tiles.hip": [],
     # Kitty encode (bit-exact quantizer) and decode
     "kitty.hip": ["-ffp-contract=off"],
     "kvq.cpp": ["-x", "hip"],

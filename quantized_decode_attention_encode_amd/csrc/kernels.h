@@ -28,6 +28,19 @@ struct DecodeShape {
                     // and n_q_heads count query rows: heads x nqry)
 };
 
+// Multi-query attend on the matrix cores (attend_tiles.hip): grid (n_split, row_blocks, B * H_kv),
+// 64 query rows (query heads x queries of one KV head) per workgroup, `chunk` units per split.
+struct TileShape {
+  int n_split;
+  int chunk;
+  int G;           // query heads per KV head
+  int n_q_heads;   // H_q
+  int nqry;        // queries per head (the newest nqry tokens of each sequence)
+  int row_blocks;  // 64-row blocks per KV head
+  float qscale;    // sm_scale * log2(e)
+  int out_fp32;
+};
+
 hipError_t launch_encode(uint8_t* buf, const Layout& L, const void* K, const void* V, int64_t ld_tok,
                          const PerSeq& seq, int max_records, hipStream_t s);
 // seq: every sequence's lengths before the append (a = quantized, b = window tokens).
@@ -72,6 +85,12 @@ hipError_t launch_decode_skvq(uint8_t* buf, const Layout& L, const DecodeShape& 
 hipError_t launch_decode_sink(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq, const void* q, float* ws,
                               void* out, const void* k_tok, const void* v_tok, hipStream_t s, hipEvent_t start,
                               hipEvent_t stop);
+
+// Multi-query attend over a KIVI cache without sinks: split kernel, then (n_split > 1) a merge
+// kernel; seq: the host's lengths (a = quantized tokens, b = window tokens). start/stop bracket
+// both launches.
+hipError_t launch_attend_tiles(const uint8_t* buf, const Layout& L, const TileShape& ts, const PerSeq& seq,
+                               const void* q, float* ws, void* out, hipStream_t s, hipEvent_t start, hipEvent_t stop);
 
 // Kitty records seq.a[b] + x (x < seq.b[b]) of every (b, h) from tokens seq.c[b] + 32 x on of
 // K[b][h], V[b][h] (row stride D, ld_tok rows per (b, h)): group sums, running sums (those of

@@ -206,6 +206,71 @@ kvq_status ensure_ready(kvq_cache* c, hipStream_t s) {
 
 namespace {
 
+// Multi-query attend on the matrix cores: 64-row blocks of each KV head's query rows, splits along
+// the units so that the grid holds about two workgroups per CU (or n_split when given).
+kvq_status tiles_enqueue(kvq_cache* c, const void* q, void* out, int32_t out_fp32, float sm_scale, void* workspace,
+                         size_t ws_bytes, int32_t n_split, void* stream, int32_t n_query, bool allow_profile) {
+  const kvq_config& cfg = c->cfg;
+  const int G = cfg.n_q_heads / cfg.n_kv_heads;
+  int max_units = 0;
+  for (int b = 0; b < cfg.batch; ++b) {
+    const int held = c->nq[b] + c->nr[b];
+    if (held < n_query)
+      return fail(KVQ_E_INVALID, "sequence %d holds %d tokens, fewer than the %d queries", b, held, n_query);
+    max_units = std::max(max_units, units_of(c->nq[b], c->nr[b], false));
+  }
+  kvq::TileShape ts;
+  ts.G = G;
+  ts.n_q_heads = cfg.n_q_heads;
+  ts.nqry = n_query;
+  ts.row_blocks = (G * n_query + 63) / 64;
+  ts.qscale = sm_scale * 1.4426950408889634f;
+  ts.out_fp32 = out_fp32 ? 1 : 0;
+  int chunk;
+  if (n_split > 0) {
+    chunk = (max_units + n_split - 1) / n_split;
+  } else {
+    int cus = 0;
+    kvq_status dst = check_device(&cus);
+    if (dst != KVQ_OK) return dst;
+    const int64_t blocks = int64_t(cfg.batch) * cfg.n_kv_heads * ts.row_blocks;
+    // splits per sequence, within what kvq_workspace_bytes(cfg, 0) provides for
+    const int64_t want = std::min<int64_t>((2 * int64_t(std::max(1, cus)) + blocks - 1) / blocks, max_auto_splits(&cfg));
+    chunk = int((max_units + want - 1) / want);
+  }
+  chunk = std::max(1, chunk);
+  ts.chunk = chunk;
+  ts.n_split = (max_units + chunk - 1) / chunk;
+  const size_t need = ts.n_split > 1
+      ? size_t(cfg.batch) * cfg.n_q_heads * n_query * ts.n_split * (cfg.head_dim + 4) * sizeof(float) : 0;
+  if (ws_bytes < need) return fail(KVQ_E_WORKSPACE, "workspace holds %zu bytes, this call needs %zu", ws_bytes, need);
+  if (need && !workspace) return fail(KVQ_E_WORKSPACE, "workspace is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  kvq_status st = ensure_ready(c, s);
+  if (st != KVQ_OK) return st;
+  PerSeq seq;
+  memset(&seq, 0, sizeof seq);
+  for (int b = 0; b < cfg.batch; ++b) {
+    seq.a[b] = c->nq[b];
+    seq.b[b] = c->nr[b];
+  }
+  const bool prof = c->profiling && allow_profile;
+  if (prof && c->ev_used + 2 > c->ev.size()) {
+    if (c->ev.size() >= size_t(2 * kMaxProfilePairs)) return fail(KVQ_E_INVALID, "profile buffer full; call kvq_profile_read");
+    for (int i = 0; i < 2; ++i) {
+      hipEvent_t ev;
+      hipError_t e = hipEventCreate(&ev);
+      if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+      c->ev.push_back(ev);
+    }
+  }
+  hipError_t e = kvq::launch_attend_tiles(c->buf, c->L, ts, seq, q, static_cast<float*>(workspace), out, s,
+                                          prof ? c->ev[c->ev_used] : nullptr, prof ? c->ev[c->ev_used + 1] : nullptr);
+  if (e != hipSuccess) return hip_fail(e, "multi-query attend launch");
+  if (prof) c->ev_used += 2;
+  return ok();
+}
+
 // Plan and enqueue one decode launch. With k_tok / v_tok set, the launch also appends one token
 // per sequence (the caller has checked that no window is full): it attends over the window
 // plus that token, stores the token in its slot and advances the device lengths.
@@ -221,9 +286,16 @@ kvq_status decode_enqueue(kvq_cache* c, const void* q, void* out, int32_t out_fp
   const int add = k_tok ? 1 : 0;  // window tokens the launch appends
   const int G = cfg.n_q_heads / cfg.n_kv_heads;
   if (is_kitty(cfg) && k_tok) return fail(KVQ_E_UNSUPPORTED, "Kitty caches append before the decode launch");
-  if (n_query < 1 || (n_query & (n_query - 1)) || G * n_query > 8)
-    return fail(KVQ_E_UNSUPPORTED, "n_query = %d: it must be a power of two with n_query x (query heads per KV head = %d) <= 8",
-                n_query, G);
+  if (n_query < 1) return fail(KVQ_E_INVALID, "n_query = %d must be >= 1", n_query);
+  if (n_query > cfg.max_tokens) return fail(KVQ_E_INVALID, "n_query = %d exceeds max_tokens %d", n_query, cfg.max_tokens);
+  // More query rows per KV head than the decode kernel holds (8), or a count that is not a power
+  // of two: the matrix-core kernel, for KIVI caches without sinks.
+  if (G * n_query > 8 || (n_query & (n_query - 1))) {
+    if (cfg.method != KVQ_METHOD_KIVI || cfg.n_sink != 0)
+      return fail(KVQ_E_UNSUPPORTED, "n_query = %d with %d query heads per KV head (more than 8 rows, or not a power of "
+                  "two) is built for KIVI caches without sinks", n_query, G);
+    return tiles_enqueue(c, q, out, out_fp32, sm_scale, workspace, ws_bytes, n_split, stream, n_query, allow_profile);
+  }
   int max_units = 0;
   int64_t total_units = 0;
   for (int b = 0; b < cfg.batch; ++b) {

@@ -225,10 +225,11 @@ def test_host_side_errors_before_any_launch():
         ws = ctypes.c_void_p(FAKE)
         assert lib.kvq_decode_attend(h, P, P, 0, 1.0, ws, 1 << 30, 0, None) == KVQ_E_INVALID
         assert b"empty" in lib.kvq_last_error()
-        # multi-query: n_query a power of two with G * n_query <= 8 (G = 2 here)
-        for nq_bad in (3, 8, 0):
-            assert lib.kvq_decode_attend_multi(h, P, P, nq_bad, 0, 1.0, ws, 1 << 30, 0, None) == KVQ_E_UNSUPPORTED
-        assert lib.kvq_decode_attend_multi(h, P, P, 4, 0, 1.0, ws, 1 << 30, 0, None) == KVQ_E_INVALID
+        # multi-query: n_query >= 1 and at most max_tokens; here every sequence is empty, so both
+        # the decode-kernel path (G * n_query <= 8, a power of two; G = 2) and the matrix-core
+        # path (3, 8) reject it before any launch
+        for nq_bad in (0, 257, 3, 8, 4):
+            assert lib.kvq_decode_attend_multi(h, P, P, nq_bad, 0, 1.0, ws, 1 << 30, 0, None) == KVQ_E_INVALID
         assert lib.kvq_decode_attend(h, P, P, 0, 1.0, None, 1 << 30, 0, None) == KVQ_E_WORKSPACE
         assert lib.kvq_decode_attend(h, P, P, 0, float("nan"), ws, 1 << 30, 0, None) == KVQ_E_INVALID
         assert lib.kvq_decode_attend(h, P, P, 0, 1.0, ws, 1 << 30, -2, None) == KVQ_E_INVALID
@@ -244,6 +245,14 @@ def test_host_side_errors_before_any_launch():
         assert lib.kvq_cache_lengths(h, nq, nr) == KVQ_OK and list(nq) == [0, 0] and list(nr) == [0, 0]
     finally:
         lib.kvq_cache_destroy(h)
+    # the matrix-core multi-query kernel is built for KIVI caches without sinks
+    for kw in (dict(n_sink=2), dict(method=1), dict(method=2, value_bits=16, kitty_n_hi=32)):
+        h = make_handle(cfg(batch=2, max_tokens=256, **kw))
+        try:
+            assert lib.kvq_decode_attend_multi(h, P, P, 8, 0, 1.0, ctypes.c_void_p(FAKE), 1 << 30, 0, None) == \
+                KVQ_E_UNSUPPORTED, kw
+        finally:
+            lib.kvq_cache_destroy(h)
 
 
 def test_encode_block_validates_on_the_host():
