@@ -280,8 +280,8 @@ kvq_status kvq_decode_attend_noalloc(kvq_cache* cache, const void* q, void* out,
  *  - at most 8 rows and n_query a power of two: the decode kernel of kvq_decode_attend, the rows
  *    sharing every code it unpacks; every method and sink setting;
  *  - otherwise the matrix-core kernel (KIVI caches without sinks; KVQ_E_UNSUPPORTED for others):
- *    64 rows per workgroup, k_hat / v_hat rebuilt once per 32 tokens as fp16 high + low pairs
- *    (22 significant bits) and multiplied on v_mfma_f32_16x16x32_f16 tiles with fp32
+ *    256 rows per workgroup, k_hat / v_hat rebuilt once per 32 tokens as fp16 high + low pairs
+ *    (within 2^-20 relative) and multiplied on v_mfma_f32_16x16x32_f16 tiles with fp32
  *    accumulation; splits along the tokens are merged by a second kernel.
  * Masked scores take a large negative finite value, so a split that sees only a query's future
  * contributes nothing to it. */

@@ -29,14 +29,14 @@ struct DecodeShape {
 };
 
 // Multi-query attend on the matrix cores (attend_tiles.hip): grid (n_split, row_blocks, B * H_kv),
-// 64 query rows (query heads x queries of one KV head) per workgroup, `chunk` units per split.
+// 256 query rows (query heads x queries of one KV head) per workgroup, `chunk` units per split.
 struct TileShape {
   int n_split;
   int chunk;
   int G;           // query heads per KV head
   int n_q_heads;   // H_q
   int nqry;        // queries per head (the newest nqry tokens of each sequence)
-  int row_blocks;  // 64-row blocks per KV head
+  int row_blocks;  // 256-row blocks per KV head
   float qscale;    // sm_scale * log2(e)
   int out_fp32;
 };

@@ -206,8 +206,8 @@ kvq_status ensure_ready(kvq_cache* c, hipStream_t s) {
 
 namespace {
 
-// Multi-query attend on the matrix cores: 64-row blocks of each KV head's query rows, splits along
-// the units so that the grid holds about two workgroups per CU (or n_split when given).
+// Multi-query attend on the matrix cores: 256-row blocks of each KV head's query rows, splits along
+// the units so that the grid holds about one workgroup per CU (or n_split when given).
 kvq_status tiles_enqueue(kvq_cache* c, const void* q, void* out, int32_t out_fp32, float sm_scale, void* workspace,
                          size_t ws_bytes, int32_t n_split, void* stream, int32_t n_query, bool allow_profile) {
   const kvq_config& cfg = c->cfg;
@@ -223,7 +223,7 @@ kvq_status tiles_enqueue(kvq_cache* c, const void* q, void* out, int32_t out_fp3
   ts.G = G;
   ts.n_q_heads = cfg.n_q_heads;
   ts.nqry = n_query;
-  ts.row_blocks = (G * n_query + 63) / 64;
+  ts.row_blocks = (G * n_query + 255) / 256;
   ts.qscale = sm_scale * 1.4426950408889634f;
   ts.out_fp32 = out_fp32 ? 1 : 0;
   int chunk;
@@ -234,8 +234,9 @@ kvq_status tiles_enqueue(kvq_cache* c, const void* q, void* out, int32_t out_fp3
     kvq_status dst = check_device(&cus);
     if (dst != KVQ_OK) return dst;
     const int64_t blocks = int64_t(cfg.batch) * cfg.n_kv_heads * ts.row_blocks;
-    // splits per sequence, within what kvq_workspace_bytes(cfg, 0) provides for
-    const int64_t want = std::min<int64_t>((2 * int64_t(std::max(1, cus)) + blocks - 1) / blocks, max_auto_splits(&cfg));
+    // splits per sequence (one 8-wave workgroup per CU), within what kvq_workspace_bytes(cfg, 0)
+    // provides for
+    const int64_t want = std::min<int64_t>((int64_t(std::max(1, cus)) + blocks - 1) / blocks, max_auto_splits(&cfg));
     chunk = int((max_units + want - 1) / want);
   }
   chunk = std::max(1, chunk);
