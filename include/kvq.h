@@ -153,6 +153,14 @@ kvq_status kvq_probe(int32_t* has_gfx950);
 /* Validate a configuration (the pages' QuantizerConfigError checks). */
 kvq_status kvq_config_check(const kvq_config* cfg);
 
+/* Kitty's channel count from its fraction ("veloxquant_mlx.cache package", KVCacheConfig: the
+ * share of key channels kept at the high width, a quarter by default): *n_hi = round(hi_fraction
+ * * head_dim), halves rounded up, the value to put in kvq_config.kitty_n_hi. Returns KVQ_OK, or
+ * KVQ_E_INVALID (and *n_hi untouched) for a NULL pointer, head_dim < 1, or a fraction that is not
+ * a finite number in [0, 1]. A count that is not a multiple of 16 is accepted here and refused
+ * by kvq_config_check. */
+kvq_status kvq_kitty_n_hi(int32_t head_dim, double hi_fraction, int32_t* n_hi);
+
 /* Device bytes the caller allocates for one cache (0 if cfg is invalid). The counterpart of the
  * standalone caches' memory_bytes() ("veloxquant_mlx.cache package", e.g.
  * PolarQuantKVCache.memory_bytes: bytes held for the cached tokens), taken here at full

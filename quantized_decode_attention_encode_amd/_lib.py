@@ -59,6 +59,7 @@ def _load():
     sig = {
         "kvq_probe": (I32, [pi32]),
         "kvq_config_check": (I32, [pcfg]),
+        "kvq_kitty_n_hi": (I32, [I32, ctypes.c_double, pi32]),
         "kvq_cache_bytes": (SZ, [pcfg]),
         "kvq_layout": (I32, [pcfg, ctypes.POINTER(LayoutInfo)]),
         "kvq_workspace_bytes": (SZ, [pcfg, I32]),
@@ -87,7 +88,7 @@ def _load():
 
 
 lib = _load()
-EXPORTED = ("kvq_probe", "kvq_config_check", "kvq_cache_bytes", "kvq_layout", "kvq_workspace_bytes",
+EXPORTED = ("kvq_probe", "kvq_config_check", "kvq_kitty_n_hi", "kvq_cache_bytes", "kvq_layout", "kvq_workspace_bytes",
             "kvq_cache_create", "kvq_cache_destroy", "kvq_reset", "kvq_cache_lengths", "kvq_encode", "kvq_encode_block",
             "kvq_prefill", "kvq_append", "kvq_decode_attend", "kvq_append_decode_attend", "kvq_decode_attend_multi", "kvq_decode_attend_noalloc",
             "kvq_profile_enable", "kvq_profile_read",

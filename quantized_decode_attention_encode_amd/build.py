@@ -29,6 +29,7 @@ PER_FILE = {
     "decode.hip": [],
     "decode_sink.hip": [],
     "decode_skvq.hip": [],
+    "decode_mfma.hip": [],
     # multi-query attend on the matrix cores
     "attend_tiles.hip": [],
     # Kitty encode (bit-exact quantizer) and decode

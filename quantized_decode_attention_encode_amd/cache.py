@@ -35,9 +35,9 @@ def make_config(batch, n_kv_heads, n_q_heads, head_dim, key_bits=2, value_bits=2
         raise ValueError(f"method must be one of {sorted(methods)}, got {method!r}")
     n_hi = 0
     if method == "kitty":
-        if not 0.0 <= kitty_hi_fraction <= 1.0:
-            raise ValueError("kitty_hi_fraction must be in [0, 1]")
-        n_hi = int(kitty_hi_fraction * head_dim + 0.5)
+        hi = ctypes.c_int32(0)
+        check(lib.kvq_kitty_n_hi(int(head_dim), float(kitty_hi_fraction), ctypes.byref(hi)))
+        n_hi = hi.value
         value_bits = 16
     return Config(batch, n_kv_heads, n_q_heads, head_dim, key_bits, value_bits, group, residual, max_tokens,
                   n_sink, methods[method], int(bool(skvq_reorder)), int(bool(skvq_clip_search)),

@@ -60,6 +60,33 @@ __device__ __forceinline__ float dpp(float v) {  // old = 0: lets the compiler f
 }
 constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowRor4 = 0x124, kRowRor8 = 0x128;
 
+// Lane bits that a producer lane j can flip without leaving its value group ((j E) >> 1) % NKG
+// (E channels per lane, NKG value groups): 0b111100 at D = 128, 0b111101 at D = 64.
+__host__ __device__ constexpr int value_group_keep_mask(int E, int NKG) {
+  int m = 0;
+  for (int bit = 0; bit < 6; ++bit) {
+    bool keep = true;
+    for (int j = 0; j < 64; ++j)
+      keep = keep && ((j * E) >> 1) % NKG == (((j ^ (1 << bit)) * E) >> 1) % NKG;
+    if (keep) m |= 1 << bit;
+  }
+  return m;
+}
+
+// The zero-term bias of the output channels of this lane: v summed over the producer lanes of
+// the value group that holds channels lane E .. lane E + E - 1 (a butterfly over the bits that
+// keep the group, then a read from the first lane of the wanted group, 2 kc / E).
+template <int D>
+__device__ __forceinline__ float value_group_bias(float v, int lane) {
+  constexpr int E = D / 64, NKG = D / 32, KEEP = value_group_keep_mask(E, NKG);
+#pragma unroll
+  for (int bit = 0; bit < 6; ++bit)
+    if (KEEP & (1 << bit)) v += __shfl_xor(v, 1 << bit, 64);
+  const int kc = (lane * E) / 32;
+  return __shfl(v, (2 * kc) / E, 64);
+}
+static_assert(value_group_keep_mask(2, 4) == 0x3C && value_group_keep_mask(1, 2) == 0x3D, "value group lanes");
+
 __device__ __forceinline__ float row_sum16(float v) {  // sum over the 16 lanes of a row, in every lane
   v += dpp<kQuadXor1>(v);
   v += dpp<kQuadXor2>(v);
@@ -138,8 +165,11 @@ struct Magic {
 };
 
 // The NH fp16 pairs of one word: pair j holds the codes at positions j (low half) and
-// j + NH (high half).
-template <int B>
+// j + NH (high half). MATRIX: the pairs feed matrix-core instructions. The compiler does not see
+// what an asm statement writes, so it would not insert the wait states an MFMA needs after a VALU
+// write of its source registers; there the and-or is written as plain code (the compiler still
+// forms v_and_or_b32 from it, with the hazard known).
+template <int B, bool MATRIX = false>
 struct Unpacker {
   uint32_t magic, mk[10];  // mk[o]: the code bits at [o, o+B) of both halves
   __device__ __forceinline__ void init() {
@@ -153,12 +183,15 @@ struct Unpacker {
       mk[o] = r;
     }
   }
-  __device__ __forceinline__ void run(uint32_t w, uint32_t* out) const {
+  __device__ __forceinline__ void run(uint32_t w, uint32_t* out) const { run_n<Magic<B>::NH>(w, out); }
+  // the first N pairs only
+  template <int N>
+  __device__ __forceinline__ void run_n(uint32_t w, uint32_t* out) const {
 #pragma unroll
-    for (int j = 0; j < Magic<B>::NH; ++j) {
+    for (int j = 0; j < N; ++j) {
       const int s = Magic<B>::sh(j);
       const uint32_t v = s > 0 ? (w << s) : (s < 0 ? (w >> -s) : w);
-      out[j] = and_or(v, mk[Magic<B>::od(j)], magic);
+      out[j] = MATRIX ? ((v & mk[Magic<B>::od(j)]) | magic) : and_or(v, mk[Magic<B>::od(j)], magic);
     }
   }
 };
@@ -186,7 +219,6 @@ struct WaveLds {
   float qsum[G][4];               // per-token key groups: the query summed over each quarter
   uint32_t A[G][D / 32][16 + 4];  // fp16 value weights per (value group, token pair), see kVScale
   float pw[G][32 + 4];            // window tokens: softmax weights
-  float red[G][64];
 };
 
 template <int D, int BK, int BV>
@@ -866,14 +898,10 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
 #pragma unroll
     for (int msk = 1; msk < 64; msk <<= 1) v += __shfl_xor(v, msk, 64);
     lt[i] = v;
-    W.red[i][lane] = st.bias[i];
   }
-  wave_sync();
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    float bsum = 0.f;
-    for (int j = 0; j < 64; ++j)
-      if (((j * E) >> 1) % NKG == kcons) bsum += W.red[i][j];
+    const float bsum = value_group_bias<D>(st.bias[i], lane);
 #pragma unroll
     for (int e = 0; e < E; ++e) o[i][e] = (st.acc[i][e] + bsum) * (1.0f / kVScale);
   }
@@ -932,6 +960,14 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
   // one thread move the counter (a device-scope atomic, performed coherently); the workgroup
   // that brings it to nvalid reads every partial back the same coherent way, then clears the
   // counter for the next call.
+  // Why this orders the partials without release/acquire fences: every partial store and load
+  // is a device-scope atomic, so it is performed at the device's coherence point (past the
+  // eight XCD L2s; no line of it stays in a non-coherent cache). s_waitcnt(0) returns only once
+  // this wave's stores are acknowledged there, the barrier extends that to the workgroup, and
+  // the counter increment is issued after it, also at the coherence point. A split that reads
+  // the count nvalid therefore increments after every other split's partials were performed,
+  // and its atomic loads read them from that same point. A fence would add an L2 writeback and
+  // invalidate in every wave (measured 204 us per long decode), which nothing here needs.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   uint32_t* cnt = sync + (int64_t(b) * L.Hkv + h);

@@ -1,0 +1,605 @@
+// decode_mfma.hip - decode attention for 4 or 8 query rows per KV head (GQA groups, or a few
+// queries per head) with both per-record products on the matrix cores.
+//
+// The decode of decode_kernel.h spends one VALU op per (key code, query row) and one per
+// (value code pair, row): at 4 rows it is VALU-bound. Here, per 32-token record and wave:
+//   scores  S^T[token][col] = sum_c code'[token][c] * B[c][col]  on v_mfma_f32_16x16x32_f16:
+//           A = the record's key codes as exact fp16 numbers 1 + c 2^(o-10) (the exponent-OR of
+//           decode_kernel.h), B = the folded scaled query q~'[row][c] = q s_c 2^(10-o) split into
+//           an fp16 high part (column 2 row) and low part (column 2 row + 1), formed per record in
+//           LDS; the constant "1" terms and the zeros leave through beta per row, as in the VALU
+//           decode; the high and low columns are added by one DPP step.
+//   values  O^T[ch][row] += sum_t vcode'[ch][t] * A_w[t][row]: A = the value codes as exact fp16
+//           numbers, B = the fp16 folded weights p s 2^(10-o) kVScale per (row, value group),
+//           written by the weight producers in exactly the token order of the converted codes.
+// The key chunks are loaded lane = token pair + 16 x quarter (a permutation of the VALU decode's
+// lane = 4 x pair + quarter), which makes each lane's converted key words its A fragments: row
+// m of a 16-token tile is token pair m, and k-group g is quarter g. The value codes reach their
+// A layout (a channel per lane, 8 tokens per k-group) through an LDS staging copy.
+// Window and sink units go through process_window of decode_kernel.h with its own running state,
+// merged with the matrix-core state at the end of the wave. Split partials and the in-kernel
+// merge are the VALU decode's.
+#include "decode_kernel.h"
+
+namespace kvq {
+namespace {
+
+typedef _Float16 h8m __attribute__((ext_vector_type(8)));
+typedef float f4m __attribute__((ext_vector_type(4)));
+
+// LDS of one wave, on top of the VALU decode's (used by the window units and the weights).
+template <int D, int NR, int BV>
+struct MfmaLds {
+  uint32_t qb[D / 32][4][16][4];  // key B fragments [k-step][k-group][column][4 dwords of fp16 pairs]
+  float beta[NR];                 // per row: q . z minus the fold constant, this record
+  float pbuf[NR][32 + 4];         // softmax weights of the record per row (token order)
+  float alpha[NR];                // running-max rescale of the record, per row
+  uint32_t vcs[D][BV];            // the record's value codes [channel][words]
+};
+
+// Maximum over the lanes c, c + 16, c + 32, c + 48 (one position in each of the four rows).
+__device__ __forceinline__ float wave_max_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+
+// Sum over the N consecutive lanes (N = 8 or 16, aligned) holding one row's key producers.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp<kQuadXor1>(v);
+  v += dpp<kQuadXor2>(v);
+  if constexpr (N == 8) {
+    v += dpp<0x141>(v);  // row_half_mirror: lane x with 7 - x of its half-row
+  } else {
+    v += dpp<kRowRor4>(v);
+    v += dpp<kRowRor8>(v);
+  }
+  return v;
+}
+
+template <int D, int BK>
+struct KeyCombo {
+  // producer combo c -> (row, k-step, k-group): 8 channels of quarter g (the channels of the
+  // A fragment of k-step ks), for one row
+  static constexpr int KS = D / 32;
+  __device__ static int row(int c) { return c / (4 * KS); }
+  __device__ static int ks(int c) { return (c / 4) % KS; }
+  __device__ static int g(int c) { return c % 4; }
+};
+
+// Channel (within the head) of element e (0..7) of the key A fragment for k-step ks and k-group
+// (= quarter) g: element e is half e % 2 of converted dword e / 2 of the fragment's words.
+template <int D, int BK>
+__device__ __forceinline__ int key_channel(int ks, int g, int e) {
+  using MK = Magic<BK>;
+  constexpr int DQ = D / 4;
+  constexpr int WQ = D * BK / 128;       // words per (token, quarter)
+  constexpr int FPW = MK::NH / 4;        // fragments per word (2, 1) or words per fragment (BK = 8: 2)
+  int word, j;
+  if constexpr (BK == 8) {               // a fragment spans two words of 2 dwords
+    word = 2 * ks + (e >> 2);
+    j = (e >> 1) & 1;
+  } else {
+    word = ks / FPW;
+    j = (ks % FPW) * 4 + (e >> 1);
+  }
+  (void)WQ;
+  const int pos = j + (e & 1) * MK::NH;  // code position within the word
+  return g * DQ + word * MK::NC + pos;
+}
+
+// Element e of a key B fragment within its two 4-channel runs (run 0 then run 1): BK 2 and 4
+// alternate the runs (a converted dword pairs positions j and j + NH), BK = 8 takes run 0 then 1.
+template <int BK>
+__host__ __device__ constexpr int key_param_slot(int e) {
+  return BK == 8 ? (e >> 2) * 4 + ((e >> 1) & 1) + 2 * (e & 1) : (e & 1) * 4 + (e >> 1);
+}
+
+template <int D, int BK>
+__device__ __forceinline__ float key_fold(int ks, int e) {
+  using MK = Magic<BK>;
+  int j;
+  if constexpr (BK == 8) j = (e >> 1) & 1;
+  else j = (ks % (MK::NH / 4)) * 4 + (e >> 1);
+  return MK::fold(j);  // fold of code position j (or j + NH: same in-half position)
+}
+
+template <int D, int BK, int BV, int NR>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape ds, PerSeq seq,
+                        const __half* __restrict__ q, float* __restrict__ ws, uint32_t* __restrict__ sync,
+                        void* __restrict__ out, const __half* __restrict__ k_app, const __half* __restrict__ v_app,
+                        uint8_t* bufw) {
+  constexpr int E = D / 64, DQ = D / 4, NKG = D / 32, KS = D / 32;
+  constexpr int WQ = D * BK / 128;
+  using MK = Magic<BK>;
+  using MV = Magic<BV>;
+  constexpr int NCOMBO = NR * KS * 4;               // key producer combos per record
+  constexpr int PL = (NCOMBO + 63) / 64;            // combos per lane
+  static_assert(NR == 4 || NR == 8, "4 or 8 query rows per KV head");
+
+  __shared__ __attribute__((aligned(16))) union {
+    struct {
+      WaveLds<D, NR> w[kWaves];
+      MfmaLds<D, NR, BV> m[kWaves];
+    } s;
+    float res[kWaves][2][NR][D + 4];
+    float mrg[3][64 * kWaves];
+  } sh;
+  __shared__ int sh_last;
+
+  const int sigma = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nq = max(0, min(seq.a[b], L.max_groups * kGroup));
+  const int nr_old = max(0, min(seq.b[b], L.R));
+  const int nr = min(nr_old + ds.append, L.R);
+  const int ngroups = nq / kGroup;
+  Causal<NR> cz;
+  {
+    const int S = nq + nr;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) cz.lim[i] = S - (ds.nqry - 1 - i % ds.nqry);
+    cz.lim_min = S - (ds.nqry - 1);
+  }
+  const int nunits = ngroups + (nr + kGroup - 1) / kGroup;
+  const int u0 = sigma * ds.chunk;
+  if (u0 >= nunits) return;
+  const int u1 = min(u0 + ds.chunk, nunits);
+  const int uq = min(u1, ngroups);
+
+  WaveLds<D, NR>& W = sh.s.w[wave];
+  MfmaLds<D, NR, BV>& M = sh.s.m[wave];
+  const int P = lane >> 2, Q = lane & 3;  // the VALU decode's lane roles (weights, window)
+  const int g = lane >> 4, col = lane & 15;  // MFMA roles: k-group / row group, column
+
+  Unpacker<BK, true> upk;  // their pairs are matrix-core operands
+  Unpacker<BV, true> upv;
+  upk.init();
+  upv.init();
+
+  // query: VALU layout (window units) and the key producers' folded channels
+  float qs[NR][E];
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      qs[i][e] = __half2float(q[(int64_t(b) * ds.n_q_heads + h * NR + i) * D + lane * E + e]) * ds.qscale;
+  float pq[PL][8], pqf[PL][8];  // per combo: q (scaled) and q * fold of its 8 channels
+#pragma unroll
+  for (int j = 0; j < PL; ++j) {
+    const int c = min(lane + 64 * j, NCOMBO - 1);
+    const int i = KeyCombo<D, BK>::row(c), ks = KeyCombo<D, BK>::ks(c), gg = KeyCombo<D, BK>::g(c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int ch = key_channel<D, BK>(ks, gg, e);
+      pq[j][e] = __half2float(q[(int64_t(b) * ds.n_q_heads + h * NR + i) * D + ch]) * ds.qscale;
+      pqf[j][e] = pq[j][e] * key_fold<D, BK>(ks, e);
+    }
+  }
+  // B columns past 2 NR stay zero
+  for (int x = lane; x < KS * 4 * 16 * 4; x += 64) (&M.qb[0][0][0][0])[x] = 0u;
+  // fold of token t's converted value code: at 2 bits the matrix-core path converts each k-group's
+  // 4 + 4 codes from word positions t % 4 (the word shifted by 8 bits for the upper four), else
+  // from their own word position
+  auto vfold = [](int t) { return BV == 2 ? MV::fold(t % 4) : MV::fold(t % MV::NC); };
+  const float vf0 = vfold(2 * P) * kVScale, vf1 = vfold(2 * P + 1) * kVScale;
+
+  // matrix-core running state: column col's row (col / 2) softmax; value sums O^T for row col
+  float m = -INFINITY, lsum = 0.0f;
+  f4m o[D / 16];
+#pragma unroll
+  for (int mt = 0; mt < D / 16; ++mt) o[mt] = f4m{0.f, 0.f, 0.f, 0.f};
+  float bias[NR];  // weight producers: zero-term bias per row
+#pragma unroll
+  for (int i = 0; i < NR; ++i) bias[i] = 0.0f;
+  // window / sink units: the VALU decode's running state
+  WaveState<D, NR> stw;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    stw.m[i] = -INFINITY;
+    stw.l[i] = 0.f;
+    stw.bias[i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) stw.acc[i][e] = 0.f;
+  }
+  const int myrow = col >> 1;
+  const bool colok = col < 2 * NR;
+  wave_sync();
+
+  const uint8_t* rec0 = buf + L.record(b, h, 0);
+  const uint64_t rb = L.rec_bytes;
+  const int ulast = max(uq - 1, 0);
+  // the record's words as this lane loads them
+  struct Regs {
+    uint32_t kc[2 * WQ];       // tokens 2 col, 2 col + 1 of quarter g (permuted chunk)
+    uint32_t kp[PL][8];        // key params of the lane's producer channels
+    uint32_t vc[E * BV];       // value codes of channels lane * E ..
+    uint32_t vp[E];            // value params (the VALU decode's producer entries)
+  };
+  auto load = [&](int u, Regs& r) {
+    const uint8_t* rec = rec0 + uint64_t(u) * rb;
+    load_words<2 * WQ>(reinterpret_cast<const uint32_t*>(rec) + (4 * col + g) * 2 * WQ, r.kc);
+#pragma unroll
+    for (int j = 0; j < PL; ++j) {
+      // the 8 channels are two runs of 4 consecutive ones: two 16-byte loads
+      const int c = min(lane + 64 * j, NCOMBO - 1);
+      const int ks = KeyCombo<D, BK>::ks(c), gg = KeyCombo<D, BK>::g(c);
+      const uint32_t* kpg = reinterpret_cast<const uint32_t*>(rec + rec_off_kparams(D, BK, BV));
+      const uint4 r0 = *reinterpret_cast<const uint4*>(kpg + key_channel<D, BK>(ks, gg, 0));
+      const uint4 r1 = *reinterpret_cast<const uint4*>(kpg + key_channel<D, BK>(ks, gg, BK == 8 ? 4 : 1));
+      const uint32_t w8[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r.kp[j][e] = w8[key_param_slot<BK>(e)];
+    }
+    load_words<E * BV>(reinterpret_cast<const uint32_t*>(rec + rec_off_vcodes(D, BK)) + lane * E * BV, r.vc);
+    load_words<E>(reinterpret_cast<const uint32_t*>(rec + rec_off_vparams(D, BK, BV)) + lane * E, r.vp);
+  };
+
+  auto process = [&](const Regs& cur, int tok0) {
+    // ---- key producers: B fragments (fp16 high / low columns) and beta per row
+#pragma unroll
+    for (int j = 0; j < PL; ++j) {
+      const int c = lane + 64 * j;
+      float bp = 0.f;
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        // q~' as fp16 high + low parts; beta takes out exactly what the matrix cores will see
+        // (high + low, not q~' itself), so the converted codes' constant 1 (times a fold factor up
+        // to 64) cancels to fp32 accuracy and only the codes' own part carries the split error
+        const float x0 = pqf[j][e] * lo_f(cur.kp[j][e]), x1 = pqf[j][e + 1] * lo_f(cur.kp[j][e + 1]);
+        const auto hh = __builtin_amdgcn_cvt_pkrtz(x0, x1);
+        const float h0 = (float)hh[0], h1 = (float)hh[1];
+        const auto ll = __builtin_amdgcn_cvt_pkrtz(x0 - h0, x1 - h1);
+        bp += pq[j][e] * hi_f(cur.kp[j][e]) - (h0 + (float)ll[0]);
+        bp += pq[j][e + 1] * hi_f(cur.kp[j][e + 1]) - (h1 + (float)ll[1]);
+        hi[e >> 1] = __builtin_bit_cast(uint32_t, hh);
+        lo[e >> 1] = __builtin_bit_cast(uint32_t, ll);
+      }
+      bp = group_sum<4 * KS>(bp);  // the 4 KS combos of one row are consecutive lanes
+      if (c < NCOMBO) {
+        const int i = KeyCombo<D, BK>::row(c), ks = KeyCombo<D, BK>::ks(c), gg = KeyCombo<D, BK>::g(c);
+        *reinterpret_cast<uint4*>(&M.qb[ks][gg][2 * i][0]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        *reinterpret_cast<uint4*>(&M.qb[ks][gg][2 * i + 1][0]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        if (c % (4 * KS) == 0) M.beta[i] = bp;
+      }
+    }
+    // ---- value codes to their A layout
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+#pragma unroll
+      for (int w = 0; w < BV; ++w) M.vcs[lane * E + e][w] = cur.vc[e * BV + w];
+    // ---- key A fragments: the lane's two tokens x its quarter, converted
+    h8m ka[2][KS];
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp) {
+      uint32_t cv[WQ][MK::NH];
+#pragma unroll
+      for (int w = 0; w < WQ; ++w) upk.run(cur.kc[tp * WQ + w], cv[w]);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint32_t f[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          if constexpr (BK == 8) f[d] = cv[2 * ks + (d >> 1)][d & 1];
+          else f[d] = cv[ks / (MK::NH / 4)][(ks % (MK::NH / 4)) * 4 + d];
+        }
+        ka[tp][ks] = __builtin_bit_cast(h8m, make_uint4(f[0], f[1], f[2], f[3]));
+      }
+    }
+    wave_sync();
+    // ---- scores on the matrix cores
+    f4m acc[2] = {f4m{0.f, 0.f, 0.f, 0.f}, f4m{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const h8m bq = __builtin_bit_cast(h8m, *reinterpret_cast<const uint4*>(&M.qb[ks][g][col][0]));
+#pragma unroll
+      for (int tp = 0; tp < 2; ++tp) acc[tp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[tp][ks], bq, acc[tp], 0, 0, 0);
+    }
+    // lane (g, col): tokens 2 (4 g + r) + tp, r < 4: the eight tokens 8 g .. 8 g + 7
+    float s[8];
+    const float bt = colok ? M.beta[myrow] : 0.f;
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float x = acc[tp][r];
+        x += dpp<kQuadXor1>(x);  // high + low columns
+        s[2 * r + tp] = x + bt;
+      }
+    if (NR > 1 && tok0 + kGroup > cz.lim_min) {  // some row's future is in this record
+      int lm = cz.lim[0];
+#pragma unroll
+      for (int i = 1; i < NR; ++i) lm = myrow == i ? cz.lim[i] : lm;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (tok0 + 8 * g + k >= lm) s[k] = kMaskScore;
+    }
+    float mx = -INFINITY;
+    if (colok) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) mx = fmaxf(mx, s[k]);
+    }
+    mx = wave_max_rows(mx);
+    if (__any(mx > m)) {  // wave-uniform: some row's maximum moves
+      const float mn = fmaxf(m, mx);
+      const float a = fast_exp2(m - mn);
+      m = mn;
+      lsum *= a;
+      if (g == 0 && colok && !(col & 1)) M.alpha[myrow] = a;
+      wave_sync();
+      const float ao = col < NR ? M.alpha[col] : 1.0f;
+#pragma unroll
+      for (int mt = 0; mt < D / 16; ++mt) o[mt] *= ao;
+#pragma unroll
+      for (int i = 0; i < NR; ++i) bias[i] *= M.alpha[i];
+    }
+    float p[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) p[k] = fast_exp2(s[k] - m);
+    if (colok && !(col & 1)) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) lsum += p[k];
+      *reinterpret_cast<float4*>(&M.pbuf[myrow][8 * g]) = make_float4(p[0], p[1], p[2], p[3]);
+      *reinterpret_cast<float4*>(&M.pbuf[myrow][8 * g + 4]) = make_float4(p[4], p[5], p[6], p[7]);
+    }
+    wave_sync();
+    // ---- weight producers (the VALU decode's lanes): fp16 folded weights, zero-term bias
+    bool bigv;
+    {
+      uint32_t mxs = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) mxs = max(mxs, cur.vp[e] & 0x7FFFu);
+      bigv = __any(mxs > big_scale_bits<BV>());
+    }
+    const float vw0 = bigv ? vf0 * (1.0f / kVBigRatio) : vf0, vw1 = bigv ? vf1 * (1.0f / kVBigRatio) : vf1;
+    const float amul = bigv ? kVBigRatio : 1.0f;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const float2 pp = *reinterpret_cast<const float2*>(&M.pbuf[i][2 * P]);
+      float br = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int idx = lane * E + e;
+        const int tp = idx & 1, k = (idx >> 1) % NKG, t = 2 * P + tp;
+        const float pv = tp ? pp.y : pp.x;
+        const __half a16 = __float2half_rn((pv * (tp ? vw1 : vw0)) * lo_f(cur.vp[e]));
+        br = __builtin_fmaf(-__half2float(a16), amul, __builtin_fmaf(pv * kVScale, hi_f(cur.vp[e]), br));
+        const int dw = (t / MV::NC) * MV::NH + (t % MV::NC) % MV::NH, hf = (t % MV::NC) / MV::NH;
+        reinterpret_cast<__half*>(&W.A[i][k][dw])[hf] = a16;
+      }
+      bias[i] += br;
+    }
+    wave_sync();
+    // ---- values on the matrix cores: A = the codes of channel 16 mt + col, k-group g, accumulated
+    // into o (one rounding per record and element, as a separate per-record sum would take); a
+    // record with weights at kVScaleBig meets o scaled down by kVBigRatio, exactly (a power of 2)
+    if (bigv) {
+#pragma unroll
+      for (int mt = 0; mt < D / 16; ++mt) o[mt] *= 1.0f / kVBigRatio;
+    }
+#pragma unroll
+    for (int k = 0; k < NKG; ++k) {
+      const h8m bw = __builtin_bit_cast(h8m, col < NR ? *reinterpret_cast<const uint4*>(&W.A[col][k][4 * g])
+                                                      : make_uint4(0, 0, 0, 0));
+#pragma unroll
+      for (int mh = 0; mh < 2; ++mh) {
+        const int mt = 2 * k + mh;
+        uint32_t f[4];
+        if constexpr (BV == 8) {
+#pragma unroll
+          for (int w2 = 0; w2 < 2; ++w2) {
+            uint32_t cv[MV::NH];
+            upv.run(M.vcs[mt * 16 + col][2 * g + w2], cv);
+            f[2 * w2] = cv[0];
+            f[2 * w2 + 1] = cv[1];
+          }
+        } else if constexpr (BV == 2) {
+          // k-group g: word positions 4 (g % 2) .. + 3 and 8 + the same, shifted down to 0 .. 3
+          // and 8 .. 11 (a runtime pick among the converted pairs would cost selects)
+          upv.template run_n<4>(M.vcs[mt * 16 + col][g >> 1] >> (8 * (g & 1)), f);
+        } else {
+          upv.run(M.vcs[mt * 16 + col][g], f);  // 4 bits: a word is one fragment
+        }
+        o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8m, make_uint4(f[0], f[1], f[2], f[3])),
+                                                       bw, o[mt], 0, 0, 0);
+      }
+    }
+    if (bigv) {
+#pragma unroll
+      for (int mt = 0; mt < D / 16; ++mt) o[mt] *= kVBigRatio;
+    }
+    wave_sync();
+  };
+
+  // quantized records, the next one loaded while the current one is computed
+  int u = u0 + wave;
+  if (u < uq) {
+    Regs ra, rbf;
+    load(u, ra);
+    load(min(u + kWaves, ulast), rbf);
+    while (true) {
+      process(ra, u * kGroup);
+      u += kWaves;
+      if (u >= uq) break;
+      load(min(u + kWaves, ulast), ra);
+      process(rbf, u * kGroup);
+      u += kWaves;
+      if (u >= uq) break;
+      load(min(u + kWaves, ulast), rbf);
+    }
+  }
+  // window units: the VALU decode's path and state
+  for (; u < u1; u += kWaves) {
+    const int tbase = (u - ngroups) * kGroup;
+    const int nvalid = min(kGroup, nr - tbase);
+    const __half* wk = reinterpret_cast<const __half*>(buf + L.wk_off + L.window(b, h)) + tbase * D;
+    const __half* wv = reinterpret_cast<const __half*>(buf + L.wv_off + L.window(b, h)) + tbase * D;
+    const int tnew = ds.append ? nr_old - tbase : -1;
+    const int64_t tok = (int64_t(b) * L.Hkv + h) * D;
+    const __half* kn = ds.append ? k_app + tok : nullptr;
+    const __half* vn = ds.append ? v_app + tok : nullptr;
+    process_window<D, NR, false>(wk, wv, nvalid, tnew, kn, vn, W, stw, qs, lane, cz, nq + tbase, nullptr);
+    if (tnew >= 0 && tnew < nvalid) {
+      __half* dk = reinterpret_cast<__half*>(bufw + L.wk_off + L.window(b, h)) + nr_old * D;
+      __half* dv = reinterpret_cast<__half*>(bufw + L.wv_off + L.window(b, h)) + nr_old * D;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        dk[lane * E + e] = kn[lane * E + e];
+        dv[lane * E + e] = vn[lane * E + e];
+      }
+    }
+  }
+
+  // ---- finish the wave: both states to LDS as (acc[D], m, l) per row, in output units
+  // matrix-core state: l per row summed over its 4 row groups, bias per (row, value group)
+  float lt = lsum;
+  lt += __shfl_xor(lt, 16, 64);
+  lt += __shfl_xor(lt, 32, 64);
+  float ltw[NR], bsum[NR], bsumw[NR];  // window l per row; the bias of this lane's value group
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    float v = (Q == 0) ? stw.l[i] : 0.f;
+#pragma unroll
+    for (int msk = 1; msk < 64; msk <<= 1) v += __shfl_xor(v, msk, 64);
+    ltw[i] = v;
+    bsum[i] = value_group_bias<D>(bias[i], lane);
+    bsumw[i] = value_group_bias<D>(stw.bias[i], lane);
+  }
+  __syncthreads();  // the union switches from the per-wave arrays to res
+  // matrix-core O^T: lane (g, col) holds channels 16 mt + 4 g + r of row col
+  if (col < NR) {
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sh.res[wave][0][col][mt * 16 + 4 * g + r] = o[mt][r];
+  }
+  if (g == 0 && colok && !(col & 1)) {
+    sh.res[wave][0][myrow][D] = m;
+    sh.res[wave][0][myrow][D + 1] = lt;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    // the bias joins the matrix-core sums (its weights' zero terms); both states in output units
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int ch = lane * E + e;
+      sh.res[wave][0][i][ch] = (sh.res[wave][0][i][ch] + bsum[i]) * (1.0f / kVScale);
+      sh.res[wave][1][i][ch] = (stw.acc[i][e] + bsumw[i]) * (1.0f / kVScale);
+    }
+    if (lane == 0) {
+      sh.res[wave][1][i][D] = stw.m[i];
+      sh.res[wave][1][i][D + 1] = ltw[i];
+    }
+  }
+  __syncthreads();
+
+  // ---- combine the 2 x kWaves states per row: the partial of each row, or the output
+  const int nvs = min(ds.n_split, (nunits + ds.chunk - 1) / ds.chunk);
+  const int64_t row0 = int64_t(b) * ds.n_q_heads + h * NR;
+  for (int idx = threadIdx.x; idx < NR * D; idx += 64 * kWaves) {
+    const int i = idx / D, ch = idx % D;
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+      for (int z = 0; z < 2; ++z) Mx = fmaxf(Mx, sh.res[w][z][i][D]);
+    float O = 0.f, Lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+      for (int z = 0; z < 2; ++z) {
+        const float mw = sh.res[w][z][i][D];
+        if (mw != -INFINITY) {
+          const float wgt = fast_exp2(mw - Mx);
+          O += wgt * sh.res[w][z][i][ch];
+          Lsum += wgt * sh.res[w][z][i][D + 1];
+        }
+      }
+    if (nvs == 1) {
+      store_out(out, ds.out_fp32, (row0 + i) * D + ch, O / Lsum);
+      continue;
+    }
+    float* dst = ws + ((row0 + i) * ds.n_split + sigma) * (D + 4);
+    put_partial(dst + ch, O);
+    if (ch == 0) {
+      put_partial(dst + D, Mx);
+      put_partial(dst + D + 1, Lsum);
+    }
+  }
+  int32_t* len_w = reinterpret_cast<int32_t*>(bufw + L.lengths(b, h));
+  if (nvs == 1) {
+    if (ds.append && threadIdx.x == 0) len_w[1] = nr;
+    return;
+  }
+  // the last split of (b, h_kv) merges, as in the VALU decode (see decode_split_kernel)
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  uint32_t* cnt = sync + (int64_t(b) * L.Hkv + h);
+  if (threadIdx.x == 0) sh_last = atomicAdd(cnt, 1u) + 1u == uint32_t(nvs);
+  __syncthreads();
+  if (!sh_last) return;
+  merge_splits<D, NR>(ws, row0, ds.n_split, nvs, sh.mrg, out, ds.out_fp32);
+  if (threadIdx.x == 0) {
+    if (ds.append) len_w[1] = nr;
+    atomicExch(cnt, 0u);
+  }
+}
+
+template <int D, int BK, int BV, int NR>
+hipError_t launch_t(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq, const void* q, float* ws,
+                    void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  dim3 grid(ds.n_split, L.Hkv, L.B);
+  uint32_t* sync = reinterpret_cast<uint32_t*>(buf + L.sync_off);
+  const __half* qh = static_cast<const __half*>(q);
+  const __half* kh = static_cast<const __half*>(ka);
+  const __half* vh = static_cast<const __half*>(va);
+  if (e0 || e1)
+    hipExtLaunchKernelGGL((decode_mfma_kernel<D, BK, BV, NR>), grid, dim3(64 * kWaves), 0, s, e0, e1, 0,
+                          static_cast<const uint8_t*>(buf), L, ds, seq, qh, ws, sync, out, kh, vh, buf);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<D, BK, BV, NR>), grid, dim3(64 * kWaves), 0, s,
+                       static_cast<const uint8_t*>(buf), L, ds, seq, qh, ws, sync, out, kh, vh, buf);
+  return hipGetLastError();
+}
+
+template <int D, int BK, int BV>
+hipError_t launch_r(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq, const void* q, float* ws,
+                    void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (ds.G == 4) return launch_t<D, BK, BV, 4>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+  if (ds.G == 8) return launch_t<D, BK, BV, 8>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+  return hipErrorInvalidValue;
+}
+
+template <int D>
+hipError_t launch_d(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq, const void* q, float* ws,
+                    void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  switch (L.bk * 16 + L.bv) {
+    case 0x22: return launch_r<D, 2, 2>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+    case 0x24: return launch_r<D, 2, 4>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+    case 0x28: return launch_r<D, 2, 8>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+    case 0x42: return launch_r<D, 4, 2>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+    case 0x44: return launch_r<D, 4, 4>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+    case 0x48: return launch_r<D, 4, 8>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+    case 0x82: return launch_r<D, 8, 2>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+    case 0x84: return launch_r<D, 8, 4>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+    case 0x88: return launch_r<D, 8, 8>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq, const void* q,
+                              float* ws, void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0,
+                              hipEvent_t e1) {
+  if (L.method != kMethodKivi || L.NS != 0) return hipErrorInvalidValue;
+  if (L.D == 128) return launch_d<128>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+  if (L.D == 64) return launch_d<64>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvq

@@ -82,6 +82,11 @@ hipError_t launch_decode(uint8_t* buf, const Layout& L, const DecodeShape& ds, c
 hipError_t launch_decode_skvq(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq, const void* q, float* ws,
                               void* out, const void* k_tok, const void* v_tok, hipStream_t s, hipEvent_t start,
                               hipEvent_t stop);
+// The decode for 4 or 8 query rows per KV head of KIVI caches without sinks, both per-record
+// products on the matrix cores (decode_mfma.hip); the same arguments and results.
+hipError_t launch_decode_mfma(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq, const void* q,
+                              float* ws, void* out, const void* k_tok, const void* v_tok, hipStream_t s,
+                              hipEvent_t start, hipEvent_t stop);
 hipError_t launch_decode_sink(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq, const void* q, float* ws,
                               void* out, const void* k_tok, const void* v_tok, hipStream_t s, hipEvent_t start,
                               hipEvent_t stop);

@@ -360,6 +360,10 @@ kvq_status decode_enqueue(kvq_cache* c, const void* q, void* out, int32_t out_fp
   if (is_kitty(cfg))
     e = kvq::launch_kitty_decode(c->buf, c->L, ds, q, ws, out, s, prof ? c->ev[c->ev_used] : nullptr,
                                  prof ? c->ev[c->ev_used + 1] : nullptr);
+  else if (cfg.method == KVQ_METHOD_KIVI && cfg.n_sink == 0 && (ds.G == 4 || ds.G == 8))
+    // 4 or 8 query rows per KV head: both per-record products on the matrix cores
+    e = kvq::launch_decode_mfma(c->buf, c->L, ds, seq, q, ws, out, k_tok, v_tok, s,
+                                prof ? c->ev[c->ev_used] : nullptr, prof ? c->ev[c->ev_used + 1] : nullptr);
   else
     e = kvq::launch_decode(c->buf, c->L, ds, seq, q, ws, out, k_tok, v_tok, s, prof ? c->ev[c->ev_used] : nullptr,
                            prof ? c->ev[c->ev_used + 1] : nullptr);
@@ -423,6 +427,15 @@ kvq_status kvq_probe(int32_t* has_gfx950) {
 }
 
 kvq_status kvq_config_check(const kvq_config* cfg) { return check_config(cfg); }
+
+kvq_status kvq_kitty_n_hi(int32_t head_dim, double hi_fraction, int32_t* n_hi) {
+  if (!n_hi) return fail(KVQ_E_INVALID, "kvq_kitty_n_hi: n_hi is NULL");
+  if (head_dim < 1) return fail(KVQ_E_INVALID, "kvq_kitty_n_hi: head_dim must be positive");
+  if (!(hi_fraction >= 0.0 && hi_fraction <= 1.0))
+    return fail(KVQ_E_INVALID, "kvq_kitty_n_hi: the fraction must be a number in [0, 1]");
+  *n_hi = int32_t(std::floor(hi_fraction * double(head_dim) + 0.5));
+  return ok();
+}
 
 size_t kvq_cache_bytes(const kvq_config* cfg) {
   if (check_config(cfg) != KVQ_OK) return 0;

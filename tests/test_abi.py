@@ -14,7 +14,7 @@ import pytest
 from quantized_decode_attention_encode_amd import _lib
 from quantized_decode_attention_encode_amd._lib import (KVQ_E_CAPACITY, KVQ_E_INVALID, KVQ_E_NODEVICE,
                                                         KVQ_E_UNSUPPORTED, KVQ_E_WORKSPACE, KVQ_OK, Config,
-                                                        LayoutInfo, lib)
+                                                        KVQError, LayoutInfo, lib)
 from tests import kvq_unpack
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -305,7 +305,22 @@ def test_kitty_config_from_python():
     assert make_config(1, 1, 1, 128, method="kitty", kitty_hi_fraction=1.0).kitty_n_hi == 128
     odd = make_config(1, 1, 1, 128, method="kitty", kitty_hi_fraction=0.3)  # 38 channels: not built
     assert odd.kitty_n_hi == 38 and lib.kvq_config_check(ctypes.byref(odd)) == KVQ_E_UNSUPPORTED
-    with pytest.raises(ValueError):
+    with pytest.raises(KVQError):
         make_config(1, 1, 1, 128, method="kitty", kitty_hi_fraction=1.5)
     with pytest.raises(ValueError):
         make_config(1, 1, 1, 128, method="polar")
+
+
+def test_kitty_fraction_to_channel_count_in_the_library():
+    """kvq_kitty_n_hi: round(fraction * head_dim), halves up; refuses NULL, head_dim < 1 and
+    fractions outside [0, 1] (NaN included) without touching the output."""
+    out = ctypes.c_int32(-7)
+    for d, f, want in ((128, 0.25, 32), (64, 0.25, 16), (128, 0.0, 0), (128, 1.0, 128),
+                       (128, 0.3, 38), (128, 0.125, 16), (96, 1 / 6, 16), (10, 0.25, 3), (10, 0.05, 1)):
+        assert lib.kvq_kitty_n_hi(d, f, ctypes.byref(out)) == KVQ_OK
+        assert out.value == want, (d, f, out.value)
+    out.value = -7
+    for d, f in ((128, -0.01), (128, 1.01), (128, float("nan")), (128, float("inf")), (0, 0.25), (-4, 0.5)):
+        assert lib.kvq_kitty_n_hi(d, f, ctypes.byref(out)) == KVQ_E_INVALID
+        assert out.value == -7
+    assert lib.kvq_kitty_n_hi(128, 0.25, None) == KVQ_E_INVALID

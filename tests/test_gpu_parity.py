@@ -72,10 +72,10 @@ def test_split_count_does_not_change_result(case):
     q = torch.from_numpy(draw.q).to(DEV)
     outs = [kvq_decode_attend(cache, q, out_fp32=True, n_split=n).cpu().numpy() for n in (0, 1, 2, 3, 7, 64)]
     # The value weights p_t * s_t enter the value dot products as fp16 (relative rounding
-    # <= 2^-12 each), and a different split count changes the running maxima they are
-    # rounded under; each result is then within 2^-12 * max|v_hat| of the exact one.
+    # <= 2^-11 each), and a different split count changes the running maxima they are
+    # rounded under; each result is then within 2^-11 * max|v_hat| of the exact one.
     vmax = max(np.abs(s.values_hat()).max() for s in oracle_prefill(draw, cfg.residual).values())
-    bound = 2 * 2.0 ** -12 * vmax + 2e-5
+    bound = 2 * 2.0 ** -11 * vmax + 2e-5
     for o in outs[1:]:
         assert np.max(np.abs(o - outs[0])) < bound
 
@@ -177,7 +177,13 @@ def test_gqa_equals_mha_with_replicated_kv():
     q = torch.from_numpy(draw.q).to(DEV)
     og = kvq_decode_attend(g, q, out_fp32=True).cpu().numpy()
     om = kvq_decode_attend(m, q, out_fp32=True).cpu().numpy()
-    assert np.max(np.abs(og - om)) < 1e-5
+    # 4 query rows per KV head run on the matrix cores, 1 row on the VALU decode: their scores
+    # agree to fp32 rounding, and each path's fp16 value weights are within 2^-11 (relative) of
+    # the exact ones, so the outputs are within 2 * 2^-11 * max|v_hat| of each other
+    vmax = max(np.abs(s.values_hat()).max() for s in oracle_prefill(draw, 32).values())
+    diff = np.abs(og - om)
+    assert diff.max() < 2 * 2.0 ** -11 * vmax + 2e-5
+    assert diff.mean() < 2e-5  # the roundings are independent: the typical difference is far smaller
 
 
 def test_poisoned_outputs_are_fully_written_and_runs_repeat_exactly():
@@ -229,7 +235,7 @@ def test_split_merge_on_a_reused_buffer(fill):
             kvq_decode_attend(c, q, out=out, out_fp32=fp32, n_split=n_split)
             o = out.float().cpu().numpy()
             assert np.isfinite(o).all(), f"{fill} n_split={n_split} fp32={fp32}: outputs left unwritten"
-            bound = (2 * 2.0 ** -12 * vmax + 2e-5) if fp32 else 2e-3
+            bound = (2 * 2.0 ** -11 * vmax + 2e-5) if fp32 else 2e-3
             assert np.max(np.abs(o - one)) < bound, f"{fill} n_split={n_split} fp32={fp32}"
 
 
