@@ -3,17 +3,18 @@
 //
 // The decode of decode_kernel.h spends one VALU op per (key code, query row) and one per
 // (value code pair, row): at 4 rows it is VALU-bound. Here, per 32-token record and wave:
-//   scores  S^T[token][col] = sum_c code'[token][c] * B[c][col]  on v_mfma_f32_16x16x32_f16:
-//           A = the record's key codes as exact fp16 numbers 1 + c 2^(o-10) (the exponent-OR of
-//           decode_kernel.h), B = the folded scaled query q~'[row][c] = q s_c 2^(10-o) split into
-//           an fp16 high part (column 2 row) and low part (column 2 row + 1), formed per record in
-//           LDS; the constant "1" terms and the zeros leave through beta per row, as in the VALU
-//           decode; the high and low columns are added by one DPP step.
+//   scores  S[r][token] = sum_c A[r][c] * code'[c][token] on v_mfma_f32_16x16x32_f16: A = the
+//           folded scaled query q~'[row][c] = q s_c 2^(10-o) split into an fp16 high part (A row
+//           2 row) and low part (row 2 row + 1), formed per record in LDS; B = the record's key
+//           codes as exact fp16 numbers 1 + c 2^(o-10) (the exponent-OR of decode_kernel.h). The
+//           constant "1" terms and the zeros leave through beta per row (the accumulator's start),
+//           as in the VALU decode; each lane adds its high and low rows, so lanes 16 g .. 16 g + 15
+//           hold the scores of query rows 2 g and 2 g + 1.
 //   values  O^T[ch][row] += sum_t vcode'[ch][t] * A_w[t][row]: A = the value codes as exact fp16
 //           numbers, B = the fp16 folded weights p s 2^(10-o) kVScale per (row, value group),
 //           written by the weight producers in exactly the token order of the converted codes.
 // The key chunks are loaded lane = token pair + 16 x quarter (a permutation of the VALU decode's
-// lane = 4 x pair + quarter), which makes each lane's converted key words its A fragments: row
+// lane = 4 x pair + quarter), which makes each lane's converted key words its B fragments: column
 // m of a 16-token tile is token pair m, and k-group g is quarter g. The value codes reach their
 // A layout (a channel per lane, 8 tokens per k-group) through an LDS staging copy.
 // Window and sink units go through process_window of decode_kernel.h with its own running state,
@@ -33,16 +34,18 @@ struct MfmaLds {
   uint32_t qb[D / 32][4][16][4];  // key B fragments [k-step][k-group][column][4 dwords of fp16 pairs]
   float beta[NR];                 // per row: q . z minus the fold constant, this record
   float pbuf[NR][32 + 4];         // softmax weights of the record per row (token order)
-  float alpha[NR];                // running-max rescale of the record, per row
   uint32_t vcs[D][BV];            // the record's value codes [channel][words]
+  uint32_t wa[16][D / 32][16 + 4];  // fp16 value weights [B column = row][value group][token pairs];
+                                    // rows past NR stay zero
 };
 
-// Maximum over the lanes c, c + 16, c + 32, c + 48 (one position in each of the four rows).
-__device__ __forceinline__ float wave_max_rows(float v) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+// Maximum over the 16 lanes of a row, in every lane.
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp<kQuadXor1>(v));
+  v = fmaxf(v, dpp<kQuadXor2>(v));
+  v = fmaxf(v, dpp<kRowRor4>(v));
+  v = fmaxf(v, dpp<kRowRor8>(v));
+  return v;
 }
 
 // Sum over the N consecutive lanes (N = 8 or 16, aligned) holding one row's key producers.
@@ -120,11 +123,14 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
   constexpr int PL = (NCOMBO + 63) / 64;            // combos per lane
   static_assert(NR == 4 || NR == 8, "4 or 8 query rows per KV head");
 
+  // per wave: the matrix-core arrays while records are computed, then the VALU decode's arrays for
+  // the window units (which come after every record of the wave)
+  union PerWave {
+    MfmaLds<D, NR, BV> m;
+    WaveLds<D, NR> w;
+  };
   __shared__ __attribute__((aligned(16))) union {
-    struct {
-      WaveLds<D, NR> w[kWaves];
-      MfmaLds<D, NR, BV> m[kWaves];
-    } s;
+    PerWave pw[kWaves];
     float res[kWaves][2][NR][D + 4];
     float mrg[3][64 * kWaves];
   } sh;
@@ -149,8 +155,8 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
   const int u1 = min(u0 + ds.chunk, nunits);
   const int uq = min(u1, ngroups);
 
-  WaveLds<D, NR>& W = sh.s.w[wave];
-  MfmaLds<D, NR, BV>& M = sh.s.m[wave];
+  WaveLds<D, NR>& W = sh.pw[wave].w;
+  MfmaLds<D, NR, BV>& M = sh.pw[wave].m;
   const int P = lane >> 2, Q = lane & 3;  // the VALU decode's lane roles (weights, window)
   const int g = lane >> 4, col = lane & 15;  // MFMA roles: k-group / row group, column
 
@@ -178,8 +184,9 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
       pqf[j][e] = pq[j][e] * key_fold<D, BK>(ks, e);
     }
   }
-  // B columns past 2 NR stay zero
+  // A rows of q~' past 2 NR and weight columns past NR stay zero
   for (int x = lane; x < KS * 4 * 16 * 4; x += 64) (&M.qb[0][0][0][0])[x] = 0u;
+  for (int x = NR * (D / 32) * 20 + lane; x < 16 * (D / 32) * 20; x += 64) (&M.wa[0][0][0])[x] = 0u;
   // fold of token t's converted value code: at 2 bits the matrix-core path converts each k-group's
   // 4 + 4 codes from word positions t % 4 (the word shifted by 8 bits for the upper four), else
   // from their own word position
@@ -187,7 +194,12 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
   const float vf0 = vfold(2 * P) * kVScale, vf1 = vfold(2 * P + 1) * kVScale;
 
   // matrix-core running state: column col's row (col / 2) softmax; value sums O^T for row col
-  float m = -INFINITY, lsum = 0.0f;
+  // matrix-core softmax state: lanes 16 g .. 16 g + 15 hold query rows 2 g and 2 g + 1 (g < NR / 2)
+  const bool rowok = g < NR / 2;
+  float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
+  int lim2[2];  // causal limits of those rows
+#pragma unroll
+  for (int j = 0; j < 2; ++j) lim2[j] = nq + nr - (ds.nqry - 1 - (2 * g + j) % ds.nqry);
   f4m o[D / 16];
 #pragma unroll
   for (int mt = 0; mt < D / 16; ++mt) o[mt] = f4m{0.f, 0.f, 0.f, 0.f};
@@ -204,8 +216,6 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
 #pragma unroll
     for (int e = 0; e < E; ++e) stw.acc[i][e] = 0.f;
   }
-  const int myrow = col >> 1;
-  const bool colok = col < 2 * NR;
   wave_sync();
 
   const uint8_t* rec0 = buf + L.record(b, h, 0);
@@ -290,60 +300,66 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
       }
     }
     wave_sync();
-    // ---- scores on the matrix cores
-    f4m acc[2] = {f4m{0.f, 0.f, 0.f, 0.f}, f4m{0.f, 0.f, 0.f, 0.f}};
+    // ---- scores on the matrix cores, S = q~' x codes^T: A = the q~' fragments (row 2 i + h: query
+    // row i, high or low part), B = the converted key codes (column m: token pair m of tile tp),
+    // beta entering as the accumulator's start in the high rows
+    float b0 = 0.f, b1 = 0.f;
+    if (rowok) {
+      b0 = M.beta[2 * g];
+      b1 = M.beta[2 * g + 1];
+    }
+    f4m acc[2] = {f4m{b0, 0.f, b1, 0.f}, f4m{b0, 0.f, b1, 0.f}};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const h8m bq = __builtin_bit_cast(h8m, *reinterpret_cast<const uint4*>(&M.qb[ks][g][col][0]));
+      const h8m aq = __builtin_bit_cast(h8m, *reinterpret_cast<const uint4*>(&M.qb[ks][g][col][0]));
 #pragma unroll
-      for (int tp = 0; tp < 2; ++tp) acc[tp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[tp][ks], bq, acc[tp], 0, 0, 0);
+      for (int tp = 0; tp < 2; ++tp) acc[tp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, ka[tp][ks], acc[tp], 0, 0, 0);
     }
-    // lane (g, col): tokens 2 (4 g + r) + tp, r < 4: the eight tokens 8 g .. 8 g + 7
-    float s[8];
-    const float bt = colok ? M.beta[myrow] : 0.f;
+    // lane (g, m): token 2 m + tp of query rows 2 g + j (high + low parts)
+    float s[2][2];
 #pragma unroll
     for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float x = acc[tp][r];
-        x += dpp<kQuadXor1>(x);  // high + low columns
-        s[2 * r + tp] = x + bt;
-      }
+      for (int j = 0; j < 2; ++j) s[tp][j] = acc[tp][2 * j] + acc[tp][2 * j + 1];
     if (NR > 1 && tok0 + kGroup > cz.lim_min) {  // some row's future is in this record
-      int lm = cz.lim[0];
 #pragma unroll
-      for (int i = 1; i < NR; ++i) lm = myrow == i ? cz.lim[i] : lm;
+      for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (tok0 + 8 * g + k >= lm) s[k] = kMaskScore;
+        for (int j = 0; j < 2; ++j)
+          if (tok0 + 2 * col + tp >= lim2[j]) s[tp][j] = kMaskScore;
     }
-    float mx = -INFINITY;
-    if (colok) {
+    float mx[2];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) mx = fmaxf(mx, s[k]);
-    }
-    mx = wave_max_rows(mx);
-    if (__any(mx > m)) {  // wave-uniform: some row's maximum moves
-      const float mn = fmaxf(m, mx);
-      const float a = fast_exp2(m - mn);
-      m = mn;
-      lsum *= a;
-      if (g == 0 && colok && !(col & 1)) M.alpha[myrow] = a;
-      wave_sync();
-      const float ao = col < NR ? M.alpha[col] : 1.0f;
+    for (int j = 0; j < 2; ++j) mx[j] = row_max16(fmaxf(s[0][j], s[1][j]));
+    if (__any(rowok && (mx[0] > mrow[0] || mx[1] > mrow[1]))) {  // some row's maximum moves
+      float a[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float mn = fmaxf(mrow[j], mx[j]);
+        a[j] = fast_exp2(mrow[j] - mn);
+        mrow[j] = mn;
+        lrow[j] *= a[j];
+      }
+      // every row's factor, wave-uniform (row 2 g + j lives in lanes 16 g ..)
+      float al[NR];
+#pragma unroll
+      for (int i = 0; i < NR; ++i)
+        al[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[i % 2]), 16 * (i / 2)));
+      float ao = 1.0f;
+#pragma unroll
+      for (int i = 0; i < NR; ++i) ao = col == i ? al[i] : ao;
 #pragma unroll
       for (int mt = 0; mt < D / 16; ++mt) o[mt] *= ao;
 #pragma unroll
-      for (int i = 0; i < NR; ++i) bias[i] *= M.alpha[i];
+      for (int i = 0; i < NR; ++i) bias[i] *= al[i];
     }
-    float p[8];
+    if (rowok) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) p[k] = fast_exp2(s[k] - m);
-    if (colok && !(col & 1)) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) lsum += p[k];
-      *reinterpret_cast<float4*>(&M.pbuf[myrow][8 * g]) = make_float4(p[0], p[1], p[2], p[3]);
-      *reinterpret_cast<float4*>(&M.pbuf[myrow][8 * g + 4]) = make_float4(p[4], p[5], p[6], p[7]);
+      for (int j = 0; j < 2; ++j) {
+        const float p0 = fast_exp2(s[0][j] - mrow[j]), p1 = fast_exp2(s[1][j] - mrow[j]);
+        lrow[j] += p0 + p1;
+        *reinterpret_cast<float2*>(&M.pbuf[2 * g + j][2 * col]) = make_float2(p0, p1);
+      }
     }
     wave_sync();
     // ---- weight producers (the VALU decode's lanes): fp16 folded weights, zero-term bias
@@ -356,9 +372,12 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
     }
     const float vw0 = bigv ? vf0 * (1.0f / kVBigRatio) : vf0, vw1 = bigv ? vf1 * (1.0f / kVBigRatio) : vf1;
     const float amul = bigv ? kVBigRatio : 1.0f;
+    float2 pw[NR];  // every row's weights first: the LDS reads need not wait for the writes below
+#pragma unroll
+    for (int i = 0; i < NR; ++i) pw[i] = *reinterpret_cast<const float2*>(&M.pbuf[i][2 * P]);
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-      const float2 pp = *reinterpret_cast<const float2*>(&M.pbuf[i][2 * P]);
+      const float2 pp = pw[i];
       float br = 0.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
@@ -368,7 +387,7 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
         const __half a16 = __float2half_rn((pv * (tp ? vw1 : vw0)) * lo_f(cur.vp[e]));
         br = __builtin_fmaf(-__half2float(a16), amul, __builtin_fmaf(pv * kVScale, hi_f(cur.vp[e]), br));
         const int dw = (t / MV::NC) * MV::NH + (t % MV::NC) % MV::NH, hf = (t % MV::NC) / MV::NH;
-        reinterpret_cast<__half*>(&W.A[i][k][dw])[hf] = a16;
+        reinterpret_cast<__half*>(&M.wa[i][k][dw])[hf] = a16;
       }
       bias[i] += br;
     }
@@ -382,8 +401,7 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
     }
 #pragma unroll
     for (int k = 0; k < NKG; ++k) {
-      const h8m bw = __builtin_bit_cast(h8m, col < NR ? *reinterpret_cast<const uint4*>(&W.A[col][k][4 * g])
-                                                      : make_uint4(0, 0, 0, 0));
+      const h8m bw = __builtin_bit_cast(h8m, *reinterpret_cast<const uint4*>(&M.wa[col][k][4 * g]));
 #pragma unroll
       for (int mh = 0; mh < 2; ++mh) {
         const int mt = 2 * k + mh;
@@ -414,21 +432,49 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
     wave_sync();
   };
 
-  // quantized records, the next one loaded while the current one is computed
+  // quantized records: NB of this wave's records in flight, the oldest computed while the others
+  // arrive (under load, memory latency is longer than one record's computation). Three fit the
+  // register budget of two waves per SIMD at 4 rows (but for 8-bit keys and values), else two.
+  constexpr int NB = (NR == 4 && !(BK == 8 && BV == 8)) ? 3 : 2;
   int u = u0 + wave;
   if (u < uq) {
-    Regs ra, rbf;
-    load(u, ra);
-    load(min(u + kWaves, ulast), rbf);
-    while (true) {
-      process(ra, u * kGroup);
-      u += kWaves;
-      if (u >= uq) break;
-      load(min(u + kWaves, ulast), ra);
-      process(rbf, u * kGroup);
-      u += kWaves;
-      if (u >= uq) break;
+    if constexpr (NB == 3) {
+      const int nmine = (uq - u + kWaves - 1) / kWaves;  // this wave's records
+      Regs ring[NB];
+#pragma unroll
+      for (int d = 0; d < NB; ++d) load(min(u + d * kWaves, ulast), ring[d]);
+      // whole rounds of NB records, straight-line, so that each slot keeps its registers (a
+      // copy of a slot in flight would wait for every load)
+      int left = nmine;
+      for (; left > NB; left -= NB) {
+#pragma unroll
+        for (int d = 0; d < NB; ++d) {
+          process(ring[d], u * kGroup);
+          load(min(u + NB * kWaves, ulast), ring[d]);
+          u += kWaves;
+        }
+      }
+#pragma unroll
+      for (int d = 0; d < NB; ++d) {
+        if (d < left) {
+          process(ring[d], u * kGroup);
+          u += kWaves;
+        }
+      }
+    } else {
+      Regs ra, rbf;
+      load(u, ra);
       load(min(u + kWaves, ulast), rbf);
+      while (true) {
+        process(ra, u * kGroup);
+        u += kWaves;
+        if (u >= uq) break;
+        load(min(u + kWaves, ulast), ra);
+        process(rbf, u * kGroup);
+        u += kWaves;
+        if (u >= uq) break;
+        load(min(u + kWaves, ulast), rbf);
+      }
     }
   }
   // window units: the VALU decode's path and state
@@ -455,9 +501,9 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
 
   // ---- finish the wave: both states to LDS as (acc[D], m, l) per row, in output units
   // matrix-core state: l per row summed over its 4 row groups, bias per (row, value group)
-  float lt = lsum;
-  lt += __shfl_xor(lt, 16, 64);
-  lt += __shfl_xor(lt, 32, 64);
+  float lt[2];  // l of rows 2 g + j, over the 16 lanes of the row group
+#pragma unroll
+  for (int j = 0; j < 2; ++j) lt[j] = row_sum16(lrow[j]);
   float ltw[NR], bsum[NR], bsumw[NR];  // window l per row; the bias of this lane's value group
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
@@ -476,9 +522,12 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
 #pragma unroll
       for (int r = 0; r < 4; ++r) sh.res[wave][0][col][mt * 16 + 4 * g + r] = o[mt][r];
   }
-  if (g == 0 && colok && !(col & 1)) {
-    sh.res[wave][0][myrow][D] = m;
-    sh.res[wave][0][myrow][D + 1] = lt;
+  if (col == 0 && rowok) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      sh.res[wave][0][2 * g + j][D] = mrow[j];
+      sh.res[wave][0][2 * g + j][D + 1] = lt[j];
+    }
   }
   __syncthreads();
 #pragma unroll
