@@ -647,14 +647,14 @@ __device__ __forceinline__ void store_out(void* out, int out_fp32, int64_t idx, 
 }
 
 // Merge the nv split partials (acc[D], m, l) of the G query heads row0 .. row0+G-1 into the
-// output, by one workgroup of 64*kWaves threads: T threads per output element each fold a
-// strided share of the splits (batches of 8 loads in flight), then meet through LDS.
+// output, by one workgroup of NT threads: T threads per output element each fold a strided
+// share of the splits (batches of 8 loads in flight), then meet through LDS.
 // pv (per-token key groups): partial channel ch is output channel pv[ch].
-template <int D, int G>
+template <int D, int G, int NT = 64 * kWaves>
 __device__ __forceinline__ void merge_splits(const float* __restrict__ ws, int64_t row0, int n_split, int nv,
-                                             float (*mrg)[64 * kWaves], void* out, int out_fp32,
+                                             float (*mrg)[NT], void* out, int out_fp32,
                                              const uint8_t* __restrict__ pv = nullptr) {
-  constexpr int NT = 64 * kWaves, NOUT = G * D;
+  constexpr int NOUT = G * D;
   constexpr int T = NOUT >= NT ? 1 : NT / NOUT;
   constexpr int NO = NOUT >= NT ? NT : NOUT;  // output elements per pass
   const int tid = threadIdx.x, r = tid / NO;

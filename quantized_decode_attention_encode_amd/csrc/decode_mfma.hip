@@ -109,9 +109,12 @@ __device__ __forceinline__ float key_fold(int ks, int e) {
   return MK::fold(j);  // fold of code position j (or j + NH: same in-half position)
 }
 
+// Waves per workgroup: one workgroup fills a CU at two waves per SIMD.
+constexpr int kMW = 8;
+
 template <int D, int BK, int BV, int NR>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2)))
-void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape ds, PerSeq seq,
+__global__ __launch_bounds__(64 * kMW) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape ds, PerSeq seq, SplitPlan plan,
                         const __half* __restrict__ q, float* __restrict__ ws, uint32_t* __restrict__ sync,
                         void* __restrict__ out, const __half* __restrict__ k_app, const __half* __restrict__ v_app,
                         uint8_t* bufw) {
@@ -130,13 +133,27 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
     WaveLds<D, NR> w;
   };
   __shared__ __attribute__((aligned(16))) union {
-    PerWave pw[kWaves];
-    float res[kWaves][2][NR][D + 4];
-    float mrg[3][64 * kWaves];
+    PerWave pw[kMW];
+    float res[kMW][2][NR][D + 4];
+    float mrg[3][64 * kMW];
   } sh;
   __shared__ int sh_last;
+  __shared__ int sh_prog[kMW];  // records each wave has computed
+  __shared__ int sh_simd[kMW];  // the SIMD each wave runs on
 
-  const int sigma = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // this workgroup's (sequence, KV head, split) from the plan
+  const int item = blockIdx.x / L.Hkv, h = blockIdx.x % L.Hkv;
+  int k = 0;  // the plan's sequence: first[k] <= item < first[k + 1]
+  {
+    int hi = L.B;
+    while (hi - k > 1) {
+      const int mid = (k + hi) >> 1;
+      if (plan.first(mid) <= item) k = mid;
+      else hi = mid;
+    }
+  }
+  const int b = plan.order[k];
+  const int nsp = plan.first(k + 1) - plan.first(k), sigma = item - plan.first(k);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nq = max(0, min(seq.a[b], L.max_groups * kGroup));
   const int nr_old = max(0, min(seq.b[b], L.R));
@@ -150,10 +167,17 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
     cz.lim_min = S - (ds.nqry - 1);
   }
   const int nunits = ngroups + (nr + kGroup - 1) / kGroup;
-  const int u0 = sigma * ds.chunk;
+  const int chunk = (nunits + nsp - 1) / nsp;
+  const int u0 = sigma * chunk;
   if (u0 >= nunits) return;
-  const int u1 = min(u0 + ds.chunk, nunits);
+  const int u1 = min(u0 + chunk, nunits);
   const int uq = min(u1, ngroups);
+  // hardware wave id register, bits 5:4: the SIMD of this wave
+  const int simd = int((__builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11)) >> 4) & 3);
+  if (lane == 0) {
+    sh_prog[wave] = 0;
+    sh_simd[wave] = simd;
+  }
 
   WaveLds<D, NR>& W = sh.pw[wave].w;
   MfmaLds<D, NR, BV>& M = sh.pw[wave].m;
@@ -216,11 +240,14 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
 #pragma unroll
     for (int e = 0; e < E; ++e) stw.acc[i][e] = 0.f;
   }
-  wave_sync();
+  __syncthreads();  // sh_prog, sh_simd are set
+  int partner = -1;  // the other wave of this workgroup on this SIMD, if any
+#pragma unroll
+  for (int w = 0; w < kMW; ++w)
+    if (w != wave && sh_simd[w] == simd) partner = w;
 
   const uint8_t* rec0 = buf + L.record(b, h, 0);
   const uint64_t rb = L.rec_bytes;
-  const int ulast = max(uq - 1, 0);
   // the record's words as this lane loads them
   struct Regs {
     uint32_t kc[2 * WQ];       // tokens 2 col, 2 col + 1 of quarter g (permuted chunk)
@@ -432,53 +459,71 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
     wave_sync();
   };
 
-  // quantized records: NB of this wave's records in flight, the oldest computed while the others
-  // arrive (under load, memory latency is longer than one record's computation). Three fit the
-  // register budget of two waves per SIMD at 4 rows (but for 8-bit keys and values), else two.
+  // quantized records [u0, uq): wave w takes u0 + w, u0 + w + kMW, ... (a fixed assignment keeps
+  // the sums in a fixed order). The two waves of a SIMD would not progress alike (the arbiter
+  // serves the older one first when both are ready), so each wave compares its record count with
+  // its SIMD partner's after every record and takes the higher issue priority while it is not
+  // ahead: both finish together. NB of a wave's records are in flight, the oldest computed while
+  // the others arrive (under load, memory latency is longer than one record's computation); three
+  // fit the register budget of two waves per SIMD at 4 rows (but for 8-bit keys and values).
   constexpr int NB = (NR == 4 && !(BK == 8 && BV == 8)) ? 3 : 2;
   int u = u0 + wave;
   if (u < uq) {
+    const int ulast = uq - 1;
+    int done = 0;
+    auto progress = [&]() {
+      ++done;
+      if (lane == 0) sh_prog[wave] = done;
+      if (partner >= 0) {
+        const int theirs = sh_prog[partner];
+        if (done <= theirs) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+      }
+    };
     if constexpr (NB == 3) {
-      const int nmine = (uq - u + kWaves - 1) / kWaves;  // this wave's records
       Regs ring[NB];
 #pragma unroll
-      for (int d = 0; d < NB; ++d) load(min(u + d * kWaves, ulast), ring[d]);
-      // whole rounds of NB records, straight-line, so that each slot keeps its registers (a
-      // copy of a slot in flight would wait for every load)
-      int left = nmine;
+      for (int d = 0; d < NB; ++d) load(min(u + d * kMW, ulast), ring[d]);
+      // whole rounds of NB records, straight-line, so that each slot keeps its registers (a copy
+      // of a slot in flight would wait for every load)
+      int left = (uq - u + kMW - 1) / kMW;  // this wave's records
       for (; left > NB; left -= NB) {
 #pragma unroll
         for (int d = 0; d < NB; ++d) {
           process(ring[d], u * kGroup);
-          load(min(u + NB * kWaves, ulast), ring[d]);
-          u += kWaves;
+          load(min(u + NB * kMW, ulast), ring[d]);
+          u += kMW;
+          progress();
         }
       }
 #pragma unroll
       for (int d = 0; d < NB; ++d) {
         if (d < left) {
           process(ring[d], u * kGroup);
-          u += kWaves;
+          u += kMW;
         }
       }
     } else {
       Regs ra, rbf;
       load(u, ra);
-      load(min(u + kWaves, ulast), rbf);
+      load(min(u + kMW, ulast), rbf);
       while (true) {
         process(ra, u * kGroup);
-        u += kWaves;
+        u += kMW;
         if (u >= uq) break;
-        load(min(u + kWaves, ulast), ra);
+        load(min(u + kMW, ulast), ra);
+        progress();
         process(rbf, u * kGroup);
-        u += kWaves;
+        u += kMW;
         if (u >= uq) break;
-        load(min(u + kWaves, ulast), rbf);
+        load(min(u + kMW, ulast), rbf);
+        progress();
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
-  // window units: the VALU decode's path and state
-  for (; u < u1; u += kWaves) {
+  // window units: the VALU decode's path and state, one per wave in turn
+  for (u = max(u0, ngroups) + wave; u < u1; u += kMW) {
     const int tbase = (u - ngroups) * kGroup;
     const int nvalid = min(kGroup, nr - tbase);
     const __half* wk = reinterpret_cast<const __half*>(buf + L.wk_off + L.window(b, h)) + tbase * D;
@@ -546,19 +591,19 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
   }
   __syncthreads();
 
-  // ---- combine the 2 x kWaves states per row: the partial of each row, or the output
-  const int nvs = min(ds.n_split, (nunits + ds.chunk - 1) / ds.chunk);
+  // ---- combine the 2 x kMW states per row: the partial of each row, or the output
+  const int nvs = (nunits + chunk - 1) / chunk;  // splits of (b, h_kv) that hold units
   const int64_t row0 = int64_t(b) * ds.n_q_heads + h * NR;
-  for (int idx = threadIdx.x; idx < NR * D; idx += 64 * kWaves) {
+  for (int idx = threadIdx.x; idx < NR * D; idx += 64 * kMW) {
     const int i = idx / D, ch = idx % D;
     float Mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
+    for (int w = 0; w < kMW; ++w)
 #pragma unroll
       for (int z = 0; z < 2; ++z) Mx = fmaxf(Mx, sh.res[w][z][i][D]);
     float O = 0.f, Lsum = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
+    for (int w = 0; w < kMW; ++w)
 #pragma unroll
       for (int z = 0; z < 2; ++z) {
         const float mw = sh.res[w][z][i][D];
@@ -591,7 +636,7 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
   if (threadIdx.x == 0) sh_last = atomicAdd(cnt, 1u) + 1u == uint32_t(nvs);
   __syncthreads();
   if (!sh_last) return;
-  merge_splits<D, NR>(ws, row0, ds.n_split, nvs, sh.mrg, out, ds.out_fp32);
+  merge_splits<D, NR, 64 * kMW>(ws, row0, ds.n_split, nvs, sh.mrg, out, ds.out_fp32);
   if (threadIdx.x == 0) {
     if (ds.append) len_w[1] = nr;
     atomicExch(cnt, 0u);
@@ -599,55 +644,56 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
 }
 
 template <int D, int BK, int BV, int NR>
-hipError_t launch_t(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq, const void* q, float* ws,
-                    void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  dim3 grid(ds.n_split, L.Hkv, L.B);
+hipError_t launch_t(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq, const SplitPlan& plan,
+                    const void* q, float* ws, void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0,
+                    hipEvent_t e1) {
+  const dim3 grid(unsigned(plan.first(L.B)) * unsigned(L.Hkv));
   uint32_t* sync = reinterpret_cast<uint32_t*>(buf + L.sync_off);
   const __half* qh = static_cast<const __half*>(q);
   const __half* kh = static_cast<const __half*>(ka);
   const __half* vh = static_cast<const __half*>(va);
   if (e0 || e1)
-    hipExtLaunchKernelGGL((decode_mfma_kernel<D, BK, BV, NR>), grid, dim3(64 * kWaves), 0, s, e0, e1, 0,
-                          static_cast<const uint8_t*>(buf), L, ds, seq, qh, ws, sync, out, kh, vh, buf);
+    hipExtLaunchKernelGGL((decode_mfma_kernel<D, BK, BV, NR>), grid, dim3(64 * kMW), 0, s, e0, e1, 0,
+                          static_cast<const uint8_t*>(buf), L, ds, seq, plan, qh, ws, sync, out, kh, vh, buf);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<D, BK, BV, NR>), grid, dim3(64 * kWaves), 0, s,
-                       static_cast<const uint8_t*>(buf), L, ds, seq, qh, ws, sync, out, kh, vh, buf);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, BK, BV, NR>), grid, dim3(64 * kMW), 0, s,
+                       static_cast<const uint8_t*>(buf), L, ds, seq, plan, qh, ws, sync, out, kh, vh, buf);
   return hipGetLastError();
 }
 
 template <int D, int BK, int BV>
-hipError_t launch_r(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq, const void* q, float* ws,
-                    void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  if (ds.G == 4) return launch_t<D, BK, BV, 4>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
-  if (ds.G == 8) return launch_t<D, BK, BV, 8>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+hipError_t launch_r(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq, const SplitPlan& plan,
+                    const void* q, float* ws, void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0,
+                    hipEvent_t e1) {
+  if (ds.G == 4) return launch_t<D, BK, BV, 4>(buf, L, ds, seq, plan, q, ws, out, ka, va, s, e0, e1);
+  if (ds.G == 8) return launch_t<D, BK, BV, 8>(buf, L, ds, seq, plan, q, ws, out, ka, va, s, e0, e1);
   return hipErrorInvalidValue;
 }
 
 template <int D>
-hipError_t launch_d(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq, const void* q, float* ws,
-                    void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+hipError_t launch_d(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq, const SplitPlan& plan,
+                    const void* q, float* ws, void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0,
+                    hipEvent_t e1) {
+#define KVQ_MFMA_CASE(BK, BV) \
+  case BK * 16 + BV: return launch_r<D, BK, BV>(buf, L, ds, seq, plan, q, ws, out, ka, va, s, e0, e1);
   switch (L.bk * 16 + L.bv) {
-    case 0x22: return launch_r<D, 2, 2>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
-    case 0x24: return launch_r<D, 2, 4>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
-    case 0x28: return launch_r<D, 2, 8>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
-    case 0x42: return launch_r<D, 4, 2>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
-    case 0x44: return launch_r<D, 4, 4>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
-    case 0x48: return launch_r<D, 4, 8>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
-    case 0x82: return launch_r<D, 8, 2>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
-    case 0x84: return launch_r<D, 8, 4>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
-    case 0x88: return launch_r<D, 8, 8>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+    KVQ_MFMA_CASE(2, 2) KVQ_MFMA_CASE(2, 4) KVQ_MFMA_CASE(2, 8)
+    KVQ_MFMA_CASE(4, 2) KVQ_MFMA_CASE(4, 4) KVQ_MFMA_CASE(4, 8)
+    KVQ_MFMA_CASE(8, 2) KVQ_MFMA_CASE(8, 4) KVQ_MFMA_CASE(8, 8)
     default: return hipErrorInvalidValue;
   }
+#undef KVQ_MFMA_CASE
 }
 
 }  // namespace
 
-hipError_t launch_decode_mfma(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq, const void* q,
-                              float* ws, void* out, const void* ka, const void* va, hipStream_t s, hipEvent_t e0,
-                              hipEvent_t e1) {
+hipError_t launch_decode_mfma(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq,
+                              const SplitPlan& plan, const void* q, float* ws, void* out, const void* ka,
+                              const void* va, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   if (L.method != kMethodKivi || L.NS != 0) return hipErrorInvalidValue;
-  if (L.D == 128) return launch_d<128>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
-  if (L.D == 64) return launch_d<64>(buf, L, ds, seq, q, ws, out, ka, va, s, e0, e1);
+  if (plan.first(0) != 0 || plan.first(L.B) == 0) return hipErrorInvalidValue;
+  if (L.D == 128) return launch_d<128>(buf, L, ds, seq, plan, q, ws, out, ka, va, s, e0, e1);
+  if (L.D == 64) return launch_d<64>(buf, L, ds, seq, plan, q, ws, out, ka, va, s, e0, e1);
   return hipErrorInvalidValue;
 }
 

@@ -14,6 +14,19 @@ struct PerSeq {
   int32_t c[kMaxBatch];
 };
 
+// Split plan of the matrix-core decode: the k-th sequence of the plan, b = order[k], is cut into
+// first[k + 1] - first[k] splits of ceil(units / splits) units each; workgroup x of the
+// one-dimensional grid takes split x / H_kv - first[k] of that sequence (the k with
+// first[k] <= x / H_kv < first[k + 1]) and KV head x % H_kv.
+struct SplitPlan {
+  uint8_t order[kMaxBatch];            // sequences, the largest splits first
+  uint32_t first2[kMaxBatch / 2 + 1];  // first[i] in the 16-bit half i % 2 of word i / 2
+  KVQ_HD int first(int i) const { return int((first2[i >> 1] >> (16 * (i & 1))) & 0xFFFFu); }
+  KVQ_HD void set(int i, int v) {
+    first2[i >> 1] = (first2[i >> 1] & ~(0xFFFFu << (16 * (i & 1)))) | (uint32_t(v) << (16 * (i & 1)));
+  }
+};
+
 // Decode launch geometry: gridDim.x = n_split workgroups per (b, h_kv), each covering
 // `chunk` consecutive units (a unit is one 32-token record, or up to 32 window tokens).
 struct DecodeShape {
@@ -84,7 +97,8 @@ hipError_t launch_decode_skvq(uint8_t* buf, const Layout& L, const DecodeShape& 
                               hipEvent_t stop);
 // The decode for 4 or 8 query rows per KV head of KIVI caches without sinks, both per-record
 // products on the matrix cores (decode_mfma.hip); the same arguments and results.
-hipError_t launch_decode_mfma(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq, const void* q,
+hipError_t launch_decode_mfma(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq,
+                              const SplitPlan& plan, const void* q,
                               float* ws, void* out, const void* k_tok, const void* v_tok, hipStream_t s,
                               hipEvent_t start, hipEvent_t stop);
 hipError_t launch_decode_sink(uint8_t* buf, const Layout& L, const DecodeShape& ds, const PerSeq& seq, const void* q, float* ws,

@@ -189,6 +189,56 @@ int target_workgroups(int cus, int max_units, int64_t total_units, int64_t seq_h
   return std::max(1, cus) * (ragged ? 3 : 2);
 }
 
+// Split plan of the matrix-core decode, whose workgroups fill a CU each. With n_split > 0,
+// sequence b gets ceil(units_b / chunk) splits, chunk = ceil(max_units / n_split). Otherwise, for
+// a number of workgroups per KV head (first cus / H_kv: one wave of workgroups), the smallest
+// per-split load c such that sum_b min(limit_b, ceil(units_b / c)) splits fit, each sequence then
+// cut into that many equal splits; limit_b keeps 16 units (two records per wave) per split and
+// the workspace's split count. The largest splits are launched first. Returns the largest split
+// count.
+constexpr int kMfmaMinUnits = 16;
+int plan_mfma(const int* units, int B, int Hkv, int n_split, int cus, int max_splits, kvq::SplitPlan& plan) {
+  int max_units = 1;
+  for (int b = 0; b < B; ++b) max_units = std::max(max_units, units[b]);
+  int ns[kvq::kMaxBatch];
+  if (n_split > 0) {
+    const int cap = std::max(1, std::min(n_split, 65535 / B));  // the plan's 16-bit prefix
+    const int chunk = (max_units + cap - 1) / cap;
+    for (int b = 0; b < B; ++b) ns[b] = (units[b] + chunk - 1) / chunk;
+  } else {
+    auto splits = [&](int b, int c) {
+      const int lim = std::max(1, std::min(max_splits, units[b] / kMfmaMinUnits));
+      return std::min(lim, (units[b] + c - 1) / c);
+    };
+    const int per_head = std::max(1, cus / std::max(1, Hkv));
+    int lo = 1, hi = max_units;  // the smallest c whose splits fit per_head workgroups
+    while (lo < hi) {
+      const int mid = lo + (hi - lo) / 2;
+      int64_t n = 0;
+      for (int b = 0; b < B; ++b) n += splits(b, mid);
+      if (n <= per_head) hi = mid;
+      else lo = mid + 1;
+    }
+    for (int b = 0; b < B; ++b) ns[b] = splits(b, lo);
+  }
+  // sequences by split size, largest first (ties: lower index first)
+  int idx[kvq::kMaxBatch];
+  for (int b = 0; b < B; ++b) idx[b] = b;
+  std::stable_sort(idx, idx + B, [&](int x, int y) {
+    return (units[x] + ns[x] - 1) / ns[x] > (units[y] + ns[y] - 1) / ns[y];
+  });
+  int most = 1, first = 0;
+  plan.set(0, 0);
+  for (int k = 0; k < B; ++k) {
+    const int b = idx[k];
+    plan.order[k] = uint8_t(b);
+    most = std::max(most, ns[b]);
+    first += ns[b];
+    plan.set(k + 1, first);
+  }
+  return most;
+}
+
 kvq_status ensure_ready(kvq_cache* c, hipStream_t s) {
   kvq_status st = check_device();
   if (st != KVQ_OK) return st;
@@ -299,17 +349,31 @@ kvq_status decode_enqueue(kvq_cache* c, const void* q, void* out, int32_t out_fp
   }
   int max_units = 0;
   int64_t total_units = 0;
+  int units[kvq::kMaxBatch];
   for (int b = 0; b < cfg.batch; ++b) {
     const int held = c->nq[b] + c->nr[b] + c->nsp[b] + add;
     if (held == 0) return fail(KVQ_E_INVALID, "sequence %d is empty", b);
     if (held < n_query)
       return fail(KVQ_E_INVALID, "sequence %d holds %d tokens, fewer than the %d queries", b, held, n_query);
     const int u = units_of(c->nq[b], c->nr[b] + add, has_sinks(c, b));
+    units[b] = u;
     max_units = std::max(max_units, u);
     total_units += int64_t(u) * cfg.n_kv_heads;
   }
-  int chunk;
-  if (n_split > 0) {
+  // 4 or 8 query rows per KV head of a KIVI cache without sinks: both per-record products on the
+  // matrix cores, with a split plan of its own
+  const bool mfma = cfg.method == KVQ_METHOD_KIVI && cfg.n_sink == 0 && (G * n_query == 4 || G * n_query == 8);
+  kvq::SplitPlan plan;
+  memset(&plan, 0, sizeof plan);
+  int chunk = 0, ns;
+  if (mfma) {
+    int cus = 0;
+    if (n_split == 0) {
+      kvq_status dst = check_device(&cus);
+      if (dst != KVQ_OK) return dst;
+    }
+    ns = plan_mfma(units, cfg.batch, cfg.n_kv_heads, n_split, cus, max_auto_splits(&cfg), plan);
+  } else if (n_split > 0) {
     chunk = (max_units + n_split - 1) / n_split;
   } else {
     int cus = 0;
@@ -319,7 +383,7 @@ kvq_status decode_enqueue(kvq_cache* c, const void* q, void* out, int32_t out_fp
     chunk = int((total_units + target - 1) / target);
     chunk = std::max(4, (chunk + 3) / 4 * 4);
   }
-  const int ns = (max_units + chunk - 1) / chunk;
+  if (!mfma) ns = (max_units + chunk - 1) / chunk;
   const size_t need = size_t(cfg.batch) * cfg.n_q_heads * n_query * ns * (cfg.head_dim + 4) * sizeof(float);
   if (ws_bytes < need) return fail(KVQ_E_WORKSPACE, "workspace holds %zu bytes, this call needs %zu", ws_bytes, need);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -360,9 +424,8 @@ kvq_status decode_enqueue(kvq_cache* c, const void* q, void* out, int32_t out_fp
   if (is_kitty(cfg))
     e = kvq::launch_kitty_decode(c->buf, c->L, ds, q, ws, out, s, prof ? c->ev[c->ev_used] : nullptr,
                                  prof ? c->ev[c->ev_used + 1] : nullptr);
-  else if (cfg.method == KVQ_METHOD_KIVI && cfg.n_sink == 0 && (ds.G == 4 || ds.G == 8))
-    // 4 or 8 query rows per KV head: both per-record products on the matrix cores
-    e = kvq::launch_decode_mfma(c->buf, c->L, ds, seq, q, ws, out, k_tok, v_tok, s,
+  else if (mfma)
+    e = kvq::launch_decode_mfma(c->buf, c->L, ds, seq, plan, q, ws, out, k_tok, v_tok, s,
                                 prof ? c->ev[c->ev_used] : nullptr, prof ? c->ev[c->ev_used + 1] : nullptr);
   else
     e = kvq::launch_decode(c->buf, c->L, ds, seq, q, ws, out, k_tok, v_tok, s, prof ? c->ev[c->ev_used] : nullptr,
