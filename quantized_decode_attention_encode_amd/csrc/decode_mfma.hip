@@ -208,9 +208,6 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
       pqf[j][e] = pq[j][e] * key_fold<D, BK>(ks, e);
     }
   }
-  // A rows of q~' past 2 NR and weight columns past NR stay zero
-  for (int x = lane; x < KS * 4 * 16 * 4; x += 64) (&M.qb[0][0][0][0])[x] = 0u;
-  for (int x = NR * (D / 32) * 20 + lane; x < 16 * (D / 32) * 20; x += 64) (&M.wa[0][0][0])[x] = 0u;
   // fold of token t's converted value code: at 2 bits the matrix-core path converts each k-group's
   // 4 + 4 codes from word positions t % 4 (the word shifted by 8 bits for the upper four), else
   // from their own word position
@@ -241,6 +238,33 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
     for (int e = 0; e < E; ++e) stw.acc[i][e] = 0.f;
   }
   __syncthreads();  // sh_prog, sh_simd are set
+  // window units first (their loads wait while the other waves compute records), on the last
+  // waves, which hold the fewest records: the VALU decode's path and state
+  for (int u = max(u0, ngroups) + (kMW - 1 - wave); u < u1; u += kMW) {
+    const int tbase = (u - ngroups) * kGroup;
+    const int nvalid = min(kGroup, nr - tbase);
+    const __half* wk = reinterpret_cast<const __half*>(buf + L.wk_off + L.window(b, h)) + tbase * D;
+    const __half* wv = reinterpret_cast<const __half*>(buf + L.wv_off + L.window(b, h)) + tbase * D;
+    const int tnew = ds.append ? nr_old - tbase : -1;
+    const int64_t tok = (int64_t(b) * L.Hkv + h) * D;
+    const __half* kn = ds.append ? k_app + tok : nullptr;
+    const __half* vn = ds.append ? v_app + tok : nullptr;
+    process_window<D, NR, false>(wk, wv, nvalid, tnew, kn, vn, W, stw, qs, lane, cz, nq + tbase, nullptr);
+    if (tnew >= 0 && tnew < nvalid) {
+      __half* dk = reinterpret_cast<__half*>(bufw + L.wk_off + L.window(b, h)) + nr_old * D;
+      __half* dv = reinterpret_cast<__half*>(bufw + L.wv_off + L.window(b, h)) + nr_old * D;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        dk[lane * E + e] = kn[lane * E + e];
+        dv[lane * E + e] = vn[lane * E + e];
+      }
+    }
+  }
+
+  // A rows of q~' past 2 NR and weight columns past NR stay zero
+  for (int x = lane; x < KS * 4 * 16 * 4; x += 64) (&M.qb[0][0][0][0])[x] = 0u;
+  for (int x = NR * (D / 32) * 20 + lane; x < 16 * (D / 32) * 20; x += 64) (&M.wa[0][0][0])[x] = 0u;
+  wave_sync();
   int partner = -1;  // the other wave of this workgroup on this SIMD, if any
 #pragma unroll
   for (int w = 0; w < kMW; ++w)
@@ -522,28 +546,6 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
     }
     __builtin_amdgcn_s_setprio(0);
   }
-  // window units: the VALU decode's path and state, one per wave in turn
-  for (u = max(u0, ngroups) + wave; u < u1; u += kMW) {
-    const int tbase = (u - ngroups) * kGroup;
-    const int nvalid = min(kGroup, nr - tbase);
-    const __half* wk = reinterpret_cast<const __half*>(buf + L.wk_off + L.window(b, h)) + tbase * D;
-    const __half* wv = reinterpret_cast<const __half*>(buf + L.wv_off + L.window(b, h)) + tbase * D;
-    const int tnew = ds.append ? nr_old - tbase : -1;
-    const int64_t tok = (int64_t(b) * L.Hkv + h) * D;
-    const __half* kn = ds.append ? k_app + tok : nullptr;
-    const __half* vn = ds.append ? v_app + tok : nullptr;
-    process_window<D, NR, false>(wk, wv, nvalid, tnew, kn, vn, W, stw, qs, lane, cz, nq + tbase, nullptr);
-    if (tnew >= 0 && tnew < nvalid) {
-      __half* dk = reinterpret_cast<__half*>(bufw + L.wk_off + L.window(b, h)) + nr_old * D;
-      __half* dv = reinterpret_cast<__half*>(bufw + L.wv_off + L.window(b, h)) + nr_old * D;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        dk[lane * E + e] = kn[lane * E + e];
-        dv[lane * E + e] = vn[lane * E + e];
-      }
-    }
-  }
-
   // ---- finish the wave: both states to LDS as (acc[D], m, l) per row, in output units
   // matrix-core state: l per row summed over its 4 row groups, bias per (row, value group)
   float lt[2];  // l of rows 2 g + j, over the 16 lanes of the row group
