@@ -51,11 +51,27 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 PEAK_FP16_MFMA_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak (no sparsity)
 
-# HBM bytes per decode launch on the long workload (no sinks) from two rocprofv3 --pmc runs
-# (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, factors from a 1 GiB device copy; see
-# profiles/kvq_long_s64k_counters.md), valid only for the decode kernel and split-plan
-# sources they were taken on (their hash).
-MEASURED_TRAFFIC = {"workload": "long", "src_sha256_16": "3b5280eddc918a86", "bytes": 202621370}
+# HBM bytes per decode launch (KIVI, no sinks, default window and splits) from two rocprofv3 --pmc
+# runs (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, factors from a 1 GiB device copy; see
+# profiles/*_counters.md), valid only for the decode kernel and split-plan sources they were
+# taken on (their hash over TRAFFIC_SOURCES).
+MEASURED_TRAFFIC = {}
+TRAFFIC_SOURCES = ("decode_kernel.h", "decode.hip", "decode_mfma.hip", "kvq.cpp")
+
+
+def cache_compression(wl, n_q, n_r):
+    """Bytes per cached token and KV head (a 32-token record: codes and fp16 (scale, zero) per
+    group), and the compression against fp16 keys and values, without and with the fp16 window."""
+    D = wl.head_dim
+    key = (32 * D * wl.key_bits // 8 + 4 * D) / 32  # codes + per-channel (scale, zero) of 32 tokens
+    val = (32 * D * wl.value_bits // 8 + 4 * D) / 32  # codes + per-token (scale, zero) per 32 channels
+    fp16 = 2 * D
+    toks = sum(n_q) + sum(n_r)
+    stored = sum(n_q) * (key + val) + sum(n_r) * 2 * fp16
+    return {"bytes_per_token_key": key, "bytes_per_token_value": val,
+            "key_vs_fp16": round(fp16 / key, 3), "kv_vs_fp16": round(2 * fp16 / (key + val), 3),
+            "kv_vs_fp16_with_window": round(toks * 2 * fp16 / stored, 3),
+            "pages": "KIVI-2bit: about 5.8x key, 4x full KV (Changelog v0.8.0)"}
 
 
 def kitty_record_bytes(D, n_hi):
@@ -250,7 +266,7 @@ def main():
         torch.cuda.synchronize()
         enc_ms.append(e0.elapsed_time(e1))
     enc_t = statistics.median(enc_ms) / 1e3
-    n_q0 = list(caches[0].lengths()[0])
+    n_q0, n_r0 = (list(x) for x in caches[0].lengths())
     enc_tokens_per_s = sum(lens) / enc_t
     enc_gbs = algorithmic_encode_bytes(wl, n_q0, args.n_sink, kitty_n_hi) / enc_t / 1e9
 
@@ -381,16 +397,24 @@ def main():
 
     traffic = None
     csrc = os.path.join(ROOT, "quantized_decode_attention_encode_amd", "csrc")
-    if (args.workload == MEASURED_TRAFFIC["workload"] and args.n_split == 0 and args.n_sink == 0
-            and args.method == "kivi" and R == wl.residual and NQ == 1):
+    measured = MEASURED_TRAFFIC.get(args.workload)
+    if (measured and args.n_split == 0 and args.n_sink == 0 and args.method == "kivi" and R == wl.residual
+            and NQ == 1):
         import hashlib
 
         h = hashlib.sha256()
-        for name in ("decode_kernel.h", "decode.hip", "kvq.cpp"):  # the kernel and the host's split plan
+        for name in TRAFFIC_SOURCES:  # the decode kernels and the host's split plan
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(f.read())
-        if h.hexdigest()[:16] == MEASURED_TRAFFIC["src_sha256_16"]:
-            traffic = MEASURED_TRAFFIC["bytes"]
+        if h.hexdigest()[:16] == measured["src_sha256_16"]:
+            traffic = measured["bytes"]
+    G = wl.n_q_heads // wl.n_kv_heads
+    if kitty_n_hi is not None:
+        decode_kernel = "kitty_decode_kernel"
+    elif args.method == "kivi" and args.n_sink == 0 and G * NQ in (4, 8):
+        decode_kernel = "decode_mfma_kernel"
+    else:
+        decode_kernel = "decode_split_kernel"
 
     result = {
         "metric": "decode-attend us/step + achieved HBM GB/s (% peak) at S_kv=64K; encode tokens/s",
@@ -431,7 +455,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
-            "kernel": "decode_split_kernel" if kitty_n_hi is None else "kitty_decode_kernel",
+            "kernel": decode_kernel,
             "kernel_avg_us": round(split_avg_ms * 1e3, 3),
             "algorithmic_bytes_per_launch": int(alg_bytes),
         } if not tiles else {
@@ -447,6 +471,8 @@ def main():
             "hbm": {"achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(achieved / PEAK_HBM_GBS, 4), "algorithmic_bytes_per_launch": int(alg_bytes)},
         },
+        "cache_compression": (cache_compression(wl, n_q0, n_r0) if kitty_n_hi is None and args.method == "kivi"
+                              else None),
         "decode_split_us": round(split_avg_ms * 1e3, 3),
         "decode_gbps": round(achieved, 1),
         "decode_frac_of_copy_bw": round(achieved / copy_gbs, 4),

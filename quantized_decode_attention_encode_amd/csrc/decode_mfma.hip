@@ -31,12 +31,17 @@ typedef float f4m __attribute__((ext_vector_type(4)));
 // LDS of one wave, on top of the VALU decode's (used by the window units and the weights).
 template <int D, int NR, int BV>
 struct MfmaLds {
-  uint32_t qb[D / 32][4][16][4];  // key B fragments [k-step][k-group][column][4 dwords of fp16 pairs]
+  // q~' A fragments [k-step][k-group][row (17: padding)][4 dwords of fp16 pairs]: a producer lane
+  // writes row 2 i + h of its own (k-step, k-group), so (k-step, k-group) blocks 68 dwords apart
+  // (4 mod 32) put 8 consecutive lanes' 16-byte writes on distinct banks
+  uint32_t qb[D / 32][4][17][4];
   float beta[NR];                 // per row: q . z minus the fold constant, this record
   float pbuf[NR][32 + 4];         // softmax weights of the record per row (token order)
   uint32_t vcs[D][BV];            // the record's value codes [channel][words]
-  uint32_t wa[16][D / 32][16 + 4];  // fp16 value weights [B column = row][value group][token pairs];
-                                    // rows past NR stay zero
+  // fp16 value weights, row r (B column) at r * kWaRow: [value group][token pairs] (20 dwords
+  // each), rows padded to an odd multiple of 4 dwords so 8 consecutive columns' 16-byte reads
+  // fall on distinct banks
+  uint32_t wa[16 * (D / 32 * 20 + 4)];  // rows past NR stay zero
 };
 
 // Maximum over the 16 lanes of a row, in every lane.
@@ -123,6 +128,7 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
   using MK = Magic<BK>;
   using MV = Magic<BV>;
   constexpr int NCOMBO = NR * KS * 4;               // key producer combos per record
+  constexpr int kWaRow = D / 32 * 20 + 4;           // dwords per weight row in LDS
   constexpr int PL = (NCOMBO + 63) / 64;            // combos per lane
   static_assert(NR == 4 || NR == 8, "4 or 8 query rows per KV head");
 
@@ -262,8 +268,8 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
   }
 
   // A rows of q~' past 2 NR and weight columns past NR stay zero
-  for (int x = lane; x < KS * 4 * 16 * 4; x += 64) (&M.qb[0][0][0][0])[x] = 0u;
-  for (int x = NR * (D / 32) * 20 + lane; x < 16 * (D / 32) * 20; x += 64) (&M.wa[0][0][0])[x] = 0u;
+  for (int x = lane; x < KS * 4 * 17 * 4; x += 64) (&M.qb[0][0][0][0])[x] = 0u;
+  for (int x = NR * kWaRow + lane; x < 16 * kWaRow; x += 64) M.wa[x] = 0u;
   wave_sync();
   int partner = -1;  // the other wave of this workgroup on this SIMD, if any
 #pragma unroll
@@ -438,7 +444,7 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
         const __half a16 = __float2half_rn((pv * (tp ? vw1 : vw0)) * lo_f(cur.vp[e]));
         br = __builtin_fmaf(-__half2float(a16), amul, __builtin_fmaf(pv * kVScale, hi_f(cur.vp[e]), br));
         const int dw = (t / MV::NC) * MV::NH + (t % MV::NC) % MV::NH, hf = (t % MV::NC) / MV::NH;
-        reinterpret_cast<__half*>(&M.wa[i][k][dw])[hf] = a16;
+        reinterpret_cast<__half*>(&M.wa[i * kWaRow + k * 20 + dw])[hf] = a16;
       }
       bias[i] += br;
     }
@@ -452,7 +458,7 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
     }
 #pragma unroll
     for (int k = 0; k < NKG; ++k) {
-      const h8m bw = __builtin_bit_cast(h8m, *reinterpret_cast<const uint4*>(&M.wa[col][k][4 * g]));
+      const h8m bw = __builtin_bit_cast(h8m, *reinterpret_cast<const uint4*>(&M.wa[col * kWaRow + k * 20 + 4 * g]));
 #pragma unroll
       for (int mh = 0; mh < 2; ++mh) {
         const int mt = 2 * k + mh;
