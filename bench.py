@@ -55,7 +55,11 @@ PEAK_FP16_MFMA_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak (no sparsity)
 # runs (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, factors from a 1 GiB device copy; see
 # profiles/*_counters.md), valid only for the decode kernel and split-plan sources they were
 # taken on (their hash over TRAFFIC_SOURCES).
-MEASURED_TRAFFIC = {}
+MEASURED_TRAFFIC = {
+    "long": {"src_sha256_16": "36cee3dfd97710b4", "bytes": 202587643},
+    "gqa": {"src_sha256_16": "36cee3dfd97710b4", "bytes": 131891645},
+    "full32": {"src_sha256_16": "36cee3dfd97710b4", "bytes": 203950590},
+}
 TRAFFIC_SOURCES = ("decode_kernel.h", "decode.hip", "decode_mfma.hip", "kvq.cpp")
 
 
