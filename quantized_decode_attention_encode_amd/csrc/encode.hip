@@ -41,7 +41,8 @@ template <int D, int BK, int BV>
 struct EncodeLds {
   static constexpr int kRecWords = D * (BK + BV + 2);
   uint32_t rec[kRecWords];       // record image
-  uint8_t vbytes[D * kGroup];    // value codes, one byte each, [d][t]
+  // value codes one byte each, [d][t]: only where a word holds fewer tokens than one load's rows
+  uint8_t vbytes[64 / (D / 8) > 32 / BV ? D * kGroup : 4];
   float2 kpar[D];                // (lo, inv) of each channel's key group
 };
 
@@ -249,33 +250,94 @@ __device__ __forceinline__ void encode_record(const __half* __restrict__ ks, con
     const int t = r + RPI * (q * NQ + j);
     lds.rec[VP_W + ((t >> 1) * NKG + c8 / 4) * 2 + (t & 1)] = g.packed | (((sink_mask >> t) & 1u) << 15);
   }
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int t = r + RPI * i;
+  // Row i's parameters live in quad lane i / NQ, slot i % NQ.
+  auto value_params = [&](int i) {
     GroupParams vp;
-    // row i's parameters live in quad lane i / NQ, slot i % NQ
     switch (i / NQ) {
       case 0: vp.lo = dpp_quad_bcast<0>(own_lo[i % NQ]); vp.inv = dpp_quad_bcast<0>(own_inv[i % NQ]); break;
       case 1: vp.lo = dpp_quad_bcast<1>(own_lo[i % NQ]); vp.inv = dpp_quad_bcast<1>(own_inv[i % NQ]); break;
       case 2: vp.lo = dpp_quad_bcast<2>(own_lo[i % NQ]); vp.inv = dpp_quad_bcast<2>(own_inv[i % NQ]); break;
       default: vp.lo = dpp_quad_bcast<3>(own_lo[i % NQ]); vp.inv = dpp_quad_bcast<3>(own_inv[i % NQ]); break;
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) lds.vbytes[(8 * c8 + e) * kGroup + t] = uint8_t(code_of<BV>(vx[i][e], vp));
-  }
-  __syncthreads();
+    return vp;
+  };
 
-  // ---- pack value codes: word w = (channel d, sub-word sw), tokens sw*32/BV .. at bit t*BV
+  // ---- value codes: word (channel d, sub-word sw) holds tokens sw*PER_WORD .. at bit t*BV
   constexpr int PER_WORD = 32 / BV;
-  for (int w = lane; w < D * BV; w += 64) {
-    const int d = w / BV, sw = w % BV;
-    const uint8_t* src = &lds.vbytes[d * kGroup + sw * PER_WORD];
-    uint32_t word = 0;
+  if constexpr (RPI <= PER_WORD) {
+    // In registers. The lane's 8 channels own T = 8*BV consecutive words of the record, and
+    // every one of them takes codes from the RPI lanes of the chunk column (lanes c8 + CH*r):
+    // the lane places its own codes at their final bits (token t = r + RPI*i sits at bit
+    // BV*(r + RPI*(i % CPW)) of sub-word i / CPW), then halving exchanges across the column
+    // (lane distance 32, 16, then 8) OR the words together while each lane keeps half of
+    // what is left, until lane r holds the M complete words T/RPI*r .. and stores them.
+    constexpr int CPW = PER_WORD / RPI;  // codes of one lane in a word
+    constexpr int T = 8 * BV;
+    constexpr int M = T / RPI;
+    uint32_t wd[T];
 #pragma unroll
-    for (int n = 0; n < PER_WORD; ++n) word |= uint32_t(src[n]) << (n * BV);
-    lds.rec[VC_W + w] = word;
+    for (int j = 0; j < T; ++j) wd[j] = 0;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const GroupParams vp = value_params(i);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        wd[e * BV + i / CPW] |= code_of<BV>(vx[i][e], vp) << ((32 / CPW) * (i % CPW));
+    }
+#pragma unroll
+    for (int j = 0; j < T; ++j) wd[j] <<= BV * r;
+    // lane bit 5 (lanes 32..63 keep the upper half of the words)
+#pragma unroll
+    for (int k = 0; k < T / 2; ++k) {
+      const auto x = __builtin_amdgcn_permlane32_swap(wd[k], wd[k + T / 2], false, false);
+      wd[k] = x[0] | x[1];
+    }
+    // lane bit 4 (odd rows of 16 lanes keep the upper half)
+#pragma unroll
+    for (int k = 0; k < T / 4; ++k) {
+      const auto x = __builtin_amdgcn_permlane16_swap(wd[k], wd[k + T / 4], false, false);
+      wd[k] = x[0] | x[1];
+    }
+    if constexpr (RPI == 8) {  // lane bit 3 (lanes 8..15 of each row keep the upper half)
+      const bool up = (lane >> 3) & 1;
+#pragma unroll
+      for (int k = 0; k < M; ++k) {
+        const uint32_t send = up ? wd[k] : wd[k + M];
+        const uint32_t keep = up ? wd[k + M] : wd[k];
+        wd[k] = keep | uint32_t(__builtin_amdgcn_mov_dpp(int(send), 0x128, 0xF, 0xF, false));  // row_ror 8
+      }
+    }
+    uint32_t* dst = &lds.rec[VC_W + T * c8 + M * r];
+    if constexpr (M % 4 == 0) {
+#pragma unroll
+      for (int k = 0; k < M; k += 4)
+        *reinterpret_cast<uint4*>(dst + k) = make_uint4(wd[k], wd[k + 1], wd[k + 2], wd[k + 3]);
+    } else {
+      static_assert(M == 2, "two words per lane");
+      *reinterpret_cast<uint2*>(dst) = make_uint2(wd[0], wd[1]);
+    }
+    __syncthreads();
+  } else {
+    // Fewer tokens per word than rows per load (D = 64, 8-bit values): one byte per code
+    // in LDS, then one lane per word gathers them.
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int t = r + RPI * i;
+      const GroupParams vp = value_params(i);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lds.vbytes[(8 * c8 + e) * kGroup + t] = uint8_t(code_of<BV>(vx[i][e], vp));
+    }
+    __syncthreads();
+    for (int w = lane; w < D * BV; w += 64) {
+      const int d = w / BV, sw = w % BV;
+      const uint8_t* src = &lds.vbytes[d * kGroup + sw * PER_WORD];
+      uint32_t word = 0;
+#pragma unroll
+      for (int n = 0; n < PER_WORD; ++n) word |= uint32_t(src[n]) << (n * BV);
+      lds.rec[VC_W + w] = word;
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   // ---- copy the record out, 16 bytes per lane per step
   constexpr int NV4 = EncodeLds<D, BK, BV>::kRecWords / 4;
