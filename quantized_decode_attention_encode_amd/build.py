@@ -24,8 +24,9 @@ COMMON = [
     f"-I{os.path.join(HERE, '..', 'include')}",
 ]
 PER_FILE = {
-    # bit-exact quantizer: one rounding per fp32 operation
-    "encode.hip": ["-ffp-contract=off"],
+    # bit-exact quantizer: one rounding per fp32 operation; no NaN inputs assumed (min / max
+    # need no canonicalizing step and fuse with their DPP lane moves)
+    "encode.hip": ["-ffp-contract=off", "-fno-honor-nans"],
     "decode.hip": [],
     "decode_sink.hip": [],
     "decode_skvq.hip": [],

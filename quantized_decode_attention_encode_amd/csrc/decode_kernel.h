@@ -126,13 +126,28 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
   return r;
 }
 
-template <int N>
+// Non-temporal loads (streaming cache policy) for record words that are read once per step.
+typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_nt __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 load_nt4(const uint32_t* p) {
+  const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// N words from p; NT: with the non-temporal policy.
+template <int N, bool NT = false>
 __device__ __forceinline__ void load_words(const uint32_t* __restrict__ p, uint32_t* out) {
   if constexpr (N % 4 == 0) {
 #pragma unroll
     for (int i = 0; i < N / 4; ++i) {
-      const uint4 v = reinterpret_cast<const uint4*>(p)[i];
+      const uint4 v = NT ? load_nt4(p + 4 * i) : reinterpret_cast<const uint4*>(p)[i];
       out[4 * i] = v.x; out[4 * i + 1] = v.y; out[4 * i + 2] = v.z; out[4 * i + 3] = v.w;
+    }
+  } else if constexpr (N % 2 == 0 && NT) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const u32x2_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_nt*>(p) + i);
+      out[2 * i] = v[0]; out[2 * i + 1] = v[1];
     }
   } else if constexpr (N % 2 == 0) {
 #pragma unroll
@@ -142,7 +157,7 @@ __device__ __forceinline__ void load_words(const uint32_t* __restrict__ p, uint3
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < N; ++i) out[i] = p[i];
+    for (int i = 0; i < N; ++i) out[i] = NT ? __builtin_nontemporal_load(p + i) : p[i];
   }
 }
 

@@ -285,23 +285,25 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
     uint32_t vc[E * BV];       // value codes of channels lane * E ..
     uint32_t vp[E];            // value params (the VALU decode's producer entries)
   };
+  // Records are read once per step: non-temporal loads (streaming cache policy), which stream
+  // them in at a higher rate here than the default policy.
   auto load = [&](int u, Regs& r) {
     const uint8_t* rec = rec0 + uint64_t(u) * rb;
-    load_words<2 * WQ>(reinterpret_cast<const uint32_t*>(rec) + (4 * col + g) * 2 * WQ, r.kc);
+    load_words<2 * WQ, true>(reinterpret_cast<const uint32_t*>(rec) + (4 * col + g) * 2 * WQ, r.kc);
 #pragma unroll
     for (int j = 0; j < PL; ++j) {
       // the 8 channels are two runs of 4 consecutive ones: two 16-byte loads
       const int c = min(lane + 64 * j, NCOMBO - 1);
       const int ks = KeyCombo<D, BK>::ks(c), gg = KeyCombo<D, BK>::g(c);
       const uint32_t* kpg = reinterpret_cast<const uint32_t*>(rec + rec_off_kparams(D, BK, BV));
-      const uint4 r0 = *reinterpret_cast<const uint4*>(kpg + key_channel<D, BK>(ks, gg, 0));
-      const uint4 r1 = *reinterpret_cast<const uint4*>(kpg + key_channel<D, BK>(ks, gg, BK == 8 ? 4 : 1));
+      const uint4 r0 = load_nt4(kpg + key_channel<D, BK>(ks, gg, 0));
+      const uint4 r1 = load_nt4(kpg + key_channel<D, BK>(ks, gg, BK == 8 ? 4 : 1));
       const uint32_t w8[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) r.kp[j][e] = w8[key_param_slot<BK>(e)];
     }
-    load_words<E * BV>(reinterpret_cast<const uint32_t*>(rec + rec_off_vcodes(D, BK)) + lane * E * BV, r.vc);
-    load_words<E>(reinterpret_cast<const uint32_t*>(rec + rec_off_vparams(D, BK, BV)) + lane * E, r.vp);
+    load_words<E * BV, true>(reinterpret_cast<const uint32_t*>(rec + rec_off_vcodes(D, BK)) + lane * E * BV, r.vc);
+    load_words<E, true>(reinterpret_cast<const uint32_t*>(rec + rec_off_vparams(D, BK, BV)) + lane * E, r.vp);
   };
 
   auto process = [&](const Regs& cur, int tok0) {

@@ -58,25 +58,78 @@ __device__ __forceinline__ float dpp_quad_bcast(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), Q | (Q << 2) | (Q << 4) | (Q << 6), 0xF, 0xF, false));
 }
 
-// Min and max over the lanes that hold the same 8 channels of a row-major tile with CH
-// 16-byte chunks per row: lanes l, l ^ CH, l ^ 2 CH, ... (CH = 8: first the other half of
-// the 16-lane row by DPP row_ror 8); then the gfx950 row swaps: with both operands equal,
-// permlane16_swap returns rows (0,0,2,2) / (1,1,3,3) and permlane32_swap rows (0,1,0,1) /
-// (2,3,2,3), lane positions within a row kept. Min and max do not care which is which.
+// 16 bytes of a row that is read once: a non-temporal load (streaming cache policy), which
+// streams the K and V rows in at a higher rate than the default policy.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4 load_streaming(const __half* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// Packed fp16 pairs: the min / max of two fp16 values is one of them, so taking it in fp16
+// gives the same value as in fp32.
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_min(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(half2v, a), __builtin_bit_cast(half2v, b)));
+}
+__device__ __forceinline__ uint32_t pk_max(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(half2v, a), __builtin_bit_cast(half2v, b)));
+}
+template <int HI>
+__device__ __forceinline__ float half_of(uint32_t w) {
+  return __half2float(__ushort_as_half(uint16_t(HI ? w >> 16 : w & 0xFFFFu)));
+}
+
+// Min and max (of fp16 pairs) over the lanes that hold the same 8 channels of a row-major
+// tile with CH 16-byte chunks per row: lanes l, l ^ CH, l ^ 2 CH, ... (CH = 8: first the other
+// half of the 16-lane row by DPP row_ror 8); then the gfx950 row swaps: with both operands
+// equal, permlane16_swap returns rows (0,0,2,2) / (1,1,3,3) and permlane32_swap rows
+// (0,1,0,1) / (2,3,2,3), lane positions within a row kept. Min and max do not care which is which.
 template <int CH>
-__device__ __forceinline__ void column_minmax(float& mn, float& mx) {
+__device__ __forceinline__ void column_minmax(uint32_t& mn, uint32_t& mx) {
   if constexpr (CH == 8) {
-    mn = fminf(mn, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0x128, 0xF, 0xF, false)));
-    mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0x128, 0xF, 0xF, false)));
+    mn = pk_min(mn, uint32_t(__builtin_amdgcn_mov_dpp(int(mn), 0x128, 0xF, 0xF, false)));
+    mx = pk_max(mx, uint32_t(__builtin_amdgcn_mov_dpp(int(mx), 0x128, 0xF, 0xF, false)));
   }
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-  mn = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  mx = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
-  const auto d = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-  mn = fminf(__uint_as_float(c[0]), __uint_as_float(c[1]));
-  mx = fmaxf(__uint_as_float(d[0]), __uint_as_float(d[1]));
+  const auto a = __builtin_amdgcn_permlane16_swap(mn, mn, false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(mx, mx, false, false);
+  mn = pk_min(a[0], a[1]);
+  mx = pk_max(b[0], b[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(mn, mn, false, false);
+  const auto d = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
+  mn = pk_min(c[0], c[1]);
+  mx = pk_max(d[0], d[1]);
+}
+
+// The quantization code of x, the fp16 in half HI of w, as the bits of an fp32 in
+// [1.5 * 2^23, 1.5 * 2^23 + L]: kCodeBias + clamp(rint((x - lo) * inv), 0, L).
+//  * x - lo is one fma-mix (fp16 x times 1, plus -lo): a single rounding of the exact
+//    difference, the same fp32 value as converting x and subtracting;
+//  * adding 1.5 * 2^23 to t = (x - lo) * inv leaves an fp32 of unit spacing wherever
+//    |t| < 2^22, so its rounding is rint's (to nearest, ties to even) and its bits are
+//    kCodeBias + rint(t); further out the clamp decides alone, and fp32 bits read as signed
+//    integers are ordered like the values, so the clamp is an integer median on the bits.
+// The low 22 bits of kCodeBias are clear: the code sits alone in the low byte, and a code
+// shifted left by s bits keeps the bias at bit 22 + s and up.
+constexpr int32_t kCodeBias = 0x4B400000;  // 1.5 * 2^23
+template <int B, int HI>
+__device__ __forceinline__ uint32_t biased_code(uint32_t w, float lo, float inv) {
+  float d;
+  if constexpr (HI)
+    asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(lo));
+  else
+    asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(lo));
+  const float t = d * inv;
+  const int32_t b = __float_as_int(t + 12582912.0f);
+  return uint32_t(min(max(b, kCodeBias), kCodeBias + (1 << B) - 1));
+}
+template <int B>
+__device__ __forceinline__ uint32_t biased_code(uint32_t w, int hi, float lo, float inv) {
+  return hi ? biased_code<B, 1>(w, lo, inv) : biased_code<B, 0>(w, lo, inv);
+}
+// Low bytes of four words, b0 in byte 0 (v_perm_b32 selectors: 0-3 bytes of the second
+// operand, 4-7 of the first, 12 a zero byte).
+__device__ __forceinline__ uint32_t low_bytes(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+  return __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u) | __builtin_amdgcn_perm(b3, b2, 0x04000c0cu);
 }
 
 // v[sel] for a lane-dependent sel < N (N a power of two) as a tree of selects on the bits of
@@ -117,20 +170,16 @@ __device__ __forceinline__ void encode_record(const __half* __restrict__ ks, con
   const int lane = threadIdx.x & 63;
   const int c8 = lane % CH, r = lane / CH;
 
-  float kx[NI][8], vx[NI][8];
+  uint32_t kw[NI][4], vw[NI][4];  // fp16 pairs: channels 8*c8 + 2w, + 1 of token r + RPI*i
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int t = r + RPI * i;
-    const uint4 kr = *reinterpret_cast<const uint4*>(ks + t * D + 8 * c8);
-    const uint4 vr = *reinterpret_cast<const uint4*>(vs + t * D + 8 * c8);
-    const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w};
-    const uint32_t vw[4] = {vr.x, vr.y, vr.z, vr.w};
+    const u32x4 kr = load_streaming(ks + t * D + 8 * c8);
+    const u32x4 vr = load_streaming(vs + t * D + 8 * c8);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      kx[i][2 * e] = __half2float(__ushort_as_half(uint16_t(kw[e] & 0xFFFF)));
-      kx[i][2 * e + 1] = __half2float(__ushort_as_half(uint16_t(kw[e] >> 16)));
-      vx[i][2 * e] = __half2float(__ushort_as_half(uint16_t(vw[e] & 0xFFFF)));
-      vx[i][2 * e + 1] = __half2float(__ushort_as_half(uint16_t(vw[e] >> 16)));
+    for (int w = 0; w < 4; ++w) {
+      kw[i][w] = kr[w];
+      vw[i][w] = vr[w];
     }
   }
 
@@ -139,32 +188,39 @@ __device__ __forceinline__ void encode_record(const __half* __restrict__ ks, con
   // parameters of 8/RPI of its channels, and they meet in LDS.
   constexpr int EK = 8 / RPI;  // key groups whose parameters this lane computes
   float kmn[8], kmx[8];
-  if (sink_mask == 0) {
+  {
+    uint32_t mn2[4], mx2[4];
+    if (sink_mask == 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float mn = kx[0][e], mx = kx[0][e];
+      for (int w = 0; w < 4; ++w) {
+        mn2[w] = kw[0][w];
+        mx2[w] = kw[0][w];
 #pragma unroll
-      for (int i = 1; i < NI; ++i) {
-        mn = fminf(mn, kx[i][e]);
-        mx = fmaxf(mx, kx[i][e]);
+        for (int i = 1; i < NI; ++i) {
+          mn2[w] = pk_min(mn2[w], kw[i][w]);
+          mx2[w] = pk_max(mx2[w], kw[i][w]);
+        }
       }
-      column_minmax<CH>(mn, mx);
-      kmn[e] = mn;
-      kmx[e] = mx;
+    } else {  // sinks stay out of the min/max (every group keeps at least 32 - 16 tokens)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        mn2[w] = 0x7C007C00u;  // +inf, +inf
+        mx2[w] = 0xFC00FC00u;  // -inf, -inf
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const bool skip = (sink_mask >> (r + RPI * i)) & 1u;
+          mn2[w] = pk_min(mn2[w], skip ? 0x7C007C00u : kw[i][w]);
+          mx2[w] = pk_max(mx2[w], skip ? 0xFC00FC00u : kw[i][w]);
+        }
+      }
     }
-  } else {  // sinks stay out of the min/max (every group keeps at least 32 - 16 tokens)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const bool skip = (sink_mask >> (r + RPI * i)) & 1u;
-        mn = fminf(mn, skip ? INFINITY : kx[i][e]);
-        mx = fmaxf(mx, skip ? -INFINITY : kx[i][e]);
-      }
-      column_minmax<CH>(mn, mx);
-      kmn[e] = mn;
-      kmx[e] = mx;
+    for (int w = 0; w < 4; ++w) {
+      column_minmax<CH>(mn2[w], mx2[w]);
+      kmn[2 * w] = half_of<0>(mn2[w]);
+      kmn[2 * w + 1] = half_of<1>(mn2[w]);
+      kmx[2 * w] = half_of<0>(mx2[w]);
+      kmx[2 * w + 1] = half_of<1>(mx2[w]);
     }
   }
 #pragma unroll
@@ -197,19 +253,25 @@ __device__ __forceinline__ void encode_record(const __half* __restrict__ ks, con
     for (int i = 0; i < NI; ++i) {
       const int t = r + RPI * i;
       const int P = t >> 1, tp = t & 1;
-      uint64_t piece = 0;
+      uint32_t c[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) piece |= uint64_t(code_of<BK>(kx[i][e], kp[e])) << (e * BK);
+      for (int e = 0; e < 8; ++e) c[e] = biased_code<BK>(kw[i][e >> 1], e & 1, kp[e].lo, kp[e].inv);
       const uint32_t word = KC_W + ((P * 4 + Q) * 2 + tp) * WQ + (cq * BK) / 32;
       const int bit = (cq * BK) % 32;
       uint8_t* base = reinterpret_cast<uint8_t*>(&lds.rec[word]) + bit / 8;
-      if constexpr (BK == 2) {
+      if constexpr (BK == 2) {  // the bias stays above the 16 bits kept
+        uint32_t piece = c[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) piece |= c[e] << (2 * e);
         *reinterpret_cast<uint16_t*>(base) = uint16_t(piece);
-      } else if constexpr (BK == 4) {
-        *reinterpret_cast<uint32_t*>(base) = uint32_t(piece);
+      } else if constexpr (BK == 4) {  // code pairs in the low byte, then the four bytes
+        uint32_t pr[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) pr[k] = c[2 * k] | (c[2 * k + 1] << 4);
+        *reinterpret_cast<uint32_t*>(base) = low_bytes(pr[0], pr[1], pr[2], pr[3]);
       } else {
-        reinterpret_cast<uint32_t*>(base)[0] = uint32_t(piece);
-        reinterpret_cast<uint32_t*>(base)[1] = uint32_t(piece >> 32);
+        reinterpret_cast<uint32_t*>(base)[0] = low_bytes(c[0], c[1], c[2], c[3]);
+        reinterpret_cast<uint32_t*>(base)[1] = low_bytes(c[4], c[5], c[6], c[7]);
       }
     }
   }
@@ -222,12 +284,10 @@ __device__ __forceinline__ void encode_record(const __half* __restrict__ ks, con
   float vmn[NI], vmx[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    float mn = vx[i][0], mx = vx[i][0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) {
-      mn = fminf(mn, vx[i][e]);
-      mx = fmaxf(mx, vx[i][e]);
-    }
+    const uint32_t mn2 = pk_min(pk_min(vw[i][0], vw[i][1]), pk_min(vw[i][2], vw[i][3]));
+    const uint32_t mx2 = pk_max(pk_max(vw[i][0], vw[i][1]), pk_max(vw[i][2], vw[i][3]));
+    float mn = fminf(half_of<0>(mn2), half_of<1>(mn2));
+    float mx = fmaxf(half_of<0>(mx2), half_of<1>(mx2));
     mn = fminf(mn, dpp_xor1(mn));
     mx = fmaxf(mx, dpp_xor1(mx));
     mn = fminf(mn, dpp_xor2(mn));
@@ -274,18 +334,26 @@ __device__ __forceinline__ void encode_record(const __half* __restrict__ ks, con
     constexpr int CPW = PER_WORD / RPI;  // codes of one lane in a word
     constexpr int T = 8 * BV;
     constexpr int M = T / RPI;
-    uint32_t wd[T];
-#pragma unroll
-    for (int j = 0; j < T; ++j) wd[j] = 0;
+    uint32_t cd[NI][8];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const GroupParams vp = value_params(i);
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        wd[e * BV + i / CPW] |= code_of<BV>(vx[i][e], vp) << ((32 / CPW) * (i % CPW));
+      for (int e = 0; e < 8; ++e) cd[i][e] = biased_code<BV>(vw[i][e >> 1], e & 1, vp.lo, vp.inv);
     }
+    uint32_t wd[T];
 #pragma unroll
-    for (int j = 0; j < T; ++j) wd[j] <<= BV * r;
+    for (int e = 0; e < 8; ++e) {
+#pragma unroll
+      for (int sw = 0; sw < BV; ++sw) {
+        const int i0 = sw * CPW;
+        uint32_t x;
+        if constexpr (CPW == 4) x = low_bytes(cd[i0][e], cd[i0 + 1][e], cd[i0 + 2][e], cd[i0 + 3][e]);
+        else if constexpr (CPW == 2) x = __builtin_amdgcn_perm(cd[i0 + 1][e], cd[i0][e], 0x0c040c00u);
+        else x = cd[i0][e] & 0xFFu;
+        wd[e * BV + sw] = x << (BV * r);
+      }
+    }
     // lane bit 5 (lanes 32..63 keep the upper half of the words)
 #pragma unroll
     for (int k = 0; k < T / 2; ++k) {
@@ -325,7 +393,8 @@ __device__ __forceinline__ void encode_record(const __half* __restrict__ ks, con
       const int t = r + RPI * i;
       const GroupParams vp = value_params(i);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) lds.vbytes[(8 * c8 + e) * kGroup + t] = uint8_t(code_of<BV>(vx[i][e], vp));
+      for (int e = 0; e < 8; ++e)
+        lds.vbytes[(8 * c8 + e) * kGroup + t] = uint8_t(biased_code<BV>(vw[i][e >> 1], e & 1, vp.lo, vp.inv));
     }
     __syncthreads();
     for (int w = lane; w < D * BV; w += 64) {
