@@ -150,8 +150,17 @@ __device__ __forceinline__ float pick(const float (&v)[N], int sel) {
   return level[0];
 }
 
+// LDS hand-off between the lanes of one wave: a wave's LDS accesses are performed in the
+// order it issues them, so keeping the compiler from moving them across this point is all
+// the ordering a single-wave exchange needs.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Quantize the 32-token tile (rows ks[0..31], vs[0..31], row stride D elements) into the
-// record at `rec_out`. Called by all 64 lanes of a single-wave workgroup. Bit t of
+// record at `rec_out`. Called by all 64 lanes of one wave, which owns `lds`. Bit t of
 // sink_mask (wave-uniform) marks token t as a sink.
 template <int D, int BK, int BV>
 __device__ __forceinline__ void encode_record(const __half* __restrict__ ks, const __half* __restrict__ vs,
@@ -236,7 +245,7 @@ __device__ __forceinline__ void encode_record(const __half* __restrict__ ks, con
     lds.kpar[ch] = make_float2(g.lo, g.inv);
     lds.rec[KP_W + ch] = g.packed;
   }
-  __syncthreads();
+  wave_lds_sync();
   GroupParams kp[8];
 #pragma unroll
   for (int e = 0; e < 8; e += 2) {
@@ -384,7 +393,7 @@ __device__ __forceinline__ void encode_record(const __half* __restrict__ ks, con
       static_assert(M == 2, "two words per lane");
       *reinterpret_cast<uint2*>(dst) = make_uint2(wd[0], wd[1]);
     }
-    __syncthreads();
+    wave_lds_sync();
   } else {
     // Fewer tokens per word than rows per load (D = 64, 8-bit values): one byte per code
     // in LDS, then one lane per word gathers them.
@@ -396,7 +405,7 @@ __device__ __forceinline__ void encode_record(const __half* __restrict__ ks, con
       for (int e = 0; e < 8; ++e)
         lds.vbytes[(8 * c8 + e) * kGroup + t] = uint8_t(biased_code<BV>(vw[i][e >> 1], e & 1, vp.lo, vp.inv));
     }
-    __syncthreads();
+    wave_lds_sync();
     for (int w = lane; w < D * BV; w += 64) {
       const int d = w / BV, sw = w % BV;
       const uint8_t* src = &lds.vbytes[d * kGroup + sw * PER_WORD];
@@ -405,7 +414,7 @@ __device__ __forceinline__ void encode_record(const __half* __restrict__ ks, con
       for (int n = 0; n < PER_WORD; ++n) word |= uint32_t(src[n]) << (n * BV);
       lds.rec[VC_W + w] = word;
     }
-    __syncthreads();
+    wave_lds_sync();
   }
 
   // ---- copy the record out, 16 bytes per lane per step
@@ -413,7 +422,7 @@ __device__ __forceinline__ void encode_record(const __half* __restrict__ ks, con
   const uint4* src4 = reinterpret_cast<const uint4*>(lds.rec);
   uint4* dst4 = reinterpret_cast<uint4*>(rec_out);
   for (int v = lane; v < NV4; v += 64) dst4[v] = src4[v];
-  __syncthreads();
+  wave_lds_sync();
 }
 
 // ------------------------------------------------------------------------------------
@@ -648,15 +657,19 @@ __global__ __launch_bounds__(128) void skvq_perm_kernel(uint8_t* __restrict__ bu
   range_permutation<D>(V + row0, L.R, rng, pm + D, threadIdx.x, blockDim.x, L.reorder);
 }
 
-// Prefill / encode: record (j0[b] + blockIdx.x) of (b = blockIdx.z, h = blockIdx.y) from
-// tokens 32*blockIdx.x .. of the caller's K, V [B][H_kv][ld_tok][D].
+// Prefill / encode: wave w of workgroup x quantizes record j0[b] + jl, jl = kEncodeWaves*x + w,
+// of (b = blockIdx.z, h = blockIdx.y) from tokens 32*jl .. of the caller's K, V
+// [B][H_kv][ld_tok][D]. The waves of a workgroup share nothing.
+constexpr int kEncodeWaves = 2;
 template <int D, int BK, int BV>
-__global__ __launch_bounds__(64) void encode_kernel(uint8_t* __restrict__ buf, Layout L,
-                                                    const __half* __restrict__ K,
-                                                    const __half* __restrict__ V, int64_t ld_tok,
-                                                    PerSeq seq /* a: first record, b: records */) {
-  __shared__ EncodeLds<D, BK, BV> lds;
-  const int jl = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+__global__ __launch_bounds__(64 * kEncodeWaves) void encode_kernel(uint8_t* __restrict__ buf, Layout L,
+                                                                   const __half* __restrict__ K,
+                                                                   const __half* __restrict__ V, int64_t ld_tok,
+                                                                   PerSeq seq /* a: first record, b: records */) {
+  __shared__ EncodeLds<D, BK, BV> lds_w[kEncodeWaves];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  EncodeLds<D, BK, BV>& lds = lds_w[wave];
+  const int jl = blockIdx.x * kEncodeWaves + wave, h = blockIdx.y, b = blockIdx.z;
   if (jl >= seq.b[b]) return;
   const int j = seq.a[b] + jl;
   if (j >= L.max_groups) return;
@@ -1103,8 +1116,8 @@ __global__ __launch_bounds__(64) void lengths_fill_kernel(uint8_t* __restrict__ 
 template <int D, int BK, int BV>
 static hipError_t launch_encode_t(uint8_t* buf, const Layout& L, const void* K, const void* V,
                                   int64_t ld_tok, const PerSeq& seq, int max_records, hipStream_t s) {
-  dim3 grid(max_records, L.Hkv, L.B);
-  hipLaunchKernelGGL((encode_kernel<D, BK, BV>), grid, dim3(64), 0, s, buf, L,
+  dim3 grid((max_records + kEncodeWaves - 1) / kEncodeWaves, L.Hkv, L.B);
+  hipLaunchKernelGGL((encode_kernel<D, BK, BV>), grid, dim3(64 * kEncodeWaves), 0, s, buf, L,
                      static_cast<const __half*>(K), static_cast<const __half*>(V), ld_tok, seq);
   return hipGetLastError();
 }
