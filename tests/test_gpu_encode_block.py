@@ -90,3 +90,30 @@ def test_block_encode_agrees_with_the_record_encoder():
     assert np.array_equal(kc.cpu().numpy(), st["kc"]) and np.array_equal(vc.cpu().numpy(), st["vc"])
     for got, want in ((ks, st["ks"]), (kz, st["kz"]), (vs, st["vs"]), (vz, st["vz"])):
         assert np.array_equal(got.cpu().numpy().view(np.uint16), np.asarray(want, F16).view(np.uint16))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bk,bv", [(k, v) for k in (2, 4, 8) for v in (2, 4, 8)])
+def test_record_encoder_on_adversarial_groups(D, bk, bv):
+    # the record encoder (packed fp16 min/max, biased codes, lane-exchanged value words) on the
+    # adversarial groups above: key groups (32 tokens of a channel) and value groups (32
+    # channels of a token) each cycle through ties, signed zeros, constant, one-ulp,
+    # subnormal-range, outlier and wide-range groups; codes, scales and zeros bit for bit
+    from quantized_decode_attention_encode_amd import KVQCache, kvq_encode, make_config
+    from tests.gpu_helpers import cfg_dict, host_buffer
+    from tests.kvq_unpack import unpack_sequence
+    T = 96
+    kg = adversarial_groups((T // 32) * D, bk, seed=2000 + D + 10 * bk + bv)
+    K = np.ascontiguousarray(kg.reshape(T // 32, D, 32).transpose(0, 2, 1).reshape(T, D))
+    V = np.ascontiguousarray(adversarial_groups(T * (D // 32), bv, seed=3000 + D + 10 * bk + bv).reshape(T, D))
+    cfg = make_config(1, 1, 1, D, bk, bv, 32, 32, 128)
+    c = KVQCache(cfg, device=DEV)
+    kvq_encode(c, torch.from_numpy(K[None, None]).to(DEV), torch.from_numpy(V[None, None]).to(DEV), [T])
+    st = unpack_sequence(host_buffer(c), cfg_dict(cfg), 0, 0)
+    assert (st["n_q"], st["n_r"]) == (T, 0)
+    for name, X, bits, per_channel, got in (("keys", K, bk, True, ("kc", "ks", "kz")),
+                                            ("values", V, bv, False, ("vc", "vs", "vz"))):
+        rc, rs, rz = oracle_block(X, bits, per_channel)
+        assert np.array_equal(np.asarray(st[got[0]]), rc), f"{name} codes"
+        assert np.array_equal(np.asarray(st[got[1]], F16).view(np.uint16), rs.view(np.uint16)), f"{name} scales"
+        assert np.array_equal(np.asarray(st[got[2]], F16).view(np.uint16), rz.view(np.uint16)), f"{name} zeros"
