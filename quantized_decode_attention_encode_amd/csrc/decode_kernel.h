@@ -756,7 +756,14 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
   } sh;
   __shared__ int sh_last;
 
-  const int sigma = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  int sigma = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  if (ds.n_hi > 0) {  // split-major: workgroup id = (split * B + sequence) * H_kv + KV head
+    const int id = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int pairs = L.Hkv * L.B;
+    sigma = id / pairs;
+    h = id % L.Hkv;
+    b = (id % pairs) / L.Hkv;
+  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   // The plan comes from the host's lengths (seq: quantized tokens, window tokens before this
   // launch's append, sinks present), never from the device copy: with an append, the split that
@@ -779,9 +786,13 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
     cz.lim_min = S - (ds.nqry - 1);
   }
   const int nunits = ngroups + (nr + kGroup - 1) / kGroup + (sinks ? 1 : 0);
-  const int u0 = sigma * ds.chunk;
+  const int hi_units = ds.n_hi * ds.chunk_hi;  // units of the first n_hi splits
+  auto split_start = [&](int sg) {
+    return sg <= ds.n_hi ? sg * ds.chunk_hi : hi_units + (sg - ds.n_hi) * ds.chunk;
+  };
+  const int u0 = split_start(sigma);
   if (u0 >= nunits) return;
-  const int u1 = min(u0 + ds.chunk, nunits);
+  const int u1 = min(split_start(sigma + 1), nunits);
   const int uq = min(u1, ngroups);  // end of the quantized units of this split
 
   WaveLds<D, G>& W = sh.w[wave];
@@ -934,7 +945,8 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
 
   // ---- combine the waves: the partial of each query head, or the output when this
   // workgroup is the sequence's only split
-  const int nvalid = min(ds.n_split, (nunits + ds.chunk - 1) / ds.chunk);
+  const int nvalid = min(ds.n_split, nunits <= hi_units ? (nunits + ds.chunk_hi - 1) / ds.chunk_hi
+                                                       : ds.n_hi + (nunits - hi_units + ds.chunk - 1) / ds.chunk);
   const int64_t row0 = int64_t(b) * ds.n_q_heads + h * G;  // first query head of this KV head
   for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
     const int i = idx / D, ch = idx % D;

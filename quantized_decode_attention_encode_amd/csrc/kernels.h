@@ -32,6 +32,13 @@ struct SplitPlan {
 struct DecodeShape {
   int n_split;
   int chunk;
+  // Skewed splits: with n_hi > 0 the first n_hi splits of every (sequence, KV head) take
+  // chunk_hi units each and the others chunk, and the workgroups run split-major (the linear
+  // workgroup id counts the (KV head, sequence) pairs first), so that the splits dispatched
+  // first, which share their CUs with later ones and win the SIMD arbiter over them, are the
+  // longer ones. n_hi = 0: every split takes chunk units, split-minor order.
+  int n_hi;
+  int chunk_hi;
   int G;            // query heads per KV head
   int n_q_heads;
   float qscale;     // sm_scale * log2(e): scores are kept in base-2 units
