@@ -195,11 +195,11 @@ int target_workgroups(int cus, int max_units, int64_t total_units, int64_t seq_h
 // first (split-major order: the first half of every sequence's splits) share their CUs with
 // the second half and win the SIMD arbiter over them; with equal chunks they finish about a
 // sixth sooner. The first n_hi = n_split / 2 splits therefore take kSkew times the units of
-// the others, which evens the pair's finish (on the 64K-token, 32-head cache, the first half
-// at 1.28, 1.44 and 1.64 times the units of the second: 40.0-40.2, 39.9-40.0 and 41.6 us,
-// against 41.2-41.7 us with equal splits). KIVI caches only: the SKVQ decode (per-token key
-// groups, its longer window) measured slower with it (44.8 -> 50.2 us on the same cache).
-constexpr double kSkew = 1.35;
+// the others, which evens the pair's finish (on the 64K-token, 32-head cache: kSkew 1.2, 1.3,
+// 1.35, 1.4 and 1.5 gave 40.1, 39.7, 39.6, 39.3 and 40.1 us, against 41.2-41.7 us with equal
+// splits). KIVI caches only: the SKVQ decode (per-token key groups, its longer window)
+// measured slower with it (44.8 -> 50.2 us on the same cache).
+constexpr double kSkew = 1.4;
 void skew_splits(int max_units, int n_split, kvq::DecodeShape& ds) {
   ds.n_hi = 0;
   ds.chunk_hi = 0;

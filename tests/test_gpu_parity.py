@@ -453,3 +453,29 @@ def test_records_with_large_value_scales(D, bv, G, boost):
         rel = (np.linalg.norm(out - ref, axis=-1) / np.linalg.norm(ref, axis=-1)).max()
         say(f"D={D} bv={bv} G={G} n_split={n_split}: max abs {err:.3e} (vmax {vmax:.1f}), row rel {rel:.2e}")
         assert err <= 2.0 ** -11 * vmax + 2e-5 and rel <= 1e-2
+
+
+@pytest.mark.parametrize("n_sink", [0, 5])
+def test_skewed_splits_match_the_oracle(n_sink):
+    # caches large enough that the automatic plan skews its splits (the first half of every
+    # (sequence, KV head)'s splits longer, split-major order): 2 sequences of 40000 and 33000
+    # tokens, 8 KV heads, 2 query heads each; sampled pairs against the oracle, and every row
+    # against one split per head
+    case = ("skew", 2, 16, 8, 128, 2, 2, None)
+    wl, draw, _ = make(case, seed=61, seq_lens=[40000, 33000], max_tokens=40960)
+    cfg = make_config(2, 8, 16, 128, 2, 2, 32, 32, 40960, n_sink=n_sink)
+    cache = gpu_prefill(draw, cfg)
+    pairs = [(0, 0), (0, 7), (1, 3)]
+    seqs = oracle_prefill(draw, 32, pairs=pairs, n_sink=n_sink)
+    assert_state_equal(host_buffer(cache), cfg, seqs, f"skew n_sink={n_sink}")
+    heads = [(b, hq) for b, h in pairs for hq in (2 * h, 2 * h + 1)]
+    ref = oracle_attend(draw.q.astype(np.float64), seqs, wl, heads=heads)
+    q = torch.from_numpy(draw.q).to(DEV)
+    out = kvq_decode_attend(cache, q, out_fp32=True).cpu().numpy()
+    say("skew n_sink", n_sink, "err", assert_close(out, ref, f"skew n_sink={n_sink}"))
+    # every row against one split per head, within the bound of the split-count test above
+    # (the fp16 value weights are rounded under each split's own running maximum)
+    one = kvq_decode_attend(cache, q, out_fp32=True, n_split=1).cpu().numpy()
+    vmax = max(np.abs(s.values_hat()).max() for s in seqs.values())
+    bound = 2 * 2.0 ** -11 * vmax + 2e-5
+    assert np.abs(out - one).max() < bound, f"auto vs one split: {np.abs(out - one).max():.3e} >= {bound:.3e}"
