@@ -12,15 +12,19 @@
 // built with -ffp-contract=off and correctly rounded fp32 division, so the codes and
 // parameters are bit-identical to any other IEEE implementation of the same steps.
 //
-// One wavefront quantizes one record (32 tokens x D channels of K and of V):
-//   * the 32 x D fp16 tile is loaded with 16-byte loads, lane = (row r, 8-channel chunk c8);
-//   * key min/max: lane-local over the lane's tokens, then a cross-row butterfly
-//     (__shfl_xor over lane distances D/8, D/4, ...) leaves every channel's range in all
+// One wavefront quantizes one record (32 tokens x D channels of K and of V); the prefill
+// kernel runs two independent waves per workgroup:
+//   * the 32 x D fp16 tile is loaded with non-temporal 16-byte loads, lane = (row r, 8-channel
+//     chunk c8), and stays in its fp16 words;
+//   * key min/max: packed fp16 pairs, lane-local over the lane's tokens, then the cross-row
+//     exchanges (DPP row rotate, permlane16/32 swaps) leave every channel's range in all
 //     lanes of its chunk;
-//   * value min/max: lane-local over 8 channels, then DPP quad butterflies (quad_perm)
-//     across the 4 chunks of a 32-channel value group;
-//   * codes are packed into the record image in LDS and the record leaves with coalesced
-//     16-byte stores.
+//   * value min/max: packed fp16 pairs over the lane's 8 channels, then DPP quad butterflies
+//     (quad_perm) across the 4 chunks of a 32-channel value group;
+//   * codes: fma-mix subtract from the fp16 half, multiply, and a round-and-clamp on the bits
+//     of t + 1.5 * 2^23 (biased_code); key codes are ORed into their pieces, value codes into
+//     words that three halving lane exchanges complete;
+//   * the record image is assembled in LDS and leaves with coalesced 16-byte stores.
 //
 // Sink tokens ("Changelog" v0.9.0, KIVI-Sink): the tokens of largest key L2 norm (squares
 // added in fp32, channel 0 first, earlier token on equal norms), chosen once per
