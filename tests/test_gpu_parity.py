@@ -455,14 +455,15 @@ def test_records_with_large_value_scales(D, bv, G, boost):
         assert err <= 2.0 ** -11 * vmax + 2e-5 and rel <= 1e-2
 
 
-@pytest.mark.parametrize("n_sink", [0, 5])
-def test_skewed_splits_match_the_oracle(n_sink):
+@pytest.mark.parametrize("n_sink,lens", [(0, (40000, 33000)), (5, (40000, 33000)), (0, (40000, 20000))])
+def test_skewed_splits_match_the_oracle(n_sink, lens):
     # caches large enough that the automatic plan skews its splits (the first half of every
-    # (sequence, KV head)'s splits longer, split-major order): 2 sequences of 40000 and 33000
-    # tokens, 8 KV heads, 2 query heads each; sampled pairs against the oracle, and every row
-    # against one split per head
+    # (sequence, KV head)'s splits longer, split-major order): 2 sequences, 8 KV heads, 2 query
+    # heads each; the shorter sequence ends in the second half of the splits (33000 tokens) or
+    # inside the first half (20000); sampled pairs against the oracle, and every row against
+    # one split per head
     case = ("skew", 2, 16, 8, 128, 2, 2, None)
-    wl, draw, _ = make(case, seed=61, seq_lens=[40000, 33000], max_tokens=40960)
+    wl, draw, _ = make(case, seed=61, seq_lens=list(lens), max_tokens=40960)
     cfg = make_config(2, 8, 16, 128, 2, 2, 32, 32, 40960, n_sink=n_sink)
     cache = gpu_prefill(draw, cfg)
     pairs = [(0, 0), (0, 7), (1, 3)]
