@@ -183,18 +183,26 @@ __device__ __forceinline__ void encode_record(const __half* __restrict__ ks, con
   const int lane = threadIdx.x & 63;
   const int c8 = lane % CH, r = lane / CH;
 
-  uint32_t kw[NI][4], vw[NI][4];  // fp16 pairs: channels 8*c8 + 2w, + 1 of token r + RPI*i
+  // fp16 pairs: channels 8*c8 + 2w, + 1 of token r + RPI*i. Every key row is requested before
+  // any value row (the scheduling barriers keep the order), so that the key groups can be
+  // computed while the value rows are still arriving.
+  uint32_t kw[NI][4], vw[NI][4];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int t = r + RPI * i;
     const u32x4 kr = load_streaming(ks + t * D + 8 * c8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) kw[i][w] = kr[w];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int t = r + RPI * i;
     const u32x4 vr = load_streaming(vs + t * D + 8 * c8);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      kw[i][w] = kr[w];
-      vw[i][w] = vr[w];
-    }
+    for (int w = 0; w < 4; ++w) vw[i][w] = vr[w];
   }
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- keys: one group per channel over the 32 tokens. Every lane of a chunk column ends up
   // with the column's min/max; each of the RPI lanes of the column then computes the
