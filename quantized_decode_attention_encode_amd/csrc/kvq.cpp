@@ -179,14 +179,15 @@ kvq_status check_device(int* cus = nullptr) {
   return ok();
 }
 
+// A ragged batch: its longest sequence holds more than 1.5 x the mean units.
+bool ragged_batch(int max_units, int64_t total_units, int64_t seq_heads) {
+  return double(max_units) * double(seq_heads) > 1.5 * double(total_units);
+}
 // Workgroups the automatic split aims for: two per CU when the sequences are about equally
 // long, three when they are ragged (max > 1.5 x mean units), where smaller chunks fill the
 // gaps the short sequences leave. Both were the fastest of 2, 3 and 4 per CU on the uniform
 // (one 64K-token sequence; 8 x 32K tokens, 4 query heads per KV head) and ragged (16
 // sequences of 1K..16K tokens) workloads.
-bool ragged_batch(int max_units, int64_t total_units, int64_t seq_heads) {
-  return double(max_units) * double(seq_heads) > 1.5 * double(total_units);
-}
 int target_workgroups(int cus, int max_units, int64_t total_units, int64_t seq_heads) {
   return std::max(1, cus) * (ragged_batch(max_units, total_units, seq_heads) ? 3 : 2);
 }
