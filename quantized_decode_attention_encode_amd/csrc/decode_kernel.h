@@ -244,22 +244,34 @@ struct RecordRegs {
   uint32_t vp[D / 64];
 };
 
+// A record is read once per step: non-temporal loads (streaming cache policy), which stream the
+// records in at a higher rate than the default policy while a lane's words of each record part
+// come in at most two 16-byte loads (2- and 4-bit codes). With 8-bit codes a lane reads its 64
+// contiguous bytes of a part in four loads, each of which touches every line of the part, and
+// the streaming policy then measured much slower (2/8 bits at S = 64K: 98.6 against 72.6 us):
+// those keep the default policy.
+template <int D, int BK, int BV>
+constexpr bool stream_records() {
+  return 2 * (D * BK / 128) <= 8 && (D / 64) * BV <= 8;
+}
+
 // KT (per-token key groups): lane (P, Q) takes the key params of its tokens 2P, 2P+1 for the
 // group of its quarter, two adjacent words at [P][group][t%2].
 template <int D, int BK, int BV, bool KT = false>
 __device__ __forceinline__ void load_record(const uint8_t* __restrict__ rec, int lane, RecordRegs<D, BK, BV>& r) {
   constexpr int E = D / 64, KW = 2 * (D * BK / 128), VW = E * BV;
-  load_words<KW>(reinterpret_cast<const uint32_t*>(rec) + lane * KW, r.kc);
-  load_words<VW>(reinterpret_cast<const uint32_t*>(rec + rec_off_vcodes(D, BK)) + lane * VW, r.vc);
+  constexpr bool NT = stream_records<D, BK, BV>();
+  load_words<KW, NT>(reinterpret_cast<const uint32_t*>(rec) + lane * KW, r.kc);
+  load_words<VW, NT>(reinterpret_cast<const uint32_t*>(rec + rec_off_vcodes(D, BK)) + lane * VW, r.vc);
   if constexpr (KT) {
     constexpr int NKG = D / 32;
     const int kg = ((lane & 3) * (D / 4)) / 32;
-    load_words<2>(reinterpret_cast<const uint32_t*>(rec + rec_off_kparams(D, BK, BV)) + ((lane >> 2) * NKG + kg) * 2,
-                  r.kp);
+    load_words<2, NT>(
+        reinterpret_cast<const uint32_t*>(rec + rec_off_kparams(D, BK, BV)) + ((lane >> 2) * NKG + kg) * 2, r.kp);
   } else {
-    load_words<E>(reinterpret_cast<const uint32_t*>(rec + rec_off_kparams(D, BK, BV)) + lane * E, r.kp);
+    load_words<E, NT>(reinterpret_cast<const uint32_t*>(rec + rec_off_kparams(D, BK, BV)) + lane * E, r.kp);
   }
-  load_words<E>(reinterpret_cast<const uint32_t*>(rec + rec_off_vparams(D, BK, BV)) + lane * E, r.vp);
+  load_words<E, NT>(reinterpret_cast<const uint32_t*>(rec + rec_off_vparams(D, BK, BV)) + lane * E, r.vp);
 }
 
 // Wavefronts per decode workgroup; each takes every kWaves-th unit of the workgroup's chunk.
@@ -764,7 +776,8 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
     h = id % L.Hkv;
     b = (id % pairs) / L.Hkv;
   }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index is wave-uniform: record indices and addresses stay in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   // The plan comes from the host's lengths (seq: quantized tokens, window tokens before this
   // launch's append, sinks present), never from the device copy: with an append, the split that
   // finishes last rewrites the device window length inside this launch, and a split that read
@@ -856,6 +869,10 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
   // are unconditional (their record index is clamped into the buffer: the last one of a
   // wave re-reads a record it never uses) so that the compiler's memory-counter waits stay
   // exact: a conditional load at a control-flow merge makes it wait for the prefetch too.
+  // At G = 1 with streamed records each register set is loaded in one place of the loop (the
+  // second set where the loop begins): with a second load site ahead of the loop, the two sites
+  // of a set were given different registers, and the copy between them waited for every load in
+  // flight.
   const uint8_t* rec0 = buf + L.record(b, h, 0);
   const uint64_t rb = L.rec_bytes;
   const int ulast = max(uq - 1, 0);
@@ -864,8 +881,11 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
     RecordRegs<D, BK, BV> ra, rbuf;
     if (u < uq) {
       load_record<D, BK, BV, KT>(rec0 + u * rb, lane, ra);
-      load_record<D, BK, BV, KT>(rec0 + min(u + kWaves, ulast) * rb, lane, rbuf);
+      if constexpr (!stream_records<D, BK, BV>())
+        load_record<D, BK, BV, KT>(rec0 + min(u + kWaves, ulast) * rb, lane, rbuf);
       while (true) {
+        if constexpr (stream_records<D, BK, BV>())
+          load_record<D, BK, BV, KT>(rec0 + min(u + kWaves, ulast) * rb, lane, rbuf);
         process_record<D, BK, BV, G, SK, KT>(ra, W, st, upk, upv, qs, qf, vf0, vf1, lane, cz, pos0 + u * kGroup);
         u += kWaves;
         if (u >= uq) break;
@@ -873,7 +893,8 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
         process_record<D, BK, BV, G, SK, KT>(rbuf, W, st, upk, upv, qs, qf, vf0, vf1, lane, cz, pos0 + u * kGroup);
         u += kWaves;
         if (u >= uq) break;
-        load_record<D, BK, BV, KT>(rec0 + min(u + kWaves, ulast) * rb, lane, rbuf);
+        if constexpr (!stream_records<D, BK, BV>())
+          load_record<D, BK, BV, KT>(rec0 + min(u + kWaves, ulast) * rb, lane, rbuf);
       }
     }
   } else {
