@@ -56,9 +56,9 @@ PEAK_FP16_MFMA_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak (no sparsity)
 # profiles/*_counters.md), valid only for the decode kernel and split-plan sources they were
 # taken on (their hash over TRAFFIC_SOURCES).
 MEASURED_TRAFFIC = {
-    "long": {"src_sha256_16": "00ac1306394b4ee8", "bytes": 202949938},
-    "gqa": {"src_sha256_16": "00ac1306394b4ee8", "bytes": 133056343},
-    "full32": {"src_sha256_16": "00ac1306394b4ee8", "bytes": 204825291},
+    "long": {"src_sha256_16": "77a754023afef747", "bytes": 202950144},
+    "gqa": {"src_sha256_16": "77a754023afef747", "bytes": 133009853},
+    "full32": {"src_sha256_16": "77a754023afef747", "bytes": 204815121},
 }
 TRAFFIC_SOURCES = ("decode_kernel.h", "decode.hip", "decode_mfma.hip", "kvq.cpp")
 

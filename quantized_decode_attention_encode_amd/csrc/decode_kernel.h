@@ -869,15 +869,16 @@ void decode_split_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape 
   // are unconditional (their record index is clamped into the buffer: the last one of a
   // wave re-reads a record it never uses) so that the compiler's memory-counter waits stay
   // exact: a conditional load at a control-flow merge makes it wait for the prefetch too.
-  // At G = 1 with streamed records each register set is loaded in one place of the loop (the
-  // second set where the loop begins): with a second load site ahead of the loop, the two sites
-  // of a set were given different registers, and the copy between them waited for every load in
-  // flight.
+  // With streamed records each register set is loaded in one place of the loop (the second set
+  // where the loop begins): with a second load site ahead of the loop, the two sites of a set
+  // were given different registers, and the copy between them waited for every load in flight.
+  // Up to 4 rows per KV head the two sets fit the registers; beyond that (and with 8-bit codes
+  // at more than one row) the next record goes to one set that is copied into the current one.
   const uint8_t* rec0 = buf + L.record(b, h, 0);
   const uint64_t rb = L.rec_bytes;
   const int ulast = max(uq - 1, 0);
   int u = u0 + wave;
-  if constexpr (G == 1) {
+  if constexpr (G == 1 || (G <= 4 && stream_records<D, BK, BV>())) {
     RecordRegs<D, BK, BV> ra, rbuf;
     if (u < uq) {
       load_record<D, BK, BV, KT>(rec0 + u * rb, lane, ra);
