@@ -56,9 +56,9 @@ PEAK_FP16_MFMA_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak (no sparsity)
 # profiles/*_counters.md), valid only for the decode kernel and split-plan sources they were
 # taken on (their hash over TRAFFIC_SOURCES).
 MEASURED_TRAFFIC = {
-    "long": {"src_sha256_16": "5d0994e0d8705ee2", "bytes": 202969187},
-    "gqa": {"src_sha256_16": "5d0994e0d8705ee2", "bytes": 132844584},
-    "full32": {"src_sha256_16": "5d0994e0d8705ee2", "bytes": 204108510},
+    "long": {"src_sha256_16": "3801177928fc4b47", "bytes": 202948095},
+    "gqa": {"src_sha256_16": "3801177928fc4b47", "bytes": 132471221},
+    "full32": {"src_sha256_16": "3801177928fc4b47", "bytes": 204023518},
 }
 TRAFFIC_SOURCES = ("decode_kernel.h", "decode.hip", "decode_mfma.hip", "kvq.cpp")
 

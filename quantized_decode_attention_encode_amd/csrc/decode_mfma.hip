@@ -503,14 +503,13 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
   // the sums in a fixed order). The two waves of a SIMD would not progress alike (the arbiter
   // serves the older one first when both are ready), so each wave compares its record count with
   // its SIMD partner's after every record and takes the higher issue priority while it is not
-  // ahead: both finish together. NB of a wave's records are in flight, the oldest computed while
-  // the others arrive (under load, memory latency is longer than one record's computation); three
-  // fit the register budget of two waves per SIMD at 4 rows (but for 8-bit keys and values).
-  // The last set is loaded only where the loop begins, the others ahead of the loop (in order,
-  // behind scheduling barriers) and after their record is computed: with every set loaded ahead
-  // of the loop, the compiler copied registers of sets still in flight on the back edge, behind a
-  // wait for every load (GQA batch 44.0 -> 42.0 us, 32-layer stack 59.5 -> 55.2 us per layer).
-  constexpr int NB = (NR == 4 && !(BK == 8 && BV == 8)) ? 3 : 2;
+  // ahead: both finish together. Two of a wave's records are in flight, the older computed while
+  // the newer arrives. The second register set is loaded only where the loop begins, the first
+  // ahead of the loop and after its record is computed, each record's loads in one fixed order:
+  // with both sets loaded ahead of the loop, the compiler copied registers of a set still in
+  // flight on the back edge, behind a wait for every load. A ring of three sets (tried at 4 rows)
+  // measured slower (GQA batch 42.0 against 40.6 us): the compiler's first wait of each round
+  // covered two of its records.
   int u = u0 + wave;
   if (u < uq) {
     const int ulast = uq - 1;
@@ -524,45 +523,19 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
         else __builtin_amdgcn_s_setprio(0);
       }
     };
-    if constexpr (NB == 3) {
-      Regs ring[NB];
-      int left = (uq - u + kMW - 1) / kMW;  // this wave's records
-      load(u, ring[0]);
-      __builtin_amdgcn_sched_barrier(0);
-      load(min(u + kMW, ulast), ring[1]);
-      __builtin_amdgcn_sched_barrier(0);
-      while (true) {
-        load(min(u + 2 * kMW, ulast), ring[2]);
-        process(ring[0], u * kGroup);
-        u += kMW;
-        if (--left == 0) break;
-        progress();
-        load(min(u + 2 * kMW, ulast), ring[0]);
-        process(ring[1], u * kGroup);
-        u += kMW;
-        if (--left == 0) break;
-        progress();
-        load(min(u + 2 * kMW, ulast), ring[1]);
-        process(ring[2], u * kGroup);
-        u += kMW;
-        if (--left == 0) break;
-        progress();
-      }
-    } else {
-      Regs ra, rbf;
-      load(u, ra);
-      while (true) {
-        load(min(u + kMW, ulast), rbf);
-        process(ra, u * kGroup);
-        u += kMW;
-        if (u >= uq) break;
-        load(min(u + kMW, ulast), ra);
-        progress();
-        process(rbf, u * kGroup);
-        u += kMW;
-        if (u >= uq) break;
-        progress();
-      }
+    Regs ra, rbf;
+    load(u, ra);
+    while (true) {
+      load(min(u + kMW, ulast), rbf);
+      process(ra, u * kGroup);
+      u += kMW;
+      if (u >= uq) break;
+      load(min(u + kMW, ulast), ra);
+      progress();
+      process(rbf, u * kGroup);
+      u += kMW;
+      if (u >= uq) break;
+      progress();
     }
     __builtin_amdgcn_s_setprio(0);
   }
