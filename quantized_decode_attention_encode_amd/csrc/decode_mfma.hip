@@ -27,6 +27,8 @@ namespace {
 
 typedef _Float16 h8m __attribute__((ext_vector_type(8)));
 typedef float f4m __attribute__((ext_vector_type(4)));
+typedef _Float16 h2m __attribute__((ext_vector_type(2)));
+constexpr h2m kNegOnes2 = {(_Float16)-1.0f, (_Float16)-1.0f};  // subtracts both halves in a dot product
 
 // LDS of one wave, on top of the VALU decode's (used by the window units and the weights).
 template <int D, int NR, int BV>
@@ -325,13 +327,18 @@ void decode_mfma_kernel(const uint8_t* __restrict__ buf, Layout L, DecodeShape d
       for (int e = 0; e < 8; e += 2) {
         // q~' as fp16 high + low parts; beta takes out exactly what the matrix cores will see
         // (high + low, not q~' itself), so the converted codes' constant 1 (times a fold factor up
-        // to 64) cancels to fp32 accuracy and only the codes' own part carries the split error
-        const float x0 = pqf[j][e] * lo_f(cur.kp[j][e]), x1 = pqf[j][e + 1] * lo_f(cur.kp[j][e + 1]);
+        // to 64) cancels to fp32 accuracy and only the codes' own part carries the split error.
+        // The product with a -0 addend is the plain product (one rounding); the parts leave beta
+        // through dot products with (-1, -1), exact products summed in fp32, with no conversion.
+        const float x0 = __builtin_fmaf(pqf[j][e], lo_f(cur.kp[j][e]), -0.0f);
+        const float x1 = __builtin_fmaf(pqf[j][e + 1], lo_f(cur.kp[j][e + 1]), -0.0f);
         const auto hh = __builtin_amdgcn_cvt_pkrtz(x0, x1);
-        const float h0 = (float)hh[0], h1 = (float)hh[1];
-        const auto ll = __builtin_amdgcn_cvt_pkrtz(x0 - h0, x1 - h1);
-        bp += pq[j][e] * hi_f(cur.kp[j][e]) - (h0 + (float)ll[0]);
-        bp += pq[j][e + 1] * hi_f(cur.kp[j][e + 1]) - (h1 + (float)ll[1]);
+        const auto ll = __builtin_amdgcn_cvt_pkrtz(__builtin_fmaf(pqf[j][e], lo_f(cur.kp[j][e]), -(float)hh[0]),
+                                                   __builtin_fmaf(pqf[j][e + 1], lo_f(cur.kp[j][e + 1]), -(float)hh[1]));
+        bp = __builtin_fmaf(pq[j][e], hi_f(cur.kp[j][e]), bp);
+        bp = __builtin_fmaf(pq[j][e + 1], hi_f(cur.kp[j][e + 1]), bp);
+        bp = __builtin_amdgcn_fdot2(hh, kNegOnes2, bp, false);
+        bp = __builtin_amdgcn_fdot2(ll, kNegOnes2, bp, false);
         hi[e >> 1] = __builtin_bit_cast(uint32_t, hh);
         lo[e >> 1] = __builtin_bit_cast(uint32_t, ll);
       }
