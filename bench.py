@@ -56,9 +56,9 @@ PEAK_FP16_MFMA_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak (no sparsity)
 # profiles/*_counters.md), valid only for the decode kernel and split-plan sources they were
 # taken on (their hash over TRAFFIC_SOURCES).
 MEASURED_TRAFFIC = {
-    "long": {"src_sha256_16": "3801177928fc4b47", "bytes": 202948095},
-    "gqa": {"src_sha256_16": "3801177928fc4b47", "bytes": 132471221},
-    "full32": {"src_sha256_16": "3801177928fc4b47", "bytes": 204023518},
+    "long": {"src_sha256_16": "811827841dc9b543", "bytes": 202966744},
+    "gqa": {"src_sha256_16": "811827841dc9b543", "bytes": 132473269},
+    "full32": {"src_sha256_16": "811827841dc9b543", "bytes": 204043793},
 }
 TRAFFIC_SOURCES = ("decode_kernel.h", "decode.hip", "decode_mfma.hip", "kvq.cpp")
 
